@@ -1,0 +1,210 @@
+/*
+ * mkv.h -- C ABI of the mixed FP8 / TQ3 paged decode-attention library for
+ * AMD MI355X (gfx950).
+ *
+ * The method (Minima-KV, arXiv 2608.23834, page 1, Abstract): a paged KV
+ * cache keeps Recent and protected Anchor pages in FP8 and moves older
+ * non-anchor pages to packed 3-bit TQ3; every live page stays addressable;
+ * format-specific kernels compute partial attention states that a globally
+ * normalised online-softmax (log-sum-exp) merge combines, with no
+ * cache-sized dense dequantised shadow.  Pages of both formats live in one
+ * PagedAttention block structure (page 2, "Technical Deep Dive", fourth
+ * bullet).  The pages specify no API, bit layout or numerics beyond that;
+ * the readings taken are stated at each declaration.
+ *
+ * General contract for every entry point:
+ *  - All pointers named "device" are device pointers owned by the caller.
+ *    The library never allocates or frees device memory, never keeps a
+ *    pointer after returning, and never synchronises the stream (except the
+ *    explicitly synchronous mkv_workspace_status).
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t, passed as
+ *    void*; NULL = the legacy default stream) in call order.
+ *  - The return value is MKV_OK (0) or a negative MKV_ERR_* code; on error
+ *    nothing was enqueued and mkv_last_error() (thread-local) describes the
+ *    failed check.  No C++ exception crosses this boundary.
+ *  - Host-checkable errors (null pointers, unsupported shapes, misalignment,
+ *    counts out of range, a workspace that is too small) are returned as
+ *    codes.  Errors found in device data (a page id outside the pool, a tier
+ *    byte that contradicts the slab an id points into, a seq_len longer than
+ *    the request's block table) are recorded in the workspace status word
+ *    (read it with mkv_workspace_status) and the affected requests' outputs
+ *    are set to NaN.  NaN or Inf inputs are outside the contract.
+ */
+#ifndef MKV_H
+#define MKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  MKV_OK = 0,
+  MKV_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  MKV_ERR_SHAPE = -2,     /* unsupported head_dim / page_size / GQA group         */
+  MKV_ERR_ALIGN = -3,     /* slabs and float tensors must be 16-byte aligned     */
+  MKV_ERR_WORKSPACE = -4, /* ws_bytes smaller than mkv_decode_workspace_bytes()  */
+  MKV_ERR_RANGE = -5,     /* a count or index is out of its valid range          */
+  MKV_ERR_HIP = -6        /* a HIP launch failed; message carries the HIP error  */
+};
+
+/* Device status bits (mkv_workspace_status). */
+enum {
+  MKV_DEV_BAD_PAGE_ID = 1,   /* block-table entry outside [0, n_fp8 + n_tq3)        */
+  MKV_DEV_BAD_TIER = 2,      /* tier byte contradicts the slab the id points into   */
+  MKV_DEV_BAD_SEQ_LEN = 4    /* seq_len < 0 or longer than the request's block table */
+};
+
+/* Tier map values: one byte per physical page id.  Recent and Anchor pages
+ * are FP8, Stale pages are TQ3 (arXiv 2608.23834, page 1, Abstract; the
+ * R/A/S names follow page 2, "Enhanced Key Takeaways", first bullet). */
+enum { MKV_TIER_RECENT = 0, MKV_TIER_ANCHOR = 1, MKV_TIER_STALE = 2, MKV_TIER_FREE = 0xFF };
+
+/* Head geometry.  Supported: head_dim in {128, 256}, page_size == 16,
+ * num_q_heads % num_kv_heads == 0 and G = num_q_heads / num_kv_heads <= 8.
+ * Query head i reads KV head i / G (grouped-query attention). */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+} mkv_layout;
+
+/* One layer's page pool.
+ *  fp8_slab: device, n_fp8 FP8 pages of mkv_fp8_page_bytes() bytes each.
+ *            Page layout [kv head][K=0,V=1][16 tokens][head_dim] E4M3FN bytes.
+ *  tq3_slab: device, n_tq3 TQ3 pages of mkv_tq3_page_bytes() bytes each.
+ *            Per KV head a block of 14*head_dim bytes: K codes, V codes,
+ *            K scales, V scales (layout in oracle/layout.py and the
+ *            kernels' headers: 8 3-bit codes per 3 bytes, one fp16 scale per
+ *            32 channels per token per KV head).
+ *  tier:     device, n_fp8 + n_tq3 bytes, shared by all layers.
+ *  Physical ids [0, n_fp8) are FP8 slots, [n_fp8, n_fp8 + n_tq3) TQ3 slots;
+ *  a page with tier R or A must have an FP8 id, tier S a TQ3 id.
+ *  k_scale / v_scale: per-layer fp32 FP8 scales (value = decode(byte) * scale). */
+typedef struct {
+  uint8_t* fp8_slab;
+  uint8_t* tq3_slab;
+  const uint8_t* tier;
+  int32_t n_fp8;
+  int32_t n_tq3;
+  float k_scale;
+  float v_scale;
+} mkv_pool;
+
+/* A decode batch: ragged CSR block tables shared by all layers.
+ *  bt_offsets: device int32[batch + 1], request b owns bt_pages[bt_offsets[b] ..
+ *              bt_offsets[b+1]); logical page j of request b is entry
+ *              bt_offsets[b] + j and holds tokens [16 j, 16 j + 16).
+ *  bt_pages:   device int32[bt_capacity], physical page ids.
+ *  seq_lens:   device int32[batch], tokens attended per request (after this
+ *              step's append: the new token is attended).
+ *  bt_capacity: host-known number of entries in bt_pages (>= bt_offsets[batch]). */
+typedef struct {
+  const int32_t* bt_offsets;
+  const int32_t* bt_pages;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t bt_capacity;
+} mkv_batch;
+
+/* Bytes of one FP8 page (2 * 16 * num_kv_heads * head_dim) and of one TQ3
+ * page (num_kv_heads * 14 * head_dim); 0 for an unsupported layout. */
+size_t mkv_fp8_page_bytes(const mkv_layout* layout);
+size_t mkv_tq3_page_bytes(const mkv_layout* layout);
+
+/* Append: quantise new tokens to FP8 on Recent pages (arXiv 2608.23834,
+ * page 1, Abstract: Recent pages are FP8).
+ *  k, v:   device fp32 [batch][n_new][num_kv_heads][head_dim].
+ *  pos:    device int32[batch]; token i of request b is written at position
+ *          pos[b] + i, i.e. logical page (pos[b]+i)/16, slot (pos[b]+i)%16.
+ *  counts: device int32[batch] or NULL; if given only the first counts[b]
+ *          (<= n_new) tokens of request b are written.
+ * Each byte is e4m3fn_RNE_saturating(fl32(x / scale)) with the pool's k_scale
+ * or v_scale.  Target pages must be FP8 ids (checked on device: entries whose
+ * id is not an FP8 slot are skipped and flagged in no status word -- the
+ * caller owns the page table).  n_new in [0, 65535]. */
+int mkv_append(const mkv_layout* layout, const mkv_pool* pool,
+               const float* k, const float* v, int32_t n_new,
+               const int32_t* bt_offsets, const int32_t* bt_pages,
+               const int32_t* pos, const int32_t* counts, int32_t batch,
+               void* stream);
+
+/* Demote: FP8 page src_fp8[i] -> TQ3 page dst_tq3[i] ("older non-anchor pages
+ * move to packed TQ3", arXiv 2608.23834, page 1, Abstract).
+ *  src_fp8, dst_tq3: device int32[n]; src in [0, n_fp8), dst in
+ *  [n_fp8, n_fp8 + n_tq3) (ids outside are skipped on device).
+ * For every head, K and V, token and 32-channel group: x = fl32(decode(e) *
+ * scale); a = max|x|; s = fp16_RNE(fl32(a / 3)) (saturating); q = nearest
+ * integer to x / s with ties to even, clamped to [-3, 3] (0 when s == 0);
+ * code u = q + 4 packed 8 per 3 bytes.  Bit-exact with the oracle.  The
+ * caller then rewrites block-table entries and tier bytes (stream-ordered)
+ * and may reuse the FP8 slots.  Demoting a page that a concurrent decode on
+ * another stream reads is a race the caller must avoid. */
+int mkv_demote_pages(const mkv_layout* layout, const mkv_pool* pool,
+                     const int32_t* src_fp8, const int32_t* dst_tq3, int32_t n,
+                     void* stream);
+
+/* Workspace size for mkv_decode_attn / mkv_decode_attn_layers with at most
+ * `batch` requests, `bt_capacity` block-table entries and `n_layers` layers.
+ * It holds the plan (compacted per-format page lists, split-K chunk tables)
+ * and the partial states; it is bounded by a constant number of split-K
+ * chunks, not by context length, so it is never a cache-sized shadow. */
+size_t mkv_decode_workspace_bytes(const mkv_layout* layout, int32_t batch,
+                                  int32_t bt_capacity, int32_t n_layers);
+
+/* Decode attention for one layer: q fp32 [batch][num_q_heads][head_dim]
+ * (device) -> out fp32 [batch][num_q_heads][head_dim] (device) and, if lse is
+ * not NULL, lse fp32 [batch][num_q_heads] (natural log of the softmax
+ * denominator including its max).  Scores are (q . k) * sm_scale.
+ * The FP8 pages of each request are attended by the FP8 partial kernel, the
+ * TQ3 pages by the TQ3 partial kernel (split-K over pages, each KV page read
+ * once per GQA group), and a log-sum-exp merge combines the partial states
+ * (arXiv 2608.23834, page 1, Abstract).  seq_len == 0 gives out = 0 and
+ * lse = -inf.  ws: device, 256-byte aligned, ws_bytes >=
+ * mkv_decode_workspace_bytes(layout, batch->batch, batch->bt_capacity, 1). */
+int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool,
+                    const mkv_batch* batch, const float* q, float sm_scale,
+                    float* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Decode attention for n_layers layers that share one tier map and one set
+ * of block tables (the pages' canary decodes 16 full-attention layers per
+ * step).  pools: host array of n_layers descriptors with equal n_fp8, n_tq3
+ * and tier.  q, out: [n_layers][batch][num_q_heads][head_dim]; lse (nullable)
+ * [n_layers][batch][num_q_heads].  The plan is computed once and every
+ * kernel launch covers all layers.  ws_bytes >= mkv_decode_workspace_bytes(
+ * layout, batch->batch, batch->bt_capacity, n_layers). */
+int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools,
+                           int32_t n_layers, const mkv_batch* batch,
+                           const float* q, float sm_scale, float* out,
+                           float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Page-table gather (test support): copy the raw bytes of logical pages
+ * [0, n_pages) of request b into out (device, n_pages records of
+ * mkv_fp8_page_bytes() bytes; a TQ3 page fills the first mkv_tq3_page_bytes()
+ * bytes of its record and the rest is zeroed).  Ids outside the pool give a
+ * record of 0xFF bytes. */
+int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool,
+                     const int32_t* bt_offsets, const int32_t* bt_pages,
+                     int32_t b, int32_t n_pages, uint8_t* out, void* stream);
+
+/* Synchronise `stream` and return the device status bits (MKV_DEV_*) left in
+ * the workspace by the last decode call on it (0 = no device-data error);
+ * negative MKV_ERR_* on failure. */
+int mkv_workspace_status(const void* ws, void* stream);
+
+/* Static description of a status code. */
+const char* mkv_status_string(int status);
+
+/* Thread-local description of the last failed call on this thread. */
+const char* mkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MKV_H */

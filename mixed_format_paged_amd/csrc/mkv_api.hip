@@ -1,0 +1,305 @@
+// mkv_api.hip -- the C ABI (include/mkv.h): argument validation, workspace
+// layout and kernel launches for mixed FP8 / TQ3 paged decode attention.
+//
+// Decode step (arXiv 2608.23834, page 1, Abstract: format-specific kernels
+// produce partial attention states, a globally normalised online-softmax
+// merge combines them, no dense shadow):
+//   plan (once per call, shared by every layer) -> FP8 partial kernel ->
+//   TQ3 partial kernel -> merge, all enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mkv.h"
+#include "mkv_format.h"
+#include "mkv_internal.h"
+
+namespace mkv {
+
+hipError_t launch_partial_mfma(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
+                               const float* q, size_t q_layer_stride, float qscale,
+                               const Plan& plan, hipStream_t stream);
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_layout(const mkv_layout* L, Geometry* g) {
+  if (!L) return fail(MKV_ERR_NULL, "layout is NULL");
+  if (L->page_size != kPage) return fail(MKV_ERR_SHAPE, "page_size %d unsupported (must be 16)", L->page_size);
+  if (L->head_dim != 128 && L->head_dim != 256)
+    return fail(MKV_ERR_SHAPE, "head_dim %d unsupported (128 or 256)", L->head_dim);
+  if (L->num_kv_heads <= 0 || L->num_q_heads <= 0 || L->num_q_heads % L->num_kv_heads)
+    return fail(MKV_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                L->num_q_heads, L->num_kv_heads);
+  const int G = L->num_q_heads / L->num_kv_heads;
+  if (G > kMaxG) return fail(MKV_ERR_SHAPE, "GQA group %d > %d unsupported", G, kMaxG);
+  g->hq = L->num_q_heads;
+  g->hkv = L->num_kv_heads;
+  g->d = L->head_dim;
+  g->G = G;
+  return MKV_OK;
+}
+
+int check_pool(const mkv_pool* p, Geometry* g, bool need_fp8, bool need_tq3, bool need_tier) {
+  if (!p) return fail(MKV_ERR_NULL, "pool is NULL");
+  if (p->n_fp8 < 0 || p->n_tq3 < 0) return fail(MKV_ERR_RANGE, "negative pool size");
+  if ((int64_t)p->n_fp8 + p->n_tq3 > 0x7fffffff) return fail(MKV_ERR_RANGE, "pool too large");
+  if (need_fp8 && !p->fp8_slab && p->n_fp8 > 0) return fail(MKV_ERR_NULL, "fp8_slab is NULL");
+  if (need_tq3 && !p->tq3_slab && p->n_tq3 > 0) return fail(MKV_ERR_NULL, "tq3_slab is NULL");
+  if (need_tier && !p->tier) return fail(MKV_ERR_NULL, "tier is NULL");
+  if (!aligned16(p->fp8_slab) || !aligned16(p->tq3_slab)) return fail(MKV_ERR_ALIGN, "slabs must be 16-byte aligned");
+  if (!(p->k_scale > 0.0f) || !(p->v_scale > 0.0f) || std::isinf(p->k_scale) || std::isinf(p->v_scale))
+    return fail(MKV_ERR_RANGE, "k_scale and v_scale must be finite and > 0");
+  g->n_fp8 = p->n_fp8;
+  g->n_tq3 = p->n_tq3;
+  return MKV_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers) {
+  WsSizes s{};
+  const int G = hq / hkv;
+  const int Le = n_layers < kMaxLayers ? n_layers : kMaxLayers;
+  const int per = Le * hkv;
+  s.chunks_target = per > 0 ? (kTargetItems + per - 1) / per : 1;
+  if (s.chunks_target < 1) s.chunks_target = 1;
+  const int by_pages = (bt_capacity + kMinChunkPages - 1) / kMinChunkPages;
+  s.chunk_cap = (s.chunks_target < by_pages ? s.chunks_target : by_pages) + batch;
+  s.np_cap = 2 * s.chunk_cap;
+  s.ni_cap = 2 * s.np_cap / kMergeFan + 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+  s.off_status = take(sizeof(int32_t));
+  s.off_totals = take(sizeof(int32_t) * T_FIELDS);
+  s.off_req = take(sizeof(int32_t) * R_FIELDS * (size_t)(batch + 1));
+  s.off_list_f = take(sizeof(int32_t) * (size_t)bt_capacity);
+  s.off_list_t = take(sizeof(int32_t) * (size_t)bt_capacity);
+  s.off_chunks_f = take(sizeof(int4) * (size_t)s.chunk_cap);
+  s.off_chunks_t = take(sizeof(int4) * (size_t)s.chunk_cap);
+  const size_t states = (size_t)Le * s.np_cap * hkv * G;
+  const size_t inter = (size_t)Le * s.ni_cap * hkv * G;
+  s.off_part_ml = take(sizeof(float) * 2 * states);
+  s.off_part_acc = take(sizeof(float) * d * states);
+  s.off_inter_ml = take(sizeof(float) * 2 * inter);
+  s.off_inter_acc = take(sizeof(float) * d * inter);
+  s.total = o;
+  return s;
+}
+
+Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
+  char* base = static_cast<char*>(ws);
+  Plan p{};
+  p.status = reinterpret_cast<int32_t*>(base + s.off_status);
+  p.totals = reinterpret_cast<int32_t*>(base + s.off_totals);
+  p.req = reinterpret_cast<int32_t*>(base + s.off_req);
+  p.list_f = reinterpret_cast<int32_t*>(base + s.off_list_f);
+  p.list_t = reinterpret_cast<int32_t*>(base + s.off_list_t);
+  p.chunks_f = reinterpret_cast<int4*>(base + s.off_chunks_f);
+  p.chunks_t = reinterpret_cast<int4*>(base + s.off_chunks_t);
+  p.part_ml = reinterpret_cast<float*>(base + s.off_part_ml);
+  p.part_acc = reinterpret_cast<float*>(base + s.off_part_acc);
+  p.inter_ml = reinterpret_cast<float*>(base + s.off_inter_ml);
+  p.inter_acc = reinterpret_cast<float*>(base + s.off_inter_acc);
+  p.batch = batch;
+  p.bt_capacity = bt_capacity;
+  p.chunk_cap = s.chunk_cap;
+  p.np_cap = s.np_cap;
+  p.ni_cap = s.ni_cap;
+  p.chunks_target = s.chunks_target;
+  return p;
+}
+
+// Which partial-kernel family the decode uses: 1 = matrix cores (default),
+// 0 = the plain VALU kernels (kept as the measured baseline).
+static int g_partial_kind = 0;
+
+}  // namespace mkv
+
+using namespace mkv;
+
+extern "C" {
+
+size_t mkv_fp8_page_bytes(const mkv_layout* layout) {
+  Geometry g{};
+  if (check_layout(layout, &g) != MKV_OK) return 0;
+  return (size_t)fp8_page_bytes(g.hkv, g.d);
+}
+
+size_t mkv_tq3_page_bytes(const mkv_layout* layout) {
+  Geometry g{};
+  if (check_layout(layout, &g) != MKV_OK) return 0;
+  return (size_t)tq3_page_bytes(g.hkv, g.d);
+}
+
+int mkv_append(const mkv_layout* layout, const mkv_pool* pool, const float* k, const float* v,
+               int32_t n_new, const int32_t* bt_offsets, const int32_t* bt_pages,
+               const int32_t* pos, const int32_t* counts, int32_t batch, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if ((rc = check_pool(pool, &g, true, false, false))) return rc;
+  if (batch < 0 || n_new < 0 || n_new > 65535) return fail(MKV_ERR_RANGE, "batch %d / n_new %d out of range", batch, n_new);
+  if ((int64_t)batch * n_new > 0x7fffffff) return fail(MKV_ERR_RANGE, "batch * n_new too large");
+  if (batch == 0 || n_new == 0) return MKV_OK;
+  if (!k || !v || !bt_offsets || !bt_pages || !pos) return fail(MKV_ERR_NULL, "k, v, bt_offsets, bt_pages and pos are required");
+  if (!aligned16(k) || !aligned16(v)) return fail(MKV_ERR_ALIGN, "k and v must be 16-byte aligned");
+  hipError_t e = launch_append(g, pool->fp8_slab, pool->k_scale, pool->v_scale, k, v, n_new,
+                               bt_offsets, bt_pages, pos, counts, batch, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "append launch");
+}
+
+int mkv_demote_pages(const mkv_layout* layout, const mkv_pool* pool, const int32_t* src_fp8,
+                     const int32_t* dst_tq3, int32_t n, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if ((rc = check_pool(pool, &g, true, true, false))) return rc;
+  if (n < 0) return fail(MKV_ERR_RANGE, "n = %d", n);
+  if ((int64_t)n * g.hkv > 0x7fffffff) return fail(MKV_ERR_RANGE, "n too large");
+  if (n == 0) return MKV_OK;
+  if (!src_fp8 || !dst_tq3) return fail(MKV_ERR_NULL, "src_fp8 and dst_tq3 are required");
+  hipError_t e = launch_demote(g, pool->fp8_slab, pool->tq3_slab, pool->k_scale, pool->v_scale,
+                               src_fp8, dst_tq3, n, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "demote launch");
+}
+
+size_t mkv_decode_workspace_bytes(const mkv_layout* layout, int32_t batch, int32_t bt_capacity,
+                                  int32_t n_layers) {
+  Geometry g{};
+  if (check_layout(layout, &g) != MKV_OK || batch < 0 || bt_capacity < 0 || n_layers < 1) return 0;
+  return workspace_sizes(g.hq, g.hkv, g.d, batch, bt_capacity, n_layers).total;
+}
+
+int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                           const mkv_batch* batch, const float* q, float sm_scale, float* out,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if (!pools || !batch) return fail(MKV_ERR_NULL, "pools and batch are required");
+  if (n_layers < 1) return fail(MKV_ERR_RANGE, "n_layers = %d", n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_pool(&pools[l], &g, true, true, true))) return rc;
+    if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
+      return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
+  }
+  const int B = batch->batch;
+  if (B < 0 || batch->bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", B, batch->bt_capacity);
+  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(MKV_ERR_RANGE, "sm_scale must be finite and > 0");
+  if (B == 0) return MKV_OK;
+  if (!batch->bt_offsets || !batch->seq_lens || (!batch->bt_pages && batch->bt_capacity > 0))
+    return fail(MKV_ERR_NULL, "bt_offsets, bt_pages and seq_lens are required");
+  if (!q || !out || !ws) return fail(MKV_ERR_NULL, "q, out and ws are required");
+  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse))) return fail(MKV_ERR_ALIGN, "q, out, lse must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
+  const WsSizes s = workspace_sizes(g.hq, g.hkv, g.d, B, batch->bt_capacity, n_layers);
+  if (ws_bytes < s.total) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, s.total);
+  const Plan plan = plan_from_ws(ws, s, B, batch->bt_capacity);
+  hipStream_t st = as_stream(stream);
+  hipError_t e = launch_plan(g, pools[0].tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, st);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  const float qscale = sm_scale * 1.4426950408889634f;       // scores in log2 units
+  const size_t q_ls = (size_t)B * g.hq * g.d;
+  const size_t lse_ls = (size_t)B * g.hq;
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int nl = (n_layers - l0) < kMaxLayers ? (n_layers - l0) : kMaxLayers;
+    LayerTable lt{};
+    for (int l = 0; l < nl; ++l) {
+      lt.fp8[l] = pools[l0 + l].fp8_slab;
+      lt.tq3[l] = pools[l0 + l].tq3_slab;
+      lt.k_scale[l] = pools[l0 + l].k_scale;
+      lt.v_scale[l] = pools[l0 + l].v_scale;
+    }
+    const float* ql = q + (size_t)l0 * q_ls;
+    for (int fmt = 0; fmt < 2; ++fmt) {
+      e = g_partial_kind ? launch_partial_mfma(fmt == 1, g, lt, nl, ql, q_ls, qscale, plan, st)
+                         : launch_partial_valu(fmt == 1, g, lt, nl, ql, q_ls, qscale, plan, st);
+      if (e != hipSuccess) return hip_fail(e, fmt ? "TQ3 partial launch" : "FP8 partial launch");
+    }
+    e = launch_merge(g, nl, plan, out + (size_t)l0 * q_ls, lse ? lse + (size_t)l0 * lse_ls : nullptr,
+                     q_ls, lse_ls, st);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return MKV_OK;
+}
+
+int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                    const float* q, float sm_scale, float* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return mkv_decode_attn_layers(layout, pool, 1, batch, q, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+                     const int32_t* bt_pages, int32_t b, int32_t n_pages, uint8_t* out, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if ((rc = check_pool(pool, &g, true, true, false))) return rc;
+  if (b < 0 || n_pages < 0) return fail(MKV_ERR_RANGE, "b %d / n_pages %d", b, n_pages);
+  if (n_pages == 0) return MKV_OK;
+  if (!bt_offsets || !bt_pages || !out) return fail(MKV_ERR_NULL, "bt_offsets, bt_pages and out are required");
+  if (!aligned16(out)) return fail(MKV_ERR_ALIGN, "out must be 16-byte aligned");
+  hipError_t e = launch_gather(g, pool->fp8_slab, pool->tq3_slab, bt_offsets, bt_pages, b, n_pages,
+                               out, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "gather launch");
+}
+
+int mkv_workspace_status(const void* ws, void* stream) {
+  if (!ws) return fail(MKV_ERR_NULL, "ws is NULL");
+  hipError_t e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  int32_t status = 0;
+  e = hipMemcpy(&status, ws, sizeof status, hipMemcpyDeviceToHost);   // status is the first field
+  if (e != hipSuccess) return hip_fail(e, "status copy");
+  return status;
+}
+
+const char* mkv_status_string(int status) {
+  switch (status) {
+    case MKV_OK: return "ok";
+    case MKV_ERR_NULL: return "null pointer";
+    case MKV_ERR_SHAPE: return "unsupported shape";
+    case MKV_ERR_ALIGN: return "misaligned pointer";
+    case MKV_ERR_WORKSPACE: return "workspace too small";
+    case MKV_ERR_RANGE: return "value out of range";
+    case MKV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* mkv_last_error(void) { return g_err; }
+
+// Selects the partial-kernel family for later decode calls in this process:
+// 1 = matrix-core kernels (default), 0 = plain VALU kernels.  Not part of
+// include/mkv.h: a measurement hook for comparing the two families.
+int mkv_internal_set_partial_kind(int kind) {
+  if (kind != 0 && kind != 1) return fail(MKV_ERR_RANGE, "kind %d", kind);
+  g_partial_kind = kind;
+  return MKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// mkv_demote.hip -- FP8 -> TQ3 page demotion (the pack).
+//
+// "Older non-anchor pages move to packed TQ3" (arXiv 2608.23834, page 1,
+// Abstract).  One workgroup per (page, KV head):
+//   phase 1: one thread per (K/V, token, 32-channel group) decodes the FP8
+//            bytes (x = fl32(decode(e) * scale)), takes the absmax, forms the
+//            fp16 scale s = fp16_RNE(fl32(a / 3)) and the codes u = q + 4,
+//            and leaves codes and scales in LDS;
+//   phase 2: each thread assembles four consecutive triples (12 bytes) of the
+//            head block from LDS in the documented slot order and stores
+//            them as three 32-bit words; scales are stored as fp16.
+#include "mkv_format.h"
+#include "mkv_internal.h"
+
+namespace mkv {
+
+template <int D>
+__global__ void __launch_bounds__(256) demote_kernel(
+    const uint8_t* __restrict__ fp8_slab, uint8_t* __restrict__ tq3_slab, int n_fp8, int n_tq3,
+    int hkv, float k_scale, float v_scale, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ dst) {
+  constexpr int G = D / 32;
+  __shared__ uint8_t codes[2][kPage][D];
+  __shared__ uint16_t scales[2][kPage][G];
+  const int page = blockIdx.x / hkv;
+  const int h = blockIdx.x - page * hkv;
+  const int s_id = src[page];
+  const int d_id = dst[page];
+  if (s_id < 0 || s_id >= n_fp8 || d_id < n_fp8 || d_id >= n_fp8 + n_tq3) return;   // uniform
+  const uint8_t* in = fp8_slab + (size_t)s_id * fp8_page_bytes(hkv, D) + (size_t)h * 2 * kPage * D;
+  uint8_t* out = tq3_slab + (size_t)(d_id - n_fp8) * tq3_page_bytes(hkv, D) + (size_t)h * tq3_head_bytes(D);
+
+  for (int grp = threadIdx.x; grp < 2 * kPage * G; grp += blockDim.x) {
+    const int kv = grp / (kPage * G);
+    const int t = (grp / G) % kPage;
+    const int g = grp % G;
+    const float sc = kv ? v_scale : k_scale;
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(in + (kv * kPage + t) * D + g * 32);
+    float x[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t word = row[w];
+#pragma unroll
+      for (int byte = 0; byte < 4; ++byte) {
+        const float val = __fmul_rn(e4m3_decode((word >> (8 * byte)) & 0xffu), sc);
+        x[w * 4 + byte] = val;
+        a = fmaxf(a, fabsf(val));
+      }
+    }
+    const uint16_t sb = tq3_scale_bits(a);
+    const float s = half_bits_to_float(sb);
+    scales[kv][t][g] = sb;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) codes[kv][t][g * 32 + c] = (uint8_t)(tq3_code(x[c], s) + 4);
+  }
+  __syncthreads();
+
+  // code region: 12 D bytes = 4 D triples; thread handles triples 4 tau .. 4 tau + 3
+  for (int tau = threadIdx.x; tau < D; tau += blockDim.x) {
+    uint32_t words[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ti = 4 * tau + q;
+      uint32_t tw = 0;
+      if (ti < 2 * D) {                                  // K triple: row t, triple (j, g)
+        const int t = ti / (D / 8);
+        const int r = ti - t * (D / 8);
+        const int j = r / G, g = r - (r / G) * G;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tw |= (uint32_t)codes[0][t][32 * g + 8 * j + k] << (3 * k);
+      } else {                                           // V triple: (j, n, p)
+        const int tv = ti - 2 * D;
+        const int p = tv % G;
+        const int jn = tv / G;
+        const int n = jn & 15, j = jn >> 4;
+        const int a = n * (D / 16) + 2 * p;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // inverse of the slot table: slot -> (channel-in-pair, token-in-quarter)
+          const int ci = (0x3c >> k) & 1;                // slots 2,3,4,5 hold channel b
+          const int rr = (0xde18 >> (2 * k)) & 3;        // slot -> r : 0,2,1,0,2,3,1,3
+          tw |= (uint32_t)codes[1][4 * j + rr][a + ci] << (3 * k);
+        }
+      }
+      // place the 24-bit triple at byte 3q of the 12-byte window
+      const int bit = 24 * q;
+      words[bit >> 5] |= tw << (bit & 31);
+      if ((bit & 31) > 8) words[(bit >> 5) + 1] |= tw >> (32 - (bit & 31));
+    }
+    uint32_t* o = reinterpret_cast<uint32_t*>(out + 12 * tau);
+    o[0] = words[0];
+    o[1] = words[1];
+    o[2] = words[2];
+  }
+  // scales: 2 * 16 * G fp16 values
+  for (int e = threadIdx.x; e < 2 * kPage * G; e += blockDim.x) {
+    const int kv = e / (kPage * G);
+    const int t = (e / G) % kPage;
+    const int g = e % G;
+    *reinterpret_cast<uint16_t*>(out + tq3_scale_off(D, kv, t, g)) = scales[kv][t][g];
+  }
+}
+
+hipError_t launch_demote(const Geometry& g, const uint8_t* fp8_slab, uint8_t* tq3_slab,
+                         float k_scale, float v_scale, const int32_t* src, const int32_t* dst,
+                         int n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  dim3 grid(n * g.hkv);
+  if (g.d == 256)
+    hipLaunchKernelGGL(demote_kernel<256>, grid, dim3(256), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
+                       g.n_tq3, g.hkv, k_scale, v_scale, src, dst);
+  else
+    hipLaunchKernelGGL(demote_kernel<128>, grid, dim3(256), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
+                       g.n_tq3, g.hkv, k_scale, v_scale, src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace mkv

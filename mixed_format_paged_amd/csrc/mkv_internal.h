@@ -1,0 +1,119 @@
+// mkv_internal.h -- plan / workspace structures shared by the host API and
+// the kernels of the mixed FP8 / TQ3 decode path.
+//
+// Split-K over pages: each request's pages are split by format (FP8 pages
+// read by the FP8 partial kernel, TQ3 pages by the TQ3 partial kernel, as the
+// format-specific kernels of arXiv 2608.23834, page 1, Abstract), each
+// format's list is cut into chunks of Pp pages, and every (layer, chunk, KV
+// head) work item produces one partial state (m, l, acc) for the G query
+// heads of its group.  A log-sum-exp merge combines all partials of a
+// request, one or two levels deep.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mkv {
+
+constexpr int kMaxLayers = 64;        // layers covered by one launch
+constexpr int kTargetItems = 512;     // split-K work items (workgroups) aimed for per format
+constexpr int kMinChunkPages = 4;     // smallest chunk
+constexpr int kMergeFan = 32;         // partials merged per first-level merge item
+constexpr int kMaxG = 8;              // query heads per KV head supported
+
+// Per-request plan fields, each an int32[batch + 1] row of req[].
+enum ReqField {
+  R_NF = 0,      // FP8 pages of the request
+  R_NT,          // TQ3 pages
+  R_TAIL,        // tokens on the last logical page (1..16), 0 for an empty request
+  R_LASTFMT,     // format of the last logical page: 0 FP8, 1 TQ3, -1 none
+  R_INVALID,     // MKV_DEV_* bits of the request; nonzero: outputs are NaN
+  R_CF_OFF,      // first FP8 chunk of the request (exclusive prefix; [batch] = total)
+  R_CT_OFF,      // first TQ3 chunk of the request
+  R_POFF,        // first partial index of the request (per layer)
+  R_M1OFF,       // first first-level merge item
+  R_IOFF,        // first intermediate (second level) slot
+  R_FIELDS
+};
+
+enum TotalField {
+  T_NCF = 0,     // FP8 chunks in total
+  T_NCT,         // TQ3 chunks in total
+  T_NP,          // partials per layer
+  T_NM1,         // first-level merge items per (layer, KV head)
+  T_NI,          // intermediate partials per layer
+  T_PPF,         // pages per FP8 chunk
+  T_PPT,         // pages per TQ3 chunk
+  T_FIELDS = 16
+};
+
+// Chunk descriptor: x = request, y = first index into the format's page list
+// (absolute, in the request's CSR range), z = pages | (tokens on its last
+// page << 16), w = partial index within the layer.
+struct Plan {
+  int32_t* status;      // [1] MKV_DEV_* bits
+  int32_t* totals;      // [T_FIELDS]
+  int32_t* req;         // [R_FIELDS][batch + 1]
+  int32_t* list_f;      // [bt_capacity] FP8 page ids, request-CSR order
+  int32_t* list_t;      // [bt_capacity] TQ3 slot ids (id - n_fp8)
+  int4* chunks_f;       // [chunk_cap]
+  int4* chunks_t;       // [chunk_cap]
+  float* part_ml;       // [L][np_cap][Hkv][G][2]  (m in log2 units, l)
+  float* part_acc;      // [L][np_cap][Hkv][G][d]
+  float* inter_ml;      // [L][ni_cap][Hkv][G][2]
+  float* inter_acc;     // [L][ni_cap][Hkv][G][d]
+  int batch;
+  int bt_capacity;
+  int chunk_cap;        // per format
+  int np_cap;           // partials per layer
+  int ni_cap;           // intermediates per layer
+  int chunks_target;    // chunks aimed for per format
+};
+
+struct WsSizes {
+  size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
+  size_t off_part_ml, off_part_acc, off_inter_ml, off_inter_acc, total;
+  int chunk_cap, np_cap, ni_cap, chunks_target;
+};
+
+WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers);
+Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity);
+
+// Per-launch layer table (passed by value as a kernel argument).
+struct LayerTable {
+  const uint8_t* fp8[kMaxLayers];
+  const uint8_t* tq3[kMaxLayers];
+  float k_scale[kMaxLayers];
+  float v_scale[kMaxLayers];
+};
+
+struct Geometry {
+  int hq, hkv, d, G;
+  int n_fp8, n_tq3;
+};
+
+// ---- launchers (each returns hipGetLastError() of its launch) --------------
+hipError_t launch_append(const Geometry& g, uint8_t* fp8_slab, float k_scale, float v_scale,
+                         const float* k, const float* v, int n_new, const int32_t* bt_offsets,
+                         const int32_t* bt_pages, const int32_t* pos, const int32_t* counts,
+                         int batch, hipStream_t stream);
+hipError_t launch_demote(const Geometry& g, const uint8_t* fp8_slab, uint8_t* tq3_slab,
+                         float k_scale, float v_scale, const int32_t* src, const int32_t* dst,
+                         int n, hipStream_t stream);
+hipError_t launch_gather(const Geometry& g, const uint8_t* fp8_slab, const uint8_t* tq3_slab,
+                         const int32_t* bt_offsets, const int32_t* bt_pages, int b, int n_pages,
+                         uint8_t* out, hipStream_t stream);
+hipError_t launch_plan(const Geometry& g, const uint8_t* tier, const int32_t* bt_offsets,
+                       const int32_t* bt_pages, const int32_t* seq_lens, const Plan& plan,
+                       hipStream_t stream);
+// Partial kernels: `tq3` selects the format.  q is [layers][batch][hq][d];
+// qscale = sm_scale * log2(e) (scores are kept in log2 units).
+hipError_t launch_partial_valu(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
+                               const float* q, size_t q_layer_stride, float qscale,
+                               const Plan& plan, hipStream_t stream);
+hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out,
+                        float* lse, size_t out_layer_stride, size_t lse_layer_stride,
+                        hipStream_t stream);
+
+}  // namespace mkv

@@ -1,0 +1,55 @@
+"""Helpers shared by the GPU tests: build the same workload on both sides.
+
+The oracle side builds its byte pool with oracle.build from CPU-drawn values;
+the HIP side builds its cache with libmkv kernels from the very same values
+(copied to the GPU).  Nothing on the oracle side comes from the HIP path.
+"""
+import math
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import attention as OA, build as OB, pool as OP
+
+ATOL = 2e-3          # max |o_gpu - o_ref|
+RTOL_L2 = 1e-3       # ||o_gpu - o_ref|| / ||o_ref||
+LSE_ATOL = 1e-3
+
+
+def need_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def oracle_side(w, st, layer_vals):
+    """Oracle pools, block tables and decode outputs for every layer."""
+    res = []
+    for vals in layer_vals:
+        k = [None if x is None else x.cpu().numpy() for x in vals["k"]]
+        v = [None if x is None else x.cpu().numpy() for x in vals["v"]]
+        pool, bt = OB.build_layer(w, st, k, v)
+        OB.step_demote(pool, st, bt)
+        o, lse = OA.decode_batch(pool, vals["q"].cpu().numpy(), st.bt_offsets, bt, st.seq_lens)
+        res.append((pool, bt, o, lse))
+    return res
+
+
+def compare(o_gpu, o_ref, lse_gpu=None, lse_ref=None, what=""):
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    err = np.abs(o_gpu - o_ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    den = float(np.linalg.norm(o_ref))
+    rel = float(np.linalg.norm(o_gpu - o_ref)) / den if den > 0 else float(np.linalg.norm(o_gpu))
+    msg = f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+    assert max_abs <= ATOL, msg
+    assert rel <= RTOL_L2, msg
+    if lse_gpu is not None:
+        lg = np.asarray(lse_gpu, dtype=np.float64)
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isneginf(lg), np.isneginf(lse_ref)), what + ": -inf pattern of lse"
+        if fin.any():
+            le = float(np.abs(lg[fin] - lse_ref[fin]).max())
+            assert le <= LSE_ATOL, f"{what}: lse err {le:.3e}"
+    return max_abs, rel

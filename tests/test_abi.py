@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports every symbol include/mkv.h declares, and
+rejects bad arguments on the host before touching the GPU.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_format_paged_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"mkv_append", "mkv_demote_pages", "mkv_decode_attn"} <= set(names)
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_page_sizes_and_shape_checks():
+    assert M.mkv_fp8_page_bytes((24, 4, 256)) == 32768
+    assert M.mkv_tq3_page_bytes((24, 4, 256)) == 14336
+    assert M.mkv_tq3_page_bytes((24, 4, 128)) == 7168
+    for bad in [(24, 4, 64), (24, 5, 256), (36, 4, 256), (24, 4, 256, 32)]:
+        assert M.mkv_fp8_page_bytes(bad) == 0
+
+
+def _call_decode(layout, pool, batch, ws_bytes=1 << 30, q=4096, out=8192, ws=256, sm=0.0625):
+    L = M.lib()
+    return L.mkv_decode_attn(ctypes.byref(M._layout(layout)), ctypes.byref(pool) if pool else None,
+                             ctypes.byref(batch) if batch else None, q, sm, out, None, ws, ws_bytes, None)
+
+
+def test_host_validation_codes():
+    L = M.lib()
+    pool = M.PoolDesc(1 << 20, 1 << 21, 1 << 22, 10, 10, 1.0, 1.0)
+    batch = M.BatchDesc(1 << 23, 1 << 24, 1 << 25, 2, 100)
+    assert _call_decode((24, 4, 100), pool, batch) == -2                      # shape
+    assert _call_decode((24, 4, 256), None, batch) == -1                      # null pool
+    assert _call_decode((24, 4, 256), pool, batch, q=None) == -1              # null q
+    assert _call_decode((24, 4, 256), pool, batch, q=8) == -3                 # misaligned q
+    assert _call_decode((24, 4, 256), pool, batch, ws=128) == -3              # ws not 256-aligned
+    assert _call_decode((24, 4, 256), pool, batch, ws_bytes=16) == -4         # workspace too small
+    assert _call_decode((24, 4, 256), pool, batch, sm=-1.0) == -5             # bad sm_scale
+    bad_pool = M.PoolDesc(1 << 20, 1 << 21, 1 << 22, -1, 10, 1.0, 1.0)
+    assert _call_decode((24, 4, 256), bad_pool, batch) == -5
+    assert "workspace" in M.mkv_status_string(-4)
+    lay = ctypes.byref(M._layout((24, 4, 256)))
+    assert L.mkv_demote_pages(lay, ctypes.byref(pool), None, None, 3, None) == -1
+    assert L.mkv_demote_pages(lay, ctypes.byref(pool), None, None, -3, None) == -5
+    assert L.mkv_append(lay, ctypes.byref(pool), 16, 16, 70000, 16, 16, 16, None, 1, None) == -5
+    assert L.mkv_append(lay, ctypes.byref(pool), 8, 16, 1, 16, 16, 16, None, 1, None) == -3
+    assert L.mkv_debug_gather(lay, ctypes.byref(pool), None, None, 0, 4, None, None) == -1
+    # zero-size work is a successful no-op that launches nothing
+    assert L.mkv_demote_pages(lay, ctypes.byref(pool), None, None, 0, None) == 0
+    empty = M.BatchDesc(None, None, None, 0, 0)
+    assert _call_decode((24, 4, 256), pool, empty) == 0
+
+
+def test_workspace_is_bounded_not_cache_sized():
+    # The workspace holds the plan and a capped number of split-K partial
+    # states; beyond 8 bytes of page lists per block-table entry it does not
+    # grow with context length, so it is never a dense shadow of the cache.
+    lay = (24, 4, 256)
+    base = M.mkv_decode_workspace_bytes(lay, 2, 7376, 16)
+    big = M.mkv_decode_workspace_bytes(lay, 2, 10 * 7376, 16)
+    assert big - base <= 8 * 9 * 7376 + 4096
+    kv_bytes_canary = 1_734_344_704
+    assert base < 0.01 * kv_bytes_canary
+    one = M.mkv_decode_workspace_bytes(lay, 1, 8192, 1)
+    assert one < 0.06 * 121_126_912
+    assert M.mkv_decode_workspace_bytes(lay, 1, 80 * 8192, 1) - one <= 8 * 79 * 8192 + 4096

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bit-exact: append (FP8 bytes), demote (TQ3 bytes), page-table gather.
+Attention: max-abs <= 2e-3 and rel-L2 <= 1e-3 on out, |lse| <= 1e-3, on the
+same quantised inputs, for small versions of every workload shape, ragged
+and empty requests, tails in either format and a multi-level merge.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_format_paged_amd as M
+import workloads as W
+from workloads.device_cache import DeviceWorkload
+from oracle import attention as OA, build as OB, fp8 as OF, layout as OL, pool as OP
+
+from gpu_util import compare, oracle_side
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(dw, sm_scale=None):
+    w = dw.w
+    L = len(dw.layers)
+    layout = (w.Hq, w.Hkv, w.d)
+    wsb = M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), L)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((L, w.B, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((L, w.B, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn_layers(layout, dw.cache.pools, dw.batch(), dw.q, sm_scale or 1 / math.sqrt(w.d), out, lse, ws)
+    status = M.mkv_workspace_status(ws)
+    return out.cpu().numpy(), lse.cpu().numpy(), status
+
+
+def _both(w, layers=None):
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda", layers=layers, keep_values=True, gen_device="cpu")
+    ref = oracle_side(w, st, dw.values)
+    return st, dw, ref
+
+
+def test_append_bitexact_edge_values():
+    hq, hkv, d = 8, 2, 128
+    rng = np.random.default_rng(0)
+    special = np.array([0.0, -0.0, 448.0, -448.0, 449.0, 463.9, 464.0, 1e30, -1e30, 2.0 ** -9, 2.0 ** -10,
+                        1.5 * 2.0 ** -9, 2.0 ** -6, 0.9 * 2.0 ** -6, 1.0625, 1.1875, 3e-8], dtype=np.float32)
+    n_tok = 40
+    k = (rng.standard_normal((1, n_tok, hkv, d)) * np.exp(rng.uniform(-8, 6, (1, n_tok, hkv, 1)))).astype(np.float32)
+    v = (rng.standard_normal((1, n_tok, hkv, d)) * 50).astype(np.float32)
+    k.reshape(-1)[:len(special)] = special
+    v.reshape(-1)[-len(special):] = special
+    for ks, vs in ((1.0, 1.0), (0.37, 2.5)):
+        pool = OP.Pool(hkv, d, 4, 1, ks, vs)
+        pages = np.array([2, 0, 3], dtype=np.int64)
+        OP.append(pool, k, v, [0, 3], pages, [5])
+        fp8 = torch.zeros((4, OL.fp8_page_bytes(hkv, d)), dtype=torch.uint8, device="cuda")
+        tq3 = torch.zeros((1, OL.tq3_page_bytes(hkv, d)), dtype=torch.uint8, device="cuda")
+        tier = torch.zeros(5, dtype=torch.uint8, device="cuda")
+        p = M.make_pool(fp8, tq3, tier, 4, 1, ks, vs)
+        dev = lambda a, dt=torch.int32: torch.as_tensor(np.asarray(a), dtype=dt, device="cuda")
+        M.mkv_append((hq, hkv, d), p, dev(k, torch.float32), dev(v, torch.float32), dev([0, 3]), dev(pages), dev([5]))
+        torch.cuda.synchronize()
+        assert np.array_equal(fp8.cpu().numpy(), pool.fp8), (ks, vs)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_demote_bitexact_random_bytes(d):
+    hq, hkv = 24, 4
+    rng = np.random.default_rng(d)
+    n = 9
+    pb = OL.fp8_page_bytes(hkv, d)
+    raw = rng.integers(0, 256, (n, pb)).astype(np.uint8)
+    raw[(raw & 0x7F) == 0x7F] = 0x7E                    # NaN codes are outside the contract
+    raw[1, :] = 0                                       # all-zero groups (s = 0)
+    raw[2, :] &= 0x87                                   # tiny magnitudes only (subnormal e4m3, fp16 subnormal scales)
+    raw[3, ::7] = 0x7E                                  # saturated maxima
+    for ks, vs in ((1.0, 1.0), (0.001, 37.0), (2.0 ** -20, 1500.0)):
+        pool = OP.Pool(hkv, d, n, n, ks, vs)
+        pool.fp8[:] = raw
+        src = np.arange(n)
+        dst = n + rng.permutation(n)
+        OP.demote(pool, src, dst)
+        fp8 = torch.as_tensor(raw, device="cuda")
+        tq3 = torch.zeros((n, OL.tq3_page_bytes(hkv, d)), dtype=torch.uint8, device="cuda")
+        tier = torch.zeros(2 * n, dtype=torch.uint8, device="cuda")
+        p = M.make_pool(fp8, tq3, tier, n, n, ks, vs)
+        M.mkv_demote_pages((hq, hkv, d), p, torch.as_tensor(src, dtype=torch.int32, device="cuda"),
+                           torch.as_tensor(dst, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        got = tq3.cpu().numpy()
+        assert np.array_equal(got, pool.tq3), (ks, vs, np.argwhere(got != pool.tq3)[:5])
+
+
+def test_build_gather_and_decode_tiny():
+    w = W.WORKLOADS["tiny-1x1024-d128"]
+    st, dw, ref = _both(w)
+    pool, bt, o_ref, lse_ref = ref[0]
+    # gather: logical page bytes, bit-exact
+    n = int(st.n_pages[0])
+    rec = torch.empty((n, OL.fp8_page_bytes(w.Hkv, w.d)), dtype=torch.uint8, device="cuda")
+    M.mkv_debug_gather((w.Hq, w.Hkv, w.d), dw.cache.pools[0], dw.bt_offsets, dw.bt, 0, n, rec)
+    torch.cuda.synchronize()
+    assert np.array_equal(rec.cpu().numpy(), OP.gather_raw(pool, st.bt_offsets, bt, 0, n))
+    assert np.array_equal(dw.bt.cpu().numpy(), bt)
+    out, lse, status = _decode(dw)
+    assert status == 0
+    compare(out[0], o_ref, lse[0], lse_ref, "tiny")
+
+
+SMALL = [
+    # (name, workload)
+    ("batch-8x1024", W.scaled(W.WORKLOADS["batch-8x16384"], lengths=("fixed", 1024), recent_tokens=128)),
+    ("ragged-7", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=7,
+                          lengths=("list", (1, 17, 0, 300, 1031, 2000, 16)), recent_tokens=64)),
+    ("no-recent-tq3-tail", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=3,
+                                    lengths=("list", (999, 33, 1)), recent_tokens=0, random_anchor_frac=0.1)),
+    ("all-fp8", W.scaled(W.WORKLOADS["batch-8x16384"], B=2, lengths=("fixed", 700), recent_tokens=1024)),
+    ("long-1x8192", W.scaled(W.WORKLOADS["long-1x131072"], lengths=("fixed", 8192))),
+    ("canary-3L", W.scaled(W.WORKLOADS["canary-2x59008-16L"], L=3, lengths=("fixed", 1500), recent_tokens=256)),
+    ("demote-4x2048", W.scaled(W.WORKLOADS["demote-64x32768"], B=4, lengths=("fixed", 2048), aging_pages=16)),
+]
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_parity_small(name, w):
+    st, dw, ref = _both(w)
+    dw.step_demote()
+    assert np.array_equal(dw.bt.cpu().numpy(), ref[0][1])
+    out, lse, status = _decode(dw)
+    assert status == 0
+    for li, (_, _, o_ref, lse_ref) in enumerate(ref):
+        compare(out[li], o_ref, lse[li], lse_ref, f"{name} layer {li}")
+
+
+def test_multilayer_equals_per_layer_and_is_deterministic():
+    w = W.scaled(W.WORKLOADS["canary-2x59008-16L"], L=3, lengths=("fixed", 900), recent_tokens=128)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    out, lse, _ = _decode(dw)
+    for _ in range(5):
+        o2, l2, _ = _decode(dw)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+    layout = (w.Hq, w.Hkv, w.d)
+    for li in range(3):
+        wsb = M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((w.B, w.Hq, w.d), device="cuda")
+        l1 = torch.empty((w.B, w.Hq), device="cuda")
+        M.mkv_decode_attn(layout, dw.cache.pools[li], dw.batch(), dw.q[li].contiguous(), 1 / math.sqrt(w.d), o1, l1, ws)
+        torch.cuda.synchronize()
+        # chunking differs with the layer count, so agreement is to tolerance
+        compare(o1.cpu().numpy(), out[li].astype(np.float64), None, None, f"layer {li}")
+
+
+def test_device_data_errors_flag_and_nan():
+    w = W.scaled(W.WORKLOADS["batch-8x16384"], B=4, lengths=("fixed", 300), recent_tokens=64)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    out0, lse0, status = _decode(dw)
+    assert status == 0
+    bt_good = dw.bt.clone()
+    # request 1: a page id outside the pool
+    dw.bt[int(st.bt_offsets[1]) + 3] = st.n_fp8 + st.n_tq3 + 5
+    # request 2: an FP8 slot whose tier byte says Stale
+    e = int(st.bt_offsets[2]) + int(st.n_pages[2]) - 1
+    free_fp8 = int(torch.nonzero(dw.cache.tier[:st.n_fp8] == M.TIER_FREE)[0])
+    dw.cache.tier[free_fp8] = M.TIER_STALE
+    dw.bt[e] = free_fp8
+    # request 3: seq_len longer than its block table
+    dw.seq_lens[3] = 300 + 16 * 5
+    out, lse, status = _decode(dw)
+    assert status == (1 | 2 | 4)
+    assert np.all(np.isnan(out[0, 1:4])) and np.all(np.isnan(lse[0, 1:4]))
+    assert np.array_equal(out[0, 0], out0[0, 0]) and np.array_equal(lse[0, 0], lse0[0, 0])
+    dw.bt.copy_(bt_good)
+    dw.seq_lens[3] = 300
+    dw.cache.tier[free_fp8] = M.TIER_FREE
+    out, lse, status = _decode(dw)
+    assert status == 0 and np.array_equal(out, out0)

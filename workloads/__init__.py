@@ -32,7 +32,7 @@ class Workload:
     Hq: int
     Hkv: int
     d: int
-    lengths: tuple            # ("fixed", n) or ("uniform", lo, hi)
+    lengths: tuple            # ("fixed", n), ("uniform", lo, hi) or ("list", (n_0, ..., n_B-1))
     recent_tokens: int
     fixed_anchor_pages: int
     random_anchor_frac: float
@@ -88,6 +88,9 @@ def make_structure(w):
     # 1. lengths
     if w.lengths[0] == "fixed":
         lens = np.full(w.B, w.lengths[1], dtype=np.int64)
+    elif w.lengths[0] == "list":
+        lens = np.array(w.lengths[1], dtype=np.int64)
+        assert len(lens) == w.B
     else:
         lens = rng.integers(w.lengths[1], w.lengths[2] + 1, size=w.B)
     n_pages = -(-lens // PAGE)
