@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Mixed FP8 / TQ3 paged decode attention on one MI355X: the canary workload.
+
+Workload (default): 2 requests x 59,008 tokens, 16 attention layers with one
+cache each, 24 query / 4 KV heads, head_dim 256, pages of 16 tokens; the last
+1,024 tokens and the first 8 pages of each request are FP8, the other 3,616
+pages per request TQ3; physical pages shuffled (the pages' direct-decode
+canary shape, arXiv 2608.23834, page 1, Abstract).  Inputs are synthetic and
+seeded (workloads/), generated on the GPU, resident in HBM before timing.
+
+One step = one decode step of the whole path, layers in sequence as a model
+runs them:
+    plan (block tables + tier map -> per-format page lists and split-K chunks)
+    for each of the 16 layers:
+        append the step's new token (K, V of both requests, FP8 E4M3)
+        FP8 partial kernel, TQ3 partial kernel, log-sum-exp merge
+    demote, in all 16 layers, the page of each request that leaves the recent
+    window (FP8 -> TQ3 pack, written to a spare TQ3 slot so the cache state
+    stays identical from step to step)
+The step is captured once in a HIP graph and replayed.
+
+Prints one JSON line.  `value` is KV GB/s: algorithmic KV bytes of the 16
+layers (every page of every request read once per layer) / step time.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="canary-2x59008-16L")
+    ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-control", action="store_true", help="skip the same-run all-FP8 control")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-units", type=int, default=6, help="(layer, request, KV head) units the oracle is timed on")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many eager steps (for rocprofv3), print nothing else")
+    return ap.parse_args()
+
+
+class Runner:
+    """Holds the device state of one workload and enqueues its decode steps."""
+
+    def __init__(self, w, st, all_fp8=False, kernel="mfma"):
+        import torch
+        import mixed_format_paged_amd as M
+        from workloads.device_cache import DeviceWorkload
+        import workloads as W
+        self.M, self.torch = M, torch
+        if all_fp8:
+            # the control: identical shapes with every page FP8 (no demotion at build)
+            import numpy as np
+            st = W.Structure(st.seq_lens, st.n_pages, st.bt_offsets,
+                             np.where(st.tiers == W.TIER_S, W.TIER_R, st.tiers).astype(np.uint8),
+                             st.staging_ids, st.staging_ids, st.n_fp8, 0,
+                             np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64))
+        self.w, self.st = w, st
+        M.set_partial_kind(1 if kernel == "mfma" else 0)
+        t0 = time.time()
+        self.dw = DeviceWorkload(w, st, "cuda", spare_tq3=w.B)
+        torch.cuda.synchronize()
+        self.build_s = time.time() - t0
+        self.layout = (w.Hq, w.Hkv, w.d)
+        self.batch = self.dw.batch()
+        self.sm_scale = 1.0 / math.sqrt(w.d)
+        dev = "cuda"
+        L, B = w.L, w.B
+        self.ws = torch.empty(M.mkv_decode_workspace_bytes(self.layout, B, self.dw.bt.numel(), 1),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((L, B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((L, B, w.Hq), dtype=torch.float32, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(12345)
+        self.k_new = torch.randn((L, B, 1, w.Hkv, w.d), generator=g, device=dev)
+        self.v_new = torch.randn((L, B, 1, w.Hkv, w.d), generator=g, device=dev)
+        self.pos = (self.dw.seq_lens - 1).clamp(min=0).contiguous()
+        # the page leaving the recent window: logical page n - recent_pages of each request
+        rec = w.recent_tokens // 16
+        ent = [int(st.bt_offsets[b]) + max(0, int(st.n_pages[b]) - rec) for b in range(B)]
+        self.dem_src = self.dw.bt[torch.as_tensor(ent, device=dev)].contiguous()
+        is_fp8 = bool((self.dem_src < st.n_fp8).all())
+        self.dem_src = self.dem_src if is_fp8 else torch.zeros(0, dtype=torch.int32, device=dev)
+        n_tq3_total = self.dw.cache.n_tq3
+        self.dem_dst = torch.arange(n_tq3_total - B, n_tq3_total, dtype=torch.int32, device=dev) + st.n_fp8
+        self.dem_dst = self.dem_dst[:self.dem_src.numel()].contiguous()
+        self.q = [self.dw.q[l].contiguous() for l in range(L)]
+
+    def step(self):
+        M, dw, lay, bat, ws = self.M, self.dw, self.layout, self.batch, self.ws
+        M.mkv_decode_plan(lay, dw.cache.pools[0], bat, 1, ws)
+        for l in range(self.w.L):
+            M.mkv_append(lay, dw.cache.pools[l], self.k_new[l], self.v_new[l], dw.bt_offsets, dw.bt, self.pos)
+            M.mkv_attend_fp8(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, ws)
+            M.mkv_attend_tq3(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, ws)
+            M.mkv_merge(lay, 1, bat, self.out[l], self.lse[l], ws)
+        if self.dem_src.numel():
+            M.mkv_demote_pages_layers(lay, dw.cache.pools, self.dem_src, self.dem_dst)
+
+    def kv_bytes(self):
+        """Algorithmic KV bytes per step: every page of every request, every layer."""
+        import numpy as np
+        st, w = self.st, self.w
+        fb = self.M.mkv_fp8_page_bytes(self.layout)
+        tb = self.M.mkv_tq3_page_bytes(self.layout)
+        n_t = int((st.tiers == 2).sum())
+        n_f = int(st.total_pages - n_t)
+        return w.L * (n_f * fb + n_t * tb), w.L * n_t * tb, n_t * tb
+
+    def time_steps(self, steps, warmup, graph=True):
+        torch = self.torch
+        run = self.step
+        if graph:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for _ in range(2):
+                    self.step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                self.step()
+            run = self.graph.replay
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def time_tq3_kernel(self, reps=20):
+        """Average duration of one TQ3 partial launch (layer 0), HIP events on its stream."""
+        torch, M = self.torch, self.M
+        M.mkv_decode_plan(self.layout, self.dw.cache.pools[0], self.batch, 1, self.ws)
+        for _ in range(3):
+            M.mkv_attend_tq3(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale, self.ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            M.mkv_attend_tq3(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale, self.ws)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def cpu_baseline(runner, units):
+    """Time the CPU oracle on a bounded sample of the same step, and check the
+    GPU's outputs for the sampled (layer, request, KV head) units against it."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from oracle import attention as OA, pool as OP
+    w, st = runner.w, runner.st
+    rng = np.random.default_rng(7)
+    picks = [(int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(units)]
+    G = w.Hq // w.Hkv
+    by_layer = {}
+    for l, b, h in picks:
+        by_layer.setdefault(l, []).append((b, h))
+    t_oracle = 0.0
+    worst = 0.0
+    worst_rel = 0.0
+    bytes_done = 0
+    tb = runner.M.mkv_tq3_page_bytes(runner.layout) // w.Hkv
+    fb = runner.M.mkv_fp8_page_bytes(runner.layout) // w.Hkv
+    out = runner.out.cpu().numpy()
+    for l, items in by_layer.items():
+        vals = W.layer_values(w, st, l, device="cuda", requests={b for b, _ in items})
+        for b, h in items:
+            T = int(st.seq_lens[b])
+            k = vals["k"][b][:, h].clone()
+            v = vals["v"][b][:, h].clone()
+            k[T - 1] = runner.k_new[l, b, 0, h]          # the step's appended token
+            v[T - 1] = runner.v_new[l, b, 0, h]
+            k, v = k.cpu().numpy(), v.cpu().numpy()
+            q = vals["q"][b, h * G:(h + 1) * G].cpu().numpy()
+            tiers = st.tiers[st.bt_offsets[b]:st.bt_offsets[b + 1]]
+            is_tq3 = tiers == W.TIER_S
+            t0 = time.perf_counter()
+            K = OP.quantized_values(k, is_tq3, 1.0)
+            V = OP.quantized_values(v, is_tq3, 1.0)
+            o, _ = OA.decode_attention(q, K[:, None, :], V[:, None, :])
+            t_oracle += time.perf_counter() - t0
+            bytes_done += int(is_tq3.sum()) * tb + int((~is_tq3).sum()) * fb
+            got = out[l, b, h * G:(h + 1) * G].astype(np.float64)
+            worst = max(worst, float(np.abs(got - o).max()))
+            worst_rel = max(worst_rel, float(np.linalg.norm(got - o) / np.linalg.norm(o)))
+        del vals
+        torch.cuda.empty_cache()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": round(bytes_done / t_oracle / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{units} (layer, request, KV head) units of the same step, each the oracle's "
+                   f"quantise -> dequantise value path and fp64 attention for its {G} query heads over "
+                   f"all {int(st.seq_lens[0])} tokens; {t_oracle:.1f} s of CPU time"),
+        "tokens_per_s": round(w.B / (t_oracle / units * w.L * w.B * w.Hkv), 6),
+        "parity_max_abs": worst, "parity_rel_l2": worst_rel,
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    w = W.WORKLOADS[a.workload]
+    st = W.make_structure(w)
+    print(f"[bench] building {w.name} cache on the GPU ...", file=sys.stderr, flush=True)
+    r = Runner(w, st, kernel=a.kernel)
+    print(f"[bench] built in {r.build_s:.1f} s", file=sys.stderr, flush=True)
+    if a.profile_steps:
+        for _ in range(a.profile_steps):
+            r.step()
+        torch.cuda.synchronize()
+        r.time_tq3_kernel(reps=5)
+        print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
+        return
+    ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
+    print(f"[bench] timed {a.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    kv_bytes, tq3_bytes, tq3_bytes_layer = r.kv_bytes()
+    k_avg, k_med = r.time_tq3_kernel()
+    status = r.M.mkv_workspace_status(r.ws)
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode-attn KV GB/s at 2x59,008 ctx, 16 layers (tokens/s and % of MI355X HBM peak alongside)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 accumulate over fp8-e4m3 / 3-bit TQ3 cache", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": int(st.seq_lens[0]), "layers": w.L,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "page": 16,
+                   "fp8_pages_per_request": int(st.n_pages[0] - (st.tiers[:st.n_pages[0]] == 2).sum()),
+                   "tq3_pages_per_request": int((st.tiers[:st.n_pages[0]] == 2).sum()),
+                   "kernel": a.kernel, "graph": not a.no_graph},
+        "tokens_per_s": round(w.B / (ms * 1e-3), 2),
+        "kv_bytes_per_step": kv_bytes,
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "device_status": status,
+        "roofline": {"bound": "hbm", "kernel": "partial_tq3",
+                     "achieved": round(tq3_bytes_layer / (k_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(tq3_bytes_layer / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(k_avg, 5), "median_launch_ms": round(k_med, 5),
+                     "bytes_per_launch": tq3_bytes_layer},
+    }
+    if not a.no_control:
+        del r
+        torch.cuda.empty_cache()
+        print("[bench] building the all-FP8 control ...", file=sys.stderr, flush=True)
+        c = Runner(w, st, all_fp8=True, kernel=a.kernel)
+        c_ms = c.time_steps(a.steps, a.warmup, graph=not a.no_graph)
+        c_bytes = c.kv_bytes()[0]
+        result["control_all_fp8"] = {"ms_per_step": round(c_ms, 5), "kv_bytes_per_step": c_bytes,
+                                     "kv_gbs": round(c_bytes / (c_ms * 1e-3) / 1e9, 2),
+                                     "compression_vs_fp8": round(c_bytes / kv_bytes, 4),
+                                     "compression_vs_bf16": round(2 * c_bytes / kv_bytes, 4),
+                                     "throughput_vs_control": round(c_ms / ms, 4)}
+        del c
+        torch.cuda.empty_cache()
+        r = None
+    if not a.no_cpu_baseline:
+        if r is None:
+            r = Runner(w, st, kernel=a.kernel)
+            r.time_steps(1, 1, graph=not a.no_graph)
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(r, a.cpu_units)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

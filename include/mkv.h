@@ -124,9 +124,9 @@ size_t mkv_tq3_page_bytes(const mkv_layout* layout);
  *  counts: device int32[batch] or NULL; if given only the first counts[b]
  *          (<= n_new) tokens of request b are written.
  * Each byte is e4m3fn_RNE_saturating(fl32(x / scale)) with the pool's k_scale
- * or v_scale.  Target pages must be FP8 ids (checked on device: entries whose
- * id is not an FP8 slot are skipped and flagged in no status word -- the
- * caller owns the page table).  n_new in [0, 65535]. */
+ * or v_scale.  Target pages must be FP8 ids; a token whose logical page lies
+ * outside the request's block table or maps to a non-FP8 id is skipped on
+ * device (the caller owns the page table).  n_new in [0, 65535]. */
 int mkv_append(const mkv_layout* layout, const mkv_pool* pool,
                const float* k, const float* v, int32_t n_new,
                const int32_t* bt_offsets, const int32_t* bt_pages,
@@ -147,6 +147,13 @@ int mkv_append(const mkv_layout* layout, const mkv_pool* pool,
 int mkv_demote_pages(const mkv_layout* layout, const mkv_pool* pool,
                      const int32_t* src_fp8, const int32_t* dst_tq3, int32_t n,
                      void* stream);
+
+/* Demote the same pages in n_layers layers with one launch.  The tier map is
+ * shared by all layers, so a page that ages leaves FP8 in every layer at once.
+ * pools: host array of n_layers descriptors with equal n_fp8 and n_tq3. */
+int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools,
+                            int32_t n_layers, const int32_t* src_fp8,
+                            const int32_t* dst_tq3, int32_t n, void* stream);
 
 /* Workspace size for mkv_decode_attn / mkv_decode_attn_layers with at most
  * `batch` requests, `bt_capacity` block-table entries and `n_layers` layers.
@@ -171,7 +178,7 @@ int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool,
                     float* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream);
 
-/* Decode attention for n_layers layers that share one tier map and one set
+/* Decode attention for n_layers (1..64) layers that share one tier map and one set
  * of block tables (the pages' canary decodes 16 full-attention layers per
  * step).  pools: host array of n_layers descriptors with equal n_fp8, n_tq3
  * and tier.  q, out: [n_layers][batch][num_q_heads][head_dim]; lse (nullable)
@@ -182,6 +189,32 @@ int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools,
                            int32_t n_layers, const mkv_batch* batch,
                            const float* q, float sm_scale, float* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* The decode path in its separate steps, for callers that run layers one at
+ * a time (a model's layers are sequential) and reuse one plan per step:
+ *
+ * mkv_decode_plan: from the tier map (pool->tier, n_fp8, n_tq3) and the block
+ *   tables, compact each request's pages into an FP8 list and a TQ3 list and
+ *   cut them into split-K chunks sized for n_layers layers per launch.  Writes
+ *   the plan into ws (ws_bytes >= mkv_decode_workspace_bytes(layout,
+ *   batch->batch, batch->bt_capacity, n_layers)).
+ * mkv_attend_fp8 / mkv_attend_tq3: the format-specific partial-attention
+ *   kernels over the FP8 (resp. TQ3) chunks of the plan in ws, for n_layers
+ *   (<= the plan's) layers; they leave partial states (m, l, acc) in ws.
+ * mkv_merge: the log-sum-exp merge of those partial states into out / lse.
+ * q, out, lse and pools as in mkv_decode_attn_layers.  The plan must come from
+ * mkv_decode_plan with the same layout, batch descriptor and tier state;
+ * between mkv_attend_* and mkv_merge the workspace must not be reused. */
+int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                    int32_t n_layers, void* ws, size_t ws_bytes, void* stream);
+int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream);
+int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream);
+int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
+              float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Page-table gather (test support): copy the raw bytes of logical pages
  * [0, n_pages) of request b into out (device, n_pages records of

@@ -13,7 +13,8 @@ __all__ = [
     "MkvError", "Layout", "PoolDesc", "BatchDesc", "lib", "make_pool", "make_batch",
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
-    "mkv_debug_gather", "mkv_workspace_status", "mkv_status_string", "mkv_last_error",
+    "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
+    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_merge", "mkv_status_string", "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
 
@@ -62,6 +63,11 @@ def lib():
         "mkv_tq3_page_bytes": (c_sz, [P(Layout)]),
         "mkv_append": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
         "mkv_demote_pages": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_vp]),
+        "mkv_demote_pages_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, c_vp, c_vp, c_i32, c_vp]),
+        "mkv_decode_plan": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_vp, c_sz, c_vp]),
+        "mkv_attend_fp8": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
+        "mkv_attend_tq3": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
+        "mkv_merge": (c_i32, [P(Layout), c_i32, P(BatchDesc), c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_decode_workspace_bytes": (c_sz, [P(Layout), c_i32, c_i32, c_i32]),
         "mkv_decode_attn": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -154,6 +160,49 @@ def mkv_demote_pages(layout, pool, src_fp8, dst_tq3, stream=None):
                                          _ptr(src_fp8, torch.int32, "src_fp8"),
                                          _ptr(dst_tq3, torch.int32, "dst_tq3"), int(src_fp8.numel()),
                                          _stream(stream)))
+
+
+def mkv_demote_pages_layers(layout, pools, src_fp8, dst_tq3, stream=None):
+    import torch
+    arr = (PoolDesc * len(pools))(*pools)
+    return _check(lib().mkv_demote_pages_layers(ctypes.byref(_layout(layout)), arr, len(pools),
+                                                _ptr(src_fp8, torch.int32, "src_fp8"),
+                                                _ptr(dst_tq3, torch.int32, "dst_tq3"), int(src_fp8.numel()),
+                                                _stream(stream)))
+
+
+def _ws(ws):
+    return _ptr(ws, None, "ws"), int(ws.numel() * ws.element_size())
+
+
+def mkv_decode_plan(layout, pool, batch, n_layers, ws, stream=None):
+    p, n = _ws(ws)
+    return _check(lib().mkv_decode_plan(ctypes.byref(_layout(layout)), ctypes.byref(pool), ctypes.byref(batch),
+                                        int(n_layers), p, n, _stream(stream)))
+
+
+def _attend(fn, layout, pools, batch, q, sm_scale, ws, stream):
+    import torch
+    arr = (PoolDesc * len(pools))(*pools)
+    p, n = _ws(ws)
+    return _check(fn(ctypes.byref(_layout(layout)), arr, len(pools), ctypes.byref(batch),
+                     _ptr(q, torch.float32, "q"), float(sm_scale), p, n, _stream(stream)))
+
+
+def mkv_attend_fp8(layout, pools, batch, q, sm_scale, ws, stream=None):
+    return _attend(lib().mkv_attend_fp8, layout, pools, batch, q, sm_scale, ws, stream)
+
+
+def mkv_attend_tq3(layout, pools, batch, q, sm_scale, ws, stream=None):
+    return _attend(lib().mkv_attend_tq3, layout, pools, batch, q, sm_scale, ws, stream)
+
+
+def mkv_merge(layout, n_layers, batch, out, lse, ws, stream=None):
+    import torch
+    p, n = _ws(ws)
+    return _check(lib().mkv_merge(ctypes.byref(_layout(layout)), int(n_layers), ctypes.byref(batch),
+                                  _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), p, n,
+                                  _stream(stream)))
 
 
 def mkv_decode_workspace_bytes(layout, batch, bt_capacity, n_layers=1):

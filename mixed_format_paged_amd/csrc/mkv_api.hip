@@ -19,6 +19,10 @@
 
 namespace mkv {
 
+// Which partial-kernel family the decode uses: 1 = matrix cores,
+// 0 = the plain VALU kernels (kept as the measured baseline).
+static int g_partial_kind = 1;
+
 hipError_t launch_partial_mfma(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, hipStream_t stream);
@@ -85,11 +89,15 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   const int G = hq / hkv;
   const int Le = n_layers < kMaxLayers ? n_layers : kMaxLayers;
   const int per = Le * hkv;
-  s.chunks_target = per > 0 ? (kTargetItems + per - 1) / per : 1;
+  s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
   const int by_pages = (bt_capacity + kMinChunkPages - 1) / kMinChunkPages;
-  s.chunk_cap = (s.chunks_target < by_pages ? s.chunks_target : by_pages) + batch;
-  s.np_cap = 2 * s.chunk_cap;
+  // chunk tables: sized for the largest chunk count any layer count can plan
+  const int target1 = (kTargetItems + hkv - 1) / hkv;
+  s.table_cap = (target1 < by_pages ? target1 : by_pages) + batch;
+  // partial states: sized for a plan made for this layer count
+  const int chunks_l = (s.chunks_target < by_pages ? s.chunks_target : by_pages) + batch;
+  s.np_cap = 2 * chunks_l;
   s.ni_cap = 2 * s.np_cap / kMergeFan + 2;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -98,8 +106,8 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.off_req = take(sizeof(int32_t) * R_FIELDS * (size_t)(batch + 1));
   s.off_list_f = take(sizeof(int32_t) * (size_t)bt_capacity);
   s.off_list_t = take(sizeof(int32_t) * (size_t)bt_capacity);
-  s.off_chunks_f = take(sizeof(int4) * (size_t)s.chunk_cap);
-  s.off_chunks_t = take(sizeof(int4) * (size_t)s.chunk_cap);
+  s.off_chunks_f = take(sizeof(int4) * (size_t)s.table_cap);
+  s.off_chunks_t = take(sizeof(int4) * (size_t)s.table_cap);
   const size_t states = (size_t)Le * s.np_cap * hkv * G;
   const size_t inter = (size_t)Le * s.ni_cap * hkv * G;
   s.off_part_ml = take(sizeof(float) * 2 * states);
@@ -126,16 +134,12 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
   p.inter_acc = reinterpret_cast<float*>(base + s.off_inter_acc);
   p.batch = batch;
   p.bt_capacity = bt_capacity;
-  p.chunk_cap = s.chunk_cap;
+  p.table_cap = s.table_cap;
   p.np_cap = s.np_cap;
   p.ni_cap = s.ni_cap;
   p.chunks_target = s.chunks_target;
   return p;
 }
-
-// Which partial-kernel family the decode uses: 1 = matrix cores (default),
-// 0 = the plain VALU kernels (kept as the measured baseline).
-static int g_partial_kind = 0;
 
 }  // namespace mkv
 
@@ -172,19 +176,34 @@ int mkv_append(const mkv_layout* layout, const mkv_pool* pool, const float* k, c
   return e == hipSuccess ? MKV_OK : hip_fail(e, "append launch");
 }
 
-int mkv_demote_pages(const mkv_layout* layout, const mkv_pool* pool, const int32_t* src_fp8,
-                     const int32_t* dst_tq3, int32_t n, void* stream) {
+int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                            const int32_t* src_fp8, const int32_t* dst_tq3, int32_t n, void* stream) {
   Geometry g{};
   int rc = check_layout(layout, &g);
   if (rc) return rc;
-  if ((rc = check_pool(pool, &g, true, true, false))) return rc;
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(MKV_ERR_RANGE, "n_layers %d not in [1, %d]", n_layers, kMaxLayers);
+  LayerTable lt{};
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_pool(&pools[l], &g, true, true, false))) return rc;
+    if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3)
+      return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8 and n_tq3", l);
+    lt.fp8[l] = pools[l].fp8_slab;
+    lt.tq3[l] = pools[l].tq3_slab;
+    lt.k_scale[l] = pools[l].k_scale;
+    lt.v_scale[l] = pools[l].v_scale;
+  }
   if (n < 0) return fail(MKV_ERR_RANGE, "n = %d", n);
-  if ((int64_t)n * g.hkv > 0x7fffffff) return fail(MKV_ERR_RANGE, "n too large");
+  if ((int64_t)n * g.hkv * n_layers > 0x7fffffff) return fail(MKV_ERR_RANGE, "n too large");
   if (n == 0) return MKV_OK;
   if (!src_fp8 || !dst_tq3) return fail(MKV_ERR_NULL, "src_fp8 and dst_tq3 are required");
-  hipError_t e = launch_demote(g, pool->fp8_slab, pool->tq3_slab, pool->k_scale, pool->v_scale,
-                               src_fp8, dst_tq3, n, as_stream(stream));
+  hipError_t e = launch_demote(g, lt, n_layers, src_fp8, dst_tq3, n, as_stream(stream));
   return e == hipSuccess ? MKV_OK : hip_fail(e, "demote launch");
+}
+
+int mkv_demote_pages(const mkv_layout* layout, const mkv_pool* pool, const int32_t* src_fp8,
+                     const int32_t* dst_tq3, int32_t n, void* stream) {
+  return mkv_demote_pages_layers(layout, pool, 1, src_fp8, dst_tq3, n, stream);
 }
 
 size_t mkv_decode_workspace_bytes(const mkv_layout* layout, int32_t batch, int32_t bt_capacity,
@@ -194,57 +213,144 @@ size_t mkv_decode_workspace_bytes(const mkv_layout* layout, int32_t batch, int32
   return workspace_sizes(g.hq, g.hkv, g.d, batch, bt_capacity, n_layers).total;
 }
 
+namespace {
+
+// Validation shared by every decode entry point.  `pools` may be NULL for
+// mkv_merge (which reads only the workspace).
+int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, void* ws, size_t ws_bytes, Geometry* g, Plan* plan,
+                   LayerTable* lt) {
+  int rc = check_layout(layout, g);
+  if (rc) return rc;
+  if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(MKV_ERR_RANGE, "n_layers %d not in [1, %d]", n_layers, kMaxLayers);
+  if (pools) {
+    for (int l = 0; l < n_layers; ++l) {
+      if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
+      if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
+        return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
+      if (lt) {
+        lt->fp8[l] = pools[l].fp8_slab;
+        lt->tq3[l] = pools[l].tq3_slab;
+        lt->k_scale[l] = pools[l].k_scale;
+        lt->v_scale[l] = pools[l].v_scale;
+      }
+    }
+  }
+  const int B = batch->batch;
+  if (B < 0 || batch->bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", B, batch->bt_capacity);
+  if (B > 0 && (!batch->bt_offsets || !batch->seq_lens || (!batch->bt_pages && batch->bt_capacity > 0)))
+    return fail(MKV_ERR_NULL, "bt_offsets, bt_pages and seq_lens are required");
+  if (B > 0 && !ws) return fail(MKV_ERR_NULL, "ws is required");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
+  const WsSizes s = workspace_sizes(g->hq, g->hkv, g->d, B, batch->bt_capacity, n_layers);
+  if (B > 0 && ws_bytes < s.total) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, s.total);
+  *plan = plan_from_ws(ws, s, B, batch->bt_capacity);
+  return MKV_OK;
+}
+
+int check_qo(const float* q, const float* out, const float* lse, float sm_scale, bool need_q, bool need_out) {
+  if (need_q) {
+    if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(MKV_ERR_RANGE, "sm_scale must be finite and > 0");
+    if (!q) return fail(MKV_ERR_NULL, "q is required");
+    if (!aligned16(q)) return fail(MKV_ERR_ALIGN, "q must be 16-byte aligned");
+  }
+  if (need_out) {
+    if (!out) return fail(MKV_ERR_NULL, "out is required");
+    if (!aligned16(out) || (lse && !aligned16(lse))) return fail(MKV_ERR_ALIGN, "out and lse must be 16-byte aligned");
+  }
+  return MKV_OK;
+}
+
+int run_attend(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers, const Plan& plan,
+               const float* q, float sm_scale, int batch, hipStream_t st) {
+  const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
+  const size_t q_ls = (size_t)batch * g.hq * g.d;
+  hipError_t e = g_partial_kind ? launch_partial_mfma(tq3, g, lt, n_layers, q, q_ls, qscale, plan, st)
+                                : launch_partial_valu(tq3, g, lt, n_layers, q, q_ls, qscale, plan, st);
+  return e == hipSuccess ? MKV_OK : hip_fail(e, tq3 ? "TQ3 partial launch" : "FP8 partial launch");
+}
+
+int run_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse, int batch,
+              hipStream_t st) {
+  hipError_t e = launch_merge(g, n_layers, plan, out, lse, (size_t)batch * g.hq * g.d,
+                              (size_t)batch * g.hq, st);
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "merge launch");
+}
+
+}  // namespace
+
+int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                    int32_t n_layers, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  int rc = prepare_decode(layout, pool, 1, batch, ws, ws_bytes, &g, &plan, nullptr);
+  if (rc) return rc;
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(MKV_ERR_RANGE, "n_layers %d not in [1, %d]", n_layers, kMaxLayers);
+  // size the plan (chunks per format) for n_layers layers per launch
+  const WsSizes s = workspace_sizes(g.hq, g.hkv, g.d, batch->batch, batch->bt_capacity, n_layers);
+  if (batch->batch > 0 && ws_bytes < s.total) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, s.total);
+  if (batch->batch == 0) return MKV_OK;
+  plan = plan_from_ws(ws, s, batch->batch, batch->bt_capacity);
+  hipError_t e = launch_plan(g, pool->tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "plan launch");
+}
+
+static int attend_entry(bool tq3, const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                        const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  LayerTable lt{};
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt);
+  if (rc) return rc;
+  if ((rc = check_qo(q, nullptr, nullptr, sm_scale, true, false))) return rc;
+  if (batch->batch == 0) return MKV_OK;
+  return run_attend(tq3, g, lt, n_layers, plan, q, sm_scale, batch->batch, as_stream(stream));
+}
+
+int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return attend_entry(false, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
+}
+
+int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return attend_entry(true, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
+}
+
+int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
+              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  int rc = prepare_decode(layout, nullptr, n_layers, batch, ws, ws_bytes, &g, &plan, nullptr);
+  if (rc) return rc;
+  if ((rc = check_qo(nullptr, out, lse, 1.0f, false, true))) return rc;
+  if (batch->batch == 0) return MKV_OK;
+  return run_merge(g, n_layers, plan, out, lse, batch->batch, as_stream(stream));
+}
+
 int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                            const mkv_batch* batch, const float* q, float sm_scale, float* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
-  int rc = check_layout(layout, &g);
+  Plan plan{};
+  LayerTable lt{};
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt);
   if (rc) return rc;
-  if (!pools || !batch) return fail(MKV_ERR_NULL, "pools and batch are required");
-  if (n_layers < 1) return fail(MKV_ERR_RANGE, "n_layers = %d", n_layers);
-  for (int l = 0; l < n_layers; ++l) {
-    if ((rc = check_pool(&pools[l], &g, true, true, true))) return rc;
-    if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
-      return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
-  }
+  if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
   const int B = batch->batch;
-  if (B < 0 || batch->bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", B, batch->bt_capacity);
-  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(MKV_ERR_RANGE, "sm_scale must be finite and > 0");
   if (B == 0) return MKV_OK;
-  if (!batch->bt_offsets || !batch->seq_lens || (!batch->bt_pages && batch->bt_capacity > 0))
-    return fail(MKV_ERR_NULL, "bt_offsets, bt_pages and seq_lens are required");
-  if (!q || !out || !ws) return fail(MKV_ERR_NULL, "q, out and ws are required");
-  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse))) return fail(MKV_ERR_ALIGN, "q, out, lse must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
-  const WsSizes s = workspace_sizes(g.hq, g.hkv, g.d, B, batch->bt_capacity, n_layers);
-  if (ws_bytes < s.total) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, s.total);
-  const Plan plan = plan_from_ws(ws, s, B, batch->bt_capacity);
   hipStream_t st = as_stream(stream);
   hipError_t e = launch_plan(g, pools[0].tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, st);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
-  const float qscale = sm_scale * 1.4426950408889634f;       // scores in log2 units
-  const size_t q_ls = (size_t)B * g.hq * g.d;
-  const size_t lse_ls = (size_t)B * g.hq;
-  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
-    const int nl = (n_layers - l0) < kMaxLayers ? (n_layers - l0) : kMaxLayers;
-    LayerTable lt{};
-    for (int l = 0; l < nl; ++l) {
-      lt.fp8[l] = pools[l0 + l].fp8_slab;
-      lt.tq3[l] = pools[l0 + l].tq3_slab;
-      lt.k_scale[l] = pools[l0 + l].k_scale;
-      lt.v_scale[l] = pools[l0 + l].v_scale;
-    }
-    const float* ql = q + (size_t)l0 * q_ls;
-    for (int fmt = 0; fmt < 2; ++fmt) {
-      e = g_partial_kind ? launch_partial_mfma(fmt == 1, g, lt, nl, ql, q_ls, qscale, plan, st)
-                         : launch_partial_valu(fmt == 1, g, lt, nl, ql, q_ls, qscale, plan, st);
-      if (e != hipSuccess) return hip_fail(e, fmt ? "TQ3 partial launch" : "FP8 partial launch");
-    }
-    e = launch_merge(g, nl, plan, out + (size_t)l0 * q_ls, lse ? lse + (size_t)l0 * lse_ls : nullptr,
-                     q_ls, lse_ls, st);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
-  }
-  return MKV_OK;
+  if ((rc = run_attend(false, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
+  if ((rc = run_attend(true, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
+  return run_merge(g, n_layers, plan, out, lse, B, st);
 }
 
 int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,

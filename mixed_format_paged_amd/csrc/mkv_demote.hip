@@ -1,7 +1,7 @@
 // mkv_demote.hip -- FP8 -> TQ3 page demotion (the pack).
 //
 // "Older non-anchor pages move to packed TQ3" (arXiv 2608.23834, page 1,
-// Abstract).  One workgroup per (page, KV head):
+// Abstract).  One workgroup per (layer, page, KV head):
 //   phase 1: one thread per (K/V, token, 32-channel group) decodes the FP8
 //            bytes (x = fl32(decode(e) * scale)), takes the absmax, forms the
 //            fp16 scale s = fp16_RNE(fl32(a / 3)) and the codes u = q + 4,
@@ -16,14 +16,18 @@ namespace mkv {
 
 template <int D>
 __global__ void __launch_bounds__(256) demote_kernel(
-    const uint8_t* __restrict__ fp8_slab, uint8_t* __restrict__ tq3_slab, int n_fp8, int n_tq3,
-    int hkv, float k_scale, float v_scale, const int32_t* __restrict__ src,
+    LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
     const int32_t* __restrict__ dst) {
   constexpr int G = D / 32;
   __shared__ uint8_t codes[2][kPage][D];
   __shared__ uint16_t scales[2][kPage][G];
-  const int page = blockIdx.x / hkv;
-  const int h = blockIdx.x - page * hkv;
+  const int layer = blockIdx.x / (n * hkv);
+  const int rest = blockIdx.x - layer * n * hkv;
+  const int page = rest / hkv;
+  const int h = rest - page * hkv;
+  const uint8_t* __restrict__ fp8_slab = lt.fp8[layer];
+  uint8_t* __restrict__ tq3_slab = lt.tq3[layer];
+  const float k_scale = lt.k_scale[layer], v_scale = lt.v_scale[layer];
   const int s_id = src[page];
   const int d_id = dst[page];
   if (s_id < 0 || s_id >= n_fp8 || d_id < n_fp8 || d_id >= n_fp8 + n_tq3) return;   // uniform
@@ -102,17 +106,16 @@ __global__ void __launch_bounds__(256) demote_kernel(
   }
 }
 
-hipError_t launch_demote(const Geometry& g, const uint8_t* fp8_slab, uint8_t* tq3_slab,
-                         float k_scale, float v_scale, const int32_t* src, const int32_t* dst,
-                         int n, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  dim3 grid(n * g.hkv);
+hipError_t launch_demote(const Geometry& g, const LayerTable& lt, int n_layers,
+                         const int32_t* src, const int32_t* dst, int n, hipStream_t stream) {
+  if (n == 0 || n_layers == 0) return hipSuccess;
+  dim3 grid(n_layers * n * g.hkv);
   if (g.d == 256)
-    hipLaunchKernelGGL(demote_kernel<256>, grid, dim3(256), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
-                       g.n_tq3, g.hkv, k_scale, v_scale, src, dst);
+    hipLaunchKernelGGL(demote_kernel<256>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
+                       g.hkv, src, dst);
   else
-    hipLaunchKernelGGL(demote_kernel<128>, grid, dim3(256), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
-                       g.n_tq3, g.hkv, k_scale, v_scale, src, dst);
+    hipLaunchKernelGGL(demote_kernel<128>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
+                       g.hkv, src, dst);
   return hipGetLastError();
 }
 

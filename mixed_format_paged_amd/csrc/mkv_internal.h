@@ -21,6 +21,7 @@ constexpr int kTargetItems = 512;     // split-K work items (workgroups) aimed f
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMergeFan = 32;         // partials merged per first-level merge item
 constexpr int kMaxG = 8;              // query heads per KV head supported
+constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4;
 
 // Per-request plan fields, each an int32[batch + 1] row of req[].
 enum ReqField {
@@ -65,16 +66,19 @@ struct Plan {
   float* inter_acc;     // [L][ni_cap][Hkv][G][d]
   int batch;
   int bt_capacity;
-  int chunk_cap;        // per format
-  int np_cap;           // partials per layer
-  int ni_cap;           // intermediates per layer
-  int chunks_target;    // chunks aimed for per format
+  int table_cap;        // chunk-table entries per format (independent of the layer count)
+  int np_cap;           // partial states per layer in this call's workspace view
+  int ni_cap;           // intermediate states per layer
+  int chunks_target;    // chunks aimed for per format (set by the planning call)
 };
 
+// Workspace layout.  The plan part (status .. chunk tables) has offsets that do
+// not depend on the layer count, so a plan made for L layers can be consumed
+// by calls for <= L layers; the state part scales with the layer count.
 struct WsSizes {
   size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
   size_t off_part_ml, off_part_acc, off_inter_ml, off_inter_acc, total;
-  int chunk_cap, np_cap, ni_cap, chunks_target;
+  int table_cap, np_cap, ni_cap, chunks_target;
 };
 
 WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers);
@@ -82,8 +86,8 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity);
 
 // Per-launch layer table (passed by value as a kernel argument).
 struct LayerTable {
-  const uint8_t* fp8[kMaxLayers];
-  const uint8_t* tq3[kMaxLayers];
+  uint8_t* fp8[kMaxLayers];
+  uint8_t* tq3[kMaxLayers];
   float k_scale[kMaxLayers];
   float v_scale[kMaxLayers];
 };
@@ -98,9 +102,8 @@ hipError_t launch_append(const Geometry& g, uint8_t* fp8_slab, float k_scale, fl
                          const float* k, const float* v, int n_new, const int32_t* bt_offsets,
                          const int32_t* bt_pages, const int32_t* pos, const int32_t* counts,
                          int batch, hipStream_t stream);
-hipError_t launch_demote(const Geometry& g, const uint8_t* fp8_slab, uint8_t* tq3_slab,
-                         float k_scale, float v_scale, const int32_t* src, const int32_t* dst,
-                         int n, hipStream_t stream);
+hipError_t launch_demote(const Geometry& g, const LayerTable& lt, int n_layers,
+                         const int32_t* src, const int32_t* dst, int n, hipStream_t stream);
 hipError_t launch_gather(const Geometry& g, const uint8_t* fp8_slab, const uint8_t* tq3_slab,
                          const int32_t* bt_offsets, const int32_t* bt_pages, int b, int n_pages,
                          uint8_t* out, hipStream_t stream);

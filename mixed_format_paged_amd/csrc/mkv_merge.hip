@@ -131,8 +131,10 @@ __global__ void __launch_bounds__(256) merge1_kernel(int n_layers, int hkv, int 
     float* lse_row = lse ? lse + layer * lse_ls + (size_t)b * hq + (size_t)h * G : nullptr;
     const float* ml = plan.part_ml + (size_t)layer * plan.np_cap * hkv * G * 2;
     const float* acc = plan.part_acc + (size_t)layer * plan.np_cap * hkv * G * D;
-    if (inval[b] || np == 0) {
-      write_special<D>(out_row, lse_row, G, inval[b] != 0);
+    const bool over = p0 + np > plan.np_cap || (np > kMergeFan && ioff[b] + k >= plan.ni_cap);
+    if (over && threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
+    if (inval[b] || np == 0 || over) {
+      write_special<D>(out_row, lse_row, G, inval[b] != 0 || over);
     } else if (np <= kMergeFan) {
       merge_states<D>(ml, acc, p0, np, hkv, h, G, out_row, lse_row, nullptr, nullptr, w, sM, sL);
     } else {
@@ -163,8 +165,9 @@ __global__ void __launch_bounds__(256) merge2_kernel(int n_layers, int hkv, int 
     const int h = (int)((item / B) % hkv);
     const int layer = (int)(item / ((long)B * hkv));
     const int np = poff[b + 1] - poff[b];
-    if (inval[b] || np <= kMergeFan) continue;                // uniform per block
     const int cnt = m1off[b + 1] - m1off[b];
+    if (inval[b] || np <= kMergeFan || poff[b + 1] > plan.np_cap || ioff[b] + cnt > plan.ni_cap)
+      continue;                                               // uniform per block
     float* out_row = out + layer * out_ls + ((size_t)b * hq + (size_t)h * G) * D;
     float* lse_row = lse ? lse + layer * lse_ls + (size_t)b * hq + (size_t)h * G : nullptr;
     merge_states<D>(plan.inter_ml + (size_t)layer * plan.ni_cap * hkv * G * 2,

@@ -50,6 +50,10 @@ __global__ void __launch_bounds__(256) partial_valu_kernel(
     const int layer = (int)(item / ((long)hkv * n_chunks));
     const int4 cd = chunks[chunk];
     const int b = cd.x, start = cd.y, count = cd.z & 0xffff, last_tok = cd.z >> 16, pidx = cd.w;
+    if (pidx >= plan.np_cap) {                 // plan made for more layers than this call
+      if (tid == 0) atomicOr(plan.status, kDevBadSeqLen);
+      continue;
+    }
     const float* qb = q + layer * q_layer_stride + ((size_t)b * hq + (size_t)h * G) * D;
     for (int idx = tid; idx < G * D; idx += 256) Qs[idx / D][idx % D] = qb[idx] * qscale;
     if (tid < G) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
@@ -131,7 +135,7 @@ static int grid_for(int items_cap) { return items_cap < 2048 ? (items_cap > 0 ? 
 hipError_t launch_partial_valu(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, hipStream_t stream) {
-  const dim3 grid(grid_for(n_layers * g.hkv * plan.chunk_cap)), block(256);
+  const dim3 grid(grid_for(n_layers * g.hkv * plan.np_cap / 2)), block(256);
   if (tq3) {
     if (g.d == 256)
       hipLaunchKernelGGL((partial_valu_kernel<true, 256>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q, q_layer_stride, qscale, plan);

@@ -21,8 +21,6 @@ namespace mkv {
 
 namespace {
 
-constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4;
-
 // Exclusive scan of one int per thread over a block of BLOCK threads.
 template <int BLOCK>
 __device__ int block_exclusive_scan(int v, int* total, int* sh) {
@@ -167,7 +165,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     carry_f += tf; carry_t += tt; carry_p += tp; carry_m += tm; carry_i += ti;
   }
   // Chunk counts cannot exceed the capacity for valid CSR offsets; guard anyway.
-  const bool over = carry_f > plan.chunk_cap || carry_t > plan.chunk_cap;
+  const bool over = carry_f > plan.table_cap || carry_t > plan.table_cap;
   if (over) { carry_f = 0; carry_t = 0; carry_p = 0; }
   if (tid == 0) {
     plan.status[0] = status | (over ? kDevBadSeqLen : 0);
@@ -197,7 +195,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     const int pp = fmt ? ppt : ppf;
     const int* cnt = fmt ? nt_row : nf_row;
     int4* out = fmt ? plan.chunks_t : plan.chunks_f;
-    for (int c = tid; c < total && c < plan.chunk_cap; c += 1024) {
+    for (int c = tid; c < total && c < plan.table_cap; c += 1024) {
       int lo = 0, hi = B - 1;                 // last b with co[b] <= c
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;

@@ -21,6 +21,14 @@ from gpu_util import compare, oracle_side
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["mfma", "valu"])
+def kind(request):
+    """Run a decode test with the matrix-core kernels and with the VALU baseline."""
+    M.set_partial_kind(1 if request.param == "mfma" else 0)
+    yield request.param
+    M.set_partial_kind(1)
+
+
 def _decode(dw, sm_scale=None):
     w = dw.w
     L = len(dw.layers)
@@ -93,7 +101,7 @@ def test_demote_bitexact_random_bytes(d):
         assert np.array_equal(got, pool.tq3), (ks, vs, np.argwhere(got != pool.tq3)[:5])
 
 
-def test_build_gather_and_decode_tiny():
+def test_build_gather_and_decode_tiny(kind):
     w = W.WORKLOADS["tiny-1x1024-d128"]
     st, dw, ref = _both(w)
     pool, bt, o_ref, lse_ref = ref[0]
@@ -124,7 +132,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("name,w", SMALL, ids=[s[0] for s in SMALL])
-def test_decode_parity_small(name, w):
+def test_decode_parity_small(name, w, kind):
     st, dw, ref = _both(w)
     dw.step_demote()
     assert np.array_equal(dw.bt.cpu().numpy(), ref[0][1])
@@ -134,7 +142,7 @@ def test_decode_parity_small(name, w):
         compare(out[li], o_ref, lse[li], lse_ref, f"{name} layer {li}")
 
 
-def test_multilayer_equals_per_layer_and_is_deterministic():
+def test_multilayer_equals_per_layer_and_is_deterministic(kind):
     w = W.scaled(W.WORKLOADS["canary-2x59008-16L"], L=3, lengths=("fixed", 900), recent_tokens=128)
     st = W.make_structure(w)
     dw = DeviceWorkload(w, st, "cuda")
@@ -154,7 +162,7 @@ def test_multilayer_equals_per_layer_and_is_deterministic():
         compare(o1.cpu().numpy(), out[li].astype(np.float64), None, None, f"layer {li}")
 
 
-def test_device_data_errors_flag_and_nan():
+def test_device_data_errors_flag_and_nan(kind):
     w = W.scaled(W.WORKLOADS["batch-8x16384"], B=4, lengths=("fixed", 300), recent_tokens=64)
     st = W.make_structure(w)
     dw = DeviceWorkload(w, st, "cuda")
