@@ -103,9 +103,7 @@ class Runner:
         M.mkv_decode_plan(lay, dw.cache.pools[0], bat, 1, ws)
         for l in range(self.w.L):
             M.mkv_append(lay, dw.cache.pools[l], self.k_new[l], self.v_new[l], dw.bt_offsets, dw.bt, self.pos)
-            M.mkv_attend_fp8(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, ws)
-            M.mkv_attend_tq3(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, ws)
-            M.mkv_merge(lay, 1, bat, self.out[l], self.lse[l], ws)
+            M.mkv_attend(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, self.out[l], self.lse[l], ws)
         if self.dem_src.numel():
             M.mkv_demote_pages_layers(lay, dw.cache.pools, self.dem_src, self.dem_dst)
 
@@ -145,17 +143,20 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def time_tq3_kernel(self, reps=20):
-        """Average duration of one TQ3 partial launch (layer 0), HIP events on its stream."""
+    def time_attend_kernel(self, reps=20):
+        """Average duration of one fused attend launch (layer 0: FP8 + TQ3 partials
+        and the merge), HIP events on the stream it is launched on."""
         torch, M = self.torch, self.M
         M.mkv_decode_plan(self.layout, self.dw.cache.pools[0], self.batch, 1, self.ws)
+        run = lambda: M.mkv_attend(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale,
+                                   self.out[0], self.lse[0], self.ws)
         for _ in range(3):
-            M.mkv_attend_tq3(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale, self.ws)
+            run()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in evs:
             a.record()
-            M.mkv_attend_tq3(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale, self.ws)
+            run()
             b.record()
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in evs)
@@ -237,13 +238,14 @@ def main():
         for _ in range(a.profile_steps):
             r.step()
         torch.cuda.synchronize()
-        r.time_tq3_kernel(reps=5)
+        r.time_attend_kernel(reps=5)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
     print(f"[bench] timed {a.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
     kv_bytes, tq3_bytes, tq3_bytes_layer = r.kv_bytes()
-    k_avg, k_med = r.time_tq3_kernel()
+    layer_bytes = kv_bytes // w.L
+    k_avg, k_med = r.time_attend_kernel()
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -260,11 +262,11 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "device_status": status,
-        "roofline": {"bound": "hbm", "kernel": "partial_tq3",
-                     "achieved": round(tq3_bytes_layer / (k_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(tq3_bytes_layer / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "attend (FP8 + TQ3 partials + merge, one layer)",
+                     "achieved": round(layer_bytes / (k_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(layer_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_launch_ms": round(k_avg, 5), "median_launch_ms": round(k_med, 5),
-                     "bytes_per_launch": tq3_bytes_layer},
+                     "bytes_per_launch": layer_bytes},
     }
     if not a.no_control:
         del r

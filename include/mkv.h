@@ -216,6 +216,15 @@ int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
 int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
               float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* mkv_attend: mkv_attend_fp8 + mkv_attend_tq3 + mkv_merge with the two
+ * partial kernels in one launch: the FP8 and TQ3 work items of the plan in ws
+ * run side by side in one grid (each item runs its own format's kernel code),
+ * then the merge.  Same arguments and plan requirements as the separate calls;
+ * results are identical to them bit for bit. */
+int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+               const mkv_batch* batch, const float* q, float sm_scale, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream);
+
 /* Page-table gather (test support): copy the raw bytes of logical pages
  * [0, n_pages) of request b into out (device, n_pages records of
  * mkv_fp8_page_bytes() bytes; a TQ3 page fills the first mkv_tq3_page_bytes()

@@ -13,7 +13,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/mkv.h"
+#include "mkv.h"
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -22,10 +22,6 @@ namespace mkv {
 // Which partial-kernel family the decode uses: 1 = matrix cores,
 // 0 = the plain VALU kernels (kept as the measured baseline).
 static int g_partial_kind = 1;
-
-hipError_t launch_partial_mfma(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
-                               const float* q, size_t q_layer_stride, float qscale,
-                               const Plan& plan, hipStream_t stream);
 
 namespace {
 
@@ -91,14 +87,18 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   const int per = Le * hkv;
   s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
+  // chunks per format <= min(pages / kMinChunkPages, max(target, pages / kMaxChunkPages)) + batch
   const int by_pages = (bt_capacity + kMinChunkPages - 1) / kMinChunkPages;
+  const int by_max = (bt_capacity + kMaxChunkPages - 1) / kMaxChunkPages;
+  auto chunk_bound = [&](int target) {
+    const int t = target > by_max ? target : by_max;
+    return (t < by_pages ? t : by_pages) + batch;
+  };
   // chunk tables: sized for the largest chunk count any layer count can plan
-  const int target1 = (kTargetItems + hkv - 1) / hkv;
-  s.table_cap = (target1 < by_pages ? target1 : by_pages) + batch;
+  s.table_cap = chunk_bound((kTargetItems + hkv - 1) / hkv);
   // partial states: sized for a plan made for this layer count
-  const int chunks_l = (s.chunks_target < by_pages ? s.chunks_target : by_pages) + batch;
+  const int chunks_l = chunk_bound(s.chunks_target);
   s.np_cap = 2 * chunks_l;
-  s.ni_cap = 2 * s.np_cap / kMergeFan + 2;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   s.off_status = take(sizeof(int32_t));
@@ -109,11 +109,8 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.off_chunks_f = take(sizeof(int4) * (size_t)s.table_cap);
   s.off_chunks_t = take(sizeof(int4) * (size_t)s.table_cap);
   const size_t states = (size_t)Le * s.np_cap * hkv * G;
-  const size_t inter = (size_t)Le * s.ni_cap * hkv * G;
   s.off_part_ml = take(sizeof(float) * 2 * states);
   s.off_part_acc = take(sizeof(float) * d * states);
-  s.off_inter_ml = take(sizeof(float) * 2 * inter);
-  s.off_inter_acc = take(sizeof(float) * d * inter);
   s.total = o;
   return s;
 }
@@ -130,13 +127,10 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
   p.chunks_t = reinterpret_cast<int4*>(base + s.off_chunks_t);
   p.part_ml = reinterpret_cast<float*>(base + s.off_part_ml);
   p.part_acc = reinterpret_cast<float*>(base + s.off_part_acc);
-  p.inter_ml = reinterpret_cast<float*>(base + s.off_inter_ml);
-  p.inter_acc = reinterpret_cast<float*>(base + s.off_inter_acc);
   p.batch = batch;
   p.bt_capacity = bt_capacity;
   p.table_cap = s.table_cap;
   p.np_cap = s.np_cap;
-  p.ni_cap = s.ni_cap;
   p.chunks_target = s.chunks_target;
   return p;
 }
@@ -266,7 +260,7 @@ int run_attend(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers, 
                const float* q, float sm_scale, int batch, hipStream_t st) {
   const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
   const size_t q_ls = (size_t)batch * g.hq * g.d;
-  hipError_t e = g_partial_kind ? launch_partial_mfma(tq3, g, lt, n_layers, q, q_ls, qscale, plan, st)
+  hipError_t e = g_partial_kind ? launch_partial_mfma(tq3 ? 1 : 0, g, lt, n_layers, q, q_ls, qscale, plan, st)
                                 : launch_partial_valu(tq3, g, lt, n_layers, q, q_ls, qscale, plan, st);
   return e == hipSuccess ? MKV_OK : hip_fail(e, tq3 ? "TQ3 partial launch" : "FP8 partial launch");
 }
@@ -333,6 +327,38 @@ int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch
   return run_merge(g, n_layers, plan, out, lse, batch->batch, as_stream(stream));
 }
 
+namespace {
+
+int run_fused(const Geometry& g, const LayerTable& lt, int n_layers, const Plan& plan, const float* q,
+              float sm_scale, float* out, float* lse, int B, hipStream_t st) {
+  if (!g_partial_kind) {                       // the VALU baseline: separate launches
+    int rc;
+    if ((rc = run_attend(false, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
+    if ((rc = run_attend(true, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
+    return run_merge(g, n_layers, plan, out, lse, B, st);
+  }
+  const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
+  hipError_t e = launch_partial_mfma(2, g, lt, n_layers, q, (size_t)B * g.hq * g.d, qscale, plan, st);
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return run_merge(g, n_layers, plan, out, lse, B, st);
+}
+
+}  // namespace
+
+int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+               const mkv_batch* batch, const float* q, float sm_scale, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  LayerTable lt{};
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt);
+  if (rc) return rc;
+  if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
+  if (batch->batch == 0) return MKV_OK;
+  return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, batch->batch, as_stream(stream));
+}
+
 int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                            const mkv_batch* batch, const float* q, float sm_scale, float* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -348,9 +374,7 @@ int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int3
   hipStream_t st = as_stream(stream);
   hipError_t e = launch_plan(g, pools[0].tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, st);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
-  if ((rc = run_attend(false, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
-  if ((rc = run_attend(true, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
-  return run_merge(g, n_layers, plan, out, lse, B, st);
+  return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, B, st);
 }
 
 int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,

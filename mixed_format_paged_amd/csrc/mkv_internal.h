@@ -19,7 +19,7 @@ namespace mkv {
 constexpr int kMaxLayers = 64;        // layers covered by one launch
 constexpr int kTargetItems = 512;     // split-K work items (workgroups) aimed for per format
 constexpr int kMinChunkPages = 4;     // smallest chunk
-constexpr int kMergeFan = 32;         // partials merged per first-level merge item
+constexpr int kMaxChunkPages = 1024;  // largest chunk (a workgroup stages its page ids in LDS)
 constexpr int kMaxG = 8;              // query heads per KV head supported
 constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4;
 
@@ -33,8 +33,6 @@ enum ReqField {
   R_CF_OFF,      // first FP8 chunk of the request (exclusive prefix; [batch] = total)
   R_CT_OFF,      // first TQ3 chunk of the request
   R_POFF,        // first partial index of the request (per layer)
-  R_M1OFF,       // first first-level merge item
-  R_IOFF,        // first intermediate (second level) slot
   R_FIELDS
 };
 
@@ -42,8 +40,6 @@ enum TotalField {
   T_NCF = 0,     // FP8 chunks in total
   T_NCT,         // TQ3 chunks in total
   T_NP,          // partials per layer
-  T_NM1,         // first-level merge items per (layer, KV head)
-  T_NI,          // intermediate partials per layer
   T_PPF,         // pages per FP8 chunk
   T_PPT,         // pages per TQ3 chunk
   T_FIELDS = 16
@@ -62,13 +58,10 @@ struct Plan {
   int4* chunks_t;       // [chunk_cap]
   float* part_ml;       // [L][np_cap][Hkv][G][2]  (m in log2 units, l)
   float* part_acc;      // [L][np_cap][Hkv][G][d]
-  float* inter_ml;      // [L][ni_cap][Hkv][G][2]
-  float* inter_acc;     // [L][ni_cap][Hkv][G][d]
   int batch;
   int bt_capacity;
   int table_cap;        // chunk-table entries per format (independent of the layer count)
   int np_cap;           // partial states per layer in this call's workspace view
-  int ni_cap;           // intermediate states per layer
   int chunks_target;    // chunks aimed for per format (set by the planning call)
 };
 
@@ -77,8 +70,8 @@ struct Plan {
 // by calls for <= L layers; the state part scales with the layer count.
 struct WsSizes {
   size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
-  size_t off_part_ml, off_part_acc, off_inter_ml, off_inter_acc, total;
-  int table_cap, np_cap, ni_cap, chunks_target;
+  size_t off_part_ml, off_part_acc, total;
+  int table_cap, np_cap, chunks_target;
 };
 
 WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers);
@@ -113,6 +106,11 @@ hipError_t launch_plan(const Geometry& g, const uint8_t* tier, const int32_t* bt
 // Partial kernels: `tq3` selects the format.  q is [layers][batch][hq][d];
 // qscale = sm_scale * log2(e) (scores are kept in log2 units).
 hipError_t launch_partial_valu(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
+                               const float* q, size_t q_layer_stride, float qscale,
+                               const Plan& plan, hipStream_t stream);
+// Matrix-core partial kernels: which = 0 FP8 items, 1 TQ3 items, 2 both
+// formats' items in one launch.
+hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, hipStream_t stream);
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out,

@@ -35,9 +35,14 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr float kRescale = 8.0f;        // log2 units
+// k-slot -> channel offset inside a TQ3 triple, in the order one triple
+// decodes into fp16 pairs: (0,6) (1,7) (3,2) (4,5)
+constexpr int kTq3SlotChannel[8] = {0, 6, 1, 7, 3, 2, 4, 5};
 
 __device__ inline h2 u2h(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ inline uint32_t h2u(h2 h) { return __builtin_bit_cast(uint32_t, h); }
@@ -55,94 +60,60 @@ __device__ inline void triple_words(const uint32_t (&c)[NW], int o, uint32_t& X,
   const uint32_t lo = c[i];
   const uint32_t hi = (s + 2 >= 4) ? c[i + 1] : lo;
   const uint32_t b0 = s, b1 = s + 1, b2 = s + 2;
-  X = __builtin_amdgcn_perm(hi, lo, b0 | (b1 << 8) | (b2 << 16) | (b2 << 24));
+  X = (s == 0) ? lo : __builtin_amdgcn_perm(hi, lo, b0 | (b1 << 8) | (b2 << 16) | (b2 << 24));
   Y = __builtin_amdgcn_perm(hi, lo, b1 | (b2 << 8) | (b0 << 16) | (b1 << 24));
   W = __builtin_amdgcn_perm(hi, lo, b1 | (b2 << 8) | (b1 << 16) | (b2 << 24));
+}
+
+// (x & mask) | c in one VOP3 instruction.  Both constants come from
+// registers: gfx9-class VOP3 encodings take no literal operand and at most
+// one scalar, so the compiler would otherwise emit a separate AND and OR.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(c));
+  return r;
 }
 
 // One triple -> four fp16 pairs of (u - 4):
 //   r[0] = (slot0, slot6)  r[1] = (slot1, slot7)  r[2] = (slot3, slot2)  r[3] = (slot4, slot5)
 // Each code is dropped into the mantissa of fp16 1024.0 at bit offset j
 // (value 1024 + u 2^j) and one packed fma maps it exactly to u - 4.
-__device__ inline void decode_triple(uint32_t X, uint32_t Y, uint32_t W, h2 (&r)[4]) {
-  const uint32_t one024 = 0x64006400u;
-  r[0] = __builtin_elementwise_fma(u2h((X & 0x001C0007u) | one024), mkh2(1.0f, 0.25f), mkh2(-1028.0f, -260.0f));
-  r[1] = __builtin_elementwise_fma(u2h((X & 0x00E00038u) | one024), mkh2(0.125f, 0.03125f), mkh2(-132.0f, -36.0f));
-  r[2] = __builtin_elementwise_fma(u2h((Y & 0x01C0000Eu) | one024), mkh2(0.5f, 0.015625f), mkh2(-516.0f, -20.0f));
-  r[3] = __builtin_elementwise_fma(u2h((W & 0x03800070u) | one024), mkh2(0.0625f, 0.0078125f), mkh2(-68.0f, -12.0f));
+__device__ inline void decode_triple(uint32_t X, uint32_t Y, uint32_t W, uint32_t one024, h2 (&r)[4]) {
+  r[0] = __builtin_elementwise_fma(u2h(and_or(X, 0x001C0007u, one024)), mkh2(1.0f, 0.25f), mkh2(-1028.0f, -260.0f));
+  r[1] = __builtin_elementwise_fma(u2h(and_or(X, 0x00E00038u, one024)), mkh2(0.125f, 0.03125f), mkh2(-132.0f, -36.0f));
+  r[2] = __builtin_elementwise_fma(u2h(and_or(Y, 0x01C0000Eu, one024)), mkh2(0.5f, 0.015625f), mkh2(-516.0f, -20.0f));
+  r[3] = __builtin_elementwise_fma(u2h(and_or(W, 0x03800070u, one024)), mkh2(0.0625f, 0.0078125f), mkh2(-68.0f, -12.0f));
 }
 
-// Per-lane page data.
-template <bool TQ3, int D>
-struct PageData;
-
+// Staging unit: the bytes a wave moves to its LDS slot in one step.  For TQ3
+// a unit is one page-head (14 d bytes: codes and scales of one KV head); for
+// FP8 a page-head (32 d bytes) is two units, its K half and its V half.  Both
+// fit a slot of d / 64 rows of 1 KB.  Lane l loads 16 bytes at l * 16 + 1024 i
+// (fully coalesced) and writes them to the same offsets of the slot; in a
+// partial last row the lanes past the end re-read an in-range address and
+// write into the slot's padding, so every load and store is unconditional.
 template <int D>
-struct PageData<true, D> {
-  static constexpr int G = D / 32;
-  static constexpr int NW = 3 * G / 4;     // dwords of a lane's code chunk
-  uint32_t kc[NW], vc[NW];                 // K / V code chunks
-  uint32_t ks[2 * G];                      // K scales of tokens 4j..4j+3, all groups
-  uint32_t vs[2];                          // V scales of tokens 4j..4j+3, the lane's group
+struct Stage {
+  static constexpr int kRows = D / 64;
+  static constexpr int kSlot = kRows * 1024;
+  u4 r[kRows];
 
-  __device__ inline void load(const uint8_t* __restrict__ blk, int lane) {
-    const int t = lane & 15, j = lane >> 4;
-    const uint8_t* kp = blk + (4 * t + j) * (3 * G);
-    const uint8_t* vp = blk + 6 * D + lane * (3 * G);
-    if constexpr (D == 256) {
+  __device__ inline void load(const uint8_t* __restrict__ src, int lane, int bytes) {
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const uint2 a = *reinterpret_cast<const uint2*>(kp + 8 * i);
-        const uint2 b = *reinterpret_cast<const uint2*>(vp + 8 * i);
-        kc[2 * i] = a.x; kc[2 * i + 1] = a.y;
-        vc[2 * i] = b.x; vc[2 * i + 1] = b.y;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        kc[i] = reinterpret_cast<const uint32_t*>(kp)[i];
-        vc[i] = reinterpret_cast<const uint32_t*>(vp)[i];
-      }
+    for (int i = 0; i < kRows; ++i) {
+      int off = 1024 * i + 16 * lane;
+      if (off >= bytes) off -= 1024 - (bytes & 1023);
+      r[i] = *reinterpret_cast<const u4*>(src + off);
     }
-    const uint4* ksp = reinterpret_cast<const uint4*>(blk + 12 * D + j * 8 * G);
+  }
+  __device__ inline void store(uint8_t* slot, int lane) const {
 #pragma unroll
-    for (int i = 0; i < G / 2; ++i) {
-      const uint4 a = ksp[i];
-      ks[4 * i] = a.x; ks[4 * i + 1] = a.y; ks[4 * i + 2] = a.z; ks[4 * i + 3] = a.w;
-    }
-    const int gn = (lane & 15) * D / 512;    // the lane's V channel group
-    const uint2 v = *reinterpret_cast<const uint2*>(blk + 13 * D + 8 * (j * G + gn));
-    vs[0] = v.x; vs[1] = v.y;
+    for (int i = 0; i < kRows; ++i) *reinterpret_cast<u4*>(slot + 1024 * i + 16 * lane) = r[i];
   }
 };
 
-template <int D>
-struct PageData<false, D> {
-  static constexpr int KW = D / 16;        // dwords of K per lane (D/4 bytes)
-  static constexpr int VW = D / 64;        // dwords of V per lane per token (D/16 bytes)
-  uint32_t k[KW];
-  uint32_t v[4][VW];
-
-  __device__ inline void load(const uint8_t* __restrict__ pg, int lane) {
-    const int t = lane & 15, j = lane >> 4, n = lane & 15;
-    const uint4* kp = reinterpret_cast<const uint4*>(pg + t * D + j * (D / 4));
-#pragma unroll
-    for (int i = 0; i < KW / 4; ++i) {
-      const uint4 a = kp[i];
-      k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint8_t* vp = pg + kPage * D + (4 * j + r) * D + n * (D / 16);
-      if constexpr (VW == 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(vp);
-        v[r][0] = a.x; v[r][1] = a.y; v[r][2] = a.z; v[r][3] = a.w;
-      } else {
-        const uint2 a = *reinterpret_cast<const uint2*>(vp);
-        v[r][0] = a.x; v[r][1] = a.y;
-      }
-    }
-  }
-};
+template <typename T>
+__device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
 // fp32 -> (fp16 hi, fp16 lo) with hi + lo = x to ~22 bits.
 __device__ inline void split_hi_lo(float x, _Float16& hi, _Float16& lo) {
@@ -152,115 +123,89 @@ __device__ inline void split_hi_lo(float x, _Float16& hi, _Float16& lo) {
 
 }  // namespace
 
-template <bool TQ3, int D>
-__global__ void __launch_bounds__(256) partial_mfma_kernel(
-    LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
-    float qscale, Plan plan) {
+enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
+
+// One work item: the partial state of (layer, chunk, KV head) over the pages
+// of one format, written to the workspace.  TQ3 is a template parameter so
+// each format's code path gets its own register allocation.
+template <int D, bool tq3>
+__device__ __forceinline__ void run_item(
+    const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
+    const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
+    uint8_t* smem, float (*sm)[kMaxG], float (*sl)[kMaxG], int (*sids)[kMaxChunkPages / kWaves],
+    h8* sq, uint32_t one024) {
   constexpr int NG = D / 32;               // 32-channel MFMA k-chunks (TQ3: scale groups)
   constexpr int NT = D / 16;               // 16-channel output tiles of P V
-  __shared__ float so[kWaves][kMaxG][D];
-  __shared__ float sm[kWaves][kMaxG], sl[kWaves][kMaxG];
-
+  constexpr int kSlot = Stage<D>::kSlot;
+  float (*so)[kMaxG][D] = reinterpret_cast<float (*)[kMaxG][D]>(smem);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;   // C/B column (query row or channel slice), row group
-  const int n_chunks = plan.totals[TQ3 ? T_NCT : T_NCF];
-  const int4* __restrict__ chunks = TQ3 ? plan.chunks_t : plan.chunks_f;
-  const int32_t* __restrict__ list = TQ3 ? plan.list_t : plan.list_f;
   const int hq = hkv * G;
-  const long items = (long)n_layers * hkv * n_chunks;
+  uint8_t* const ring = smem + wave * 2 * kSlot;
+    const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
+    const int32_t* __restrict__ list = tq3 ? plan.list_t : plan.list_f;
+    const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
+    const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
+    const size_t head_off = tq3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D;
+    const int upp = tq3 ? 1 : 2;              // staging units per page
+    const int unit_bytes = tq3 ? tq3_head_bytes(D) : kPage * D;
 
-  for (long item = blockIdx.x; item < items; item += gridDim.x) {
-    const int h = (int)(item % hkv);
-    const int chunk = (int)((item / hkv) % n_chunks);
-    const int layer = (int)(item / ((long)hkv * n_chunks));
-    const int4 cd = chunks[chunk];
-    const int b = cd.x, start = cd.y, count = cd.z & 0xffff, last_tok = cd.z >> 16, pidx = cd.w;
-    if (pidx >= plan.np_cap) {               // plan made for more layers than this call
-      if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
-      continue;
-    }
-    const float ks_layer = TQ3 ? 1.0f : lt.k_scale[layer];
-    const uint8_t* __restrict__ slab = TQ3 ? lt.tq3[layer] : lt.fp8[layer];
-    const size_t page_bytes = TQ3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
-    const size_t head_off = TQ3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D;
-
-    // ---- B operand of the score MFMAs: hi rows 0..G-1, lo rows 8..8+G-1 ----
-    h8 qf[NG];
-    {
-      const int row = n < 8 ? n : n - 8;
+    // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
+    //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder ----
+    for (int e = threadIdx.x; e < NG * 64; e += 256) {
+      const int g = e >> 6, ln = e & 63;
+      const int nn = ln & 15, jj = ln >> 4;
+      const int row = nn < 8 ? nn : nn - 8;
       const bool use = row < G;
       const float* qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
       const float sc = qscale * ks_layer;
+      const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
+      const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
+      const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      h8 frag;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int c0 = TQ3 ? 32 * g + 8 * j : j * (D / 4) + 8 * g;
-        const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
-        const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
-        float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        // TQ3 slot order of the k-slots: (0,6) (1,7) (3,2) (4,5)
-        const int perm[8] = {0, 6, 1, 7, 3, 2, 4, 5};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (TQ3 ? v[perm[e]] : v[e]) * sc;
-          _Float16 hi, lo;
-          split_hi_lo(x, hi, lo);
-          qf[g][e] = !use ? (_Float16)0.0f : (n < 8 ? hi : lo);
-        }
+      for (int k = 0; k < 8; ++k) {
+        const float x = (tq3 ? v[kTq3SlotChannel[k]] : v[k]) * sc;
+        _Float16 hi, lo;
+        split_hi_lo(x, hi, lo);
+        frag[k] = !use ? (_Float16)0.0f : (nn < 8 ? hi : lo);
       }
+      sq[e] = frag;
     }
 
-    // ---- per-wave online softmax over pages wave, wave+4, ... ----
+    const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
+    const int my_units = my_pages * upp;
+    // page ids of this wave's pages (chunks are capped at kMaxChunkPages) -> LDS
+    for (int k = lane; k < my_pages; k += 64) sids[wave][k] = list[start + wave + kWaves * k];
+    __syncthreads();
+
     f4 O[NT];
 #pragma unroll
     for (int T = 0; T < NT; ++T) O[T] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;
     float l_run = 0.0f;
-    const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
-    int ids = 0;                              // page ids of this wave's pages, one per lane (batches of 64)
+    h4 pa_keep = h4{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
 
-    PageData<TQ3, D> cur, nxt;
-    if (my_pages > 0) {
-      ids = lane < my_pages ? list[start + wave + kWaves * lane] : 0;
-      const int pid = __builtin_amdgcn_readfirstlane(ids);
-      cur.load(slab + (size_t)pid * page_bytes + head_off, lane);
+    // One unit in flight per wave: while unit u is computed from its LDS slot,
+    // unit u+1 travels HBM -> VGPR; at the top of the next step it is written
+    // to the other slot and unit u+2 is requested.
+    Stage<D> st;
+    auto unit_src = [&](int u) {
+      const int uu = u < my_units ? u : my_units - 1;   // past the end: re-read the last unit
+      const int pid = __builtin_amdgcn_readfirstlane(sids[wave][uu / upp]);
+      return slab + (size_t)pid * page_bytes + head_off + (size_t)(uu % upp) * unit_bytes;
+    };
+    if (my_units > 0) {
+      st.load(unit_src(0), lane, unit_bytes);
+      st.store(ring, lane);
+      st.load(unit_src(1), lane, unit_bytes);
     }
-    for (int k = 0; k < my_pages; ++k) {
-      if (k + 1 < my_pages) {
-        if (((k + 1) & 63) == 0)
-          ids = (k + 1 + lane < my_pages) ? list[start + wave + kWaves * (k + 1 + lane)] : 0;
-        const int pid = __builtin_amdgcn_readlane(ids, (k + 1) & 63);
-        nxt.load(slab + (size_t)pid * page_bytes + head_off, lane);
-      }
-      const int e = wave + kWaves * k;
-      const int ntok = (e == count - 1) ? last_tok : kPage;
 
-      // scores for tokens 4j..4j+3 (rows) of query row n (column)
-      f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        h8 a;
-        if constexpr (TQ3) {
-          uint32_t X, Y, W;
-          triple_words(cur.kc, 3 * g, X, Y, W);
-          h2 r[4];
-          decode_triple(X, Y, W, r);
-          a = h8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-          const f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[g], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          const h2 s01 = u2h(cur.ks[2 * g]), s23 = u2h(cur.ks[2 * g + 1]);
-          s[0] = fmaf(sg[0], (float)s01[0], s[0]);
-          s[1] = fmaf(sg[1], (float)s01[1], s[1]);
-          s[2] = fmaf(sg[2], (float)s23[0], s[2]);
-          s[3] = fmaf(sg[3], (float)s23[1], s[3]);
-        } else {
-          const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[2 * g], 1.0f, false);
-          const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[2 * g], 1.0f, true);
-          const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[2 * g + 1], 1.0f, false);
-          const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[2 * g + 1], 1.0f, true);
-          a = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[g], s, 0, 0, 0);
-        }
-      }
+    // online-softmax update for a page's scores (tokens 4j..4j+3 of query-row
+    // column n); returns the A operand of P V
+    auto softmax = [&](f4 s, int ntok) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         s[r] += dpp_ror8(s[r]);               // hi + lo query rows
@@ -283,61 +228,129 @@ __global__ void __launch_bounds__(256) partial_mfma_kernel(
           for (int T = 0; T < NT; ++T) O[T][r] *= ar;
         }
       }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = exp2f(s[r] - m_run);
-        l_run += p[r];
-      }
-      // A operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder
       h4 pa;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(s[r] - m_run);
+        l_run += p;
         _Float16 hi, lo;
-        split_hi_lo(p[r], hi, lo);
-        pa[r] = n < 8 ? hi : lo;
+        split_hi_lo(p, hi, lo);
+        pa[r] = n < 8 ? hi : lo;                // A rows 0..7 fp16(p), rows 8..15 the remainder
       }
+      return pa;
+    };
 
-      if constexpr (TQ3) {
-        const h2 sv01 = u2h(cur.vs[0]), sv23 = u2h(cur.vs[1]);
+    for (int u = 0; u < my_units; ++u) {
+      if (u > 0) {
+        st.store(ring + (u & 1) * kSlot, lane);      // unit u, requested during unit u-1
+        st.load(unit_src(u + 1), lane, unit_bytes);
+      }
+      const uint8_t* pg = ring + (u & 1) * kSlot;
+      const int k = u / upp;                  // page of the wave
+      const int e = wave + kWaves * k;        // page of the chunk
+      const int ntok = (e == count - 1) ? last_tok : kPage;
+      if (tq3) {
+        // ---- TQ3 page-head: scores, softmax, P V ----
+        constexpr int GB = 3 * NG;                          // bytes of a lane's code chunk
+        uint32_t kc[GB / 4];
+        const uint8_t* kp = pg + (4 * (lane & 15) + j) * GB;
+#pragma unroll
+        for (int i = 0; i < GB / 4; ++i) kc[i] = lds_load<uint32_t>(kp + 4 * i);
+        auto k_operand = [&](int g) {
+          uint32_t X, Y, W;
+          triple_words(kc, 3 * g, X, Y, W);
+          h2 r[4];
+          decode_triple(X, Y, W, one024, r);
+          return __builtin_bit_cast(h8, u4{h2u(r[0]), h2u(r[1]), h2u(r[2]), h2u(r[3])});
+        };
+        f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        h8 a = k_operand(0);                    // the next group decodes while an MFMA runs
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          if (g + 1 < NG) a = k_operand(g + 1);
+          const u2 sk = lds_load<u2>(pg + 12 * D + 8 * (j * NG + g));   // scales of tokens 4j..4j+3, group g
+          const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
+          s[0] = fmaf(sg[0], (float)s01[0], s[0]);
+          s[1] = fmaf(sg[1], (float)s01[1], s[1]);
+          s[2] = fmaf(sg[2], (float)s23[0], s[2]);
+          s[3] = fmaf(sg[3], (float)s23[1], s[3]);
+          __builtin_amdgcn_sched_barrier(0);   // bounds the live operands to two groups
+        }
+        const h4 pa = softmax(s, ntok);
+        uint32_t vc[GB / 4];
+        const uint8_t* vp = pg + 6 * D + lane * GB;
+#pragma unroll
+        for (int i = 0; i < GB / 4; ++i) vc[i] = lds_load<uint32_t>(vp + 4 * i);
+        const int gn = (lane & 15) * D / 512;    // the lane's V channel group
+        const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
+        const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
 #pragma unroll
         for (int pp = 0; pp < NG; ++pp) {
           uint32_t X, Y, W;
-          triple_words(cur.vc, 3 * pp, X, Y, W);
+          triple_words(vc, 3 * pp, X, Y, W);
           h2 r[4];
-          decode_triple(X, Y, W, r);
+          decode_triple(X, Y, W, one024, r);
+          // V = (u - 4) s as an exact fp16 pair hi + lo
           const h2 hi0 = r[0] * sv01, hi1 = r[1] * sv23, hi2 = r[2] * sv01, hi3 = r[3] * sv23;
           const h2 lo0 = __builtin_elementwise_fma(r[0], sv01, -hi0);
           const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
           const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
           const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
-          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{hi0[0], hi0[1], hi1[0], hi1[1]}, O[2 * pp], 0, 0, 0);
-          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{lo0[0], lo0[1], lo1[0], lo1[1]}, O[2 * pp], 0, 0, 0);
-          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{hi2[0], hi2[1], hi3[0], hi3[1]}, O[2 * pp + 1], 0, 0, 0);
-          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{lo2[0], lo2[1], lo3[0], lo3[1]}, O[2 * pp + 1], 0, 0, 0);
+          // alternate the two accumulators so no MFMA waits on the one before it
+          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(hi0), h2u(hi1)}), O[2 * pp], 0, 0, 0);
+          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(hi2), h2u(hi3)}), O[2 * pp + 1], 0, 0, 0);
+          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
+          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-        constexpr int VW = D / 64;
+      } else if ((u & 1) == 0) {
+        // ---- FP8 K half: scores and softmax; P is kept for the V half ----
+        const uint8_t* kp = pg + (lane & 15) * D + j * (D / 4);
+        f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int T = 0; T < NT; T += 2) {
-          const int wi = T >> 2, bo = T & 3;           // dword and byte of channel T in a token row
-          const uint32_t sel = bo | ((4 + bo) << 8) | ((bo + 1) << 16) | ((5 + bo) << 24);
-          const uint32_t w01 = __builtin_amdgcn_perm(cur.v[1][wi], cur.v[0][wi], sel);
-          const uint32_t w23 = __builtin_amdgcn_perm(cur.v[3][wi], cur.v[2][wi], sel);
-          const h2 a01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false);   // channel T, tokens 0,1
-          const h2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true);    // channel T+1
-          const h2 a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false);
-          const h2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true);
-          O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{a01[0], a01[1], a23[0], a23[1]}, O[T], 0, 0, 0);
-          O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, h4{b01[0], b01[1], b23[0], b23[1]}, O[T + 1], 0, 0, 0);
-          (void)VW;
+        for (int g = 0; g < NG; ++g) {
+          const u2 w = lds_load<u2>(kp + 8 * g);
+          const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
+          const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
+          const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
+          const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
+          const h8 a = __builtin_bit_cast(h8, u4{h2u(p0), h2u(p1), h2u(p2), h2u(p3)});
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], s, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        pa_keep = softmax(s, ntok);
+      } else {
+        // ---- FP8 V half: P V (FP8 values are exact in fp16) ----
+        constexpr int VW = D / 64;                 // dwords of one token row of the lane's channels
+        const uint8_t* vp = pg + (4 * j) * D + (lane & 15) * (D / 16);
+#pragma unroll
+        for (int wi = 0; wi < VW; ++wi) {
+          const uint32_t r0 = lds_load<uint32_t>(vp + 4 * wi);
+          const uint32_t r1 = lds_load<uint32_t>(vp + D + 4 * wi);
+          const uint32_t r2 = lds_load<uint32_t>(vp + 2 * D + 4 * wi);
+          const uint32_t r3 = lds_load<uint32_t>(vp + 3 * D + 4 * wi);
+#pragma unroll
+          for (int bo = 0; bo < 4; bo += 2) {
+            const int T = 4 * wi + bo;
+            const uint32_t sel = bo | ((4 + bo) << 8) | ((bo + 1) << 16) | ((5 + bo) << 24);
+            const uint32_t w01 = __builtin_amdgcn_perm(r1, r0, sel);
+            const uint32_t w23 = __builtin_amdgcn_perm(r3, r2, sel);
+            const h2 a01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false);   // channel T, tokens 0,1
+            const h2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true);    // channel T+1
+            const h2 a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false);
+            const h2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true);
+            O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_keep, __builtin_bit_cast(h4, u2{h2u(a01), h2u(a23)}), O[T], 0, 0, 0);
+            O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_keep, __builtin_bit_cast(h4, u2{h2u(b01), h2u(b23)}), O[T + 1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (k + 1 < my_pages) cur = nxt;
     }
+    __syncthreads();                              // the staging ring becomes the merge buffer
 
     // ---- wave state -> LDS: O rows i (hi) + i + 8 (lo) live in lanes l and l ^ 32 ----
-    const float vscale = TQ3 ? 1.0f : lt.v_scale[layer];
+    const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);             // sum over the four token rows of column n
 #pragma unroll
@@ -380,26 +393,83 @@ __global__ void __launch_bounds__(256) partial_mfma_kernel(
         ml[2 * i + 1] = L;
       }
     }
+}
+
+// MODE selects which format's work items the launch takes (kBoth: the FP8
+// items first, then the TQ3 items, in one grid so the small FP8 share runs
+// alongside the TQ3 stream; each item runs its own format's code path).
+template <int D, int MODE>
+__global__ void __launch_bounds__(256, 2) attend_kernel(
+    LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
+    float qscale, Plan plan) {
+  constexpr int NG = D / 32;
+  constexpr int kSlot = Stage<D>::kSlot;
+  constexpr int kStageBytes = kWaves * 2 * kSlot;
+  constexpr int kMergeBytes = kWaves * kMaxG * D * 4;
+  // the staging ring and the end-of-item merge buffer share LDS
+  __shared__ __align__(16) uint8_t smem[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
+  __shared__ float sm[kWaves][kMaxG], sl[kWaves][kMaxG];
+  __shared__ int sids[kWaves][kMaxChunkPages / kWaves];
+  __shared__ h8 sq[NG * 64];                 // score-MFMA B operands, [group][lane]
+
+  const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
+  const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
+  const long items_f = (long)n_layers * hkv * ncf;
+  const long items_t = (long)n_layers * hkv * nct;
+  const long items = items_f + items_t;
+  uint32_t one024 = 0x64006400u;             // fp16 1024.0 in both halves, kept in a VGPR
+  asm volatile("" : "+v"(one024));
+
+  for (long item = blockIdx.x; item < items; item += gridDim.x) {
+    const bool tq3 = item >= items_f;
+    const long it = tq3 ? item - items_f : item;
+    const int nch = tq3 ? nct : ncf;
+    const int h = (int)(it % hkv);
+    const int chunk = (int)((it / hkv) % nch);
+    const int layer = (int)(it / ((long)hkv * nch));
+    const int4 cd = (tq3 ? plan.chunks_t : plan.chunks_f)[chunk];
+    const int b = cd.x, start = cd.y, count = cd.z & 0xffff, last_tok = cd.z >> 16, pidx = cd.w;
+    if (pidx >= plan.np_cap) {               // plan made for more layers than this call
+      if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
+      continue;
+    }
+    if (MODE != kFp8Only && tq3)
+      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+                        smem, sm, sl, sids, sq, one024);
+    if (MODE != kTq3Only && !tq3)
+      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+                         smem, sm, sl, sids, sq, one024);
     __syncthreads();
   }
 }
 
-hipError_t launch_partial_mfma(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers,
+
+static dim3 attend_grid(long cap) {
+  return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));
+}
+
+template <int MODE>
+static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
+                            size_t q_ls, float qscale, const Plan& plan, hipStream_t stream) {
+  const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2);
+  const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(256);
+  if (g.d == 256)
+    hipLaunchKernelGGL((attend_kernel<256, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                       q_ls, qscale, plan);
+  else
+    hipLaunchKernelGGL((attend_kernel<128, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                       q_ls, qscale, plan);
+}
+
+hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, hipStream_t stream) {
-  long cap = (long)n_layers * g.hkv * (plan.np_cap / 2);
-  const dim3 grid((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048)), block(256);
-  if (tq3) {
-    if (g.d == 256)
-      hipLaunchKernelGGL((partial_mfma_kernel<true, 256>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q, q_layer_stride, qscale, plan);
-    else
-      hipLaunchKernelGGL((partial_mfma_kernel<true, 128>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q, q_layer_stride, qscale, plan);
-  } else {
-    if (g.d == 256)
-      hipLaunchKernelGGL((partial_mfma_kernel<false, 256>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q, q_layer_stride, qscale, plan);
-    else
-      hipLaunchKernelGGL((partial_mfma_kernel<false, 128>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q, q_layer_stride, qscale, plan);
-  }
+  if (which == 0)
+    launch_attend_t<kFp8Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
+  else if (which == 1)
+    launch_attend_t<kTq3Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
+  else
+    launch_attend_t<kBoth>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
   return hipGetLastError();
 }
 

@@ -135,34 +135,28 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   }
   const int status = sh[0];
   __syncthreads();
-  const int ppf = max(kMinChunkPages, (TF + plan.chunks_target - 1) / plan.chunks_target);
-  const int ppt = max(kMinChunkPages, (TT + plan.chunks_target - 1) / plan.chunks_target);
+  const int ppf = min(kMaxChunkPages, max(kMinChunkPages, (TF + plan.chunks_target - 1) / plan.chunks_target));
+  const int ppt = min(kMaxChunkPages, max(kMinChunkPages, (TT + plan.chunks_target - 1) / plan.chunks_target));
   // per-request counts and their prefix sums
-  int carry_f = 0, carry_t = 0, carry_p = 0, carry_m = 0, carry_i = 0;
+  int carry_f = 0, carry_t = 0, carry_p = 0;
   for (int base = 0; base < B; base += 1024) {
     const int b = base + tid;
-    int nfc = 0, ntc = 0, np = 0, m1 = 0, ni = 0;
+    int nfc = 0, ntc = 0, np = 0;
     if (b < B) {
       nfc = (nf_row[b] + ppf - 1) / ppf;
       ntc = (nt_row[b] + ppt - 1) / ppt;
       np = nfc + ntc;
-      m1 = max(1, (np + kMergeFan - 1) / kMergeFan);
-      ni = np > kMergeFan ? m1 : 0;
     }
-    int tf, tt, tp, tm, ti;
+    int tf, tt, tp;
     const int ef = block_exclusive_scan<1024>(nfc, &tf, sh);
     const int et = block_exclusive_scan<1024>(ntc, &tt, sh);
     const int ep = block_exclusive_scan<1024>(np, &tp, sh);
-    const int em = block_exclusive_scan<1024>(m1, &tm, sh);
-    const int ei = block_exclusive_scan<1024>(ni, &ti, sh);
     if (b < B) {
       req_row(plan, R_CF_OFF)[b] = carry_f + ef;   // chunk offsets (exclusive) per format
       req_row(plan, R_CT_OFF)[b] = carry_t + et;
       req_row(plan, R_POFF)[b] = carry_p + ep;
-      req_row(plan, R_M1OFF)[b] = carry_m + em;
-      req_row(plan, R_IOFF)[b] = carry_i + ei;
     }
-    carry_f += tf; carry_t += tt; carry_p += tp; carry_m += tm; carry_i += ti;
+    carry_f += tf; carry_t += tt; carry_p += tp;
   }
   // Chunk counts cannot exceed the capacity for valid CSR offsets; guard anyway.
   const bool over = carry_f > plan.table_cap || carry_t > plan.table_cap;
@@ -172,13 +166,9 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     req_row(plan, R_CF_OFF)[B] = carry_f;
     req_row(plan, R_CT_OFF)[B] = carry_t;
     req_row(plan, R_POFF)[B] = carry_p;
-    req_row(plan, R_M1OFF)[B] = carry_m;
-    req_row(plan, R_IOFF)[B] = carry_i;
     plan.totals[T_NCF] = carry_f;
     plan.totals[T_NCT] = carry_t;
     plan.totals[T_NP] = carry_p;
-    plan.totals[T_NM1] = carry_m;
-    plan.totals[T_NI] = carry_i;
     plan.totals[T_PPF] = ppf;
     plan.totals[T_PPT] = ppt;
   }
