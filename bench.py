@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-control", action="store_true", help="skip the same-run all-FP8 control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-units", type=int, default=6, help="(layer, request, KV head) units the oracle is timed on")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many eager steps (for rocprofv3), print nothing else")
     return ap.parse_args()
@@ -143,24 +145,74 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def time_attend_kernel(self, reps=20):
-        """Average duration of one fused attend launch (layer 0: FP8 + TQ3 partials
-        and the merge), HIP events on the stream it is launched on."""
+    def time_kernels(self, reps=32):
+        """Average and median duration of the partial-attention launch (both
+        formats, one layer) and of the merge launch, with HIP events recorded
+        on the stream the kernels are launched on.  Launch i reads layer
+        i mod L, so, as in the step, no launch finds its layer's pages in the
+        last-level cache from the launch before."""
         torch, M = self.torch, self.M
-        M.mkv_decode_plan(self.layout, self.dw.cache.pools[0], self.batch, 1, self.ws)
-        run = lambda: M.mkv_attend(self.layout, [self.dw.cache.pools[0]], self.batch, self.q[0], self.sm_scale,
-                                   self.out[0], self.lse[0], self.ws)
-        for _ in range(3):
-            run()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in evs:
-            a.record()
-            run()
-            b.record()
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in evs)
-        return sum(ms) / len(ms), ms[len(ms) // 2]
+        lay, bat, ws, L = self.layout, self.batch, self.ws, self.w.L
+        M.mkv_decode_plan(lay, self.dw.cache.pools[0], bat, 1, ws)
+        part = lambda l: M.mkv_attend_partials(lay, [self.dw.cache.pools[l]], bat, self.q[l], self.sm_scale, ws)
+        merge = lambda l: M.mkv_merge(lay, 1, bat, self.out[l], self.lse[l], ws)
+        res = {}
+        for name in ("partials", "merge"):
+            for l in range(min(L, 3)):
+                part(l)
+                merge(l)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for i, (a, b) in enumerate(evs):
+                l = i % L
+                if name == "merge":
+                    part(l)
+                a.record()
+                part(l) if name == "partials" else merge(l)
+                b.record()
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in evs)
+            res[name] = (sum(ms) / len(ms), ms[len(ms) // 2])
+        return res
+
+
+def kernel_source_hash():
+    """Hash of the sources the partial-attention kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("mkv_partial_mfma.hip", "mkv_internal.h", "mkv_format.h"):
+        with open(os.path.join(ROOT, "mixed_format_paged_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per partial-attention launch from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attend_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return int(float(rec["hbm_bytes_per_launch"]))
+
+
+def copy_calibration(nbytes, reps):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(runner, units):
@@ -227,6 +279,9 @@ def main():
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration, 5)
+        return
     import torch
     import workloads as W
     w = W.WORKLOADS[a.workload]
@@ -238,14 +293,16 @@ def main():
         for _ in range(a.profile_steps):
             r.step()
         torch.cuda.synchronize()
-        r.time_attend_kernel(reps=5)
+        r.time_kernels(reps=5)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
     print(f"[bench] timed {a.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
     kv_bytes, tq3_bytes, tq3_bytes_layer = r.kv_bytes()
     layer_bytes = kv_bytes // w.L
-    k_avg, k_med = r.time_attend_kernel()
+    kt = r.time_kernels()
+    k_avg, k_med = kt["partials"]
+    traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -262,11 +319,12 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "device_status": status,
-        "roofline": {"bound": "hbm", "kernel": "attend (FP8 + TQ3 partials + merge, one layer)",
+        "roofline": {"bound": "hbm", "kernel": "attend_kernel: FP8 + TQ3 partial attention, one layer",
                      "achieved": round(layer_bytes / (k_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(layer_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(k_avg, 5), "median_launch_ms": round(k_med, 5),
+                     "traffic": traffic, "avg_launch_ms": round(k_avg, 5), "median_launch_ms": round(k_med, 5),
                      "bytes_per_launch": layer_bytes},
+        "merge_kernel": {"avg_launch_ms": round(kt["merge"][0], 5), "median_launch_ms": round(kt["merge"][1], 5)},
     }
     if not a.no_control:
         del r

@@ -215,6 +215,13 @@ int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
                    size_t ws_bytes, void* stream);
 int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
               float* lse, void* ws, size_t ws_bytes, void* stream);
+/* mkv_attend_partials: mkv_attend_fp8 and mkv_attend_tq3 in one launch (the
+ * FP8 and TQ3 work items of the plan side by side in one grid, each running
+ * its own format's code); the partial states it leaves in ws are bit-identical
+ * to those of the two separate calls. */
+int mkv_attend_partials(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                        const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* mkv_attend: mkv_attend_fp8 + mkv_attend_tq3 + mkv_merge with the two
  * partial kernels in one launch: the FP8 and TQ3 work items of the plan in ws

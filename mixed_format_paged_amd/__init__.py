@@ -14,7 +14,7 @@ __all__ = [
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
-    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_merge", "mkv_attend", "mkv_status_string", "mkv_last_error",
+    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_status_string", "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
 
@@ -67,6 +67,7 @@ def lib():
         "mkv_decode_plan": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_vp, c_sz, c_vp]),
         "mkv_attend_fp8": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
         "mkv_attend_tq3": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
+        "mkv_attend_partials": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
         "mkv_merge": (c_i32, [P(Layout), c_i32, P(BatchDesc), c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_attend": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_decode_workspace_bytes": (c_sz, [P(Layout), c_i32, c_i32, c_i32]),
@@ -196,6 +197,10 @@ def mkv_attend_fp8(layout, pools, batch, q, sm_scale, ws, stream=None):
 
 def mkv_attend_tq3(layout, pools, batch, q, sm_scale, ws, stream=None):
     return _attend(lib().mkv_attend_tq3, layout, pools, batch, q, sm_scale, ws, stream)
+
+
+def mkv_attend_partials(layout, pools, batch, q, sm_scale, ws, stream=None):
+    return _attend(lib().mkv_attend_partials, layout, pools, batch, q, sm_scale, ws, stream)
 
 
 def mkv_merge(layout, n_layers, batch, out, lse, ws, stream=None):

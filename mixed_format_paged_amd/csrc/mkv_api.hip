@@ -256,13 +256,21 @@ int check_qo(const float* q, const float* out, const float* lse, float sm_scale,
   return MKV_OK;
 }
 
-int run_attend(bool tq3, const Geometry& g, const LayerTable& lt, int n_layers, const Plan& plan,
+// which: 0 FP8 items, 1 TQ3 items, 2 both (one launch for the matrix-core
+// kernels, two for the VALU baseline).
+int run_attend(int which, const Geometry& g, const LayerTable& lt, int n_layers, const Plan& plan,
                const float* q, float sm_scale, int batch, hipStream_t st) {
   const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
   const size_t q_ls = (size_t)batch * g.hq * g.d;
-  hipError_t e = g_partial_kind ? launch_partial_mfma(tq3 ? 1 : 0, g, lt, n_layers, q, q_ls, qscale, plan, st)
-                                : launch_partial_valu(tq3, g, lt, n_layers, q, q_ls, qscale, plan, st);
-  return e == hipSuccess ? MKV_OK : hip_fail(e, tq3 ? "TQ3 partial launch" : "FP8 partial launch");
+  hipError_t e;
+  if (g_partial_kind) {
+    e = launch_partial_mfma(which, g, lt, n_layers, q, q_ls, qscale, plan, st);
+  } else {
+    e = hipSuccess;
+    if (which != 1) e = launch_partial_valu(false, g, lt, n_layers, q, q_ls, qscale, plan, st);
+    if (e == hipSuccess && which != 0) e = launch_partial_valu(true, g, lt, n_layers, q, q_ls, qscale, plan, st);
+  }
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "partial-attention launch");
 }
 
 int run_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse, int batch,
@@ -290,7 +298,7 @@ int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_ba
   return e == hipSuccess ? MKV_OK : hip_fail(e, "plan launch");
 }
 
-static int attend_entry(bool tq3, const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int attend_entry(int which, const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                         const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                         size_t ws_bytes, void* stream) {
   Geometry g{};
@@ -301,19 +309,25 @@ static int attend_entry(bool tq3, const mkv_layout* layout, const mkv_pool* pool
   if (rc) return rc;
   if ((rc = check_qo(q, nullptr, nullptr, sm_scale, true, false))) return rc;
   if (batch->batch == 0) return MKV_OK;
-  return run_attend(tq3, g, lt, n_layers, plan, q, sm_scale, batch->batch, as_stream(stream));
+  return run_attend(which, g, lt, n_layers, plan, q, sm_scale, batch->batch, as_stream(stream));
 }
 
 int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                    const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                    size_t ws_bytes, void* stream) {
-  return attend_entry(false, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
+  return attend_entry(0, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
 }
 
 int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                    const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                    size_t ws_bytes, void* stream) {
-  return attend_entry(true, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
+  return attend_entry(1, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
+}
+
+int mkv_attend_partials(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                        const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return attend_entry(2, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
 }
 
 int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
@@ -331,16 +345,8 @@ namespace {
 
 int run_fused(const Geometry& g, const LayerTable& lt, int n_layers, const Plan& plan, const float* q,
               float sm_scale, float* out, float* lse, int B, hipStream_t st) {
-  if (!g_partial_kind) {                       // the VALU baseline: separate launches
-    int rc;
-    if ((rc = run_attend(false, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
-    if ((rc = run_attend(true, g, lt, n_layers, plan, q, sm_scale, B, st))) return rc;
-    return run_merge(g, n_layers, plan, out, lse, B, st);
-  }
-  const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
-  hipError_t e = launch_partial_mfma(2, g, lt, n_layers, q, (size_t)B * g.hq * g.d, qscale, plan, st);
-  if (e != hipSuccess) return hip_fail(e, "attend launch");
-  return run_merge(g, n_layers, plan, out, lse, B, st);
+  const int rc = run_attend(2, g, lt, n_layers, plan, q, sm_scale, B, st);
+  return rc ? rc : run_merge(g, n_layers, plan, out, lse, B, st);
 }
 
 }  // namespace

@@ -187,3 +187,41 @@ def test_device_data_errors_flag_and_nan(kind):
     dw.cache.tier[free_fp8] = M.TIER_FREE
     out, lse, status = _decode(dw)
     assert status == 0 and np.array_equal(out, out0)
+
+
+def test_phase_split_calls_are_bit_identical(kind):
+    """plan + attend_fp8 + attend_tq3 + merge, plan + attend_partials + merge,
+    plan + attend, and decode_attn_layers give the same bytes, and match the
+    oracle."""
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=5, L=2,
+                 lengths=("list", (3000, 17, 0, 1200, 4100)), recent_tokens=64)
+    st, dw, ref = _both(w)
+    layout = (w.Hq, w.Hkv, w.d)
+    L = 2
+    sm = 1 / math.sqrt(w.d)
+    wsb = M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), L)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bat = dw.batch()
+    outs = []
+    for variant in ("separate", "partials", "attend"):
+        out = torch.full((L, w.B, w.Hq, w.d), float("nan"), device="cuda")
+        lse = torch.full((L, w.B, w.Hq), float("nan"), device="cuda")
+        M.mkv_decode_plan(layout, dw.cache.pools[0], bat, L, ws)
+        if variant == "separate":
+            M.mkv_attend_fp8(layout, dw.cache.pools, bat, dw.q, sm, ws)
+            M.mkv_attend_tq3(layout, dw.cache.pools, bat, dw.q, sm, ws)
+            M.mkv_merge(layout, L, bat, out, lse, ws)
+        elif variant == "partials":
+            M.mkv_attend_partials(layout, dw.cache.pools, bat, dw.q, sm, ws)
+            M.mkv_merge(layout, L, bat, out, lse, ws)
+        else:
+            M.mkv_attend(layout, dw.cache.pools, bat, dw.q, sm, out, lse, ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    o4, l4, status = _decode(dw)
+    assert status == 0
+    outs.append((o4, l4))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+    for li, (_, _, o_ref, lse_ref) in enumerate(ref):
+        compare(outs[0][0][li], o_ref, outs[0][1][li], lse_ref, f"layer {li}")
