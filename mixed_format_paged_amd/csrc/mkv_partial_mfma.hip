@@ -7,8 +7,9 @@
 //
 //  * Work item = (layer, chunk of pages, KV head); a workgroup of 4 waves
 //    takes one item, wave w the pages w, w+4, ...; each KV page is read once
-//    for the whole GQA group.  The 4 wave states are merged in LDS and one
-//    partial (m, l, acc) per item is written.
+//    for the whole GQA group, copied HBM -> LDS by LDS-DMA loads a few units
+//    ahead of use.  The 4 wave states are merged in LDS and one partial
+//    (m, l, acc) per item is written.
 //  * Scores S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = 16 tokens x 32
 //    channels of K, B = 32 channels x 16 query rows.  Query rows 0..G-1 hold
 //    fp16(q) and rows 8..8+G-1 the fp16 remainder q - fp16(q), so one DPP
@@ -16,11 +17,13 @@
 //    each MFMA covers exactly one 32-channel scale group and the fp32 group
 //    scale multiplies its result; codes enter the MFMA as exact fp16 (u - 4).
 //  * Online softmax in log2 units with a lazy rescale: the running max moves
-//    only when a page's max exceeds it by more than 8 (p <= 2^8, safe in fp16).
-//  * P V with v_mfma_f32_16x16x16_f16: A = P (rows 0..G-1 fp16(p), rows
-//    8..8+G-1 the remainder), B = 16 tokens x 16 channels of V.  TQ3 V is
-//    (u - 4) * s split into an exact fp16 pair hi + lo (two MFMAs); FP8 V is
-//    exact in fp16 (one MFMA).
+//    only when a page's max exceeds it by more than 15 (p <= 2^15, finite in
+//    fp16).
+//  * P V: A = P (rows 0..G-1 fp16(p), rows 8..8+G-1 the remainder).  TQ3 V
+//    is (u - 4) * s split into an exact fp16 pair hi + lo; one
+//    v_mfma_f32_16x16x32_f16 per 16-channel tile takes both, its k index
+//    running over (token, part) with P repeated for the two parts.  FP8 V is
+//    exact in fp16 (v_mfma_f32_16x16x16_f16, k = the page's 16 tokens).
 //  Lane maps follow the byte layout in mkv_format.h: a TQ3 lane's triples
 //  arrive in one aligned chunk, and each triple becomes four fp16 pairs with
 //  one mask-and-or and one packed fma per pair.
@@ -39,7 +42,13 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr float kRescale = 8.0f;        // log2 units
+#ifndef MKV_STAGES
+#define MKV_STAGES 2
+#endif
+constexpr int kStages = MKV_STAGES;     // LDS slots per wave (kStages - 1 units in flight)
+// The running max moves only when a page's max exceeds it by more than
+// kRescale (log2 units), so p <= 2^15 stays finite in fp16.
+constexpr float kRescale = 15.0f;
 // k-slot -> channel offset inside a TQ3 triple, in the order one triple
 // decodes into fp16 pairs: (0,6) (1,7) (3,2) (4,5)
 constexpr int kTq3SlotChannel[8] = {0, 6, 1, 7, 3, 2, 4, 5};
@@ -47,6 +56,26 @@ constexpr int kTq3SlotChannel[8] = {0, 6, 1, 7, 3, 2, 4, 5};
 __device__ inline h2 u2h(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ inline uint32_t h2u(h2 h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ inline h2 mkh2(float a, float b) { return h2{(_Float16)a, (_Float16)b}; }
+
+// {x[l], x[l ^ 32]} and {x[l], x[l ^ 16]} (in either order) with one VALU
+// permute (gfx950 v_permlane32_swap / v_permlane16_swap): reductions over the
+// four 16-lane rows without an LDS round trip.
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float dpp_ror8(float x) {             // lane l <- lane (l ^ 8) within each 16-lane row
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
@@ -85,31 +114,57 @@ __device__ inline void decode_triple(uint32_t X, uint32_t Y, uint32_t W, uint32_
   r[3] = __builtin_elementwise_fma(u2h(and_or(W, 0x03800070u, one024)), mkh2(0.0625f, 0.0078125f), mkh2(-68.0f, -12.0f));
 }
 
-// Staging unit: the bytes a wave moves to its LDS slot in one step.  For TQ3
-// a unit is one page-head (14 d bytes: codes and scales of one KV head); for
-// FP8 a page-head (32 d bytes) is two units, its K half and its V half.  Both
-// fit a slot of d / 64 rows of 1 KB.  Lane l loads 16 bytes at l * 16 + 1024 i
-// (fully coalesced) and writes them to the same offsets of the slot; in a
-// partial last row the lanes past the end re-read an in-range address and
-// write into the slot's padding, so every load and store is unconditional.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Staging unit: the bytes a wave moves to one LDS slot.  For TQ3 a unit is
+// one page-head (14 d bytes: codes and scales of one KV head); for FP8 a
+// page-head (32 d bytes) is two units, its K half and its V half.  Both fit a
+// slot of d / 64 rows of 1 KB.  The copy goes straight from HBM to LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes of row i land at slot + 1024 i
+// + 16 l), so a wave keeps kStages - 1 units in flight without holding them
+// in registers.  In a partial last row the lanes past the end re-read an
+// in-range address and fill the slot's padding, so every load is issued
+// unconditionally and the wave's count of outstanding loads is static.
 template <int D>
 struct Stage {
   static constexpr int kRows = D / 64;
   static constexpr int kSlot = kRows * 1024;
-  u4 r[kRows];
 
-  __device__ inline void load(const uint8_t* __restrict__ src, int lane, int bytes) {
+  __device__ static inline void issue(const uint8_t* __restrict__ src, uint8_t* slot, int lane, int bytes) {
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot));
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       int off = 1024 * i + 16 * lane;
       if (off >= bytes) off -= 1024 - (bytes & 1023);
-      r[i] = *reinterpret_cast<const u4*>(src + off);
+      // M0 holds the LDS row base; one wait state between the M0 write and
+      // the LDS-DMA load that reads it
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(src + off), "s"(lds + 1024 * i) : "memory", "m0");
     }
   }
-  __device__ inline void store(uint8_t* slot, int lane) const {
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) *reinterpret_cast<u4*>(slot + 1024 * i + 16 * lane) = r[i];
-  }
+};
+
+// Wait until at most N vector-memory instructions of this wave are in flight.
+// The staging loads are opaque to the compiler (its own conservative wait on
+// any LDS-DMA before any LDS read would drain the pipeline), so the waits on
+// staged units are placed by hand; the memory clobber keeps the LDS reads of a
+// slot after the wait for its unit.
+template <int N>
+__device__ inline void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// LDS layout of the 4 wave states at the end of an item: channel c = n (D/16)
+// + T of query row i of wave w.  Slices of D/16 channels are padded by one
+// float and rows by 8, so the 32 lanes that store one (T, r) at a time (16
+// slices x 2 rows) hit distinct banks, and reads along c stay conflict-free.
+template <int D>
+struct MergeLayout {
+  static constexpr int kSlice = D / 16 + 1;
+  static constexpr int kRow = 16 * kSlice + 8;
+  static constexpr int kWave = kMaxG * kRow;
+  static constexpr int kBytes = kWaves * kWave * 4;
+  __device__ static inline int at(int w, int i, int n, int T) { return w * kWave + i * kRow + n * kSlice + T; }
 };
 
 template <typename T>
@@ -128,7 +183,7 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 // One work item: the partial state of (layer, chunk, KV head) over the pages
 // of one format, written to the workspace.  TQ3 is a template parameter so
 // each format's code path gets its own register allocation.
-template <int D, bool tq3>
+template <int D, bool tq3, int kStages>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
@@ -137,12 +192,12 @@ __device__ __forceinline__ void run_item(
   constexpr int NG = D / 32;               // 32-channel MFMA k-chunks (TQ3: scale groups)
   constexpr int NT = D / 16;               // 16-channel output tiles of P V
   constexpr int kSlot = Stage<D>::kSlot;
-  float (*so)[kMaxG][D] = reinterpret_cast<float (*)[kMaxG][D]>(smem);
+  float* const so = reinterpret_cast<float*>(smem);   // wave states, MergeLayout<D>
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;   // C/B column (query row or channel slice), row group
   const int hq = hkv * G;
-  uint8_t* const ring = smem + wave * 2 * kSlot;
+  uint8_t* const ring = smem + wave * kStages * kSlot;
     const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
     const int32_t* __restrict__ list = tq3 ? plan.list_t : plan.list_f;
     const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
@@ -188,19 +243,18 @@ __device__ __forceinline__ void run_item(
     float l_run = 0.0f;
     h4 pa_keep = h4{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
 
-    // One unit in flight per wave: while unit u is computed from its LDS slot,
-    // unit u+1 travels HBM -> VGPR; at the top of the next step it is written
-    // to the other slot and unit u+2 is requested.
-    Stage<D> st;
+    // kStages - 1 units in flight per wave: at step u the wave requests unit
+    // u + kStages - 1 into the slot it finished with at step u - 1, waits for
+    // unit u, and computes from its slot.  Past the end it re-requests the
+    // last unit (an L2 hit) so the number of loads in flight stays constant.
     auto unit_src = [&](int u) {
-      const int uu = u < my_units ? u : my_units - 1;   // past the end: re-read the last unit
+      const int uu = u < my_units ? u : my_units - 1;
       const int pid = __builtin_amdgcn_readfirstlane(sids[wave][uu / upp]);
       return slab + (size_t)pid * page_bytes + head_off + (size_t)(uu % upp) * unit_bytes;
     };
     if (my_units > 0) {
-      st.load(unit_src(0), lane, unit_bytes);
-      st.store(ring, lane);
-      st.load(unit_src(1), lane, unit_bytes);
+#pragma unroll
+      for (int k = 0; k < kStages - 1; ++k) Stage<D>::issue(unit_src(k), ring + k * kSlot, lane, unit_bytes);
     }
 
     // online-softmax update for a page's scores (tokens 4j..4j+3 of query-row
@@ -212,12 +266,11 @@ __device__ __forceinline__ void run_item(
         if (4 * j + r >= ntok) s[r] = -INFINITY;
       }
       float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
-      pm = fmaxf(pm, __shfl_xor(pm, 32));
+      pm = max_xor32(max_xor16(pm));
       const bool need = pm > m_run + kRescale;
       if (__any(need)) {
         const float m_new = need ? pm : m_run;
-        const float alpha = exp2f(m_run - m_new);   // 0 on the first page (m_run = -inf)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first page (m_run = -inf)
         l_run *= alpha;
         m_run = m_new;
         // O rows 4j + r belong to query-row columns 4j + r
@@ -231,7 +284,7 @@ __device__ __forceinline__ void run_item(
       h4 pa;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[r] - m_run);
+        const float p = __builtin_amdgcn_exp2f(s[r] - m_run);   // v_exp_f32; 0 for masked tokens
         l_run += p;
         _Float16 hi, lo;
         split_hi_lo(p, hi, lo);
@@ -240,12 +293,14 @@ __device__ __forceinline__ void run_item(
       return pa;
     };
 
+    int slot_cur = 0, slot_next = kStages - 1;
     for (int u = 0; u < my_units; ++u) {
-      if (u > 0) {
-        st.store(ring + (u & 1) * kSlot, lane);      // unit u, requested during unit u-1
-        st.load(unit_src(u + 1), lane, unit_bytes);
-      }
-      const uint8_t* pg = ring + (u & 1) * kSlot;
+      Stage<D>::issue(unit_src(u + kStages - 1), ring + slot_next * kSlot, lane, unit_bytes);
+      wait_vmem<(kStages - 1) * Stage<D>::kRows>();     // unit u has landed
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* pg = ring + slot_cur * kSlot;
+      slot_next = slot_cur;
+      slot_cur = slot_cur + 1 == kStages ? 0 : slot_cur + 1;
       const int k = u / upp;                  // page of the wave
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
@@ -278,6 +333,7 @@ __device__ __forceinline__ void run_item(
           __builtin_amdgcn_sched_barrier(0);   // bounds the live operands to two groups
         }
         const h4 pa = softmax(s, ntok);
+        const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
         uint32_t vc[GB / 4];
         const uint8_t* vp = pg + 6 * D + lane * GB;
 #pragma unroll
@@ -297,11 +353,12 @@ __device__ __forceinline__ void run_item(
           const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
           const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
           const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
-          // alternate the two accumulators so no MFMA waits on the one before it
-          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(hi0), h2u(hi1)}), O[2 * pp], 0, 0, 0);
-          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(hi2), h2u(hi3)}), O[2 * pp + 1], 0, 0, 0);
-          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
-          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
+          // hi and lo share one MFMA: k = 8 j + e runs over (token 4 j + (e & 3),
+          // part e >> 2), with P repeated for both parts
+          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              pa2, __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
+          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              pa2, __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else if ((u & 1) == 0) {
@@ -347,19 +404,19 @@ __device__ __forceinline__ void run_item(
         }
       }
     }
+    wait_vmem<0>();                               // no staging load may land after this point
     __syncthreads();                              // the staging ring becomes the merge buffer
 
     // ---- wave state -> LDS: O rows i (hi) + i + 8 (lo) live in lanes l and l ^ 32 ----
     const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);             // sum over the four token rows of column n
+    l_run = sum_xor32(sum_xor16(l_run));        // sum over the four token rows of column n
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float tot = O[T][r] + __shfl_xor(O[T][r], 32);
+        const float tot = sum_xor32(O[T][r]);
         const int row = 4 * j + r;
-        if (j < 2 && row < G) so[wave][row][n * (D / 16) + T] = tot * vscale;
+        if (j < 2 && row < G) so[MergeLayout<D>::at(wave, row, n, T)] = tot * vscale;
       }
     }
     if (j == 0 && n < G) {
@@ -381,7 +438,7 @@ __device__ __forceinline__ void run_item(
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wgt = (sm[w][i] == -INFINITY) ? 0.0f : exp2f(sm[w][i] - M);
-        acc = fmaf(wgt, so[w][i][c], acc);
+        acc = fmaf(wgt, so[MergeLayout<D>::at(w, i, c / (D / 16), c % (D / 16))], acc);
       }
       pa_out[idx] = acc;
       if (c == 0) {
@@ -398,14 +455,17 @@ __device__ __forceinline__ void run_item(
 // MODE selects which format's work items the launch takes (kBoth: the FP8
 // items first, then the TQ3 items, in one grid so the small FP8 share runs
 // alongside the TQ3 stream; each item runs its own format's code path).
+#ifndef MKV_OCC
+#define MKV_OCC 3
+#endif
 template <int D, int MODE>
-__global__ void __launch_bounds__(256, 2) attend_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
     LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
     float qscale, Plan plan) {
   constexpr int NG = D / 32;
   constexpr int kSlot = Stage<D>::kSlot;
-  constexpr int kStageBytes = kWaves * 2 * kSlot;
-  constexpr int kMergeBytes = kWaves * kMaxG * D * 4;
+  constexpr int kStageBytes = kWaves * kStages * kSlot;
+  constexpr int kMergeBytes = MergeLayout<D>::kBytes;
   // the staging ring and the end-of-item merge buffer share LDS
   __shared__ __align__(16) uint8_t smem[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
   __shared__ float sm[kWaves][kMaxG], sl[kWaves][kMaxG];
@@ -434,10 +494,10 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(
       continue;
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+      run_item<D, true, kStages>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
                         smem, sm, sl, sids, sq, one024);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+      run_item<D, false, kStages>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
                          smem, sm, sl, sids, sq, one024);
     __syncthreads();
   }

@@ -69,7 +69,7 @@ def test_host_validation_codes():
 def test_workspace_is_bounded_not_cache_sized():
     # The workspace holds the plan (8 bytes of page lists per block-table
     # entry) and the split-K partial states, whose count is capped by a
-    # constant target plus one chunk per 1024 pages.  It stays a small
+    # constant target plus one chunk per 512 pages.  It stays a small
     # fraction of the KV bytes it reads, never a dense shadow of the cache.
     lay = (24, 4, 256)
     tq3_page, fp8_page = M.mkv_tq3_page_bytes(lay), M.mkv_fp8_page_bytes(lay)
