@@ -17,7 +17,7 @@
 namespace mkv {
 
 constexpr int kMaxLayers = 64;        // layers covered by one launch
-constexpr int kTargetItems = 512;     // split-K work items (workgroups) aimed for per format
+constexpr int kTargetItems = 1024;    // split-K work items (workgroups) aimed for per format: 4 per CU
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk (a workgroup stages its page ids in LDS)
 constexpr int kMaxG = 8;              // query heads per KV head supported

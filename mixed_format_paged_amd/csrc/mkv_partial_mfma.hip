@@ -42,10 +42,6 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-#ifndef MKV_STAGES
-#define MKV_STAGES 2
-#endif
-constexpr int kStages = MKV_STAGES;     // LDS slots per wave (kStages - 1 units in flight)
 // The running max moves only when a page's max exceeds it by more than
 // kRescale (log2 units), so p <= 2^15 stays finite in fp16.
 constexpr float kRescale = 15.0f;
@@ -115,34 +111,51 @@ __device__ inline void decode_triple(uint32_t X, uint32_t Y, uint32_t W, uint32_
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+// Page lists and chunk tables are read-only during the launch: read them
+// through the constant address space so the (wave-uniform) loads go to the
+// scalar unit and never count against the vector-memory counter that the
+// staging waits below rely on.
+typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
+typedef int i4v __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) i4v* cptr_i4;
+
+// Per-head-dim constants and the LDS plan of a 4-wave workgroup:
+//   [ring: 4 waves x 2 slots x kSlot][sq: score-MFMA B operands, NG x 64 x 16 B]
+// (40 KB at d = 256, so four workgroups share a CU).  At the end of an item
+// the whole block is reused for the merge of the 4 wave states.
+template <int D>
+struct Geo {
+  static constexpr int NG = D / 32;                 // 32-channel MFMA k-chunks (TQ3: scale groups)
+  static constexpr int NT = D / 16;                 // 16-channel output tiles of P V
+  static constexpr int kRows = D / 64;              // 1 KB rows of a staging slot
+  static constexpr int kSlot = kRows * 1024;
+  static constexpr int kRing = kWaves * 2 * kSlot;
+  static constexpr int kSq = NG * 64 * 16;
+  static constexpr int kLds = kRing + kSq;
+};
 
 // Staging unit: the bytes a wave moves to one LDS slot.  For TQ3 a unit is
 // one page-head (14 d bytes: codes and scales of one KV head); for FP8 a
 // page-head (32 d bytes) is two units, its K half and its V half.  Both fit a
 // slot of d / 64 rows of 1 KB.  The copy goes straight from HBM to LDS
-// (global_load_lds_dwordx4: lane l's 16 bytes of row i land at slot + 1024 i
-// + 16 l), so a wave keeps kStages - 1 units in flight without holding them
-// in registers.  In a partial last row the lanes past the end re-read an
-// in-range address and fill the slot's padding, so every load is issued
-// unconditionally and the wave's count of outstanding loads is static.
+// (global_load_lds_dwordx4, non-temporal: lane l's 16 bytes of row i land at
+// slot + 1024 i + 16 l), so the unit in flight holds no registers.  In a
+// partial last row the lanes past the end re-read an in-range address and
+// fill the slot's padding, so every load is issued unconditionally and the
+// wave's count of outstanding loads is static.
 template <int D>
-struct Stage {
-  static constexpr int kRows = D / 64;
-  static constexpr int kSlot = kRows * 1024;
-
-  __device__ static inline void issue(const uint8_t* __restrict__ src, uint8_t* slot, int lane, int bytes) {
-    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot));
+__device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slot, int lane, int bytes) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot));
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      int off = 1024 * i + 16 * lane;
-      if (off >= bytes) off -= 1024 - (bytes & 1023);
-      // M0 holds the LDS row base; one wait state between the M0 write and
-      // the LDS-DMA load that reads it
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :: "v"(src + off), "s"(lds + 1024 * i) : "memory", "m0");
-    }
+  for (int i = 0; i < Geo<D>::kRows; ++i) {
+    int off = 1024 * i + 16 * lane;
+    if (off >= bytes) off -= 1024 - (bytes & 1023);
+    // M0 holds the LDS row base; one wait state between the M0 write and the
+    // LDS-DMA load that reads it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(src + off), "s"(lds + 1024 * i) : "memory", "m0");
   }
-};
+}
 
 // Wait until at most N vector-memory instructions of this wave are in flight.
 // The staging loads are opaque to the compiler (its own conservative wait on
@@ -158,22 +171,215 @@ __device__ inline void wait_vmem() {
 // + T of query row i of wave w.  Slices of D/16 channels are padded by one
 // float and rows by 8, so the 32 lanes that store one (T, r) at a time (16
 // slices x 2 rows) hit distinct banks, and reads along c stay conflict-free.
+// The wave maxima and denominators follow the states.
 template <int D>
 struct MergeLayout {
   static constexpr int kSlice = D / 16 + 1;
   static constexpr int kRow = 16 * kSlice + 8;
   static constexpr int kWave = kMaxG * kRow;
-  static constexpr int kBytes = kWaves * kWave * 4;
+  static constexpr int kStates = kWaves * kWave;                 // floats
+  static constexpr int kBytes = (kStates + 2 * kWaves * kMaxG) * 4;
   __device__ static inline int at(int w, int i, int n, int T) { return w * kWave + i * kRow + n * kSlice + T; }
 };
+static_assert(MergeLayout<256>::kBytes <= Geo<256>::kLds, "merge buffer must fit the staging block");
+static_assert(MergeLayout<128>::kBytes <= Geo<128>::kLds, "merge buffer must fit the staging block");
 
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
-// fp32 -> (fp16 hi, fp16 lo) with hi + lo = x to ~22 bits.
-__device__ inline void split_hi_lo(float x, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)x;
-  lo = (_Float16)(x - (float)hi);
+__device__ inline h2 pkrtz(float a, float b) { return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b)); }
+
+// Four fp32 values -> the fp16 operand of this lane's MFMA row: rows 0..7
+// (lo_sel = 0) take hi = fp16(x) (round toward zero), rows 8..15 (lo_sel = -1)
+// the remainder fp16(x - hi); hi + lo = x to ~20 bits.
+__device__ inline h4 split_rows(const float (&x)[4], float lo_sel) {
+  const h2 h01 = pkrtz(x[0], x[1]), h23 = pkrtz(x[2], x[3]);
+  const float y0 = fmaf((float)h01[0], lo_sel, x[0]);
+  const float y1 = fmaf((float)h01[1], lo_sel, x[1]);
+  const float y2 = fmaf((float)h23[0], lo_sel, x[2]);
+  const float y3 = fmaf((float)h23[1], lo_sel, x[3]);
+  const h2 r01 = pkrtz(y0, y1), r23 = pkrtz(y2, y3);
+  return __builtin_shufflevector(r01, r23, 0, 1, 2, 3);
+}
+
+// Per-wave running state of the online softmax: O (16 query rows x d
+// channels, C layout of the P V MFMAs), the running max and denominator of the
+// query-row column n this lane holds in the score layout.
+template <int D>
+struct WaveState {
+  f4 O[Geo<D>::NT];
+  float m_run, l_run;
+
+  __device__ inline void init() {
+#pragma unroll
+    for (int T = 0; T < Geo<D>::NT; ++T) O[T] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+  }
+
+  // Online-softmax update for a page's scores s (tokens 4j..4j+3 of query-row
+  // column n, log2 units, hi and lo query rows not yet added); returns the A
+  // operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder.
+  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
+    if (ntok < kPage) {                         // a request's last page: mask its tail
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * j + r >= ntok) s[r] = -INFINITY;
+    }
+    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    pm = max_xor32(max_xor16(pm));
+    const bool need = pm > m_run + kRescale;
+    if (__any(need)) {
+      const float m_new = need ? pm : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first page (m_run = -inf)
+      l_run *= alpha;
+      m_run = m_new;
+      // O rows 4j + r belong to query-row columns 4j + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * j + r);
+#pragma unroll
+        for (int T = 0; T < Geo<D>::NT; ++T) O[T][r] *= ar;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(s[r] - m_run);   // v_exp_f32; 0 for masked tokens
+      l_run += p[r];
+    }
+    return split_rows(p, lo_sel);
+  }
+};
+
+// Scores of one TQ3 page-head staged at pg: one 16x16x32 MFMA per 32-channel
+// scale group, its result scaled by the group's fp16 scale of each token.
+template <int D>
+__device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j, uint32_t one024) {
+  constexpr int NG = Geo<D>::NG, GB = 3 * NG;       // bytes of a lane's code chunk
+  uint32_t kc[GB / 4];
+  const uint8_t* kp = pg + (4 * (lane & 15) + j) * GB;
+#pragma unroll
+  for (int i = 0; i < GB / 4; ++i) kc[i] = lds_load<uint32_t>(kp + 4 * i);
+  auto k_operand = [&](int g) {
+    uint32_t X, Y, W;
+    triple_words(kc, 3 * g, X, Y, W);
+    h2 r[4];
+    decode_triple(X, Y, W, one024, r);
+    return __builtin_bit_cast(h8, u4{h2u(r[0]), h2u(r[1]), h2u(r[2]), h2u(r[3])});
+  };
+  auto k_scales = [&](int g) { return lds_load<u2>(pg + 12 * D + 8 * (j * NG + g)); };  // tokens 4j..4j+3
+  f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  h8 a = k_operand(0);
+  h8 bq = sq[lane];
+  u2 sk = k_scales(0);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    u2 sk_next = sk;
+    if (g + 1 < NG) {                      // group g + 1 decodes and loads while the MFMA runs
+      a = k_operand(g + 1);
+      bq = sq[(g + 1) * 64 + lane];
+      sk_next = k_scales(g + 1);
+    }
+    const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
+    s[0] = fmaf(sg[0], (float)s01[0], s[0]);
+    s[1] = fmaf(sg[1], (float)s01[1], s[1]);
+    s[2] = fmaf(sg[2], (float)s23[0], s[2]);
+    s[3] = fmaf(sg[3], (float)s23[1], s[3]);
+    sk = sk_next;
+    // pins the order: group g's scaling is done, and at most group g + 1's
+    // operands are live, before group g + 1's MFMA (instruction selection
+    // would otherwise sink every scaling below all eight MFMAs and keep all
+    // their results live)
+    asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(sk) :: "memory");
+  }
+  return s;
+}
+
+// P V of one TQ3 page-head: V = (u - 4) s as an exact fp16 pair hi + lo; one
+// 16x16x32 MFMA per 16-channel tile takes both, its k index running over
+// (token 4j + (e & 3), part e >> 2) with P repeated for the two parts.
+template <int D>
+__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j, uint32_t one024) {
+  constexpr int NG = Geo<D>::NG, GB = 3 * NG;
+  const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
+  uint32_t vc[GB / 4];
+  const uint8_t* vp = pg + 6 * D + lane * GB;
+#pragma unroll
+  for (int i = 0; i < GB / 4; ++i) vc[i] = lds_load<uint32_t>(vp + 4 * i);
+  const int gn = (lane & 15) * D / 512;      // the lane's V channel group
+  const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
+  const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
+#pragma unroll
+  for (int pp = 0; pp < NG; ++pp) {
+    uint32_t X, Y, W;
+    triple_words(vc, 3 * pp, X, Y, W);
+    h2 r[4];
+    decode_triple(X, Y, W, one024, r);
+    const h2 hi0 = r[0] * sv01, hi1 = r[1] * sv23, hi2 = r[2] * sv01, hi3 = r[3] * sv23;
+    const h2 lo0 = __builtin_elementwise_fma(r[0], sv01, -hi0);
+    const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
+    const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
+    const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
+    O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        pa2, __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
+    O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        pa2, __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Scores of one FP8 K half staged at pg (16 tokens x d channels, E4M3):
+// codes convert exactly to fp16; lane (n, j) takes channels j d/4 + 8 g + e.
+template <int D>
+__device__ inline f4 fp8_scores(const uint8_t* pg, const h8* sq, int lane, int j) {
+  const uint8_t* kp = pg + (lane & 15) * D + j * (D / 4);
+  f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int g = 0; g < Geo<D>::NG; ++g) {
+    const u2 w = lds_load<u2>(kp + 8 * g);
+    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
+    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
+    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
+    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
+    const h8 a = __builtin_bit_cast(h8, u4{h2u(p0), h2u(p1), h2u(p2), h2u(p3)});
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], s, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return s;
+}
+
+// P V of one FP8 V half staged at pg: B = 16 tokens x 16 channels per tile
+// (FP8 values are exact in fp16); lane (n, j) holds tokens 4j..4j+3 of
+// channels n d/16 + T.
+template <int D>
+__device__ inline void fp8_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j) {
+  constexpr int VW = D / 64;                 // dwords of one token row of the lane's channels
+  const uint8_t* vp = pg + (4 * j) * D + (lane & 15) * (D / 16);
+#pragma unroll
+  for (int wi = 0; wi < VW; ++wi) {
+    const uint32_t r0 = lds_load<uint32_t>(vp + 4 * wi);
+    const uint32_t r1 = lds_load<uint32_t>(vp + D + 4 * wi);
+    const uint32_t r2 = lds_load<uint32_t>(vp + 2 * D + 4 * wi);
+    const uint32_t r3 = lds_load<uint32_t>(vp + 3 * D + 4 * wi);
+#pragma unroll
+    for (int bo = 0; bo < 4; bo += 2) {
+      const int T = 4 * wi + bo;
+      const uint32_t sel = bo | ((4 + bo) << 8) | ((bo + 1) << 16) | ((5 + bo) << 24);
+      const uint32_t w01 = __builtin_amdgcn_perm(r1, r0, sel);
+      const uint32_t w23 = __builtin_amdgcn_perm(r3, r2, sel);
+      const h2 a01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false);   // channel T, tokens 0,1
+      const h2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true);    // channel T+1
+      const h2 a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false);
+      const h2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true);
+      O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(a01), h2u(a23)}), O[T], 0, 0, 0);
+      O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(b01), h2u(b23)}), O[T + 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 }  // namespace
@@ -182,295 +388,187 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 
 // One work item: the partial state of (layer, chunk, KV head) over the pages
 // of one format, written to the workspace.  TQ3 is a template parameter so
-// each format's code path gets its own register allocation.
-template <int D, bool tq3, int kStages>
+// each format's code path gets its own register allocation, and each loop
+// body is straight-line code (no per-unit branch for the allocator to split
+// the accumulators at).
+template <int D, bool tq3>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
-    uint8_t* smem, float (*sm)[kMaxG], float (*sl)[kMaxG], int (*sids)[kMaxChunkPages / kWaves],
-    h8* sq, uint32_t one024) {
-  constexpr int NG = D / 32;               // 32-channel MFMA k-chunks (TQ3: scale groups)
-  constexpr int NT = D / 16;               // 16-channel output tiles of P V
-  constexpr int kSlot = Stage<D>::kSlot;
-  float* const so = reinterpret_cast<float*>(smem);   // wave states, MergeLayout<D>
+    uint8_t* smem, uint32_t one024) {
+  using GD = Geo<D>;
+  constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;   // C/B column (query row or channel slice), row group
+  const float lo_sel = n < 8 ? 0.0f : -1.0f;  // MFMA rows 8..15 carry the fp16 remainders
   const int hq = hkv * G;
-  uint8_t* const ring = smem + wave * kStages * kSlot;
-    const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
-    const int32_t* __restrict__ list = tq3 ? plan.list_t : plan.list_f;
-    const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
-    const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
-    const size_t head_off = tq3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D;
-    const int upp = tq3 ? 1 : 2;              // staging units per page
-    const int unit_bytes = tq3 ? tq3_head_bytes(D) : kPage * D;
+  uint8_t* const slot0 = smem + wave * 2 * kSlot;
+  uint8_t* const slot1 = slot0 + kSlot;
+  h8* const sq = reinterpret_cast<h8*>(smem + GD::kRing);
+  const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
+  const cptr_i32 list = (cptr_i32)(tq3 ? plan.list_t : plan.list_f);
+  const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
+  const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
+  const uint8_t* __restrict__ head = slab + (tq3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D);
+  const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
+  // page k of this wave (clamped: past the end the last page is re-read, an
+  // L2 hit, so every wave issues the same number of staging loads)
+  auto page_src = [&](int k) {
+    const int kk = k < my_pages ? k : my_pages - 1;
+    return head + (size_t)list[start + wave + kWaves * kk] * page_bytes;
+  };
 
-    // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
-    //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder ----
-    for (int e = threadIdx.x; e < NG * 64; e += 256) {
-      const int g = e >> 6, ln = e & 63;
-      const int nn = ln & 15, jj = ln >> 4;
-      const int row = nn < 8 ? nn : nn - 8;
-      const bool use = row < G;
-      const float* qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
-      const float sc = qscale * ks_layer;
-      const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
-      const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
-      const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
-      const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-      h8 frag;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x = (tq3 ? v[kTq3SlotChannel[k]] : v[k]) * sc;
-        _Float16 hi, lo;
-        split_hi_lo(x, hi, lo);
-        frag[k] = !use ? (_Float16)0.0f : (nn < 8 ? hi : lo);
-      }
-      sq[e] = frag;
+  // first unit(s) in flight before the query fragments are built
+  if (my_pages > 0) {
+    if (tq3) {
+      stage_issue<D>(page_src(0), slot0, lane, tq3_head_bytes(D));
+    } else {
+      const uint8_t* p0 = page_src(0);
+      stage_issue<D>(p0, slot0, lane, kPage * D);
+      stage_issue<D>(p0 + kPage * D, slot1, lane, kPage * D);
     }
+  }
 
-    const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
-    const int my_units = my_pages * upp;
-    // page ids of this wave's pages (chunks are capped at kMaxChunkPages) -> LDS
-    for (int k = lane; k < my_pages; k += 64) sids[wave][k] = list[start + wave + kWaves * k];
-    __syncthreads();
-
-    f4 O[NT];
+  // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
+  //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder ----
+  for (int e = threadIdx.x; e < NG * 64; e += 256) {
+    const int g = e >> 6, ln = e & 63;
+    const int nn = ln & 15, jj = ln >> 4;
+    const int row = nn < 8 ? nn : nn - 8;
+    const bool use = row < G;
+    const float* qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
+    const float sc = qscale * ks_layer;
+    const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
+    const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
+    const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    float x0[4], x1[4];
 #pragma unroll
-    for (int T = 0; T < NT; ++T) O[T] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY;
-    float l_run = 0.0f;
-    h4 pa_keep = h4{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-
-    // kStages - 1 units in flight per wave: at step u the wave requests unit
-    // u + kStages - 1 into the slot it finished with at step u - 1, waits for
-    // unit u, and computes from its slot.  Past the end it re-requests the
-    // last unit (an L2 hit) so the number of loads in flight stays constant.
-    auto unit_src = [&](int u) {
-      const int uu = u < my_units ? u : my_units - 1;
-      const int pid = __builtin_amdgcn_readfirstlane(sids[wave][uu / upp]);
-      return slab + (size_t)pid * page_bytes + head_off + (size_t)(uu % upp) * unit_bytes;
-    };
-    if (my_units > 0) {
-#pragma unroll
-      for (int k = 0; k < kStages - 1; ++k) Stage<D>::issue(unit_src(k), ring + k * kSlot, lane, unit_bytes);
+    for (int k = 0; k < 4; ++k) {
+      x0[k] = (use ? (tq3 ? v[kTq3SlotChannel[k]] : v[k]) : 0.0f) * sc;
+      x1[k] = (use ? (tq3 ? v[kTq3SlotChannel[k + 4]] : v[k + 4]) : 0.0f) * sc;
     }
+    const float sel = nn < 8 ? 0.0f : -1.0f;
+    sq[e] = __builtin_shufflevector(split_rows(x0, sel), split_rows(x1, sel), 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __syncthreads();
 
-    // online-softmax update for a page's scores (tokens 4j..4j+3 of query-row
-    // column n); returns the A operand of P V
-    auto softmax = [&](f4 s, int ntok) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r] += dpp_ror8(s[r]);               // hi + lo query rows
-        if (4 * j + r >= ntok) s[r] = -INFINITY;
-      }
-      float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      pm = max_xor32(max_xor16(pm));
-      const bool need = pm > m_run + kRescale;
-      if (__any(need)) {
-        const float m_new = need ? pm : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first page (m_run = -inf)
-        l_run *= alpha;
-        m_run = m_new;
-        // O rows 4j + r belong to query-row columns 4j + r
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * j + r);
-#pragma unroll
-          for (int T = 0; T < NT; ++T) O[T][r] *= ar;
-        }
-      }
-      h4 pa;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[r] - m_run);   // v_exp_f32; 0 for masked tokens
-        l_run += p;
-        _Float16 hi, lo;
-        split_hi_lo(p, hi, lo);
-        pa[r] = n < 8 ? hi : lo;                // A rows 0..7 fp16(p), rows 8..15 the remainder
-      }
-      return pa;
-    };
-
-    int slot_cur = 0, slot_next = kStages - 1;
-    for (int u = 0; u < my_units; ++u) {
-      Stage<D>::issue(unit_src(u + kStages - 1), ring + slot_next * kSlot, lane, unit_bytes);
-      wait_vmem<(kStages - 1) * Stage<D>::kRows>();     // unit u has landed
+  WaveState<D> st;
+  st.init();
+  if (tq3) {
+    // two slots: page k+1 travels while page k is computed
+    for (int k = 0; k < my_pages; ++k) {
+      uint8_t* const cur = (k & 1) ? slot1 : slot0;
+      uint8_t* const nxt = (k & 1) ? slot0 : slot1;
+      stage_issue<D>(page_src(k + 1), nxt, lane, tq3_head_bytes(D));
+      wait_vmem<kRows>();                     // page k has landed
       __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* pg = ring + slot_cur * kSlot;
-      slot_next = slot_cur;
-      slot_cur = slot_cur + 1 == kStages ? 0 : slot_cur + 1;
-      const int k = u / upp;                  // page of the wave
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
-      if (tq3) {
-        // ---- TQ3 page-head: scores, softmax, P V ----
-        constexpr int GB = 3 * NG;                          // bytes of a lane's code chunk
-        uint32_t kc[GB / 4];
-        const uint8_t* kp = pg + (4 * (lane & 15) + j) * GB;
-#pragma unroll
-        for (int i = 0; i < GB / 4; ++i) kc[i] = lds_load<uint32_t>(kp + 4 * i);
-        auto k_operand = [&](int g) {
-          uint32_t X, Y, W;
-          triple_words(kc, 3 * g, X, Y, W);
-          h2 r[4];
-          decode_triple(X, Y, W, one024, r);
-          return __builtin_bit_cast(h8, u4{h2u(r[0]), h2u(r[1]), h2u(r[2]), h2u(r[3])});
-        };
-        f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        h8 a = k_operand(0);                    // the next group decodes while an MFMA runs
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          if (g + 1 < NG) a = k_operand(g + 1);
-          const u2 sk = lds_load<u2>(pg + 12 * D + 8 * (j * NG + g));   // scales of tokens 4j..4j+3, group g
-          const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
-          s[0] = fmaf(sg[0], (float)s01[0], s[0]);
-          s[1] = fmaf(sg[1], (float)s01[1], s[1]);
-          s[2] = fmaf(sg[2], (float)s23[0], s[2]);
-          s[3] = fmaf(sg[3], (float)s23[1], s[3]);
-          __builtin_amdgcn_sched_barrier(0);   // bounds the live operands to two groups
-        }
-        const h4 pa = softmax(s, ntok);
-        const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
-        uint32_t vc[GB / 4];
-        const uint8_t* vp = pg + 6 * D + lane * GB;
-#pragma unroll
-        for (int i = 0; i < GB / 4; ++i) vc[i] = lds_load<uint32_t>(vp + 4 * i);
-        const int gn = (lane & 15) * D / 512;    // the lane's V channel group
-        const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
-        const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
-#pragma unroll
-        for (int pp = 0; pp < NG; ++pp) {
-          uint32_t X, Y, W;
-          triple_words(vc, 3 * pp, X, Y, W);
-          h2 r[4];
-          decode_triple(X, Y, W, one024, r);
-          // V = (u - 4) s as an exact fp16 pair hi + lo
-          const h2 hi0 = r[0] * sv01, hi1 = r[1] * sv23, hi2 = r[2] * sv01, hi3 = r[3] * sv23;
-          const h2 lo0 = __builtin_elementwise_fma(r[0], sv01, -hi0);
-          const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
-          const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
-          const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
-          // hi and lo share one MFMA: k = 8 j + e runs over (token 4 j + (e & 3),
-          // part e >> 2), with P repeated for both parts
-          O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              pa2, __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
-          O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              pa2, __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else if ((u & 1) == 0) {
-        // ---- FP8 K half: scores and softmax; P is kept for the V half ----
-        const uint8_t* kp = pg + (lane & 15) * D + j * (D / 4);
-        f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const u2 w = lds_load<u2>(kp + 8 * g);
-          const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
-          const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
-          const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
-          const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
-          const h8 a = __builtin_bit_cast(h8, u4{h2u(p0), h2u(p1), h2u(p2), h2u(p3)});
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], s, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        pa_keep = softmax(s, ntok);
-      } else {
-        // ---- FP8 V half: P V (FP8 values are exact in fp16) ----
-        constexpr int VW = D / 64;                 // dwords of one token row of the lane's channels
-        const uint8_t* vp = pg + (4 * j) * D + (lane & 15) * (D / 16);
-#pragma unroll
-        for (int wi = 0; wi < VW; ++wi) {
-          const uint32_t r0 = lds_load<uint32_t>(vp + 4 * wi);
-          const uint32_t r1 = lds_load<uint32_t>(vp + D + 4 * wi);
-          const uint32_t r2 = lds_load<uint32_t>(vp + 2 * D + 4 * wi);
-          const uint32_t r3 = lds_load<uint32_t>(vp + 3 * D + 4 * wi);
-#pragma unroll
-          for (int bo = 0; bo < 4; bo += 2) {
-            const int T = 4 * wi + bo;
-            const uint32_t sel = bo | ((4 + bo) << 8) | ((bo + 1) << 16) | ((5 + bo) << 24);
-            const uint32_t w01 = __builtin_amdgcn_perm(r1, r0, sel);
-            const uint32_t w23 = __builtin_amdgcn_perm(r3, r2, sel);
-            const h2 a01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false);   // channel T, tokens 0,1
-            const h2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true);    // channel T+1
-            const h2 a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false);
-            const h2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true);
-            O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_keep, __builtin_bit_cast(h4, u2{h2u(a01), h2u(a23)}), O[T], 0, 0, 0);
-            O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_keep, __builtin_bit_cast(h4, u2{h2u(b01), h2u(b23)}), O[T + 1], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      const f4 s = tq3_scores<D>(cur, sq, lane, j, one024);
+      const h4 pa = st.softmax(s, ntok, lo_sel, j);
+      tq3_pv<D>(cur, pa, st.O, lane, j, one024);
     }
-    wait_vmem<0>();                               // no staging load may land after this point
-    __syncthreads();                              // the staging ring becomes the merge buffer
+  } else {
+    // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
+    // page k is computed, and V of page k+1 while K of page k+1 is
+    for (int k = 0; k < my_pages; ++k) {
+      wait_vmem<kRows>();                     // K of page k has landed
+      __builtin_amdgcn_sched_barrier(0);
+      const int e = wave + kWaves * k;
+      const int ntok = (e == count - 1) ? last_tok : kPage;
+      const f4 s = fp8_scores<D>(slot0, sq, lane, j);
+      const h4 pa = st.softmax(s, ntok, lo_sel, j);
+      const uint8_t* pn = page_src(k + 1);
+      stage_issue<D>(pn, slot0, lane, kPage * D);
+      wait_vmem<kRows>();                     // V of page k has landed
+      __builtin_amdgcn_sched_barrier(0);
+      fp8_pv<D>(slot1, pa, st.O, lane, j);
+      stage_issue<D>(pn + kPage * D, slot1, lane, kPage * D);
+    }
+  }
+  wait_vmem<0>();                               // no staging load may land after this point
+  __syncthreads();                              // the staging block becomes the merge buffer
 
-    // ---- wave state -> LDS: O rows i (hi) + i + 8 (lo) live in lanes l and l ^ 32 ----
-    const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
-    l_run = sum_xor32(sum_xor16(l_run));        // sum over the four token rows of column n
+  // ---- merge of the 4 wave states: each wave rescales its rows to the
+  //      common maximum, then the workgroup sums the 4 states in a fixed order
+  float* const so = reinterpret_cast<float*>(smem);
+  float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][kMaxG]
+  float* const sl = sm + kWaves * kMaxG;
+  const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
+  if (j == 0 && n < G) {
+    sm[wave * kMaxG + n] = st.m_run;
+    sl[wave * kMaxG + n] = l_tot;
+  }
+  __syncthreads();
+  // O rows 4j + r (lanes j < 2 after adding the lo rows of lanes l ^ 32)
+  const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
+  float wr[4];
 #pragma unroll
-    for (int T = 0; T < NT; ++T) {
+  for (int r = 0; r < 4; ++r) {
+    const int row = (4 * j + r) & (kMaxG - 1);
+    float M = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float tot = sum_xor32(O[T][r]);
-        const int row = 4 * j + r;
-        if (j < 2 && row < G) so[MergeLayout<D>::at(wave, row, n, T)] = tot * vscale;
-      }
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + row]);
+    const float mw = sm[wave * kMaxG + row];
+    wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * vscale;
+  }
+  // tiles T and T + NT/2 share one permlane32 swap: lanes 0..31 end up with
+  // tile T's rows 4j + r (hi + lo), lanes 32..63 with tile T + NT/2's
+  const int jj = j & 1, thalf = j >> 1;
+#pragma unroll
+  for (int T = 0; T < GD::NT / 2; ++T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.O[T][r]),
+                                                       __float_as_uint(st.O[T + GD::NT / 2][r]), false, false);
+      const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      const int row = 4 * jj + r;
+      if (row < G) so[MergeLayout<D>::at(wave, row, n, T + thalf * (GD::NT / 2))] = tot * wr[r];
     }
-    if (j == 0 && n < G) {
-      sm[wave][n] = m_run;
-      sl[wave][n] = l_run;
-    }
-    __syncthreads();
+  }
+  __syncthreads();
 
-    // ---- merge the 4 wave states and write the item's partial ----
-    const size_t slot = ((size_t)layer * plan.np_cap + pidx) * hkv + h;
-    float* __restrict__ ml = plan.part_ml + slot * G * 2;
-    float* __restrict__ pa_out = plan.part_acc + slot * G * D;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-      const int i = idx / D, c = idx - (idx / D) * D;
-      float M = -INFINITY;
+  const size_t pslot = ((size_t)layer * plan.np_cap + pidx) * hkv + h;
+  float* __restrict__ ml = plan.part_ml + pslot * G * 2;
+  float* __restrict__ pa_out = plan.part_acc + pslot * G * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int i = idx / D, c = idx - (idx / D) * D;
+    const int at0 = MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+    float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w][i]);
-      float acc = 0.0f;
+    for (int w = 0; w < kWaves; ++w) acc += so[at0 + w * MergeLayout<D>::kWave];
+    pa_out[idx] = acc;
+  }
+  if (threadIdx.x < G) {
+    const int i = threadIdx.x;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float wgt = (sm[w][i] == -INFINITY) ? 0.0f : exp2f(sm[w][i] - M);
-        acc = fmaf(wgt, so[MergeLayout<D>::at(w, i, c / (D / 16), c % (D / 16))], acc);
-      }
-      pa_out[idx] = acc;
-      if (c == 0) {
-        float L = 0.0f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + i]);
+    float L = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          L += (sm[w][i] == -INFINITY) ? 0.0f : sl[w][i] * exp2f(sm[w][i] - M);
-        ml[2 * i] = M;
-        ml[2 * i + 1] = L;
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm[w * kMaxG + i];
+      L += (mw == -INFINITY) ? 0.0f : sl[w * kMaxG + i] * __builtin_amdgcn_exp2f(mw - M);
     }
+    ml[2 * i] = M;
+    ml[2 * i + 1] = L;
+  }
 }
 
 // MODE selects which format's work items the launch takes (kBoth: the FP8
 // items first, then the TQ3 items, in one grid so the small FP8 share runs
 // alongside the TQ3 stream; each item runs its own format's code path).
+// 40 KB of LDS and at most 128 VGPRs per thread: four workgroups per CU.
 #ifndef MKV_OCC
-#define MKV_OCC 3
+#define MKV_OCC 4
 #endif
 template <int D, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
     LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
     float qscale, Plan plan) {
-  constexpr int NG = D / 32;
-  constexpr int kSlot = Stage<D>::kSlot;
-  constexpr int kStageBytes = kWaves * kStages * kSlot;
-  constexpr int kMergeBytes = MergeLayout<D>::kBytes;
-  // the staging ring and the end-of-item merge buffer share LDS
-  __shared__ __align__(16) uint8_t smem[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
-  __shared__ float sm[kWaves][kMaxG], sl[kWaves][kMaxG];
-  __shared__ int sids[kWaves][kMaxChunkPages / kWaves];
-  __shared__ h8 sq[NG * 64];                 // score-MFMA B operands, [group][lane]
+  __shared__ __align__(16) uint8_t smem[Geo<D>::kLds];
 
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
@@ -487,22 +585,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MKV_OC
     const int h = (int)(it % hkv);
     const int chunk = (int)((it / hkv) % nch);
     const int layer = (int)(it / ((long)hkv * nch));
-    const int4 cd = (tq3 ? plan.chunks_t : plan.chunks_f)[chunk];
-    const int b = cd.x, start = cd.y, count = cd.z & 0xffff, last_tok = cd.z >> 16, pidx = cd.w;
+    const i4v cd = ((cptr_i4)(tq3 ? plan.chunks_t : plan.chunks_f))[chunk];
+    const int b = cd[0], start = cd[1], count = cd[2] & 0xffff, last_tok = cd[2] >> 16, pidx = cd[3];
     if (pidx >= plan.np_cap) {               // plan made for more layers than this call
       if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
       continue;
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true, kStages>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
-                        smem, sm, sl, sids, sq, one024);
+      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false, kStages>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
-                         smem, sm, sl, sids, sq, one024);
+      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024);
     __syncthreads();
   }
 }
-
 
 static dim3 attend_grid(long cap) {
   return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));

@@ -8,10 +8,11 @@
 //                  pages, check ids and tiers, and compact them into an FP8
 //                  list (tier R/A) and a TQ3 list (tier S) in logical order,
 //                  stored in the request's own CSR range.
-//   plan_chunks    (one workgroup): choose pages-per-chunk for each format so
-//                  that the whole batch yields about kTargetItems work items,
-//                  prefix-sum chunk / partial / merge counts over requests and
-//                  write the chunk tables.
+//   plan_chunks    (one workgroup): choose one pages-per-chunk for both
+//                  formats so that the whole batch yields about kTargetItems
+//                  work items (one per workgroup slot of the GPU), prefix-sum
+//                  chunk and partial counts over requests and write the chunk
+//                  tables.
 // Device-data errors set MKV_DEV_* bits and mark the request invalid (its
 // outputs become NaN); nothing is ever read out of bounds.
 #include "mkv_format.h"
@@ -135,8 +136,13 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   }
   const int status = sh[0];
   __syncthreads();
-  const int ppf = min(kMaxChunkPages, max(kMinChunkPages, (TF + plan.chunks_target - 1) / plan.chunks_target));
-  const int ppt = min(kMaxChunkPages, max(kMinChunkPages, (TT + plan.chunks_target - 1) / plan.chunks_target));
+  // One chunk size for both formats, so the work items of a launch are of
+  // equal size whatever the mix: about chunks_target chunks in all, less one
+  // tail chunk per request and format, so the items fill one wave of
+  // workgroups.
+  const int tgt = max(1, plan.chunks_target - 2 * B);
+  const int ppf = min(kMaxChunkPages, max(kMinChunkPages, (TF + TT + tgt - 1) / tgt));
+  const int ppt = ppf;
   // per-request counts and their prefix sums
   int carry_f = 0, carry_t = 0, carry_p = 0;
   for (int base = 0; base < B; base += 1024) {
