@@ -17,7 +17,13 @@
 namespace mkv {
 
 constexpr int kMaxLayers = 64;        // layers covered by one launch
-constexpr int kTargetItems = 1024;    // split-K work items (workgroups) aimed for per format: 4 per CU
+#ifndef MKV_WAVES
+#define MKV_WAVES 4
+#endif
+constexpr int kItemWaves = MKV_WAVES;  // waves (of 64 lanes) that share one split-K work item
+// split-K work items aimed for per launch: one wave of workgroups at four
+// waves per SIMD on 256 CUs
+constexpr int kTargetItems = 4096 / kItemWaves;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk (a workgroup stages its page ids in LDS)
 constexpr int kMaxG = 8;              // query heads per KV head supported

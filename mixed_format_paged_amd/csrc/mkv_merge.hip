@@ -3,37 +3,82 @@
 // Minima-KV combines the format-specific partial attention states through a
 // globally normalised online-softmax merge (arXiv 2608.23834, page 1,
 // Abstract): with partials (m_p, l_p, acc_p) in log2 units,
-//   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p acc_p 2^(m_p - M) / L,
-//   lse = (M + log2 L) * ln 2.
-// The order of summation is fixed (partial index order), so results are
-// bitwise reproducible run to run.
+//   M = max_p m_p,  w_p = 2^(m_p - M),  L = sum_p l_p w_p,
+//   o = sum_p acc_p w_p / L,  lse = (M + log2 L) * ln 2.
+// One launch merges any number of partials per request.  A workgroup takes
+// (layer, request, KV head, slice of kSliceC channels):
+//   1. each thread requests its share of the partial states (registers) and
+//      the workgroup the (m, l) pairs of the request (LDS), in one go;
+//   2. M per query head, then the weights w_p into LDS (one exp2 per partial
+//      and head, shared by every channel of the slice) and L: one wave per
+//      head, lanes strided over partials, DPP / permlane reductions;
+//   3. each (head, channel) pair of the slice is summed by several threads
+//      over interleaved partials, and their sums are added in a fixed order.
+// Every sum runs in a fixed order, so results are bitwise reproducible.
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
 namespace mkv {
 
 namespace {
+
 __device__ inline const int* req_row(const Plan& p, int field) { return p.req + (size_t)field * (p.batch + 1); }
+
+constexpr int kThreads = 256;
+#ifndef MKV_MERGE_SLICE
+#define MKV_MERGE_SLICE 8
+#endif
+constexpr int kSliceC = MKV_MERGE_SLICE;                       // channels per workgroup
+constexpr int kTileP = 512;                      // partials whose weights sit in LDS at once
+constexpr int kReg = 32;                         // partial states a thread prefetches into registers
+
+// Reductions over a wave without LDS: DPP row rotates inside each 16-lane
+// row, then the gfx950 permlane swaps across rows; every lane gets the result.
+template <int K>
+__device__ inline float ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + K, 0xf, 0xf, false));
+}
+__device__ inline float wave_max(float x) {
+  x = fmaxf(x, ror<1>(x));
+  x = fmaxf(x, ror<2>(x));
+  x = fmaxf(x, ror<4>(x));
+  x = fmaxf(x, ror<8>(x));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float wave_sum(float x) {
+  x += ror<1>(x);
+  x += ror<2>(x);
+  x += ror<4>(x);
+  x += ror<8>(x);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace
 
-// Single-launch merge: one workgroup per (layer, request, KV head, slice of
-// kSliceC channels).  Waves reduce M and L per query head over all the
-// request's partials (both formats); each thread then accumulates one
-// (head, channel) output over the partials in index order.  No intermediate
-// states and no second launch, whatever the number of partials.
-constexpr int kSliceC = 32;
-
 template <int D>
-__global__ void __launch_bounds__(256) merge_slices_kernel(int n_layers, int hkv, int G, Plan plan,
-                                                           float* __restrict__ out, float* __restrict__ lse,
-                                                           size_t out_ls, size_t lse_ls) {
+__global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int G, Plan plan,
+                                                         float* __restrict__ out, float* __restrict__ lse,
+                                                         size_t out_ls, size_t lse_ls) {
   constexpr int NS = D / kSliceC;
+  __shared__ float sw[kTileP * kMaxG];          // weights of the current tile, [p][i]
+  __shared__ float sml[kTileP * kMaxG * 2];     // (m, l) of the current tile, [p][i][2]
+  __shared__ float sred[kThreads];              // per-thread sums, [sub][pair]
   __shared__ float sM[kMaxG], sL[kMaxG];
   const int B = plan.batch;
   const int* poff = req_row(plan, R_POFF);
   const int* inval = req_row(plan, R_INVALID);
   const int hq = hkv * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int npair = G * kSliceC;
+  const int nsub = kThreads / npair;            // threads per pair
+  const int pair = tid % npair, sub = tid / npair;
+  const int pi = pair / kSliceC, pc = pair % kSliceC;
   const long items = (long)n_layers * B * hkv * NS;
   for (long item = blockIdx.x; item < items; item += gridDim.x) {
     const int cs = (int)(item % NS);
@@ -41,49 +86,87 @@ __global__ void __launch_bounds__(256) merge_slices_kernel(int n_layers, int hkv
     const int b = (int)((item / ((long)NS * hkv)) % B);
     const int layer = (int)(item / ((long)NS * hkv * B));
     const int p0 = poff[b], np = poff[b + 1] - poff[b];
-    float* out_row = out + layer * out_ls + ((size_t)b * hq + (size_t)h * G) * D;
+    float* out_row = out + layer * out_ls + ((size_t)b * hq + (size_t)h * G) * D + cs * kSliceC;
     float* lse_row = lse ? lse + layer * lse_ls + (size_t)b * hq + (size_t)h * G : nullptr;
-    if (inval[b] || np == 0 || p0 + np > plan.np_cap) {   // uniform per block
+    if (inval[b] || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
       const bool nan = inval[b] != 0 || np != 0;
-      for (int idx = tid; idx < G * kSliceC; idx += 256)
-        out_row[(idx / kSliceC) * D + cs * kSliceC + idx % kSliceC] = nan ? __int_as_float(0x7fc00000) : 0.0f;
+      if (tid < npair) out_row[(size_t)pi * D + pc] = nan ? __int_as_float(0x7fc00000) : 0.0f;
       if (cs == 0 && lse_row && tid < G) lse_row[tid] = nan ? __int_as_float(0x7fc00000) : -INFINITY;
       continue;
     }
     const size_t sstride = (size_t)hkv * G;                 // states between consecutive partials
     const float* ml = plan.part_ml + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * 2;
-    const float* acc = plan.part_acc + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * D;
-    // M and L of head i by wave i % 4, lanes strided over the partials
-    for (int i = wave; i < G; i += 4) {
-      float M = -INFINITY;
-      for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[(p * sstride + i) * 2]);
+    const float* acc = plan.part_acc + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * D
+                       + cs * kSliceC;
+    // 1. This thread's partial states of the tile go to registers and the
+    //    tile's (m, l) of every query head to LDS, all requested at once.
+    // 2. M per query head (first tile), then the weights and L of the tile:
+    //    one wave per head.
+    // 3. The (head, channel) sums over interleaved partials.
+    float a = 0.0f;
+    for (int t0 = 0; t0 < np; t0 += kTileP) {
+      const int nt = np - t0 < kTileP ? np - t0 : kTileP;
+      const float* ap = acc + (size_t)pi * D + pc + (size_t)t0 * sstride * D;
+      const int cnt = sub < nsub ? (nt - sub + nsub - 1) / nsub : 0;   // this thread's partials
+      const bool in_regs = nt <= nsub * kReg;                        // uniform
+      float av[kReg];
+      if (in_regs) {
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-      float L = 0.0f;
-      if (M != -INFINITY)
-        for (int p = lane; p < np; p += 64) {
-          const float m = ml[(p * sstride + i) * 2];
-          if (m != -INFINITY) L += ml[(p * sstride + i) * 2 + 1] * exp2f(m - M);
-        }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-      if (lane == 0) { sM[i] = M; sL[i] = L; }
-    }
-    __syncthreads();
-    if (tid < G * kSliceC) {
-      const int i = tid / kSliceC, c = cs * kSliceC + tid % kSliceC;
-      const float M = sM[i];
-      const float* ap = acc + (size_t)i * D + c;
-      const float* mp = ml + (size_t)i * 2;
-      float a = 0.0f;
-#pragma unroll 8
-      for (int p = 0; p < np; ++p) {
-        const float m = mp[p * sstride * 2];
-        const float v = ap[p * sstride * D];
-        a = fmaf(m == -INFINITY ? 0.0f : exp2f(m - M), v, a);
+        for (int k = 0; k < kReg; ++k)
+          av[k] = k < cnt ? ap[(size_t)(sub + k * nsub) * sstride * D] : 0.0f;
       }
-      const float L = sL[i];
-      out_row[(size_t)i * D + c] = L > 0.0f ? a / L : 0.0f;
+      for (int idx = tid; idx < nt * 2 * G; idx += kThreads) {      // (m, l) rows of 2G floats
+        const int p = idx / (2 * G), k = idx - p * (2 * G);
+        sml[idx] = ml[(t0 + p) * sstride * 2 + k];
+      }
+      __syncthreads();
+      if (t0 == 0) {
+        for (int i = wave; i < G; i += kThreads / 64) {
+          float M = -INFINITY;
+          for (int p = lane; p < nt; p += 64) M = fmaxf(M, sml[p * 2 * G + 2 * i]);
+          M = wave_max(M);
+          if (lane == 0) { sM[i] = M; sL[i] = 0.0f; }
+        }
+        if (nt < np) {                                              // rare: the other tiles' maxima
+          __syncthreads();
+          for (int i = wave; i < G; i += kThreads / 64) {
+            float M = sM[i];
+            for (int p = nt + lane; p < np; p += 64) M = fmaxf(M, ml[(p * sstride + i) * 2]);
+            M = wave_max(M);
+            if (lane == 0) sM[i] = M;
+          }
+        }
+        __syncthreads();
+      }
+      for (int i = wave; i < G; i += kThreads / 64) {
+        const float M = sM[i];
+        float l = 0.0f;
+        for (int p = lane; p < nt; p += 64) {
+          const float m = sml[p * 2 * G + 2 * i];
+          const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+          sw[p * G + i] = w;
+          l += sml[p * 2 * G + 2 * i + 1] * w;
+        }
+        l = wave_sum(l);
+        if (lane == 0) sL[i] += l;
+      }
+      __syncthreads();
+      if (in_regs) {
+#pragma unroll
+        for (int k = 0; k < kReg; ++k)
+          if (k < cnt) a = fmaf(sw[(sub + k * nsub) * G + pi], av[k], a);
+      } else {
+        for (int k = 0; k < cnt; ++k) a = fmaf(sw[(sub + k * nsub) * G + pi], ap[(size_t)(sub + k * nsub) * sstride * D], a);
+      }
+      __syncthreads();
+    }
+    sred[tid] = a;
+    __syncthreads();
+    if (tid < npair) {
+      float o = 0.0f;
+      for (int s = 0; s < nsub; ++s) o += sred[s * npair + tid];
+      const float L = sL[pi];
+      out_row[(size_t)pi * D + pc] = L > 0.0f ? o / L : 0.0f;
     }
     if (cs == 0 && lse_row && tid < G)
       lse_row[tid] = sL[tid] > 0.0f ? (sM[tid] + log2f(sL[tid])) * 0.69314718055994531f : -INFINITY;
@@ -94,11 +177,11 @@ __global__ void __launch_bounds__(256) merge_slices_kernel(int n_layers, int hkv
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse,
                         size_t out_ls, size_t lse_ls, hipStream_t stream) {
   const long cap = (long)n_layers * plan.batch * g.hkv * (g.d / kSliceC);
-  const dim3 grid((unsigned)(cap < 4096 ? (cap > 0 ? cap : 1) : 4096));
+  const dim3 grid((unsigned)(cap < 8192 ? (cap > 0 ? cap : 1) : 8192));
   if (g.d == 256)
-    hipLaunchKernelGGL(merge_slices_kernel<256>, grid, dim3(256), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
   else
-    hipLaunchKernelGGL(merge_slices_kernel<128>, grid, dim3(256), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
   return hipGetLastError();
 }
 

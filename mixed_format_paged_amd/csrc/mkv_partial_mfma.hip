@@ -41,7 +41,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kItemWaves;
+constexpr int kThreads = 64 * kWaves;
 // The running max moves only when a page's max exceeds it by more than
 // kRescale (log2 units), so p <= 2^15 stays finite in fp16.
 constexpr float kRescale = 15.0f;
@@ -178,11 +179,11 @@ struct MergeLayout {
   static constexpr int kRow = 16 * kSlice + 8;
   static constexpr int kWave = kMaxG * kRow;
   static constexpr int kStates = kWaves * kWave;                 // floats
-  static constexpr int kBytes = (kStates + 2 * kWaves * kMaxG) * 4;
+  static constexpr int kBytes = (kStates + (2 * kWaves + 1) * kMaxG) * 4;
   __device__ static inline int at(int w, int i, int n, int T) { return w * kWave + i * kRow + n * kSlice + T; }
 };
-static_assert(MergeLayout<256>::kBytes <= Geo<256>::kLds, "merge buffer must fit the staging block");
-static_assert(MergeLayout<128>::kBytes <= Geo<128>::kLds, "merge buffer must fit the staging block");
+template <int D>
+constexpr int kSmemBytes = Geo<D>::kLds > MergeLayout<D>::kBytes ? Geo<D>::kLds : MergeLayout<D>::kBytes;
 
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
@@ -414,17 +415,15 @@ __device__ __forceinline__ void run_item(
   const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
   // page k of this wave (clamped: past the end the last page is re-read, an
   // L2 hit, so every wave issues the same number of staging loads)
-  auto page_src = [&](int k) {
-    const int kk = k < my_pages ? k : my_pages - 1;
-    return head + (size_t)list[start + wave + kWaves * kk] * page_bytes;
-  };
+  auto page_id = [&](int k) { return list[start + wave + kWaves * (k < my_pages ? k : my_pages - 1)]; };
+  auto page_src = [&](int id) { return head + (size_t)id * page_bytes; };
 
   // first unit(s) in flight before the query fragments are built
   if (my_pages > 0) {
     if (tq3) {
-      stage_issue<D>(page_src(0), slot0, lane, tq3_head_bytes(D));
+      stage_issue<D>(page_src(page_id(0)), slot0, lane, tq3_head_bytes(D));
     } else {
-      const uint8_t* p0 = page_src(0);
+      const uint8_t* p0 = page_src(page_id(0));
       stage_issue<D>(p0, slot0, lane, kPage * D);
       stage_issue<D>(p0 + kPage * D, slot1, lane, kPage * D);
     }
@@ -432,7 +431,7 @@ __device__ __forceinline__ void run_item(
 
   // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
   //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder ----
-  for (int e = threadIdx.x; e < NG * 64; e += 256) {
+  for (int e = threadIdx.x; e < NG * 64; e += kThreads) {
     const int g = e >> 6, ln = e & 63;
     const int nn = ln & 15, jj = ln >> 4;
     const int row = nn < 8 ? nn : nn - 8;
@@ -458,10 +457,13 @@ __device__ __forceinline__ void run_item(
   st.init();
   if (tq3) {
     // two slots: page k+1 travels while page k is computed
+    int id_next = page_id(1);                 // page ids travel one page ahead of their loads
     for (int k = 0; k < my_pages; ++k) {
       uint8_t* const cur = (k & 1) ? slot1 : slot0;
       uint8_t* const nxt = (k & 1) ? slot0 : slot1;
-      stage_issue<D>(page_src(k + 1), nxt, lane, tq3_head_bytes(D));
+      const uint8_t* const nsrc = page_src(id_next);
+      id_next = page_id(k + 2);
+      stage_issue<D>(nsrc, nxt, lane, tq3_head_bytes(D));
       wait_vmem<kRows>();                     // page k has landed
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
@@ -473,6 +475,7 @@ __device__ __forceinline__ void run_item(
   } else {
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
     // page k is computed, and V of page k+1 while K of page k+1 is
+    int id_next = page_id(1);
     for (int k = 0; k < my_pages; ++k) {
       wait_vmem<kRows>();                     // K of page k has landed
       __builtin_amdgcn_sched_barrier(0);
@@ -480,7 +483,8 @@ __device__ __forceinline__ void run_item(
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D>(slot0, sq, lane, j);
       const h4 pa = st.softmax(s, ntok, lo_sel, j);
-      const uint8_t* pn = page_src(k + 1);
+      const uint8_t* pn = page_src(id_next);
+      id_next = page_id(k + 2);
       stage_issue<D>(pn, slot0, lane, kPage * D);
       wait_vmem<kRows>();                     // V of page k has landed
       __builtin_amdgcn_sched_barrier(0);
@@ -491,32 +495,35 @@ __device__ __forceinline__ void run_item(
   wait_vmem<0>();                               // no staging load may land after this point
   __syncthreads();                              // the staging block becomes the merge buffer
 
-  // ---- merge of the 4 wave states: each wave rescales its rows to the
-  //      common maximum, then the workgroup sums the 4 states in a fixed order
+  // ---- merge of the wave states: each wave rescales its rows to the common
+  //      maximum, then the workgroup sums the states in a fixed order
   float* const so = reinterpret_cast<float*>(smem);
-  float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][kMaxG]
-  float* const sl = sm + kWaves * kMaxG;
+  float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][kMaxG] maxima, then [kMaxG] their max
+  float* const sl = sm + kWaves * kMaxG;                 // [kWaves][kMaxG]
+  float* const sM = sl + kWaves * kMaxG;                 // [kMaxG]
   const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
   if (j == 0 && n < G) {
     sm[wave * kMaxG + n] = st.m_run;
     sl[wave * kMaxG + n] = l_tot;
   }
   __syncthreads();
-  // O rows 4j + r (lanes j < 2 after adding the lo rows of lanes l ^ 32)
+  if (threadIdx.x < kMaxG) {
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + threadIdx.x]);
+    sM[threadIdx.x] = M;
+  }
+  __syncthreads();
+  // O rows 4jj + r: after the swap below, lanes 0..31 (j < 2) hold the rows of
+  // tile T, lanes 32..63 those of tile T + NT/2
+  const int jj = j & 1, thalf = j >> 1;
   const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
   float wr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = (4 * j + r) & (kMaxG - 1);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + row]);
+    const int row = 4 * jj + r;
     const float mw = sm[wave * kMaxG + row];
-    wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * vscale;
+    wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
   }
-  // tiles T and T + NT/2 share one permlane32 swap: lanes 0..31 end up with
-  // tile T's rows 4j + r (hi + lo), lanes 32..63 with tile T + NT/2's
-  const int jj = j & 1, thalf = j >> 1;
 #pragma unroll
   for (int T = 0; T < GD::NT / 2; ++T) {
 #pragma unroll
@@ -533,21 +540,18 @@ __device__ __forceinline__ void run_item(
   const size_t pslot = ((size_t)layer * plan.np_cap + pidx) * hkv + h;
   float* __restrict__ ml = plan.part_ml + pslot * G * 2;
   float* __restrict__ pa_out = plan.part_acc + pslot * G * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int i = idx / D, c = idx - (idx / D) * D;
-    const int at0 = MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+    const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
     float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += so[at0 + w * MergeLayout<D>::kWave];
-    pa_out[idx] = acc;
+#pragma unroll 4
+    for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
+    __builtin_nontemporal_store(acc, pa_out + idx);   // streamed out: read once, by the merge
   }
   if (threadIdx.x < G) {
     const int i = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + i]);
+    const float M = sM[i];
     float L = 0.0f;
-#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm[w * kMaxG + i];
       L += (mw == -INFINITY) ? 0.0f : sl[w * kMaxG + i] * __builtin_amdgcn_exp2f(mw - M);
@@ -565,10 +569,10 @@ __device__ __forceinline__ void run_item(
 #define MKV_OCC 4
 #endif
 template <int D, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
     LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
     float qscale, Plan plan) {
-  __shared__ __align__(16) uint8_t smem[Geo<D>::kLds];
+  __shared__ __align__(16) uint8_t smem[kSmemBytes<D>];
 
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
@@ -607,7 +611,7 @@ template <int MODE>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, hipStream_t stream) {
   const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2);
-  const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(256);
+  const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(kThreads);
   if (g.d == 256)
     hipLaunchKernelGGL((attend_kernel<256, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan);
