@@ -6,7 +6,7 @@
 //   M = max_p m_p,  w_p = 2^(m_p - M),  L = sum_p l_p w_p,
 //   o = sum_p acc_p w_p / L,  lse = (M + log2 L) * ln 2.
 // One launch merges any number of partials per request.  A workgroup takes
-// (layer, request, KV head, slice of kSliceC channels):
+// (layer, request, KV head, slice of 32 channels), 512 threads:
 //   1. each thread requests its share of the partial states (registers) and
 //      the workgroup the (m, l) pairs of the request (LDS), in one go;
 //   2. M per query head, then the weights w_p into LDS (one exp2 per partial
@@ -24,13 +24,14 @@ namespace {
 
 __device__ inline const int* req_row(const Plan& p, int field) { return p.req + (size_t)field * (p.batch + 1); }
 
-constexpr int kThreads = 256;
-#ifndef MKV_MERGE_SLICE
-#define MKV_MERGE_SLICE 8
-#endif
-constexpr int kSliceC = MKV_MERGE_SLICE;                       // channels per workgroup
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 512;
+constexpr int kSliceC = 32;                      // channels per workgroup
+constexpr int kQuads = kSliceC / 4;              // float4 columns of a slice
+constexpr int kSubs = kThreads / (kMaxG * kQuads);   // threads sharing one (head, float4 column)
 constexpr int kTileP = 512;                      // partials whose weights sit in LDS at once
-constexpr int kReg = 32;                         // partial states a thread prefetches into registers
+constexpr int kReg = 16;                         // partial states (float4) a thread prefetches
 
 // Reductions over a wave without LDS: DPP row rotates inside each 16-lane
 // row, then the gfx950 permlane swaps across rows; every lane gets the result.
@@ -61,6 +62,10 @@ __device__ inline float wave_sum(float x) {
 
 }  // namespace
 
+// Thread t takes float4 column q = t % kQuads of the slice, query head
+// i = (t / kQuads) % kMaxG (idle when i >= G) and every kSubs-th partial from
+// sub = t / (kQuads kMaxG): its loads are 16-byte vectors, and the kQuads
+// threads of one (partial, head) read one contiguous 128-byte line.
 template <int D>
 __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int G, Plan plan,
                                                          float* __restrict__ out, float* __restrict__ lse,
@@ -68,17 +73,15 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   constexpr int NS = D / kSliceC;
   __shared__ float sw[kTileP * kMaxG];          // weights of the current tile, [p][i]
   __shared__ float sml[kTileP * kMaxG * 2];     // (m, l) of the current tile, [p][i][2]
-  __shared__ float sred[kThreads];              // per-thread sums, [sub][pair]
+  __shared__ f4v sred[kThreads];                // per-thread sums, [sub][i][q]
   __shared__ float sM[kMaxG], sL[kMaxG];
   const int B = plan.batch;
   const int* poff = req_row(plan, R_POFF);
   const int* inval = req_row(plan, R_INVALID);
   const int hq = hkv * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int npair = G * kSliceC;
-  const int nsub = kThreads / npair;            // threads per pair
-  const int pair = tid % npair, sub = tid / npair;
-  const int pi = pair / kSliceC, pc = pair % kSliceC;
+  const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
+  const bool live = pi < G;
   const long items = (long)n_layers * B * hkv * NS;
   for (long item = blockIdx.x; item < items; item += gridDim.x) {
     const int cs = (int)(item % NS);
@@ -90,36 +93,35 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
     float* lse_row = lse ? lse + layer * lse_ls + (size_t)b * hq + (size_t)h * G : nullptr;
     if (inval[b] || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
       const bool nan = inval[b] != 0 || np != 0;
-      if (tid < npair) out_row[(size_t)pi * D + pc] = nan ? __int_as_float(0x7fc00000) : 0.0f;
+      if (sub == 0 && live)
+        *reinterpret_cast<f4v*>(out_row + (size_t)pi * D + 4 * qc) = nan ? f4v{NAN, NAN, NAN, NAN} : f4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (cs == 0 && lse_row && tid < G) lse_row[tid] = nan ? __int_as_float(0x7fc00000) : -INFINITY;
       continue;
     }
     const size_t sstride = (size_t)hkv * G;                 // states between consecutive partials
     const float* ml = plan.part_ml + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * 2;
     const float* acc = plan.part_acc + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * D
-                       + cs * kSliceC;
-    // 1. This thread's partial states of the tile go to registers and the
-    //    tile's (m, l) of every query head to LDS, all requested at once.
-    // 2. M per query head (first tile), then the weights and L of the tile:
-    //    one wave per head.
-    // 3. The (head, channel) sums over interleaved partials.
-    float a = 0.0f;
+                       + cs * kSliceC + (size_t)(live ? pi : 0) * D + 4 * qc;
+    f4v a = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     for (int t0 = 0; t0 < np; t0 += kTileP) {
       const int nt = np - t0 < kTileP ? np - t0 : kTileP;
-      const float* ap = acc + (size_t)pi * D + pc + (size_t)t0 * sstride * D;
-      const int cnt = sub < nsub ? (nt - sub + nsub - 1) / nsub : 0;   // this thread's partials
-      const bool in_regs = nt <= nsub * kReg;                        // uniform
-      float av[kReg];
+      const float* ap = acc + (size_t)t0 * sstride * D;
+      const int cnt = live ? (nt - sub + kSubs - 1) / kSubs : 0;   // this thread's partials
+      const bool in_regs = nt <= kSubs * kReg;                   // uniform
+      // 1. this thread's partial states to registers, the tile's (m, l) to LDS
+      f4v av[kReg];
       if (in_regs) {
 #pragma unroll
         for (int k = 0; k < kReg; ++k)
-          av[k] = k < cnt ? ap[(size_t)(sub + k * nsub) * sstride * D] : 0.0f;
+          av[k] = k < cnt ? *reinterpret_cast<const f4v*>(ap + (size_t)(sub + k * kSubs) * sstride * D)
+                          : f4v{0.0f, 0.0f, 0.0f, 0.0f};
       }
       for (int idx = tid; idx < nt * 2 * G; idx += kThreads) {      // (m, l) rows of 2G floats
         const int p = idx / (2 * G), k = idx - p * (2 * G);
         sml[idx] = ml[(t0 + p) * sstride * 2 + k];
       }
       __syncthreads();
+      // 2. M per query head (first tile), then the tile's weights and L
       if (t0 == 0) {
         for (int i = wave; i < G; i += kThreads / 64) {
           float M = -INFINITY;
@@ -127,7 +129,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
           M = wave_max(M);
           if (lane == 0) { sM[i] = M; sL[i] = 0.0f; }
         }
-        if (nt < np) {                                              // rare: the other tiles' maxima
+        if (nt < np) {                                              // the other tiles' maxima
           __syncthreads();
           for (int i = wave; i < G; i += kThreads / 64) {
             float M = sM[i];
@@ -151,22 +153,25 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
         if (lane == 0) sL[i] += l;
       }
       __syncthreads();
+      // 3. this thread's interleaved partials, in index order
       if (in_regs) {
 #pragma unroll
         for (int k = 0; k < kReg; ++k)
-          if (k < cnt) a = fmaf(sw[(sub + k * nsub) * G + pi], av[k], a);
+          if (k < cnt) a += sw[(sub + k * kSubs) * G + pi] * av[k];
       } else {
-        for (int k = 0; k < cnt; ++k) a = fmaf(sw[(sub + k * nsub) * G + pi], ap[(size_t)(sub + k * nsub) * sstride * D], a);
+        for (int k = 0; k < cnt; ++k)
+          a += sw[(sub + k * kSubs) * G + pi] * *reinterpret_cast<const f4v*>(ap + (size_t)(sub + k * kSubs) * sstride * D);
       }
       __syncthreads();
     }
     sred[tid] = a;
     __syncthreads();
-    if (tid < npair) {
-      float o = 0.0f;
-      for (int s = 0; s < nsub; ++s) o += sred[s * npair + tid];
+    if (sub == 0 && live) {
+      f4v o = a;
+      for (int s = 1; s < kSubs; ++s) o += sred[s * kQuads * kMaxG + tid];
       const float L = sL[pi];
-      out_row[(size_t)pi * D + pc] = L > 0.0f ? o / L : 0.0f;
+      const f4v r = L > 0.0f ? o / L : f4v{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<f4v*>(out_row + (size_t)pi * D + 4 * qc) = r;
     }
     if (cs == 0 && lse_row && tid < G)
       lse_row[tid] = sL[tid] > 0.0f ? (sM[tid] + log2f(sL[tid])) * 0.69314718055994531f : -INFINITY;
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse,
                         size_t out_ls, size_t lse_ls, hipStream_t stream) {
   const long cap = (long)n_layers * plan.batch * g.hkv * (g.d / kSliceC);
-  const dim3 grid((unsigned)(cap < 8192 ? (cap > 0 ? cap : 1) : 8192));
+  const dim3 grid((unsigned)(cap < 4096 ? (cap > 0 ? cap : 1) : 4096));
   if (g.d == 256)
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
   else
