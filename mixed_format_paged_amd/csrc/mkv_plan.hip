@@ -22,32 +22,63 @@ namespace mkv {
 
 namespace {
 
-// Exclusive scan of one int per thread over a block of BLOCK threads.
-template <int BLOCK>
-__device__ int block_exclusive_scan(int v, int* total, int* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < BLOCK; off <<= 1) {
-    int add = (tid >= off) ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+// Exclusive scan of one value per thread over a block of BLOCK threads (T is
+// int or a pair of int counts packed in a 64-bit word, which add field-wise
+// as long as each field's total stays below 2^32).  Each wave scans its 64
+// values with shuffles, one wave scans the wave totals, two barriers in all.
+template <int BLOCK, typename T>
+__device__ T block_exclusive_scan(T v, T* total, T* sh) {
+  static_assert(BLOCK % 64 == 0 && BLOCK / 64 <= 64, "block of whole waves");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  T x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  const int incl = sh[tid];
-  *total = sh[BLOCK - 1];
+  if (lane == 63) sh[wave] = x;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    T w = lane < BLOCK / 64 ? sh[lane] : T(0);
+#pragma unroll
+    for (int o = 1; o < BLOCK / 64; o <<= 1) {
+      const T y = __shfl_up(w, o);
+      if (lane >= o) w += y;
+    }
+    if (lane < BLOCK / 64) sh[64 + lane] = w;                       // inclusive wave prefix
+  }
+  __syncthreads();
+  const T before = wave ? sh[64 + wave - 1] : T(0);
+  *total = sh[64 + BLOCK / 64 - 1];
+  __syncthreads();                                              // sh is reused by the caller
+  return before + x - v;
 }
+
+// Bitwise OR of the MKV_DEV_* bits over the block (__syncthreads_or is a
+// logical OR, so one call per bit).
+__device__ inline int block_or_bits(int v) {
+  return (__syncthreads_or(v & kDevBadPageId) ? kDevBadPageId : 0) |
+         (__syncthreads_or(v & kDevBadTier) ? kDevBadTier : 0) |
+         (__syncthreads_or(v & kDevBadSeqLen) ? kDevBadSeqLen : 0);
+}
+
+__device__ inline uint64_t pack2(int a, int b) { return (uint64_t)(uint32_t)a | ((uint64_t)(uint32_t)b << 32); }
+__device__ inline int lo32(uint64_t x) { return (int)(uint32_t)x; }
+__device__ inline int hi32(uint64_t x) { return (int)(uint32_t)(x >> 32); }
 
 __device__ inline int* req_row(const Plan& p, int field) { return p.req + (size_t)field * (p.batch + 1); }
 
+constexpr int kClassifyThreads = 1024;
+constexpr int kClassifyPages = 8;
+
 }  // namespace
 
-__global__ void __launch_bounds__(256) plan_classify(
+__global__ void __launch_bounds__(kClassifyThreads) plan_classify(
     const uint8_t* __restrict__ tier, int n_fp8, int n_tq3, const int32_t* __restrict__ bt_offsets,
     const int32_t* __restrict__ bt_pages, const int32_t* __restrict__ seq_lens, Plan plan) {
-  __shared__ int sh[256];
+  constexpr int P = kClassifyPages;                 // consecutive logical pages per thread
+  constexpr int SUPER = kClassifyThreads * P;
+  __shared__ int sh[128];
   __shared__ int s_last;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -66,44 +97,48 @@ __global__ void __launch_bounds__(256) plan_classify(
     return;
   }
   if (tid == 0) s_last = -1;
-  int nf = 0;      // FP8 pages so far (block-uniform)
+  int nf = 0;      // FP8 pages before the current super-block (block-uniform)
   int err = 0;     // per-thread error bits
-  for (int base = 0; base < n; base += 256) {
-    const int lp = base + tid;
-    int is_f = 0, id = -1;
-    if (lp < n) {
-      id = bt_pages[off0 + lp];
-      if (id < 0 || id >= n_fp8 + n_tq3) {
+  for (int base = 0; base < n; base += SUPER) {
+    const int lp0 = base + tid * P;
+    // every id first, then every tier byte: two dependent round trips per super-block
+    int id[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) id[k] = lp0 + k < n ? bt_pages[off0 + lp0 + k] : -1;
+    int isf = 0, cnt = 0;                          // bit k: page k is FP8
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if (lp0 + k >= n) continue;
+      if (id[k] < 0 || id[k] >= n_fp8 + n_tq3) {
         err |= kDevBadPageId;
+        continue;
+      }
+      const int tr = tier[id[k]];
+      if (tr == kTierRecent || tr == kTierAnchor) {
+        if (id[k] < n_fp8) { isf |= 1 << k; ++cnt; } else err |= kDevBadTier;
+      } else if (tr == kTierStale) {
+        if (id[k] < n_fp8) err |= kDevBadTier;
       } else {
-        const int tr = tier[id];
-        if (tr == kTierRecent || tr == kTierAnchor) {
-          if (id < n_fp8) is_f = 1; else err |= kDevBadTier;
-        } else if (tr == kTierStale) {
-          if (id < n_fp8) err |= kDevBadTier;
-        } else {
-          err |= kDevBadTier;
-        }
+        err |= kDevBadTier;
       }
     }
     int tot;
-    const int fpos = block_exclusive_scan<256>(is_f, &tot, sh);
-    if (lp < n) {
-      if (is_f) plan.list_f[off0 + nf + fpos] = id;
-      else plan.list_t[off0 + (lp - nf - fpos)] = id - n_fp8;
-      if (lp == n - 1) s_last = is_f ? 0 : 1;
+    const int fpos = block_exclusive_scan<kClassifyThreads>(cnt, &tot, sh);
+    int fb = 0;                                    // FP8 pages before page k within this thread
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int lp = lp0 + k;
+      if (lp >= n) continue;
+      const bool f = (isf >> k) & 1;
+      if (f) plan.list_f[off0 + nf + fpos + fb] = id[k];
+      else plan.list_t[off0 + (lp - nf - fpos - fb)] = id[k] - n_fp8;
+      fb += f;
+      if (lp == n - 1) s_last = f ? 0 : 1;
     }
     nf += tot;
   }
-  // block OR of the error bits
-  sh[tid] = err;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) sh[tid] |= sh[tid + s];
-    __syncthreads();
-  }
+  const int e = block_or_bits(err);
   if (tid == 0) {
-    const int e = sh[0];
     req_row(plan, R_NF)[b] = e ? 0 : nf;
     req_row(plan, R_NT)[b] = e ? 0 : n - nf;
     req_row(plan, R_TAIL)[b] = n ? sl - 16 * (n - 1) : 0;
@@ -113,7 +148,7 @@ __global__ void __launch_bounds__(256) plan_classify(
 }
 
 __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ bt_offsets, Plan plan) {
-  __shared__ int sh[1024];
+  __shared__ uint64_t sh[128];
   const int tid = threadIdx.x;
   const int B = plan.batch;
   int* nf_row = req_row(plan, R_NF);
@@ -125,17 +160,10 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     st += nt_row[b];
     serr |= req_row(plan, R_INVALID)[b];
   }
-  int TF, TT;
-  block_exclusive_scan<1024>(sf, &TF, sh);
-  block_exclusive_scan<1024>(st, &TT, sh);
-  sh[tid] = serr;
-  __syncthreads();
-  for (int s = 512; s > 0; s >>= 1) {
-    if (tid < s) sh[tid] |= sh[tid + s];
-    __syncthreads();
-  }
-  const int status = sh[0];
-  __syncthreads();
+  uint64_t tot2;
+  block_exclusive_scan<1024>(pack2(sf, st), &tot2, sh);
+  const int TF = lo32(tot2), TT = hi32(tot2);
+  const int status = block_or_bits(serr);
   // One chunk size for both formats, so the work items of a launch are of
   // equal size whatever the mix: about chunks_target chunks in all, less one
   // tail chunk per request and format, so the items fill one wave of
@@ -153,10 +181,11 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       ntc = (nt_row[b] + ppt - 1) / ppt;
       np = nfc + ntc;
     }
-    int tf, tt, tp;
-    const int ef = block_exclusive_scan<1024>(nfc, &tf, sh);
-    const int et = block_exclusive_scan<1024>(ntc, &tt, sh);
-    const int ep = block_exclusive_scan<1024>(np, &tp, sh);
+    uint64_t t2;
+    const uint64_t e2 = block_exclusive_scan<1024>(pack2(nfc, ntc), &t2, sh);
+    const int ef = lo32(e2), et = hi32(e2), ep = ef + et;
+    const int tf = lo32(t2), tt = hi32(t2), tp = tf + tt;
+    (void)np;
     if (b < B) {
       req_row(plan, R_CF_OFF)[b] = carry_f + ef;   // chunk offsets (exclusive) per format
       req_row(plan, R_CT_OFF)[b] = carry_t + et;
@@ -214,7 +243,7 @@ hipError_t launch_plan(const Geometry& g, const uint8_t* tier, const int32_t* bt
                        hipStream_t stream) {
   hipError_t e;
   if (plan.batch > 0) {
-    hipLaunchKernelGGL(plan_classify, dim3(plan.batch), dim3(256), 0, stream, tier, g.n_fp8,
+    hipLaunchKernelGGL(plan_classify, dim3(plan.batch), dim3(kClassifyThreads), 0, stream, tier, g.n_fp8,
                        g.n_tq3, bt_offsets, bt_pages, seq_lens, plan);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
