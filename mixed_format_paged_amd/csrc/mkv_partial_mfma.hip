@@ -413,8 +413,7 @@ __device__ __forceinline__ void run_item(
   const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
   const uint8_t* __restrict__ head = slab + (tq3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D);
   const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
-  // page k of this wave (clamped: past the end the last page is re-read, an
-  // L2 hit, so every wave issues the same number of staging loads)
+  // page k of this wave (clamped, so reading one id past the end stays in range)
   auto page_id = [&](int k) { return list[start + wave + kWaves * (k < my_pages ? k : my_pages - 1)]; };
   auto page_src = [&](int id) { return head + (size_t)id * page_bytes; };
 
@@ -461,10 +460,14 @@ __device__ __forceinline__ void run_item(
     for (int k = 0; k < my_pages; ++k) {
       uint8_t* const cur = (k & 1) ? slot1 : slot0;
       uint8_t* const nxt = (k & 1) ? slot0 : slot1;
-      const uint8_t* const nsrc = page_src(id_next);
-      id_next = page_id(k + 2);
-      stage_issue<D>(nsrc, nxt, lane, tq3_head_bytes(D));
-      wait_vmem<kRows>();                     // page k has landed
+      if (k + 1 < my_pages) {                 // wave-uniform
+        const uint8_t* const nsrc = page_src(id_next);
+        id_next = page_id(k + 2);
+        stage_issue<D>(nsrc, nxt, lane, tq3_head_bytes(D));
+        wait_vmem<kRows>();                   // page k has landed, page k+1 in flight
+      } else {
+        wait_vmem<0>();                       // the last page has landed
+      }
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
@@ -483,13 +486,18 @@ __device__ __forceinline__ void run_item(
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D>(slot0, sq, lane, j);
       const h4 pa = st.softmax(s, ntok, lo_sel, j);
+      const bool more = k + 1 < my_pages;     // wave-uniform
       const uint8_t* pn = page_src(id_next);
       id_next = page_id(k + 2);
-      stage_issue<D>(pn, slot0, lane, kPage * D);
-      wait_vmem<kRows>();                     // V of page k has landed
+      if (more) {
+        stage_issue<D>(pn, slot0, lane, kPage * D);
+        wait_vmem<kRows>();                   // V of page k has landed, K of page k+1 in flight
+      } else {
+        wait_vmem<0>();
+      }
       __builtin_amdgcn_sched_barrier(0);
       fp8_pv<D>(slot1, pa, st.O, lane, j);
-      stage_issue<D>(pn + kPage * D, slot1, lane, kPage * D);
+      if (more) stage_issue<D>(pn + kPage * D, slot1, lane, kPage * D);
     }
   }
   wait_vmem<0>();                               // no staging load may land after this point
