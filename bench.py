@@ -12,8 +12,9 @@ One step = one decode step of the whole path, layers in sequence as a model
 runs them:
     plan (block tables + tier map -> per-format page lists and split-K chunks)
     for each of the 16 layers:
-        append the step's new token (K, V of both requests, FP8 E4M3)
-        FP8 partial kernel, TQ3 partial kernel, log-sum-exp merge
+        append the step's new token (K, V of both requests, FP8 E4M3), inside
+        the partial-attention launch (mkv_append_attend)
+        FP8 and TQ3 partial kernels (one launch), log-sum-exp merge
     demote, in all 16 layers, the page of each request that leaves the recent
     window (FP8 -> TQ3 pack, written to a spare TQ3 slot so the cache state
     stays identical from step to step)
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="canary-2x59008-16L")
     ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with its own launch (mkv_append) instead of inside the attend launch")
     ap.add_argument("--no-control", action="store_true", help="skip the same-run all-FP8 control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-units", type=int, default=6, help="(layer, request, KV head) units the oracle is timed on")
@@ -56,7 +59,7 @@ def parse():
 class Runner:
     """Holds the device state of one workload and enqueues its decode steps."""
 
-    def __init__(self, w, st, all_fp8=False, kernel="mfma"):
+    def __init__(self, w, st, all_fp8=False, kernel="mfma", fused_append=True):
         import torch
         import mixed_format_paged_amd as M
         from workloads.device_cache import DeviceWorkload
@@ -70,6 +73,7 @@ class Runner:
                              st.staging_ids, st.staging_ids, st.n_fp8, 0,
                              np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64))
         self.w, self.st = w, st
+        self.fused_append = fused_append and kernel == "mfma"
         M.set_partial_kind(1 if kernel == "mfma" else 0)
         t0 = time.time()
         self.dw = DeviceWorkload(w, st, "cuda", spare_tq3=w.B)
@@ -104,8 +108,12 @@ class Runner:
         M, dw, lay, bat, ws = self.M, self.dw, self.layout, self.batch, self.ws
         M.mkv_decode_plan(lay, dw.cache.pools[0], bat, 1, ws)
         for l in range(self.w.L):
-            M.mkv_append(lay, dw.cache.pools[l], self.k_new[l], self.v_new[l], dw.bt_offsets, dw.bt, self.pos)
-            M.mkv_attend(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, self.out[l], self.lse[l], ws)
+            if self.fused_append:
+                M.mkv_append_attend(lay, [dw.cache.pools[l]], bat, self.k_new[l], self.v_new[l], self.q[l],
+                                    self.sm_scale, self.out[l], self.lse[l], ws)
+            else:
+                M.mkv_append(lay, dw.cache.pools[l], self.k_new[l], self.v_new[l], dw.bt_offsets, dw.bt, self.pos)
+                M.mkv_attend(lay, [dw.cache.pools[l]], bat, self.q[l], self.sm_scale, self.out[l], self.lse[l], ws)
         if self.dem_src.numel():
             M.mkv_demote_pages_layers(lay, dw.cache.pools, self.dem_src, self.dem_dst)
 
@@ -287,7 +295,7 @@ def main():
     w = W.WORKLOADS[a.workload]
     st = W.make_structure(w)
     print(f"[bench] building {w.name} cache on the GPU ...", file=sys.stderr, flush=True)
-    r = Runner(w, st, kernel=a.kernel)
+    r = Runner(w, st, kernel=a.kernel, fused_append=not a.separate_append)
     print(f"[bench] built in {r.build_s:.1f} s", file=sys.stderr, flush=True)
     if a.profile_steps:
         for _ in range(a.profile_steps):
@@ -314,7 +322,8 @@ def main():
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "page": 16,
                    "fp8_pages_per_request": int(st.n_pages[0] - (st.tiers[:st.n_pages[0]] == 2).sum()),
                    "tq3_pages_per_request": int((st.tiers[:st.n_pages[0]] == 2).sum()),
-                   "kernel": a.kernel, "graph": not a.no_graph},
+                   "kernel": a.kernel, "graph": not a.no_graph,
+                   "append": "separate launch" if a.separate_append else "inside the attend launch"},
         "tokens_per_s": round(w.B / (ms * 1e-3), 2),
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -330,7 +339,7 @@ def main():
         del r
         torch.cuda.empty_cache()
         print("[bench] building the all-FP8 control ...", file=sys.stderr, flush=True)
-        c = Runner(w, st, all_fp8=True, kernel=a.kernel)
+        c = Runner(w, st, all_fp8=True, kernel=a.kernel, fused_append=not a.separate_append)
         c_ms = c.time_steps(a.steps, a.warmup, graph=not a.no_graph)
         c_bytes = c.kv_bytes()[0]
         result["control_all_fp8"] = {"ms_per_step": round(c_ms, 5), "kv_bytes_per_step": c_bytes,
@@ -343,7 +352,7 @@ def main():
         r = None
     if not a.no_cpu_baseline:
         if r is None:
-            r = Runner(w, st, kernel=a.kernel)
+            r = Runner(w, st, kernel=a.kernel, fused_append=not a.separate_append)
             r.time_steps(1, 1, graph=not a.no_graph)
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(r, a.cpu_units)

@@ -232,6 +232,23 @@ int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers
                const mkv_batch* batch, const float* q, float sm_scale, float* out, float* lse,
                void* ws, size_t ws_bytes, void* stream);
 
+/* mkv_append_attend: mkv_append of each request's newest token followed by
+ * mkv_attend, with the append done inside the partial-attention launch (a
+ * decode step appends, then attends over tokens [0, seq_len): arXiv
+ * 2608.23834, page 1, Abstract, Recent pages in FP8).
+ *  k_new, v_new: device fp32 [n_layers][batch][Hkv][head_dim], 16-byte
+ *    aligned: K and V of the token at position seq_lens[b] - 1 of request b.
+ *    That token's logical page (the request's last) must be an FP8 page of
+ *    the pool (tier Recent); it is written exactly as mkv_append writes it.
+ *  The other arguments and the plan requirements are those of mkv_attend
+ *  (the plan counts the new token: seq_lens include it).  Results, and the
+ *  cache bytes written, are identical to mkv_append + mkv_attend.  Needs the
+ *  matrix-core kernels (returns MKV_ERR_RANGE otherwise). */
+int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                      const mkv_batch* batch, const float* k_new, const float* v_new,
+                      const float* q, float sm_scale, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Page-table gather (test support): copy the raw bytes of logical pages
  * [0, n_pages) of request b into out (device, n_pages records of
  * mkv_fp8_page_bytes() bytes; a TQ3 page fills the first mkv_tq3_page_bytes()

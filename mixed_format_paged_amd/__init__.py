@@ -14,7 +14,7 @@ __all__ = [
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
-    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_status_string", "mkv_last_error",
+    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_status_string", "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
 
@@ -70,6 +70,8 @@ def lib():
         "mkv_attend_partials": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_sz, c_vp]),
         "mkv_merge": (c_i32, [P(Layout), c_i32, P(BatchDesc), c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_attend": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "mkv_append_attend": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
+                                      c_vp, c_sz, c_vp]),
         "mkv_decode_workspace_bytes": (c_sz, [P(Layout), c_i32, c_i32, c_i32]),
         "mkv_decode_attn": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -209,6 +211,17 @@ def mkv_merge(layout, n_layers, batch, out, lse, ws, stream=None):
     return _check(lib().mkv_merge(ctypes.byref(_layout(layout)), int(n_layers), ctypes.byref(batch),
                                   _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), p, n,
                                   _stream(stream)))
+
+
+def mkv_append_attend(layout, pools, batch, k_new, v_new, q, sm_scale, out, lse, ws, stream=None):
+    """mkv_append of each request's newest token + mkv_attend, in the same launches."""
+    import torch
+    arr = (PoolDesc * len(pools))(*pools)
+    p, n = _ws(ws)
+    return _check(lib().mkv_append_attend(ctypes.byref(_layout(layout)), arr, len(pools), ctypes.byref(batch),
+                                          _ptr(k_new, torch.float32, "k_new"), _ptr(v_new, torch.float32, "v_new"),
+                                          _ptr(q, torch.float32, "q"), float(sm_scale), _ptr(out, torch.float32, "out"),
+                                          _ptr(lse, torch.float32, "lse"), p, n, _stream(stream)))
 
 
 def mkv_attend(layout, pools, batch, q, sm_scale, out, lse, ws, stream=None):

@@ -264,7 +264,7 @@ int run_attend(int which, const Geometry& g, const LayerTable& lt, int n_layers,
   const size_t q_ls = (size_t)batch * g.hq * g.d;
   hipError_t e;
   if (g_partial_kind) {
-    e = launch_partial_mfma(which, g, lt, n_layers, q, q_ls, qscale, plan, st);
+    e = launch_partial_mfma(which, g, lt, n_layers, q, q_ls, qscale, plan, AppendIn{nullptr, nullptr, 0}, st);
   } else {
     e = hipSuccess;
     if (which != 1) e = launch_partial_valu(false, g, lt, n_layers, q, q_ls, qscale, plan, st);
@@ -363,6 +363,31 @@ int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers
   if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
   if (batch->batch == 0) return MKV_OK;
   return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, batch->batch, as_stream(stream));
+}
+
+int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                      const mkv_batch* batch, const float* k_new, const float* v_new,
+                      const float* q, float sm_scale, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  LayerTable lt{};
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt);
+  if (rc) return rc;
+  if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
+  if (!k_new || !v_new) return fail(MKV_ERR_NULL, "k_new and v_new are required");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(MKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
+  if (!g_partial_kind) return fail(MKV_ERR_RANGE, "mkv_append_attend needs the matrix-core partial kernels");
+  if (batch->batch == 0) return MKV_OK;
+  const int B = batch->batch;
+  hipStream_t st = as_stream(stream);
+  const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
+  const size_t q_ls = (size_t)B * g.hq * g.d;
+  const AppendIn ap{k_new, v_new, (size_t)B * g.hkv * g.d};
+  hipError_t e = launch_partial_mfma(2, g, lt, n_layers, q, q_ls, qscale, plan, ap, st);
+  if (e != hipSuccess) return hip_fail(e, "partial-attention launch");
+  return run_merge(g, n_layers, plan, out, lse, B, st);
 }
 
 int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,

@@ -53,7 +53,11 @@ enum TotalField {
 
 // Chunk descriptor: x = request, y = first index into the format's page list
 // (absolute, in the request's CSR range), z = pages | (tokens on its last
-// page << 16), w = partial index within the layer.
+// page << 16) | (kChunkHoldsTail if its last page is the request's last
+// logical page), w = partial index within the layer.
+constexpr int kChunkHoldsTail = 1 << 30;
+__host__ __device__ inline int chunk_pages(int z) { return z & 0xffff; }
+__host__ __device__ inline int chunk_last_tok(int z) { return (z >> 16) & 0x1f; }
 struct Plan {
   int32_t* status;      // [1] MKV_DEV_* bits
   int32_t* totals;      // [T_FIELDS]
@@ -116,9 +120,17 @@ hipError_t launch_partial_valu(bool tq3, const Geometry& g, const LayerTable& lt
                                const Plan& plan, hipStream_t stream);
 // Matrix-core partial kernels: which = 0 FP8 items, 1 TQ3 items, 2 both
 // formats' items in one launch.
+// New-token rows appended by the partial-attention launch itself (k == NULL:
+// none): k, v fp32 [n_layers][batch][Hkv][d], row stride `ls` floats per layer.
+struct AppendIn {
+  const float* k;
+  const float* v;
+  size_t ls;
+};
+
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
-                               const Plan& plan, hipStream_t stream);
+                               const Plan& plan, const AppendIn& ap, hipStream_t stream);
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out,
                         float* lse, size_t out_layer_stride, size_t lse_layer_stride,
                         hipStream_t stream);

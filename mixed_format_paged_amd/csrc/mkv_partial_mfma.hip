@@ -396,7 +396,7 @@ template <int D, bool tq3>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
-    uint8_t* smem, uint32_t one024) {
+    uint8_t* smem, uint32_t one024, const AppendIn* ap) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
   const int lane = threadIdx.x & 63;
@@ -416,6 +416,28 @@ __device__ __forceinline__ void run_item(
   // page k of this wave (clamped, so reading one id past the end stays in range)
   auto page_id = [&](int k) { return list[start + wave + kWaves * (k < my_pages ? k : my_pages - 1)]; };
   auto page_src = [&](int id) { return head + (size_t)id * page_bytes; };
+
+  // The step's new token, appended in the same launch: the FP8 chunk that
+  // holds a request's last logical page (always FP8: it is Recent) writes
+  // head h's K and V rows of the token into it, E4M3 round-to-nearest-even
+  // saturating like mkv_append, before anything of that page is staged; the
+  // wave that stages the page is the one that writes it, so its own loads
+  // come after its stores.
+  if (!tq3 && ap && ap->k && wave == (count - 1) % kWaves) {
+    uint8_t* page = lt.fp8[layer] + (size_t)list[start + count - 1] * page_bytes;
+    const int slot = last_tok - 1;
+    const size_t row = layer * ap->ls + ((size_t)b * hkv + h) * D;
+    const float ksc = lt.k_scale[layer], vsc = lt.v_scale[layer];
+    for (int e4 = lane; e4 < 2 * D / 4; e4 += 64) {
+      const int kv = e4 >= D / 4, c = 4 * (e4 - kv * (D / 4));
+      const float4 x = *reinterpret_cast<const float4*>((kv ? ap->v : ap->k) + row + c);
+      const float sc = kv ? vsc : ksc;
+      const uint32_t w = e4m3_encode(__fdiv_rn(x.x, sc)) | (e4m3_encode(__fdiv_rn(x.y, sc)) << 8) |
+                         (e4m3_encode(__fdiv_rn(x.z, sc)) << 16) | (e4m3_encode(__fdiv_rn(x.w, sc)) << 24);
+      *reinterpret_cast<uint32_t*>(page + ((h * 2 + kv) * kPage + slot) * D + c) = w;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stores done before the page is staged
+  }
 
   // first unit(s) in flight before the query fragments are built
   if (my_pages > 0) {
@@ -579,7 +601,7 @@ __device__ __forceinline__ void run_item(
 template <int D, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
     LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
-    float qscale, Plan plan) {
+    float qscale, Plan plan, AppendIn ap) {
   __shared__ __align__(16) uint8_t smem[kSmemBytes<D>];
 
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
@@ -598,15 +620,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M
     const int chunk = (int)((it / hkv) % nch);
     const int layer = (int)(it / ((long)hkv * nch));
     const i4v cd = ((cptr_i4)(tq3 ? plan.chunks_t : plan.chunks_f))[chunk];
-    const int b = cd[0], start = cd[1], count = cd[2] & 0xffff, last_tok = cd[2] >> 16, pidx = cd[3];
+    const int b = cd[0], start = cd[1], count = chunk_pages(cd[2]), last_tok = chunk_last_tok(cd[2]), pidx = cd[3];
+    const bool holds_tail = (cd[2] & kChunkHoldsTail) != 0;
     if (pidx >= plan.np_cap) {               // plan made for more layers than this call
       if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
       continue;
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024);
+      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024,
+                        nullptr);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024);
+      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024,
+                         holds_tail ? &ap : nullptr);
     __syncthreads();
   }
 }
@@ -617,26 +642,27 @@ static dim3 attend_grid(long cap) {
 
 template <int MODE>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
-                            size_t q_ls, float qscale, const Plan& plan, hipStream_t stream) {
+                            size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
+                            hipStream_t stream) {
   const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2);
   const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(kThreads);
   if (g.d == 256)
     hipLaunchKernelGGL((attend_kernel<256, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                       q_ls, qscale, plan);
+                       q_ls, qscale, plan, ap);
   else
     hipLaunchKernelGGL((attend_kernel<128, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                       q_ls, qscale, plan);
+                       q_ls, qscale, plan, ap);
 }
 
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
-                               const Plan& plan, hipStream_t stream) {
+                               const Plan& plan, const AppendIn& ap, hipStream_t stream) {
   if (which == 0)
-    launch_attend_t<kFp8Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
+    launch_attend_t<kFp8Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else if (which == 1)
-    launch_attend_t<kTq3Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
+    launch_attend_t<kTq3Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else
-    launch_attend_t<kBoth>(g, lt, n_layers, q, q_layer_stride, qscale, plan, stream);
+    launch_attend_t<kBoth>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   return hipGetLastError();
 }
 

@@ -231,9 +231,10 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const int nchunks = co[b + 1] - co[b];
       const int start = local * pp;
       const int count = min(pp, cnt[b] - start);
-      const int last_tok = (local == nchunks - 1 && lastfmt[b] == fmt) ? tail[b] : 16;
+      const bool holds_tail = local == nchunks - 1 && lastfmt[b] == fmt;
+      const int last_tok = holds_tail ? tail[b] : 16;
       const int pidx = po[b] + (fmt ? (cf[b + 1] - cf[b]) : 0) + local;
-      out[c] = make_int4(b, bt_offsets[b] + start, count | (last_tok << 16), pidx);
+      out[c] = make_int4(b, bt_offsets[b] + start, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
     }
   }
 }

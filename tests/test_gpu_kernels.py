@@ -225,3 +225,46 @@ def test_phase_split_calls_are_bit_identical(kind):
         assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
     for li, (_, _, o_ref, lse_ref) in enumerate(ref):
         compare(outs[0][0][li], o_ref, outs[0][1][li], lse_ref, f"layer {li}")
+
+
+def test_append_attend_equals_append_then_attend():
+    """mkv_append_attend writes the same cache bytes and gives the same
+    outputs, bit for bit, as mkv_append followed by mkv_attend."""
+    M.set_partial_kind(1)
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=4, L=2,
+                 lengths=("list", (2000, 17, 1025, 3100)), recent_tokens=64)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    layout = (w.Hq, w.Hkv, w.d)
+    L, B = 2, w.B
+    sm = 1 / math.sqrt(w.d)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    k_new = torch.randn((L, B, w.Hkv, w.d), generator=g, device="cuda") * 3
+    v_new = torch.randn((L, B, w.Hkv, w.d), generator=g, device="cuda") * 3
+    pos = (dw.seq_lens - 1).to(torch.int32)
+    fp8_0 = [p.clone() for p in dw.cache.fp8]
+    wsb = M.mkv_decode_workspace_bytes(layout, B, dw.bt.numel(), L)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bat = dw.batch()
+    res = []
+    for fused in (False, True):
+        for l in range(L):
+            dw.cache.fp8[l].copy_(fp8_0[l])
+        out = torch.full((L, B, w.Hq, w.d), float("nan"), device="cuda")
+        lse = torch.full((L, B, w.Hq), float("nan"), device="cuda")
+        M.mkv_decode_plan(layout, dw.cache.pools[0], bat, L, ws)
+        if fused:
+            M.mkv_append_attend(layout, dw.cache.pools, bat, k_new, v_new, dw.q, sm, out, lse, ws)
+        else:
+            for l in range(L):
+                M.mkv_append(layout, dw.cache.pools[l], k_new[l].unsqueeze(1).contiguous(),
+                             v_new[l].unsqueeze(1).contiguous(), dw.bt_offsets, dw.bt, pos)
+            M.mkv_attend(layout, dw.cache.pools, bat, dw.q, sm, out, lse, ws)
+        torch.cuda.synchronize()
+        assert M.mkv_workspace_status(ws) == 0
+        res.append(([s.cpu().numpy() for s in dw.cache.fp8], out.cpu().numpy(), lse.cpu().numpy()))
+    for l in range(L):
+        assert np.array_equal(res[0][0][l], res[1][0][l]), f"layer {l}: cache bytes differ"
+        assert not np.array_equal(res[0][0][l], fp8_0[l].cpu().numpy())   # the append did write
+    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
