@@ -96,9 +96,13 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   };
   // chunk tables: sized for the largest chunk count any layer count can plan
   s.table_cap = chunk_bound((kTargetItems + hkv - 1) / hkv);
-  // partial states: sized for a plan made for this layer count
-  const int chunks_l = chunk_bound(s.chunks_target);
-  s.np_cap = 2 * chunks_l;
+  // partial states per layer of a plan made for this layer count.  The planner
+  // takes pp >= pages / max(1, target - 2 batch) pages per chunk (or pp =
+  // kMaxChunkPages) and each request adds at most one part-filled chunk per
+  // format, so NP < max(target, pages / kMaxChunkPages) + 2 batch; and never
+  // more than one chunk per kMinChunkPages pages plus one per request and format.
+  const int t = s.chunks_target > by_max ? s.chunks_target : by_max;
+  s.np_cap = t + 2 * batch < 2 * (by_pages + batch) ? t + 2 * batch : 2 * (by_pages + batch);
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   s.off_status = take(sizeof(int32_t));
