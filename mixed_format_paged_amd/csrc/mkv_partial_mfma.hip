@@ -220,8 +220,10 @@ struct WaveState {
 
   // Online-softmax update for a page's scores s (tokens 4j..4j+3 of query-row
   // column n, log2 units, hi and lo query rows not yet added); returns the A
-  // operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder.
-  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j) {
+  // operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder.  On a wave's
+  // first page (wave-uniform `first`) O and l are still zero: the max is
+  // taken as is and nothing is rescaled.
+  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
     if (ntok < kPage) {                         // a request's last page: mask its tail
@@ -232,7 +234,9 @@ struct WaveState {
     float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     pm = max_xor32(max_xor16(pm));
     const bool need = pm > m_run + kRescale;
-    if (__any(need)) {
+    if (first) {
+      m_run = pm;
+    } else if (__any(need)) {
       const float m_new = need ? pm : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first page (m_run = -inf)
       l_run *= alpha;
@@ -494,7 +498,7 @@ __device__ __forceinline__ void run_item(
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = tq3_scores<D>(cur, sq, lane, j, one024);
-      const h4 pa = st.softmax(s, ntok, lo_sel, j);
+      const h4 pa = st.softmax(s, ntok, lo_sel, j, k == 0);
       tq3_pv<D>(cur, pa, st.O, lane, j, one024);
     }
   } else {
@@ -507,7 +511,7 @@ __device__ __forceinline__ void run_item(
       const int e = wave + kWaves * k;
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D>(slot0, sq, lane, j);
-      const h4 pa = st.softmax(s, ntok, lo_sel, j);
+      const h4 pa = st.softmax(s, ntok, lo_sel, j, k == 0);
       const bool more = k + 1 < my_pages;     // wave-uniform
       const uint8_t* pn = page_src(id_next);
       id_next = page_id(k + 2);
@@ -544,7 +548,9 @@ __device__ __forceinline__ void run_item(
   }
   __syncthreads();
   // O rows 4jj + r: after the swap below, lanes 0..31 (j < 2) hold the rows of
-  // tile T, lanes 32..63 those of tile T + NT/2
+  // tile T, lanes 32..63 those of tile T + NT/2.  All kMaxG rows are stored
+  // (rows >= G hold values nobody reads), so the stores need no lane mask and
+  // take their row and tile from the instruction offset.
   const int jj = j & 1, thalf = j >> 1;
   const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
   float wr[4];
@@ -561,8 +567,7 @@ __device__ __forceinline__ void run_item(
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.O[T][r]),
                                                        __float_as_uint(st.O[T + GD::NT / 2][r]), false, false);
       const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-      const int row = 4 * jj + r;
-      if (row < G) so[MergeLayout<D>::at(wave, row, n, T + thalf * (GD::NT / 2))] = tot * wr[r];
+      so[MergeLayout<D>::at(wave, 4 * jj + r, n, T + thalf * (GD::NT / 2))] = tot * wr[r];
     }
   }
   __syncthreads();
