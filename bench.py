@@ -184,6 +184,37 @@ class Runner:
         return res
 
 
+def time_materialize(runner, reps=8):
+    """The dense shadow the decode path avoids: dequantise every page of every
+    request of one layer to BF16 K and V (mkv_materialize, one launch per
+    request), timed with HIP events on the launching stream; launch set i reads
+    layer i mod L.  Returns (avg ms, bytes read, bytes written) per layer."""
+    torch, M = runner.torch, runner.M
+    w, st = runner.w, runner.st
+    n_pages = [int(x) for x in st.n_pages]
+    shape = (max(n_pages) * 16, w.Hkv, w.d)
+    K = torch.empty(shape, dtype=torch.int16, device="cuda")
+    V = torch.empty(shape, dtype=torch.int16, device="cuda")
+
+    def run(l):
+        for b in range(w.B):
+            M.mkv_materialize(runner.layout, runner.dw.cache.pools[l], runner.batch, b, 0, n_pages[b], K, V)
+
+    run(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        run(i % w.L)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    read = runner.kv_bytes()[0] // w.L
+    written = sum(n_pages) * 16 * w.Hkv * w.d * 2 * 2
+    del K, V
+    return ms, read, written
+
+
 def kernel_source_hash():
     """Hash of the sources the partial-attention kernel is compiled from."""
     import hashlib
@@ -302,6 +333,7 @@ def main():
             r.step()
         torch.cuda.synchronize()
         r.time_kernels(reps=5)
+        time_materialize(r, reps=2)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
@@ -310,6 +342,7 @@ def main():
     layer_bytes = kv_bytes // w.L
     kt = r.time_kernels()
     k_avg, k_med = kt["partials"]
+    mat_ms, mat_read, mat_written = time_materialize(r)
     traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
@@ -334,6 +367,12 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(k_avg, 5), "median_launch_ms": round(k_med, 5),
                      "bytes_per_launch": layer_bytes},
         "merge_kernel": {"avg_launch_ms": round(kt["merge"][0], 5), "median_launch_ms": round(kt["merge"][1], 5)},
+        # the dense BF16 shadow the decode path avoids, for one layer (all pages of every request)
+        "materialize_dense_bf16": {"avg_ms_per_layer": round(mat_ms, 5), "bytes_read": mat_read,
+                                   "bytes_written": mat_written,
+                                   "gbs": round((mat_read + mat_written) / (mat_ms * 1e-3) / 1e9, 2),
+                                   "frac_of_peak": round((mat_read + mat_written) / (mat_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "vs_decode_launch": round(mat_ms / k_avg, 3)},
     }
     if not a.no_control:
         del r

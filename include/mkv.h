@@ -258,6 +258,26 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool,
                      const int32_t* bt_offsets, const int32_t* bt_pages,
                      int32_t b, int32_t n_pages, uint8_t* out, void* stream);
 
+/* Materialise: dequantise logical pages [page_lo, page_lo + n_pages) of
+ * request b to dense bfloat16 K and V.  The pages' quality profile runs on
+ * materialised pages while their decode path reads the mixed pages in place
+ * without a dense dequantised buffer (arXiv 2608.23834, page 1, Abstract;
+ * page 2, "Technical Deep Dive"): this call builds that buffer, for
+ * consumers that need dense values and as the measured comparison.
+ *  k_out, v_out: device uint16 (bf16 bits) [n_pages * 16][num_kv_heads]
+ *    [head_dim], 16-byte aligned; token 16 i + t of the output is slot t of
+ *    logical page page_lo + i.
+ * Element values: an FP8 page gives bf16_RNE(fl32(decode(e) * scale)) with the
+ * pool's k_scale / v_scale; a TQ3 page gives bf16_RNE((u - 4) * s) (exact in
+ * fp32 before the rounding).  A page's format follows its id (< n_fp8: FP8);
+ * the tier map is not read.  A logical page outside the request's block
+ * table, or an id outside the pool, gives bf16 NaN (0x7FC0) for all its
+ * elements.  Tokens past the request's seq_len are converted like the
+ * others.  0 <= b < batch->batch; page_lo, n_pages >= 0 (n_pages == 0: no-op). */
+int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                    int32_t b, int32_t page_lo, int32_t n_pages, uint16_t* k_out,
+                    uint16_t* v_out, void* stream);
+
 /* Synchronise `stream` and return the device status bits (MKV_DEV_*) left in
  * the workspace by the last decode call on it (0 = no device-data error);
  * negative MKV_ERR_* on failure. */

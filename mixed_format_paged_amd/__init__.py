@@ -14,7 +14,8 @@ __all__ = [
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
-    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_status_string", "mkv_last_error",
+    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_status_string",
+    "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
 
@@ -76,6 +77,7 @@ def lib():
         "mkv_decode_attn": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_debug_gather": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
+        "mkv_materialize": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
         "mkv_workspace_status": (c_i32, [c_vp, c_vp]),
         "mkv_status_string": (ctypes.c_char_p, [c_i32]),
         "mkv_last_error": (ctypes.c_char_p, []),
@@ -263,6 +265,19 @@ def mkv_debug_gather(layout, pool, bt_offsets, bt_pages, b, n_pages, out, stream
                                          _ptr(bt_offsets, torch.int32, "bt_offsets"),
                                          _ptr(bt_pages, torch.int32, "bt_pages"), int(b), int(n_pages),
                                          _ptr(out, torch.uint8, "out"), _stream(stream)))
+
+
+def mkv_materialize(layout, pool, batch, b, page_lo, n_pages, k_out, v_out, stream=None):
+    """Dense bf16 K and V (int16 tensors holding bf16 bits, or torch.bfloat16)
+    [n_pages * 16][Hkv][d] of logical pages [page_lo, page_lo + n_pages) of request b."""
+    lay = _layout(layout)
+    need = int(n_pages) * 16 * lay.num_kv_heads * lay.head_dim
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if t is not None and (t.element_size() != 2 or t.numel() < need):
+            raise MkvError(-101, f"{name} must hold {need} 2-byte elements")
+    return _check(lib().mkv_materialize(ctypes.byref(_layout(layout)), ctypes.byref(pool), ctypes.byref(batch),
+                                        int(b), int(page_lo), int(n_pages), _ptr(k_out, name="k_out"),
+                                        _ptr(v_out, name="v_out"), _stream(stream)))
 
 
 def mkv_workspace_status(ws, stream=None):

@@ -433,6 +433,26 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32
   return e == hipSuccess ? MKV_OK : hip_fail(e, "gather launch");
 }
 
+int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
+                    int32_t page_lo, int32_t n_pages, uint16_t* k_out, uint16_t* v_out, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if ((rc = check_pool(pool, &g, true, true, false))) return rc;
+  if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
+  if (b < 0 || b >= batch->batch || page_lo < 0 || n_pages < 0)
+    return fail(MKV_ERR_RANGE, "b %d (batch %d) / page_lo %d / n_pages %d", b, batch->batch, page_lo, n_pages);
+  if ((int64_t)page_lo + n_pages > 0x7fffffff / kPage) return fail(MKV_ERR_RANGE, "page range too large");
+  if (n_pages == 0) return MKV_OK;
+  if (!batch->bt_offsets || !batch->bt_pages || !k_out || !v_out)
+    return fail(MKV_ERR_NULL, "bt_offsets, bt_pages, k_out and v_out are required");
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(MKV_ERR_ALIGN, "k_out and v_out must be 16-byte aligned");
+  hipError_t e = launch_materialize(g, pool->fp8_slab, pool->tq3_slab, pool->k_scale, pool->v_scale,
+                                    batch->bt_offsets, batch->bt_pages, batch->bt_capacity, b, page_lo,
+                                    n_pages, k_out, v_out, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "materialize launch");
+}
+
 int mkv_workspace_status(const void* ws, void* stream) {
   if (!ws) return fail(MKV_ERR_NULL, "ws is NULL");
   hipError_t e = hipStreamSynchronize(as_stream(stream));

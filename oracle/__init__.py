@@ -14,6 +14,7 @@ written from the Minima-KV pages (arXiv 2608.23834, abstract on page 1; the
 * ``layout``    -- byte layout of FP8 and TQ3 pages, 8-codes-in-3-bytes packing
 * ``pool``      -- a byte-level page pool: append, FP8->TQ3 demotion, page-table gather
 * ``attention`` -- dense fp64 softmax decode attention and the log-sum-exp merge
+* ``dense``     -- bf16 rounding and the dense materialisation of pages
 
 Every floating-point step of attention is carried out in fp64 on the
 dequantised values; quantisation steps are done exactly (integer / exact
@@ -28,4 +29,4 @@ SDPA cross-check and merge invariance).  The pages' own headline figures
 parity unpinned, because the model, control and tier mix behind them are not
 given on the pages.
 """
-from . import fp8, tq3, layout, pool, attention, build  # noqa: F401
+from . import fp8, tq3, layout, pool, attention, build, dense  # noqa: F401

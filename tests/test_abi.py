@@ -60,6 +60,11 @@ def test_host_validation_codes():
     assert L.mkv_append(lay, ctypes.byref(pool), 16, 16, 70000, 16, 16, 16, None, 1, None) == -5
     assert L.mkv_append(lay, ctypes.byref(pool), 8, 16, 1, 16, 16, 16, None, 1, None) == -3
     assert L.mkv_debug_gather(lay, ctypes.byref(pool), None, None, 0, 4, None, None) == -1
+    assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 2, 0, 1, 16, 16, None) == -5  # b >= batch
+    assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 0, -1, 1, 16, 16, None) == -5
+    assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 0, 0, 1, 8, 16, None) == -3   # misaligned
+    assert L.mkv_materialize(lay, ctypes.byref(pool), None, 0, 0, 1, 16, 16, None) == -1
+    assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 0, 0, 0, None, None, None) == 0
     # zero-size work is a successful no-op that launches nothing
     assert L.mkv_demote_pages(lay, ctypes.byref(pool), None, None, 0, None) == 0
     empty = M.BatchDesc(None, None, None, 0, 0)

@@ -268,3 +268,38 @@ def test_append_attend_equals_append_then_attend():
         assert np.array_equal(res[0][0][l], res[1][0][l]), f"layer {l}: cache bytes differ"
         assert not np.array_equal(res[0][0][l], fp8_0[l].cpu().numpy())   # the append did write
     assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+
+
+@pytest.mark.parametrize("d,scales", [(128, (0.75, 1.25)), (256, (1.0, 1.0))])
+def test_materialize_bitexact(d, scales):
+    """mkv_materialize on the oracle's own pool bytes equals the oracle's dense
+    bf16 bits: whole requests, a range starting inside and running past the
+    end of a block table (NaN pages), and an id outside the pool."""
+    from oracle import dense as OD
+    w = W.scaled(W.WORKLOADS["tiny-1x1024-d128"], d=d, B=3, lengths=("list", (1024, 300, 17)))
+    st = W.make_structure(w)
+    vals = W.layer_values(w, st, 0)
+    pool, bt = OB.build_layer(w, st, [x.numpy() for x in vals["k"]], [x.numpy() for x in vals["v"]], *scales)
+    bt = bt.copy()
+    bt[int(st.bt_offsets[2])] = pool.n_fp8 + pool.n_tq3 + 3          # request 2, page 0: not in the pool
+    dev = "cuda"
+    fp8_d = torch.from_numpy(pool.fp8).to(dev)
+    tq3_d = torch.from_numpy(pool.tq3).to(dev)
+    tier_d = torch.from_numpy(pool.tier).to(dev)
+    pd = M.make_pool(fp8_d, tq3_d, tier_d, pool.n_fp8, pool.n_tq3, *scales)
+    batch = M.make_batch(torch.as_tensor(st.bt_offsets, dtype=torch.int32, device=dev),
+                         torch.as_tensor(bt, dtype=torch.int32, device=dev),
+                         torch.as_tensor(st.seq_lens, dtype=torch.int32, device=dev))
+    layout = (w.Hq, w.Hkv, w.d)
+    n = [int(x) for x in st.n_pages]
+    for b, lo, cnt in [(0, 0, n[0]), (1, 5, n[1] - 5 + 3), (2, 0, n[2]), (0, n[0] - 1, 1)]:
+        K = torch.full((cnt * 16, w.Hkv, w.d), 0x1234, dtype=torch.int16, device=dev)
+        V = torch.full_like(K, 0x1234)
+        M.mkv_materialize(layout, pd, batch, b, lo, cnt, K, V)
+        torch.cuda.synchronize()
+        Kr, Vr = OD.materialize(pool, st.bt_offsets, bt, b, lo, cnt)
+        assert np.array_equal(K.cpu().numpy().view(np.uint16), Kr), (b, lo, cnt)
+        assert np.array_equal(V.cpu().numpy().view(np.uint16), Vr), (b, lo, cnt)
+    assert (Kr[:16] != OD.BF16_NAN).all()
+    with pytest.raises(M.MkvError):
+        M.mkv_materialize(layout, pd, batch, 3, 0, 1, K, V)                  # b outside the batch
