@@ -215,6 +215,86 @@ def time_materialize(runner, reps=8):
     return ms, read, written
 
 
+def time_demote_pack(runner, n_pages=8192, reps=5):
+    """The pack kernel at the 64 requests x 128 aging pages scale: n_pages FP8
+    pages of random E4M3 bytes (no NaN codes) demoted into n_pages TQ3 slots,
+    one layer (mkv_demote_pages), timed with HIP events.  Returns (avg ms, bytes
+    read + written)."""
+    torch, M = runner.torch, runner.M
+    lay = runner.layout
+    fb, tb = M.mkv_fp8_page_bytes(lay), M.mkv_tq3_page_bytes(lay)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    fp8 = torch.randint(0, 254, (n_pages, fb), dtype=torch.uint8, generator=g, device="cuda")
+    fp8 += (fp8 >= 0x7F).to(torch.uint8)              # skip the NaN codes 0x7F and 0xFF
+    tq3 = torch.empty((n_pages, tb), dtype=torch.uint8, device="cuda")
+    tier = torch.full((2 * n_pages,), M.TIER_FREE, dtype=torch.uint8, device="cuda")
+    pool = M.make_pool(fp8, tq3, tier, n_pages, n_pages)
+    src = torch.arange(n_pages, dtype=torch.int32, device="cuda")
+    dst = src + n_pages
+    M.mkv_demote_pages(lay, pool, src, dst)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        M.mkv_demote_pages(lay, pool, src, dst)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    del fp8, tq3
+    return ms, n_pages * (fb + tb)
+
+
+def time_lifecycle(runner, reps=8):
+    """mkv_lifecycle_step at a page boundary of the canary (every request starts
+    a page and ages one Recent page into TQ3 in all layers), on block-table rows
+    with one spare entry; the tables, tier map and free stacks are restored
+    between repetitions (not timed).  Returns (avg ms, pages demoted)."""
+    torch, M = runner.torch, runner.M
+    w, st, dw = runner.w, runner.st, runner.dw
+    dev = "cuda"
+    n_fp8, n_tq3 = dw.cache.n_fp8, dw.cache.n_tq3
+    n_pages = [int(x) for x in st.n_pages]
+    offs = [0]
+    for n in n_pages:
+        offs.append(offs[-1] + n + 1)
+    bt0 = torch.full((offs[-1],), -1, dtype=torch.int32, device=dev)
+    for b in range(w.B):
+        bt0[offs[b]:offs[b] + n_pages[b]] = dw.bt[int(st.bt_offsets[b]):int(st.bt_offsets[b + 1])]
+    seq0 = torch.tensor([16 * n for n in n_pages], dtype=torch.int32, device=dev)
+    tier = dw.cache.tier
+    tier0 = tier.clone()
+    free_f = torch.nonzero(tier[:n_fp8] == M.TIER_FREE).flatten().to(torch.int32)
+    free_t = (torch.nonzero(tier[n_fp8:] == M.TIER_FREE).flatten() + n_fp8).to(torch.int32)
+    ff0 = torch.zeros(n_fp8, dtype=torch.int32, device=dev)
+    tf0 = torch.zeros(n_tq3, dtype=torch.int32, device=dev)
+    ff0[:free_f.numel()] = free_f
+    tf0[:free_t.numel()] = free_t
+    tops0 = torch.tensor([free_f.numel(), free_t.numel()], dtype=torch.int32, device=dev)
+    offs_d = torch.tensor(offs, dtype=torch.int32, device=dev)
+    bt, seq, ff, tf, tops = bt0.clone(), seq0.clone(), ff0.clone(), tf0.clone(), tops0.clone()
+    ws = torch.zeros(M.mkv_lifecycle_workspace_bytes(w.B), dtype=torch.uint8, device=dev)
+    R = w.recent_tokens // 16
+    ms = []
+    for _ in range(reps):
+        for x, x0 in ((bt, bt0), (seq, seq0), (tier, tier0), (ff, ff0), (tf, tf0), (tops, tops0)):
+            x.copy_(x0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        M.mkv_lifecycle_step(runner.layout, dw.cache.pools, offs_d, bt, seq, tier, ff, tf, tops, R, ws)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    status = M.mkv_workspace_status(ws)
+    demoted = int(tops0[1] - tops[1])
+    tier.copy_(tier0)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"lifecycle step status {status}")
+    return sum(ms[1:]) / (reps - 1), demoted
+
+
 def kernel_source_hash():
     """Hash of the sources the partial-attention kernel is compiled from."""
     import hashlib
@@ -334,6 +414,8 @@ def main():
         torch.cuda.synchronize()
         r.time_kernels(reps=5)
         time_materialize(r, reps=2)
+        time_demote_pack(r, reps=2)
+        time_lifecycle(r, reps=3)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
@@ -343,6 +425,8 @@ def main():
     kt = r.time_kernels()
     k_avg, k_med = kt["partials"]
     mat_ms, mat_read, mat_written = time_materialize(r)
+    dem_ms, dem_bytes = time_demote_pack(r)
+    lc_ms, lc_demoted = time_lifecycle(r)
     traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
@@ -373,6 +457,13 @@ def main():
                                    "gbs": round((mat_read + mat_written) / (mat_ms * 1e-3) / 1e9, 2),
                                    "frac_of_peak": round((mat_read + mat_written) / (mat_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                    "vs_decode_launch": round(mat_ms / k_avg, 3)},
+        # the pack kernel alone at the 64 x 128 aging-page scale (random E4M3 pages, one layer)
+        "demote_pack_8192_pages": {"avg_ms": round(dem_ms, 5), "bytes": dem_bytes,
+                                   "gbs": round(dem_bytes / (dem_ms * 1e-3) / 1e9, 2),
+                                   "frac_of_peak": round(dem_bytes / (dem_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        # mkv_lifecycle_step at a page boundary: FP8 pops, aging into TQ3 in all layers, table updates
+        "lifecycle_step_page_boundary": {"avg_ms": round(lc_ms, 5), "layers": w.L,
+                                         "pages_demoted_per_layer": lc_demoted},
     }
     if not a.no_control:
         del r

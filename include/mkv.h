@@ -55,7 +55,8 @@ enum {
 enum {
   MKV_DEV_BAD_PAGE_ID = 1,   /* block-table entry outside [0, n_fp8 + n_tq3)        */
   MKV_DEV_BAD_TIER = 2,      /* tier byte contradicts the slab the id points into   */
-  MKV_DEV_BAD_SEQ_LEN = 4    /* seq_len < 0 or longer than the request's block table */
+  MKV_DEV_BAD_SEQ_LEN = 4,   /* seq_len < 0 or longer than the request's block table */
+  MKV_DEV_NO_FREE_PAGE = 8   /* lifecycle: too few free ids, or a stack top outside its array */
 };
 
 /* Tier map values: one byte per physical page id.  Recent and Anchor pages
@@ -278,8 +279,57 @@ int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_ba
                     int32_t b, int32_t page_lo, int32_t n_pages, uint16_t* k_out,
                     uint16_t* v_out, void* stream);
 
+/* ---- page lifecycle ------------------------------------------------------
+ * Recent and protected Anchor pages stay FP8, older non-anchor pages move to
+ * packed TQ3, and every live-request page stays addressable (arXiv
+ * 2608.23834, page 1, Abstract).  The pages describe no allocator; these
+ * calls implement one on the device, with these readings:
+ *  - Free ids are two stacks: fp8_free[0 .. free_tops[0]) holds free FP8 ids,
+ *    tq3_free[0 .. free_tops[1]) free TQ3 ids (physical ids n_fp8 ...); a pop
+ *    takes the entry just below the top.  A free id has tier MKV_TIER_FREE.
+ *  - Which pages are Anchors is the caller's policy: it writes tier A.
+ *
+ * mkv_lifecycle_step: one decode step adds one token to every request.  A
+ *   request whose seq_len is a multiple of 16 starts logical page seq_len/16:
+ *   it pops an FP8 id, written into its block-table row, tier Recent.  Its
+ *   page count is then n + 1 and, with a Recent window of recent_pages pages,
+ *   logical page n - recent_pages leaves the window: if its tier is Recent it
+ *   pops a TQ3 id and is demoted (mkv_demote_pages' rule) in every layer, its
+ *   block-table entry is switched to the TQ3 id (tier Stale) and its FP8 id
+ *   (tier free) is pushed back; Anchor pages stay FP8 and other tiers are
+ *   left alone.  seq_lens[b] += 1.  Requests pop in request order and the
+ *   freed FP8 ids are pushed in the same order after the pops, so the result
+ *   is deterministic.  Run it before the step's append (mkv_append or
+ *   mkv_append_attend at position seq_lens[b] - 1) and decode plan.
+ *   All or nothing: a full block-table row (bt_offsets[b+1] - bt_offsets[b]
+ *   entries), an id outside the pool, a tier that contradicts an id, too few
+ *   free ids or a stack top outside its array change nothing and set
+ *   MKV_DEV_* bits in the workspace status (mkv_workspace_status).
+ *   pools: host array of n_layers descriptors sharing n_fp8, n_tq3 and the
+ *   tier map `tier` (device, written).  bt_offsets: device int32[batch + 1];
+ *   bt_pages (int32[bt_capacity]), seq_lens (int32[batch]), fp8_free
+ *   (int32[n_fp8]), tq3_free (int32[n_tq3]) and free_tops (int32[2]) are
+ *   device arrays, read and written.  ws: device, 256-byte aligned, ws_bytes
+ *   >= mkv_lifecycle_workspace_bytes(batch).
+ * mkv_lifecycle_release: every live page (the first ceil(seq_len / 16)
+ *   entries of the row) of the listed requests goes back to its stack, in
+ *   list order then logical order; its tier becomes free and the request's
+ *   seq_len 0.  requests: device int32[n_req], each listed at most once.
+ *   All or nothing as above; ws_bytes >= mkv_lifecycle_workspace_bytes(0). */
+size_t mkv_lifecycle_workspace_bytes(int32_t batch);
+int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                       const int32_t* bt_offsets, int32_t* bt_pages, int32_t* seq_lens,
+                       int32_t batch, int32_t bt_capacity, uint8_t* tier, int32_t* fp8_free,
+                       int32_t* tq3_free, int32_t* free_tops, int32_t recent_pages, void* ws,
+                       size_t ws_bytes, void* stream);
+int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool,
+                          const int32_t* bt_offsets, const int32_t* bt_pages, int32_t* seq_lens,
+                          int32_t batch, int32_t bt_capacity, uint8_t* tier, int32_t* fp8_free,
+                          int32_t* tq3_free, int32_t* free_tops, const int32_t* requests,
+                          int32_t n_req, void* ws, size_t ws_bytes, void* stream);
+
 /* Synchronise `stream` and return the device status bits (MKV_DEV_*) left in
- * the workspace by the last decode call on it (0 = no device-data error);
+ * the workspace by the last decode or lifecycle call on it (0 = no device-data error);
  * negative MKV_ERR_* on failure. */
 int mkv_workspace_status(const void* ws, void* stream);
 

@@ -14,7 +14,8 @@ __all__ = [
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
-    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_status_string",
+    "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
+    "mkv_lifecycle_release", "mkv_status_string",
     "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
@@ -78,6 +79,11 @@ def lib():
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_debug_gather": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
         "mkv_materialize": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+        "mkv_lifecycle_workspace_bytes": (c_sz, [c_i32]),
+        "mkv_lifecycle_step": (c_i32, [P(Layout), P(PoolDesc), c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                       c_vp, c_i32, c_vp, c_sz, c_vp]),
+        "mkv_lifecycle_release": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
         "mkv_workspace_status": (c_i32, [c_vp, c_vp]),
         "mkv_status_string": (ctypes.c_char_p, [c_i32]),
         "mkv_last_error": (ctypes.c_char_p, []),
@@ -278,6 +284,44 @@ def mkv_materialize(layout, pool, batch, b, page_lo, n_pages, k_out, v_out, stre
     return _check(lib().mkv_materialize(ctypes.byref(_layout(layout)), ctypes.byref(pool), ctypes.byref(batch),
                                         int(b), int(page_lo), int(n_pages), _ptr(k_out, name="k_out"),
                                         _ptr(v_out, name="v_out"), _stream(stream)))
+
+
+def mkv_lifecycle_workspace_bytes(batch):
+    return lib().mkv_lifecycle_workspace_bytes(int(batch))
+
+
+def _pool_array(pools):
+    pools = list(pools)
+    arr = (PoolDesc * len(pools))(*pools)
+    arr._keep = pools
+    return arr
+
+
+def mkv_lifecycle_step(layout, pools, bt_offsets, bt_pages, seq_lens, tier, fp8_free, tq3_free, free_tops,
+                       recent_pages, ws, stream=None):
+    """One decode step's page lifecycle (new FP8 pages, aging into TQ3 in every
+    layer, block-table / tier / free-stack updates); int32 / uint8 device tensors."""
+    import torch
+    arr = _pool_array(pools)
+    return _check(lib().mkv_lifecycle_step(
+        ctypes.byref(_layout(layout)), arr, len(arr), _ptr(bt_offsets, torch.int32, "bt_offsets"),
+        _ptr(bt_pages, torch.int32, "bt_pages"), _ptr(seq_lens, torch.int32, "seq_lens"), int(seq_lens.numel()),
+        int(bt_pages.numel()), _ptr(tier, torch.uint8, "tier"), _ptr(fp8_free, torch.int32, "fp8_free"),
+        _ptr(tq3_free, torch.int32, "tq3_free"), _ptr(free_tops, torch.int32, "free_tops"), int(recent_pages),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mkv_lifecycle_release(layout, pool, bt_offsets, bt_pages, seq_lens, tier, fp8_free, tq3_free, free_tops,
+                          requests, ws, stream=None):
+    """Return every live page of the listed requests to the free stacks."""
+    import torch
+    return _check(lib().mkv_lifecycle_release(
+        ctypes.byref(_layout(layout)), ctypes.byref(pool), _ptr(bt_offsets, torch.int32, "bt_offsets"),
+        _ptr(bt_pages, torch.int32, "bt_pages"), _ptr(seq_lens, torch.int32, "seq_lens"), int(seq_lens.numel()),
+        int(bt_pages.numel()), _ptr(tier, torch.uint8, "tier"), _ptr(fp8_free, torch.int32, "fp8_free"),
+        _ptr(tq3_free, torch.int32, "tq3_free"), _ptr(free_tops, torch.int32, "free_tops"),
+        _ptr(requests, torch.int32, "requests"), int(requests.numel()), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mkv_workspace_status(ws, stream=None):

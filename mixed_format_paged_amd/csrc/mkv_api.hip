@@ -453,6 +453,77 @@ int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_ba
   return e == hipSuccess ? MKV_OK : hip_fail(e, "materialize launch");
 }
 
+size_t mkv_lifecycle_workspace_bytes(int32_t batch) {
+  if (batch < 0) return 0;
+  return align_up(sizeof(int32_t) * (4 + 3 * (size_t)batch), 256);
+}
+
+namespace {
+
+// Checks shared by the lifecycle calls: layout, pools (equal sizes, the tier
+// map given), the batch tables and the free stacks.
+int check_lifecycle(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers, const int32_t* bt_offsets,
+                    const void* bt_pages, int32_t* seq_lens, int32_t batch, int32_t bt_capacity, uint8_t* tier,
+                    int32_t* fp8_free, int32_t* tq3_free, int32_t* free_tops, void* ws, size_t ws_bytes,
+                    size_t ws_need, Geometry* g, LayerTable* lt) {
+  int rc = check_layout(layout, g);
+  if (rc) return rc;
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(MKV_ERR_RANGE, "n_layers %d not in [1, %d]", n_layers, kMaxLayers);
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
+    if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != tier)
+      return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map passed in", l);
+    if (lt) {
+      lt->fp8[l] = pools[l].fp8_slab;
+      lt->tq3[l] = pools[l].tq3_slab;
+      lt->k_scale[l] = pools[l].k_scale;
+      lt->v_scale[l] = pools[l].v_scale;
+    }
+  }
+  if (batch < 0 || bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", batch, bt_capacity);
+  if (!bt_offsets || !bt_pages || !seq_lens || !tier || !fp8_free || !tq3_free || !free_tops || !ws)
+    return fail(MKV_ERR_NULL, "tables, tier map, free stacks, free_tops and ws are required");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < ws_need) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, ws_need);
+  return MKV_OK;
+}
+
+}  // namespace
+
+int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                       const int32_t* bt_offsets, int32_t* bt_pages, int32_t* seq_lens, int32_t batch,
+                       int32_t bt_capacity, uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free,
+                       int32_t* free_tops, int32_t recent_pages, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  LayerTable lt{};
+  int rc = check_lifecycle(layout, pools, n_layers, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier,
+                           fp8_free, tq3_free, free_tops, ws, ws_bytes, mkv_lifecycle_workspace_bytes(batch), &g, &lt);
+  if (rc) return rc;
+  if (recent_pages < 1) return fail(MKV_ERR_RANGE, "recent_pages %d must be >= 1", recent_pages);
+  if ((int64_t)n_layers * batch * g.hkv > 0x7fffffff) return fail(MKV_ERR_RANGE, "batch too large");
+  hipError_t e = launch_lifecycle_step(g, lt, n_layers, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier,
+                                       fp8_free, tq3_free, free_tops, recent_pages, static_cast<int32_t*>(ws),
+                                       as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "lifecycle launch");
+}
+
+int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+                          const int32_t* bt_pages, int32_t* seq_lens, int32_t batch, int32_t bt_capacity,
+                          uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free, int32_t* free_tops,
+                          const int32_t* requests, int32_t n_req, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  int rc = check_lifecycle(layout, pool, 1, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free,
+                           tq3_free, free_tops, ws, ws_bytes, mkv_lifecycle_workspace_bytes(0), &g, nullptr);
+  if (rc) return rc;
+  if (n_req < 0) return fail(MKV_ERR_RANGE, "n_req %d", n_req);
+  if (n_req > 0 && !requests) return fail(MKV_ERR_NULL, "requests is required");
+  hipError_t e = launch_lifecycle_release(g, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free,
+                                          tq3_free, free_tops, requests, n_req, static_cast<int32_t*>(ws),
+                                          as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "lifecycle release launch");
+}
+
 int mkv_workspace_status(const void* ws, void* stream) {
   if (!ws) return fail(MKV_ERR_NULL, "ws is NULL");
   hipError_t e = hipStreamSynchronize(as_stream(stream));

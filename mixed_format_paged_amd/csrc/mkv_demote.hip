@@ -9,6 +9,10 @@
 //   phase 2: each thread assembles four consecutive triples (12 bytes) of the
 //            head block from LDS in the documented slot order and stores
 //            them as three 32-bit words; scales are stored as fp16.
+// The lifecycle's variant takes its page count from device memory and also
+// rewrites each demoted page's block-table entry, tier bytes and free-stack
+// slot (one workgroup per page does it; nothing else in the launch reads
+// them, and the FP8 slot it frees is only reused by a later launch).
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -17,7 +21,7 @@ namespace mkv {
 template <int D>
 __global__ void __launch_bounds__(256) demote_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
-    const int32_t* __restrict__ dst) {
+    const int32_t* __restrict__ dst, const int32_t* __restrict__ n_dev, TableUpdate upd) {
   constexpr int G = D / 32;
   __shared__ uint8_t codes[2][kPage][D];
   __shared__ uint16_t scales[2][kPage][G];
@@ -28,9 +32,16 @@ __global__ void __launch_bounds__(256) demote_kernel(
   const uint8_t* __restrict__ fp8_slab = lt.fp8[layer];
   uint8_t* __restrict__ tq3_slab = lt.tq3[layer];
   const float k_scale = lt.k_scale[layer], v_scale = lt.v_scale[layer];
+  if (n_dev && page >= *n_dev) return;                                              // uniform
   const int s_id = src[page];
   const int d_id = dst[page];
   if (s_id < 0 || s_id >= n_fp8 || d_id < n_fp8 || d_id >= n_fp8 + n_tq3) return;   // uniform
+  if (upd.bt_pages && layer == 0 && h == 0 && threadIdx.x == 0) {
+    upd.bt_pages[upd.entry[page]] = d_id;
+    upd.tier[d_id] = kTierStale;
+    upd.tier[s_id] = kTierFree;
+    upd.fp8_free[*upd.push_base + page] = s_id;
+  }
   const uint8_t* in = fp8_slab + (size_t)s_id * fp8_page_bytes(hkv, D) + (size_t)h * 2 * kPage * D;
   uint8_t* out = tq3_slab + (size_t)(d_id - n_fp8) * tq3_page_bytes(hkv, D) + (size_t)h * tq3_head_bytes(D);
 
@@ -106,17 +117,24 @@ __global__ void __launch_bounds__(256) demote_kernel(
   }
 }
 
-hipError_t launch_demote(const Geometry& g, const LayerTable& lt, int n_layers,
-                         const int32_t* src, const int32_t* dst, int n, hipStream_t stream) {
+hipError_t launch_demote_listed(const Geometry& g, const LayerTable& lt, int n_layers, const int32_t* src,
+                                const int32_t* dst, int n, const int32_t* n_dev, const TableUpdate* upd,
+                                hipStream_t stream) {
   if (n == 0 || n_layers == 0) return hipSuccess;
   dim3 grid(n_layers * n * g.hkv);
+  const TableUpdate u = upd ? *upd : TableUpdate{nullptr, nullptr, nullptr, nullptr, nullptr};
   if (g.d == 256)
     hipLaunchKernelGGL(demote_kernel<256>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
-                       g.hkv, src, dst);
+                       g.hkv, src, dst, n_dev, u);
   else
     hipLaunchKernelGGL(demote_kernel<128>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
-                       g.hkv, src, dst);
+                       g.hkv, src, dst, n_dev, u);
   return hipGetLastError();
+}
+
+hipError_t launch_demote(const Geometry& g, const LayerTable& lt, int n_layers,
+                         const int32_t* src, const int32_t* dst, int n, hipStream_t stream) {
+  return launch_demote_listed(g, lt, n_layers, src, dst, n, nullptr, nullptr, stream);
 }
 
 }  // namespace mkv

@@ -27,7 +27,7 @@ constexpr int kTargetItems = 4096 / kItemWaves;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk (a workgroup stages its page ids in LDS)
 constexpr int kMaxG = 8;              // query heads per KV head supported
-constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4;
+constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8;
 
 // Per-request plan fields, each an int32[batch + 1] row of req[].
 enum ReqField {
@@ -107,6 +107,27 @@ hipError_t launch_append(const Geometry& g, uint8_t* fp8_slab, float k_scale, fl
                          int batch, hipStream_t stream);
 hipError_t launch_demote(const Geometry& g, const LayerTable& lt, int n_layers,
                          const int32_t* src, const int32_t* dst, int n, hipStream_t stream);
+// Block-table, tier and free-stack updates done by the demote kernel for the
+// page lifecycle (bt_pages == NULL: none).
+struct TableUpdate {
+  int32_t* bt_pages;
+  uint8_t* tier;
+  int32_t* fp8_free;
+  const int32_t* entry;       // [n] block-table entry of each demoted page
+  const int32_t* push_base;   // device: free-stack slot of the first freed FP8 id
+};
+// Demote src[i] -> dst[i] for i < *n_dev (n_dev == NULL: i < n); n bounds the grid.
+hipError_t launch_demote_listed(const Geometry& g, const LayerTable& lt, int n_layers, const int32_t* src,
+                                const int32_t* dst, int n, const int32_t* n_dev, const TableUpdate* upd,
+                                hipStream_t stream);
+hipError_t launch_lifecycle_step(const Geometry& g, const LayerTable& lt, int n_layers, const int32_t* bt_offsets,
+                                 int32_t* bt_pages, int32_t* seq_lens, int batch, int bt_capacity, uint8_t* tier,
+                                 int32_t* fp8_free, int32_t* tq3_free, int32_t* tops, int recent, int32_t* ws,
+                                 hipStream_t stream);
+hipError_t launch_lifecycle_release(const Geometry& g, const int32_t* bt_offsets, const int32_t* bt_pages,
+                                    int32_t* seq_lens, int batch, int bt_capacity, uint8_t* tier, int32_t* fp8_free,
+                                    int32_t* tq3_free, int32_t* tops, const int32_t* requests, int n_req, int32_t* ws,
+                                    hipStream_t stream);
 hipError_t launch_gather(const Geometry& g, const uint8_t* fp8_slab, const uint8_t* tq3_slab,
                          const int32_t* bt_offsets, const int32_t* bt_pages, int b, int n_pages,
                          uint8_t* out, hipStream_t stream);

@@ -303,3 +303,80 @@ def test_materialize_bitexact(d, scales):
     assert (Kr[:16] != OD.BF16_NAN).all()
     with pytest.raises(M.MkvError):
         M.mkv_materialize(layout, pd, batch, 3, 0, 1, K, V)                  # b outside the batch
+
+
+def test_lifecycle_steps_match_the_oracle():
+    """mkv_lifecycle_step (+ the step's mkv_append) from the same start state as
+    the oracle: block table, seq_lens, tier map, free stacks, tops and every
+    slab byte agree bit for bit at every checkpoint; an anchor set by the
+    caller stays FP8; a request released mid-way regrows from zero (ragged
+    lengths); a step that cannot get free pages changes nothing."""
+    from oracle import lifecycle as LC
+    hq, hkv, d, R, L, B, cap, n_fp8, n_tq3 = 4, 2, 128, 3, 2, 3, 12, 14, 30
+    layout = (hq, hkv, d)
+    rng = np.random.default_rng(7)
+    tier = np.full(n_fp8 + n_tq3, OP.TIER_FREE, dtype=np.uint8)
+    pools = [OP.Pool(hkv, d, n_fp8, n_tq3, tier=tier) for _ in range(L)]
+    t = LC.Tables(np.arange(B + 1) * cap, np.full(B * cap, -1), np.zeros(B, dtype=np.int64), tier,
+                  rng.permutation(n_fp8), n_fp8 + rng.permutation(n_tq3), [n_fp8, n_tq3])
+    dev = "cuda"
+    i32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32, device=dev).contiguous()
+    fp8_d = [torch.from_numpy(p.fp8).to(dev) for p in pools]
+    tq3_d = [torch.from_numpy(p.tq3).to(dev) for p in pools]
+    tier_d = torch.from_numpy(tier).to(dev)
+    pd = [M.make_pool(fp8_d[l], tq3_d[l], tier_d, n_fp8, n_tq3) for l in range(L)]
+    offs_d, bt_d, sl_d = i32(t.bt_offsets), i32(t.bt_pages), i32(t.seq_lens)
+    ff_d, tf_d, tops_d = i32(t.fp8_free), i32(t.tq3_free), i32(t.tops)
+    ws = torch.zeros(M.mkv_lifecycle_workspace_bytes(B), dtype=torch.uint8, device=dev)
+
+    def same(what):
+        torch.cuda.synchronize()
+        assert np.array_equal(bt_d.cpu().numpy(), t.bt_pages), what
+        assert np.array_equal(sl_d.cpu().numpy(), t.seq_lens), what
+        assert np.array_equal(tier_d.cpu().numpy(), tier), what
+        assert list(tops_d.cpu().numpy()) == list(t.tops), what
+        assert np.array_equal(ff_d.cpu().numpy()[:t.tops[0]], t.fp8_free[:t.tops[0]]), what
+        assert np.array_equal(tf_d.cpu().numpy()[:t.tops[1]], t.tq3_free[:t.tops[1]]), what
+        for l in range(L):
+            assert np.array_equal(fp8_d[l].cpu().numpy(), pools[l].fp8), (what, l)
+            assert np.array_equal(tq3_d[l].cpu().numpy(), pools[l].tq3), (what, l)
+
+    def step_both(what, append=None):
+        assert LC.step(pools, t, R) == 0, what
+        M.mkv_lifecycle_step(layout, pd, offs_d, bt_d, sl_d, tier_d, ff_d, tf_d, tops_d, R, ws)
+        assert M.mkv_workspace_status(ws) == 0, what
+        if append is None:
+            return
+        kk, vv = append
+        for l in range(L):
+            OP.append(pools[l], kk[l], vv[l], t.bt_offsets, t.bt_pages, t.seq_lens - 1)
+            M.mkv_append(layout, pd[l], torch.from_numpy(kk[l].copy()).to(dev),
+                         torch.from_numpy(vv[l].copy()).to(dev), offs_d, bt_d, sl_d - 1)
+
+    T = 150
+    k = rng.standard_normal((L, B, T, 1, hkv, d)).astype(np.float32) * 3
+    v = rng.standard_normal((L, B, T, 1, hkv, d)).astype(np.float32) * 3
+    for step in range(T):
+        step_both(f"step {step}", (k[:, :, step], v[:, :, step]))
+        if step == 30:                              # the caller protects request 0's page 1
+            pid = int(t.bt_pages[t.bt_offsets[0] + 1])
+            assert tier[pid] == OP.TIER_R
+            tier[pid] = OP.TIER_A
+            tier_d[pid] = OP.TIER_A
+        if step == 60:                              # request 2 ends; its slot regrows from zero
+            assert LC.release(pools[0], t, [2]) == 0
+            M.mkv_lifecycle_release(layout, pd[0], offs_d, bt_d, sl_d, tier_d, ff_d, tf_d, tops_d, i32([2]), ws)
+            assert M.mkv_workspace_status(ws) == 0
+        if step % 16 in (0, 15) or step == 60 or step == T - 1:
+            same(f"step {step}")
+    assert list(t.seq_lens) == [T, T, T - 61]
+    # up to a page boundary of requests 0 and 1, then a step with one free FP8 id
+    for i in range((16 - T % 16) % 16):
+        step_both(f"advance {i}")
+    t.tops[0] = 1
+    tops_d[0] = 1
+    same("before the failing step")
+    assert LC.step(pools, t, R) == LC.NO_FREE_PAGE
+    M.mkv_lifecycle_step(layout, pd, offs_d, bt_d, sl_d, tier_d, ff_d, tf_d, tops_d, R, ws)
+    assert M.mkv_workspace_status(ws) == LC.NO_FREE_PAGE
+    same("after the failing step")
