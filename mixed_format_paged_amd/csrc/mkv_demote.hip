@@ -1,14 +1,19 @@
 // mkv_demote.hip -- FP8 -> TQ3 page demotion (the pack).
 //
-// "Older non-anchor pages move to packed TQ3" (arXiv 2608.23834, page 1,
+// Older non-anchor pages move to packed TQ3 (arXiv 2608.23834, page 1,
 // Abstract).  One workgroup per (layer, page, KV head):
-//   phase 1: one thread per (K/V, token, 32-channel group) decodes the FP8
-//            bytes (x = fl32(decode(e) * scale)), takes the absmax, forms the
-//            fp16 scale s = fp16_RNE(fl32(a / 3)) and the codes u = q + 4,
-//            and leaves codes and scales in LDS;
-//   phase 2: each thread assembles four consecutive triples (12 bytes) of the
-//            head block from LDS in the documented slot order and stores
-//            them as three 32-bit words; scales are stored as fp16.
+//   phase 1: one thread per (K/V, token, 32-channel group) converts its 32 FP8
+//            bytes (x = fl32(decode(e) * scale), decode exact through the
+//            hardware E4M3 conversion), takes the absmax, forms the fp16
+//            scale s = fp16_RNE(fl32(a / 3)) and the codes u = q + 4 (q the
+//            nearest integer to x / s, ties to even, from exact fp32
+//            thresholds).  A K group's 32 codes are exactly four triples of
+//            its token row, packed in registers and stored as triple words;
+//            a V group's codes are OR-ed, two channels at a time, into the
+//            triple words of their (token quarter, channel pair).
+//   phase 2: each thread packs four consecutive triple words into the 12
+//            bytes of the head block and stores them with one 12-byte store;
+//            the scales follow as 16-byte chunks.
 // The lifecycle's variant takes its page count from device memory and also
 // rewrites each demoted page's block-table entry, tier bytes and free-stack
 // slot (one workgroup per page does it; nothing else in the launch reads
@@ -18,20 +23,20 @@
 
 namespace mkv {
 
+typedef uint32_t u3v __attribute__((ext_vector_type(3)));
+
 template <int D>
 __global__ void __launch_bounds__(256) demote_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
     const int32_t* __restrict__ dst, const int32_t* __restrict__ n_dev, TableUpdate upd) {
   constexpr int G = D / 32;
-  __shared__ uint8_t codes[2][kPage][D];
-  __shared__ uint16_t scales[2][kPage][G];
+  constexpr int NTRI = 4 * D;                        // triples of a head block: 2D of K, 2D of V
+  __shared__ __align__(16) uint32_t tw[NTRI];        // one word per triple (24 bits used)
+  __shared__ __align__(16) uint16_t sc[D];           // the 2D scale bytes, in block order
   const int layer = blockIdx.x / (n * hkv);
   const int rest = blockIdx.x - layer * n * hkv;
   const int page = rest / hkv;
   const int h = rest - page * hkv;
-  const uint8_t* __restrict__ fp8_slab = lt.fp8[layer];
-  uint8_t* __restrict__ tq3_slab = lt.tq3[layer];
-  const float k_scale = lt.k_scale[layer], v_scale = lt.v_scale[layer];
   if (n_dev && page >= *n_dev) return;                                              // uniform
   const int s_id = src[page];
   const int d_id = dst[page];
@@ -42,79 +47,86 @@ __global__ void __launch_bounds__(256) demote_kernel(
     upd.tier[s_id] = kTierFree;
     upd.fp8_free[*upd.push_base + page] = s_id;
   }
+  const uint8_t* __restrict__ fp8_slab = lt.fp8[layer];
+  uint8_t* __restrict__ tq3_slab = lt.tq3[layer];
+  const float k_scale = lt.k_scale[layer], v_scale = lt.v_scale[layer];
   const uint8_t* in = fp8_slab + (size_t)s_id * fp8_page_bytes(hkv, D) + (size_t)h * 2 * kPage * D;
   uint8_t* out = tq3_slab + (size_t)(d_id - n_fp8) * tq3_page_bytes(hkv, D) + (size_t)h * tq3_head_bytes(D);
+
+  for (int e = threadIdx.x; e < NTRI / 4; e += blockDim.x) reinterpret_cast<uint4*>(tw)[e] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
 
   for (int grp = threadIdx.x; grp < 2 * kPage * G; grp += blockDim.x) {
     const int kv = grp / (kPage * G);
     const int t = (grp / G) % kPage;
     const int g = grp % G;
-    const float sc = kv ? v_scale : k_scale;
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(in + (kv * kPage + t) * D + g * 32);
+    const float scl = kv ? v_scale : k_scale;
+    const uint4* row = reinterpret_cast<const uint4*>(in + (kv * kPage + t) * D + g * 32);
+    const uint4 r0 = row[0], r1 = row[1];
+    const uint32_t words[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     float x[32];
     float a = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const uint32_t word = row[w];
-#pragma unroll
-      for (int byte = 0; byte < 4; ++byte) {
-        const float val = __fmul_rn(e4m3_decode((word >> (8 * byte)) & 0xffu), sc);
-        x[w * 4 + byte] = val;
-        a = fmaxf(a, fabsf(val));
-      }
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(words[w], 1.0f, false);   // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(words[w], 1.0f, true);    // bytes 2, 3
+      x[4 * w] = lo[0];
+      x[4 * w + 1] = lo[1];
+      x[4 * w + 2] = hi[0];
+      x[4 * w + 3] = hi[1];
     }
+    if (scl != 1.0f) {                               // uniform; x * 1 is x exactly
+#pragma unroll
+      for (int c = 0; c < 32; ++c) x[c] = __fmul_rn(x[c], scl);
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) a = fmaxf(a, fabsf(x[c]));
     const uint16_t sb = tq3_scale_bits(a);
     const float s = half_bits_to_float(sb);
-    scales[kv][t][g] = sb;
+    sc[(tq3_scale_off(D, kv, t, g) - 12 * D) / 2] = sb;
+    // |q| counts the exact fp32 thresholds 0.5 s, 1.5 s (inclusive: ties to
+    // even) and 2.5 s below |x|; s == 0 gives q = 0 through infinite thresholds
+    const bool zero = s == 0.0f;
+    const float t1 = zero ? INFINITY : 0.5f * s, t2 = zero ? INFINITY : 1.5f * s, t3 = zero ? INFINITY : 2.5f * s;
+    uint32_t u[32];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) codes[kv][t][g * 32 + c] = (uint8_t)(tq3_code(x[c], s) + 4);
+    for (int c = 0; c < 32; ++c) {
+      const float ax = fabsf(x[c]);
+      const uint32_t m = (uint32_t)(ax > t1) + (uint32_t)(ax >= t2) + (uint32_t)(ax > t3);
+      u[c] = (__float_as_uint(x[c]) >> 31) ? 4u - m : 4u + m;
+    }
+    if (kv == 0) {
+      // K: channels 8j .. 8j + 7 of the group are triple (j, g) of row t, slot k = channel
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w |= u[8 * j + k] << (3 * k);
+        tw[t * (D / 8) + j * G + g] = w;
+      }
+    } else {
+      // V: channels (a, a + 1) of token t sit in triple (t / 4, n, p) at slots
+      // of (channel in pair, t % 4); four tokens share a triple, so OR them in
+      const int r = t & 3;
+      const int s0 = 3 * tq3_v_slot(0, r), s1 = 3 * tq3_v_slot(1, r);
+#pragma unroll
+      for (int pc = 0; pc < 16; ++pc) {
+        const int c = g * 32 + 2 * pc;               // channel a of the pair
+        const int n = c / (D / 16), p = (c % (D / 16)) / 2;
+        atomicOr(&tw[2 * D + ((t >> 2) * 16 + n) * G + p], (u[2 * pc] << s0) | (u[2 * pc + 1] << s1));
+      }
+    }
   }
   __syncthreads();
 
-  // code region: 12 D bytes = 4 D triples; thread handles triples 4 tau .. 4 tau + 3
-  for (int tau = threadIdx.x; tau < D; tau += blockDim.x) {
-    uint32_t words[3] = {0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ti = 4 * tau + q;
-      uint32_t tw = 0;
-      if (ti < 2 * D) {                                  // K triple: row t, triple (j, g)
-        const int t = ti / (D / 8);
-        const int r = ti - t * (D / 8);
-        const int j = r / G, g = r - (r / G) * G;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) tw |= (uint32_t)codes[0][t][32 * g + 8 * j + k] << (3 * k);
-      } else {                                           // V triple: (j, n, p)
-        const int tv = ti - 2 * D;
-        const int p = tv % G;
-        const int jn = tv / G;
-        const int n = jn & 15, j = jn >> 4;
-        const int a = n * (D / 16) + 2 * p;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // inverse of the slot table: slot -> (channel-in-pair, token-in-quarter)
-          const int ci = (0x3c >> k) & 1;                // slots 2,3,4,5 hold channel b
-          const int rr = (0xde18 >> (2 * k)) & 3;        // slot -> r : 0,2,1,0,2,3,1,3
-          tw |= (uint32_t)codes[1][4 * j + rr][a + ci] << (3 * k);
-        }
-      }
-      // place the 24-bit triple at byte 3q of the 12-byte window
-      const int bit = 24 * q;
-      words[bit >> 5] |= tw << (bit & 31);
-      if ((bit & 31) > 8) words[(bit >> 5) + 1] |= tw >> (32 - (bit & 31));
-    }
-    uint32_t* o = reinterpret_cast<uint32_t*>(out + 12 * tau);
-    o[0] = words[0];
-    o[1] = words[1];
-    o[2] = words[2];
+  // four triples = 12 bytes per thread, one 12-byte store each
+  for (int tau = threadIdx.x; tau < NTRI / 4; tau += blockDim.x) {
+    const uint4 q = reinterpret_cast<const uint4*>(tw)[tau];
+    const u3v w = {q.x | (q.y << 24), (q.y >> 8) | (q.z << 16), (q.z >> 16) | (q.w << 8)};
+    *reinterpret_cast<u3v*>(out + 12 * tau) = w;
   }
-  // scales: 2 * 16 * G fp16 values
-  for (int e = threadIdx.x; e < 2 * kPage * G; e += blockDim.x) {
-    const int kv = e / (kPage * G);
-    const int t = (e / G) % kPage;
-    const int g = e % G;
-    *reinterpret_cast<uint16_t*>(out + tq3_scale_off(D, kv, t, g)) = scales[kv][t][g];
-  }
+  for (int e = threadIdx.x; e < 2 * D / 16; e += blockDim.x)
+    reinterpret_cast<uint4*>(out + 12 * D)[e] = reinterpret_cast<const uint4*>(sc)[e];
 }
 
 hipError_t launch_demote_listed(const Geometry& g, const LayerTable& lt, int n_layers, const int32_t* src,
