@@ -9,7 +9,9 @@ page 1, Abstract; page 2, "Enhanced Key Takeaways", third bullet, and
 "Technical Deep Dive", second bullet).  So the oracle computes the plain
 definition: dense softmax attention in fp64 over the dequantised cache.
 
-Readings: single query token per request; query head i reads KV head
+Readings: one query token per request (decode_batch) or the request's last
+T tokens as queries (decode_batch_multi: query token t of T attends to the
+tokens at positions [0, seq_len - T + t], causal); query head i reads KV head
 i // (Hq / Hkv); softmax scale 1 / sqrt(d) unless given; tokens at or beyond
 seq_len are absent; seq_len = 0 gives o = 0 and lse = -inf; lse is the
 natural log of the softmax denominator including the running max.
@@ -103,4 +105,22 @@ def decode_batch(pool, q, bt_offsets, bt_pages, seq_lens, sm_scale=None):
     for b in range(B):
         K, V = gather_kv(pool, bt_offsets, bt_pages, b, int(seq_lens[b]))
         out[b], lse[b] = decode_attention(q[b], K, V, sm_scale)
+    return out, lse
+
+
+def decode_batch_multi(pool, q, bt_offsets, bt_pages, seq_lens, sm_scale=None):
+    """Multi-query decode: q [B][T][Hq][d] holds the queries of each request's
+    last T tokens (positions seq_len - T .. seq_len - 1); query token t attends
+    to the tokens at positions [0, seq_len - T + t] (none if that is empty).
+    Returns (out [B][T][Hq][d], lse [B][T][Hq])."""
+    from .pool import gather_kv
+    B, T, Hq, d = q.shape
+    out = np.zeros((B, T, Hq, d))
+    lse = np.zeros((B, T, Hq))
+    for b in range(B):
+        sl = int(seq_lens[b])
+        K, V = gather_kv(pool, bt_offsets, bt_pages, b, sl)
+        for t in range(T):
+            n = max(0, sl - T + t + 1)
+            out[b, t], lse[b, t] = decode_attention(q[b, t], K[:n], V[:n], sm_scale)
     return out, lse

@@ -11,6 +11,7 @@ import pytest
 import torch
 from hypothesis import given, settings, strategies as st
 
+import workloads as W
 from oracle import attention as A
 
 
@@ -132,3 +133,38 @@ def test_merge_two_part_closed_form():
         assert np.allclose(o[i], (s1[2][i] / s1[1][i]) * a + (s2[2][i] / s2[1][i]) * b, atol=1e-12)
     o_e, lse_e = A.merge_states([A.partial_state(q, K[:0], V[:0])])
     assert np.all(o_e == 0) and np.all(np.isneginf(lse_e))
+
+
+def test_multi_query_is_causal_and_matches_a_masked_library_softmax():
+    """decode_batch_multi against torch's SDPA in fp64 with an explicit causal
+    mask over the last T positions; T = 1 equals decode_batch; queries whose
+    visible prefix is empty give 0 / -inf."""
+    import torch
+    from oracle import build, pool as P
+    w = W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, lengths=("list", (300, 2)))
+    st = W.make_structure(w)
+    vals = W.layer_values(w, st, 0)
+    pool, bt = build.build_layer(w, st, [x.numpy() for x in vals["k"]], [x.numpy() for x in vals["v"]])
+    T = 4
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((w.B, T, w.Hq, w.d)).astype(np.float32)
+    out, lse = A.decode_batch_multi(pool, q, st.bt_offsets, bt, st.seq_lens)
+    G = w.Hq // w.Hkv
+    for b in range(w.B):
+        sl = int(st.seq_lens[b])
+        K, V = P.gather_kv(pool, st.bt_offsets, bt, b, sl)
+        for t in range(T):
+            vis = sl - T + t + 1
+            if vis <= 0:
+                assert np.all(out[b, t] == 0) and np.all(np.isneginf(lse[b, t]))
+                continue
+            for i in range(w.Hq):
+                h = i // G
+                mask = torch.zeros(1, sl, dtype=torch.float64)
+                mask[0, vis:] = -float("inf")
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q[b, t, i].astype(np.float64))[None, None],
+                    torch.from_numpy(K[:, h])[None], torch.from_numpy(V[:, h])[None], attn_mask=mask[None])
+                assert np.allclose(out[b, t, i], ref[0, 0].numpy(), rtol=0, atol=1e-12)
+    o1, l1 = A.decode_batch(pool, q[:, -1], st.bt_offsets, bt, st.seq_lens)
+    assert np.array_equal(o1, out[:, -1]) and np.array_equal(l1, lse[:, -1])
