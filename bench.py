@@ -215,6 +215,36 @@ def time_materialize(runner, reps=8):
     return ms, read, written
 
 
+def time_multi_query(runner, T=4, reps=8):
+    """mkv_decode_attn_multi (plan + partials + merge) on one layer of the
+    canary with each request's last T tokens as causal queries, timed with HIP
+    events; launch set i reads layer i mod L.  Returns (avg ms per layer)."""
+    torch, M = runner.torch, runner.M
+    w = runner.w
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    q = torch.randn((1, w.B, T, w.Hq, w.d), generator=g, device="cuda")
+    out = torch.empty((1, w.B, T, w.Hq, w.d), device="cuda")
+    lse = torch.empty((1, w.B, T, w.Hq), device="cuda")
+    ws = torch.empty(M.mkv_decode_workspace_bytes_multi(runner.layout, w.B, runner.dw.bt.numel(), 1, T),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(l):
+        M.mkv_decode_attn_multi(runner.layout, [runner.dw.cache.pools[l]], runner.batch, q, runner.sm_scale, out, lse, ws)
+
+    run(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        run(i % w.L)
+        b.record()
+    torch.cuda.synchronize()
+    if M.mkv_workspace_status(ws) != 0:
+        raise RuntimeError("multi-query decode status")
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
 def time_demote_pack(runner, n_pages=8192, reps=5):
     """The pack kernel at the 64 requests x 128 aging pages scale: n_pages FP8
     pages of random E4M3 bytes (no NaN codes) demoted into n_pages TQ3 slots,
@@ -416,6 +446,7 @@ def main():
         time_materialize(r, reps=2)
         time_demote_pack(r, reps=2)
         time_lifecycle(r, reps=3)
+        time_multi_query(r, reps=2)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
@@ -427,6 +458,7 @@ def main():
     mat_ms, mat_read, mat_written = time_materialize(r)
     dem_ms, dem_bytes = time_demote_pack(r)
     lc_ms, lc_demoted = time_lifecycle(r)
+    mq_ms = time_multi_query(r, T=4)
     traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
@@ -464,6 +496,11 @@ def main():
         # mkv_lifecycle_step at a page boundary: FP8 pops, aging into TQ3 in all layers, table updates
         "lifecycle_step_page_boundary": {"avg_ms": round(lc_ms, 5), "layers": w.L,
                                          "pages_demoted_per_layer": lc_demoted},
+        # each request's last 4 tokens as causal queries, one layer per call (plan + partials + merge)
+        "multi_query_4_tokens": {"avg_ms_per_layer": round(mq_ms, 5),
+                                 "query_tokens_per_s": round(w.B * 4 / (mq_ms * 1e-3), 1),
+                                 "kv_gbs_per_query_token": round(4 * layer_bytes / (mq_ms * 1e-3) / 1e9, 2),
+                                 "vs_single_query_launch": round(mq_ms / k_avg, 3)},
     }
     if not a.no_control:
         del r

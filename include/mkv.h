@@ -250,6 +250,29 @@ int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n
                       const float* q, float sm_scale, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Multi-query decode: each request's last n_query tokens (positions
+ * seq_len - n_query .. seq_len - 1, already appended) are queries, and query
+ * token t attends causally to the tokens at positions [0, seq_len - n_query +
+ * t] (none if that range is empty: out = 0, lse = -inf), over the same mixed
+ * pages and with the same format-specific partial kernels and log-sum-exp
+ * merge as mkv_decode_attn (arXiv 2608.23834, page 1, Abstract: direct
+ * heterogeneous decode).  n_query in [1, 16].  pools, n_layers and batch as
+ * in mkv_decode_attn_layers (the plan is made by this call).
+ *  q, out: device fp32 [n_layers][batch][n_query][num_q_heads][head_dim];
+ *  lse (nullable): [n_layers][batch][n_query][num_q_heads].
+ *  ws_bytes >= mkv_decode_workspace_bytes_multi(layout, batch->batch,
+ *  batch->bt_capacity, n_layers, n_query).  The query rows of a KV head
+ *  (n_query * G) are taken 8 at a time: one split-K work item per chunk, KV
+ *  head and 8 rows, so a page is read ceil(n_query * G / 8) times, not
+ *  n_query times.  n_query == 1 is mkv_decode_attn_layers.  Needs the
+ *  matrix-core kernels for n_query > 1 (MKV_ERR_RANGE otherwise). */
+size_t mkv_decode_workspace_bytes_multi(const mkv_layout* layout, int32_t batch,
+                                        int32_t bt_capacity, int32_t n_layers, int32_t n_query);
+int mkv_decode_attn_multi(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                          const mkv_batch* batch, int32_t n_query, const float* q,
+                          float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* Page-table gather (test support): copy the raw bytes of logical pages
  * [0, n_pages) of request b into out (device, n_pages records of
  * mkv_fp8_page_bytes() bytes; a TQ3 page fills the first mkv_tq3_page_bytes()

@@ -15,7 +15,7 @@ __all__ = [
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
     "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
-    "mkv_lifecycle_release", "mkv_status_string",
+    "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
     "mkv_last_error",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
 ]
@@ -80,6 +80,9 @@ def lib():
         "mkv_debug_gather": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
         "mkv_materialize": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
         "mkv_lifecycle_workspace_bytes": (c_sz, [c_i32]),
+        "mkv_decode_workspace_bytes_multi": (c_sz, [P(Layout), c_i32, c_i32, c_i32, c_i32]),
+        "mkv_decode_attn_multi": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_i32, c_vp, c_f32, c_vp, c_vp,
+                                          c_vp, c_sz, c_vp]),
         "mkv_lifecycle_step": (c_i32, [P(Layout), P(PoolDesc), c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
                                        c_vp, c_i32, c_vp, c_sz, c_vp]),
         "mkv_lifecycle_release": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
@@ -284,6 +287,22 @@ def mkv_materialize(layout, pool, batch, b, page_lo, n_pages, k_out, v_out, stre
     return _check(lib().mkv_materialize(ctypes.byref(_layout(layout)), ctypes.byref(pool), ctypes.byref(batch),
                                         int(b), int(page_lo), int(n_pages), _ptr(k_out, name="k_out"),
                                         _ptr(v_out, name="v_out"), _stream(stream)))
+
+
+def mkv_decode_workspace_bytes_multi(layout, batch, bt_capacity, n_layers, n_query):
+    return lib().mkv_decode_workspace_bytes_multi(ctypes.byref(_layout(layout)), int(batch), int(bt_capacity),
+                                                  int(n_layers), int(n_query))
+
+
+def mkv_decode_attn_multi(layout, pools, batch, q, sm_scale, out, lse, ws, stream=None):
+    """Causal multi-query decode: q, out [L][B][T][Hq][d], lse [L][B][T][Hq] (T = q.shape[2])."""
+    import torch
+    arr = _pool_array(pools)
+    p, n = _ws(ws)
+    return _check(lib().mkv_decode_attn_multi(ctypes.byref(_layout(layout)), arr, len(arr), ctypes.byref(batch),
+                                              int(q.shape[2]), _ptr(q, torch.float32, "q"), float(sm_scale),
+                                              _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), p, n,
+                                              _stream(stream)))
 
 
 def mkv_lifecycle_workspace_bytes(batch):

@@ -80,11 +80,15 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
-WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers) {
+WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers, int n_query) {
   WsSizes s{};
   const int G = hq / hkv;
+  const int R = n_query * G;                         // query rows per KV head
+  const int nblk = (R + kRowBlock - 1) / kRowBlock;
   const int Le = n_layers < kMaxLayers ? n_layers : kMaxLayers;
-  const int per = Le * hkv;
+  const int per = Le * hkv * nblk;
+  s.n_query = n_query;
+  s.nblk = nblk;
   s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
   // chunks per format <= min(pages / kMinChunkPages, max(target, pages / kMaxChunkPages)) + batch
@@ -112,7 +116,7 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.off_list_t = take(sizeof(int32_t) * (size_t)bt_capacity);
   s.off_chunks_f = take(sizeof(int4) * (size_t)s.table_cap);
   s.off_chunks_t = take(sizeof(int4) * (size_t)s.table_cap);
-  const size_t states = (size_t)Le * s.np_cap * hkv * G;
+  const size_t states = (size_t)Le * s.np_cap * hkv * R;
   s.off_part_ml = take(sizeof(float) * 2 * states);
   s.off_part_acc = take(sizeof(float) * d * states);
   s.total = o;
@@ -136,6 +140,8 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
   p.table_cap = s.table_cap;
   p.np_cap = s.np_cap;
   p.chunks_target = s.chunks_target;
+  p.n_query = s.n_query;
+  p.nblk = s.nblk;
   return p;
 }
 
@@ -217,7 +223,7 @@ namespace {
 // mkv_merge (which reads only the workspace).
 int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                    const mkv_batch* batch, void* ws, size_t ws_bytes, Geometry* g, Plan* plan,
-                   LayerTable* lt) {
+                   LayerTable* lt, int n_query = 1) {
   int rc = check_layout(layout, g);
   if (rc) return rc;
   if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
@@ -241,7 +247,7 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
     return fail(MKV_ERR_NULL, "bt_offsets, bt_pages and seq_lens are required");
   if (B > 0 && !ws) return fail(MKV_ERR_NULL, "ws is required");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
-  const WsSizes s = workspace_sizes(g->hq, g->hkv, g->d, B, batch->bt_capacity, n_layers);
+  const WsSizes s = workspace_sizes(g->hq, g->hkv, g->d, B, batch->bt_capacity, n_layers, n_query);
   if (B > 0 && ws_bytes < s.total) return fail(MKV_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, s.total);
   *plan = plan_from_ws(ws, s, B, batch->bt_capacity);
   return MKV_OK;
@@ -410,6 +416,41 @@ int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int3
   hipError_t e = launch_plan(g, pools[0].tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, st);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, B, st);
+}
+
+size_t mkv_decode_workspace_bytes_multi(const mkv_layout* layout, int32_t batch, int32_t bt_capacity,
+                                        int32_t n_layers, int32_t n_query) {
+  Geometry g{};
+  if (check_layout(layout, &g) != MKV_OK || batch < 0 || bt_capacity < 0 || n_layers < 1 || n_query < 1 ||
+      n_query > kMaxQuery)
+    return 0;
+  return workspace_sizes(g.hq, g.hkv, g.d, batch, bt_capacity, n_layers, n_query).total;
+}
+
+int mkv_decode_attn_multi(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                          const mkv_batch* batch, int32_t n_query, const float* q, float sm_scale,
+                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g{};
+  Plan plan{};
+  LayerTable lt{};
+  if (!pools) return fail(MKV_ERR_NULL, "pools is NULL");
+  if (n_query < 1 || n_query > kMaxQuery) return fail(MKV_ERR_RANGE, "n_query %d not in [1, %d]", n_query, kMaxQuery);
+  int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt, n_query);
+  if (rc) return rc;
+  if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
+  if (n_query > 1 && !g_partial_kind) return fail(MKV_ERR_RANGE, "multi-query decode needs the matrix-core kernels");
+  const int B = batch->batch;
+  if (B == 0) return MKV_OK;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = launch_plan(g, pools[0].tier, batch->bt_offsets, batch->bt_pages, batch->seq_lens, plan, st);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  if (n_query == 1) return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, B, st);
+  const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
+  const size_t rows = (size_t)B * n_query * g.hq;
+  e = launch_partial_mfma(2, g, lt, n_layers, q, rows * g.d, qscale, plan, AppendIn{nullptr, nullptr, 0}, st);
+  if (e != hipSuccess) return hip_fail(e, "partial-attention launch");
+  e = launch_merge(g, n_layers, plan, out, lse, rows * g.d, rows, st);
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "merge launch");
 }
 
 int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,

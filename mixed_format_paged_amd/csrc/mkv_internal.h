@@ -39,6 +39,8 @@ enum ReqField {
   R_CF_OFF,      // first FP8 chunk of the request (exclusive prefix; [batch] = total)
   R_CT_OFF,      // first TQ3 chunk of the request
   R_POFF,        // first partial index of the request (per layer)
+  R_PREVFMT,     // format of logical page n - 2: 0 FP8, 1 TQ3, -1 none
+  R_PREVIDX,     // its absolute index in that format's page list (-1: none)
   R_FIELDS
 };
 
@@ -73,7 +75,15 @@ struct Plan {
   int table_cap;        // chunk-table entries per format (independent of the layer count)
   int np_cap;           // partial states per layer in this call's workspace view
   int chunks_target;    // chunks aimed for per format (set by the planning call)
+  // Query rows: n_query tokens per request (the request's last n_query
+  // positions, causal) times G heads per KV head, R = n_query * G rows, taken
+  // in blocks of up to kRowBlock rows; one work item per (chunk, KV head,
+  // block).  Partial states hold R rows per KV head.
+  int n_query;
+  int nblk;
 };
+constexpr int kRowBlock = 8;          // query rows of one work item (MFMA rows 0..7, their remainders 8..15)
+constexpr int kMaxQuery = 16;         // query tokens per request
 
 // Workspace layout.  The plan part (status .. chunk tables) has offsets that do
 // not depend on the layer count, so a plan made for L layers can be consumed
@@ -82,9 +92,10 @@ struct WsSizes {
   size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
   size_t off_part_ml, off_part_acc, total;
   int table_cap, np_cap, chunks_target;
+  int n_query, nblk;
 };
 
-WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers);
+WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers, int n_query = 1);
 Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity);
 
 // Per-launch layer table (passed by value as a kernel argument).

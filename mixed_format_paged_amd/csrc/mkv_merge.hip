@@ -6,7 +6,9 @@
 //   M = max_p m_p,  w_p = 2^(m_p - M),  L = sum_p l_p w_p,
 //   o = sum_p acc_p w_p / L,  lse = (M + log2 L) * ln 2.
 // One launch merges any number of partials per request.  A workgroup takes
-// (layer, request, KV head, slice of 32 channels), 512 threads:
+// (layer, request, KV head, group of up to 8 query rows, slice of 32
+// channels), 512 threads (a KV head has R = T G rows: T query tokens per
+// request times G heads; row r = t G + g goes to out[b][t][h G + g]):
 //   1. each thread requests its share of the partial states (registers) and
 //      the workgroup the (m, l) pairs of the request (LDS), in one go;
 //   2. M per query head, then the weights w_p into LDS (one exp2 per partial
@@ -62,15 +64,18 @@ __device__ inline float wave_sum(float x) {
 
 }  // namespace
 
-// Thread t takes float4 column q = t % kQuads of the slice, query head
-// i = (t / kQuads) % kMaxG (idle when i >= G) and every kSubs-th partial from
+// Thread t takes float4 column q = t % kQuads of the slice, query row
+// i = (t / kQuads) % kMaxG of the row group (idle past its rows) and every kSubs-th partial from
 // sub = t / (kQuads kMaxG): its loads are 16-byte vectors, and the kQuads
 // threads of one (partial, head) read one contiguous 128-byte line.
 template <int D>
-__global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int G, Plan plan,
+__global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int Gh, Plan plan,
                                                          float* __restrict__ out, float* __restrict__ lse,
                                                          size_t out_ls, size_t lse_ls) {
   constexpr int NS = D / kSliceC;
+  const int T = plan.n_query;
+  const int R = T * Gh;                                     // rows per KV head
+  const int NRG = (R + kMaxG - 1) / kMaxG;                  // row groups
   __shared__ float sw[kTileP * kMaxG];          // weights of the current tile, [p][i]
   __shared__ float sml[kTileP * kMaxG * 2];     // (m, l) of the current tile, [p][i][2]
   __shared__ f4v sred[kThreads];                // per-thread sums, [sub][i][q]
@@ -78,30 +83,38 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   const int B = plan.batch;
   const int* poff = req_row(plan, R_POFF);
   const int* inval = req_row(plan, R_INVALID);
-  const int hq = hkv * G;
+  const int hq = hkv * Gh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
-  const bool live = pi < G;
-  const long items = (long)n_layers * B * hkv * NS;
+  const long items = (long)n_layers * B * hkv * NRG * NS;
+  // output element of row r of request b, KV head h
+  auto out_at = [&](int layer, int b, int h, int r) {
+    const int t = r / Gh;
+    return ((size_t)(b * T + t) * hq + (size_t)h * Gh + (r - t * Gh));
+  };
   for (long item = blockIdx.x; item < items; item += gridDim.x) {
     const int cs = (int)(item % NS);
-    const int h = (int)((item / NS) % hkv);
-    const int b = (int)((item / ((long)NS * hkv)) % B);
-    const int layer = (int)(item / ((long)NS * hkv * B));
+    const int rg = (int)((item / NS) % NRG);
+    const int h = (int)((item / ((long)NS * NRG)) % hkv);
+    const int b = (int)((item / ((long)NS * NRG * hkv)) % B);
+    const int layer = (int)(item / ((long)NS * NRG * hkv * B));
+    const int r0 = rg * kMaxG;
+    const int G = R - r0 < kMaxG ? R - r0 : kMaxG;          // rows of this group
+    const bool live = pi < G;
     const int p0 = poff[b], np = poff[b + 1] - poff[b];
-    float* out_row = out + layer * out_ls + ((size_t)b * hq + (size_t)h * G) * D + cs * kSliceC;
-    float* lse_row = lse ? lse + layer * lse_ls + (size_t)b * hq + (size_t)h * G : nullptr;
+    float* out_row = out + layer * out_ls + out_at(layer, b, h, r0 + (live ? pi : 0)) * D + cs * kSliceC;
+    float* lse_l = lse ? lse + layer * lse_ls : nullptr;
     if (inval[b] || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
       const bool nan = inval[b] != 0 || np != 0;
       if (sub == 0 && live)
-        *reinterpret_cast<f4v*>(out_row + (size_t)pi * D + 4 * qc) = nan ? f4v{NAN, NAN, NAN, NAN} : f4v{0.0f, 0.0f, 0.0f, 0.0f};
-      if (cs == 0 && lse_row && tid < G) lse_row[tid] = nan ? __int_as_float(0x7fc00000) : -INFINITY;
+        *reinterpret_cast<f4v*>(out_row + 4 * qc) = nan ? f4v{NAN, NAN, NAN, NAN} : f4v{0.0f, 0.0f, 0.0f, 0.0f};
+      if (cs == 0 && lse_l && tid < G) lse_l[out_at(layer, b, h, r0 + tid)] = nan ? __int_as_float(0x7fc00000) : -INFINITY;
       continue;
     }
-    const size_t sstride = (size_t)hkv * G;                 // states between consecutive partials
-    const float* ml = plan.part_ml + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * 2;
-    const float* acc = plan.part_acc + ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * G * D
-                       + cs * kSliceC + (size_t)(live ? pi : 0) * D + 4 * qc;
+    const size_t sstride = (size_t)hkv * R;                 // states between consecutive partials
+    const size_t st0 = ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * R + r0;
+    const float* ml = plan.part_ml + st0 * 2;
+    const float* acc = plan.part_acc + st0 * D + cs * kSliceC + (size_t)(live ? pi : 0) * D + 4 * qc;
     f4v a = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     for (int t0 = 0; t0 < np; t0 += kTileP) {
       const int nt = np - t0 < kTileP ? np - t0 : kTileP;
@@ -171,17 +184,18 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
       for (int s = 1; s < kSubs; ++s) o += sred[s * kQuads * kMaxG + tid];
       const float L = sL[pi];
       const f4v r = L > 0.0f ? o / L : f4v{0.0f, 0.0f, 0.0f, 0.0f};
-      *reinterpret_cast<f4v*>(out_row + (size_t)pi * D + 4 * qc) = r;
+      *reinterpret_cast<f4v*>(out_row + 4 * qc) = r;
     }
-    if (cs == 0 && lse_row && tid < G)
-      lse_row[tid] = sL[tid] > 0.0f ? (sM[tid] + log2f(sL[tid])) * 0.69314718055994531f : -INFINITY;
+    if (cs == 0 && lse_l && tid < G)
+      lse_l[out_at(layer, b, h, r0 + tid)] = sL[tid] > 0.0f ? (sM[tid] + log2f(sL[tid])) * 0.69314718055994531f : -INFINITY;
     __syncthreads();
   }
 }
 
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse,
                         size_t out_ls, size_t lse_ls, hipStream_t stream) {
-  const long cap = (long)n_layers * plan.batch * g.hkv * (g.d / kSliceC);
+  const int R = plan.n_query * g.G;
+  const long cap = (long)n_layers * plan.batch * g.hkv * ((R + kMaxG - 1) / kMaxG) * (g.d / kSliceC);
   const dim3 grid((unsigned)(cap < 4096 ? (cap > 0 ? cap : 1) : 4096));
   if (g.d == 256)
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);

@@ -46,6 +46,7 @@ constexpr int kThreads = 64 * kWaves;
 // The running max moves only when a page's max exceeds it by more than
 // kRescale (log2 units), so p <= 2^15 stays finite in fp16.
 constexpr float kRescale = 15.0f;
+constexpr int kNoMask = 1 << 20;
 // k-slot -> channel offset inside a TQ3 triple, in the order one triple
 // decodes into fp16 pairs: (0,6) (1,7) (3,2) (4,5)
 constexpr int kTq3SlotChannel[8] = {0, 6, 1, 7, 3, 2, 4, 5};
@@ -223,10 +224,24 @@ struct WaveState {
   // operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder.  On a wave's
   // first page (wave-uniform `first`) O and l are still zero: the max is
   // taken as is and nothing is rescaled.
-  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first) {
+  //
+  // MQ (several query tokens per request, causal): token slot k of the page
+  // lies dist0 - k tokens before the request's last token, and the lane's
+  // query row may see it only if that distance is at least `lim` (dist0 =
+  // kNoMask: the page is wholly visible).  A row may then see nothing of a
+  // page, even a wave's first, so a running max of -inf is taken as 0 in the
+  // exponent.
+  template <bool MQ>
+  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first, int dist0 = 0, int lim = 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
-    if (ntok < kPage) {                         // a request's last page: mask its tail
+    if (MQ) {
+      if (dist0 < kNoMask) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (dist0 - (4 * j + r) < lim) s[r] = -INFINITY;
+      }
+    } else if (ntok < kPage) {                  // a request's last page: mask its tail
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * j + r >= ntok) s[r] = -INFINITY;
@@ -249,14 +264,27 @@ struct WaveState {
         for (int T = 0; T < Geo<D>::NT; ++T) O[T][r] *= ar;
       }
     }
+    const float m_use = (MQ && m_run == -INFINITY) ? 0.0f : m_run;
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(s[r] - m_run);   // v_exp_f32; 0 for masked tokens
+      p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);   // v_exp_f32; 0 for masked tokens
       l_run += p[r];
     }
     return split_rows(p, lo_sel);
   }
+};
+
+// Query rows of a work item.  Single-query decode: the G heads of the KV
+// head (r0 = 0, rows = R = G, T = 1).  Multi-query: row r = t G + g of the
+// request's R = T G rows (query token t, head g), the block holding rows
+// r0 .. r0 + rows - 1; query token t is the request's position
+// seq_len - T + t and sees the tokens at most that far.
+struct RowBlock {
+  int T, r0, rows, R;
+  int tail_e;    // page of the chunk that is the request's last logical page (-1: none)
+  int prev_e;    // page of the chunk that is the request's logical page n - 2 (-1: none)
+  int req_last;  // tokens on the request's last page
 };
 
 // Scores of one TQ3 page-head staged at pg: one 16x16x32 MFMA per 32-channel
@@ -396,11 +424,11 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 // each format's code path gets its own register allocation, and each loop
 // body is straight-line code (no per-unit branch for the allocator to split
 // the accumulators at).
-template <int D, bool tq3>
+template <int D, bool tq3, bool MQ>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
-    uint8_t* smem, uint32_t one024, const AppendIn* ap) {
+    uint8_t* smem, uint32_t one024, const AppendIn* ap, const RowBlock& rb) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
   const int lane = threadIdx.x & 63;
@@ -460,8 +488,14 @@ __device__ __forceinline__ void run_item(
     const int g = e >> 6, ln = e & 63;
     const int nn = ln & 15, jj = ln >> 4;
     const int row = nn < 8 ? nn : nn - 8;
-    const bool use = row < G;
-    const float* qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
+    const bool use = row < rb.rows;
+    const float* qrow;
+    if (MQ) {
+      const int r = rb.r0 + (use ? row : 0), t = r / G;
+      qrow = q + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
+    } else {
+      qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
+    }
     const float sc = qscale * ks_layer;
     const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
     const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
@@ -480,6 +514,15 @@ __device__ __forceinline__ void run_item(
 
   WaveState<D> st;
   st.init();
+  // MQ: the lane's query row may see tokens at least `lim` before the end
+  int lim = 0;
+  if (MQ) {
+    const int row = n & 7;
+    lim = row < rb.rows ? rb.T - 1 - (rb.r0 + row) / G : 0;
+  }
+  auto dist0_of = [&](int e) {
+    return e == rb.tail_e ? last_tok - 1 : (e == rb.prev_e ? rb.req_last + kPage - 1 : kNoMask);
+  };
   if (tq3) {
     // two slots: page k+1 travels while page k is computed
     int id_next = page_id(1);                 // page ids travel one page ahead of their loads
@@ -498,7 +541,7 @@ __device__ __forceinline__ void run_item(
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = tq3_scores<D>(cur, sq, lane, j, one024);
-      const h4 pa = st.softmax(s, ntok, lo_sel, j, k == 0);
+      const h4 pa = st.template softmax<MQ>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim);
       tq3_pv<D>(cur, pa, st.O, lane, j, one024);
     }
   } else {
@@ -511,7 +554,7 @@ __device__ __forceinline__ void run_item(
       const int e = wave + kWaves * k;
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D>(slot0, sq, lane, j);
-      const h4 pa = st.softmax(s, ntok, lo_sel, j, k == 0);
+      const h4 pa = st.template softmax<MQ>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim);
       const bool more = k + 1 < my_pages;     // wave-uniform
       const uint8_t* pn = page_src(id_next);
       id_next = page_id(k + 2);
@@ -536,7 +579,7 @@ __device__ __forceinline__ void run_item(
   float* const sl = sm + kWaves * kMaxG;                 // [kWaves][kMaxG]
   float* const sM = sl + kWaves * kMaxG;                 // [kMaxG]
   const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
-  if (j == 0 && n < G) {
+  if (j == 0 && n < rb.rows) {
     sm[wave * kMaxG + n] = st.m_run;
     sl[wave * kMaxG + n] = l_tot;
   }
@@ -572,10 +615,11 @@ __device__ __forceinline__ void run_item(
   }
   __syncthreads();
 
-  const size_t pslot = ((size_t)layer * plan.np_cap + pidx) * hkv + h;
-  float* __restrict__ ml = plan.part_ml + pslot * G * 2;
-  float* __restrict__ pa_out = plan.part_acc + pslot * G * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  // partial states [layer][partial][KV head][R rows]; this block's rows from r0
+  const size_t pslot = (((size_t)layer * plan.np_cap + pidx) * hkv + h) * rb.R + rb.r0;
+  float* __restrict__ ml = plan.part_ml + pslot * 2;
+  float* __restrict__ pa_out = plan.part_acc + pslot * D;
+  for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
     const int i = idx / D, c = idx - (idx / D) * D;
     const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
     float acc = 0.0f;
@@ -583,7 +627,7 @@ __device__ __forceinline__ void run_item(
     for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
     __builtin_nontemporal_store(acc, pa_out + idx);   // streamed out: read once, by the merge
   }
-  if (threadIdx.x < G) {
+  if (threadIdx.x < rb.rows) {
     const int i = threadIdx.x;
     const float M = sM[i];
     float L = 0.0f;
@@ -603,7 +647,10 @@ __device__ __forceinline__ void run_item(
 #ifndef MKV_OCC
 #define MKV_OCC 4
 #endif
-template <int D, int MODE>
+// MQ: several query tokens per request (plan.n_query), their rows split in
+// plan.nblk blocks, one work item per (chunk, KV head, block); causal masks on
+// the request's last two logical pages.
+template <int D, int MODE, bool MQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
     LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
     float qscale, Plan plan, AppendIn ap) {
@@ -611,8 +658,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M
 
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
-  const long items_f = (long)n_layers * hkv * ncf;
-  const long items_t = (long)n_layers * hkv * nct;
+  const int nblk = MQ ? plan.nblk : 1;
+  const long items_f = (long)n_layers * hkv * ncf * nblk;
+  const long items_t = (long)n_layers * hkv * nct * nblk;
   const long items = items_f + items_t;
   uint32_t one024 = 0x64006400u;             // fp16 1024.0 in both halves, kept in a VGPR
   asm volatile("" : "+v"(one024));
@@ -621,22 +669,37 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M
     const bool tq3 = item >= items_f;
     const long it = tq3 ? item - items_f : item;
     const int nch = tq3 ? nct : ncf;
-    const int h = (int)(it % hkv);
-    const int chunk = (int)((it / hkv) % nch);
-    const int layer = (int)(it / ((long)hkv * nch));
+    const int blk = MQ ? (int)(it % nblk) : 0;
+    const long itc = MQ ? it / nblk : it;
+    const int h = (int)(itc % hkv);
+    const int chunk = (int)((itc / hkv) % nch);
+    const int layer = (int)(itc / ((long)hkv * nch));
     const i4v cd = ((cptr_i4)(tq3 ? plan.chunks_t : plan.chunks_f))[chunk];
     const int b = cd[0], start = cd[1], count = chunk_pages(cd[2]), last_tok = chunk_last_tok(cd[2]), pidx = cd[3];
     const bool holds_tail = (cd[2] & kChunkHoldsTail) != 0;
-    if (pidx >= plan.np_cap) {               // plan made for more layers than this call
+    if (pidx >= plan.np_cap) {               // plan made for fewer layers than this call
       if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
       continue;
     }
+    RowBlock rb{1, 0, G, G, -1, -1, 0};
+    if (MQ) {
+      const cptr_i32 req = (cptr_i32)plan.req;
+      const int rowlen = plan.batch + 1;
+      const int prev_fmt = req[R_PREVFMT * rowlen + b], prev_idx = req[R_PREVIDX * rowlen + b];
+      rb.T = plan.n_query;
+      rb.R = rb.T * G;
+      rb.r0 = blk * kRowBlock;
+      rb.rows = rb.R - rb.r0 < kRowBlock ? rb.R - rb.r0 : kRowBlock;
+      rb.tail_e = holds_tail ? count - 1 : -1;
+      rb.prev_e = (prev_fmt == (tq3 ? 1 : 0) && prev_idx >= start && prev_idx < start + count) ? prev_idx - start : -1;
+      rb.req_last = req[R_TAIL * rowlen + b];
+    }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024,
-                        nullptr);
+      run_item<D, true, MQ>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
+                            one024, nullptr, rb);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem, one024,
-                         holds_tail ? &ap : nullptr);
+      run_item<D, false, MQ>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
+                             one024, (!MQ && holds_tail) ? &ap : nullptr, rb);
     __syncthreads();
   }
 }
@@ -645,29 +708,31 @@ static dim3 attend_grid(long cap) {
   return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));
 }
 
-template <int MODE>
+template <int MODE, bool MQ>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
                             hipStream_t stream) {
-  const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2);
+  const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2) * (MQ ? plan.nblk : 1);
   const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(kThreads);
   if (g.d == 256)
-    hipLaunchKernelGGL((attend_kernel<256, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+    hipLaunchKernelGGL((attend_kernel<256, MODE, MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan, ap);
   else
-    hipLaunchKernelGGL((attend_kernel<128, MODE>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+    hipLaunchKernelGGL((attend_kernel<128, MODE, MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan, ap);
 }
 
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream) {
-  if (which == 0)
-    launch_attend_t<kFp8Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  if (plan.n_query > 1)        // multi-query: both formats in one launch, no in-launch append
+    launch_attend_t<kBoth, true>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  else if (which == 0)
+    launch_attend_t<kFp8Only, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else if (which == 1)
-    launch_attend_t<kTq3Only>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+    launch_attend_t<kTq3Only, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else
-    launch_attend_t<kBoth>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+    launch_attend_t<kBoth, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   return hipGetLastError();
 }
 

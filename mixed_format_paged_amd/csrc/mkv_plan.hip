@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kClassifyThreads) plan_classify(
   constexpr int P = kClassifyPages;                 // consecutive logical pages per thread
   constexpr int SUPER = kClassifyThreads * P;
   __shared__ int sh[128];
-  __shared__ int s_last;
+  __shared__ int s_last, s_prev_fmt, s_prev_idx;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int off0 = bt_offsets[b], off1 = bt_offsets[b + 1];
@@ -93,10 +93,12 @@ __global__ void __launch_bounds__(kClassifyThreads) plan_classify(
       req_row(plan, R_TAIL)[b] = 0;
       req_row(plan, R_LASTFMT)[b] = -1;
       req_row(plan, R_INVALID)[b] = kDevBadSeqLen;
+      req_row(plan, R_PREVFMT)[b] = -1;
+      req_row(plan, R_PREVIDX)[b] = -1;
     }
     return;
   }
-  if (tid == 0) s_last = -1;
+  if (tid == 0) { s_last = -1; s_prev_fmt = -1; s_prev_idx = -1; }
   int nf = 0;      // FP8 pages before the current super-block (block-uniform)
   int err = 0;     // per-thread error bits
   for (int base = 0; base < n; base += SUPER) {
@@ -130,10 +132,12 @@ __global__ void __launch_bounds__(kClassifyThreads) plan_classify(
       const int lp = lp0 + k;
       if (lp >= n) continue;
       const bool f = (isf >> k) & 1;
-      if (f) plan.list_f[off0 + nf + fpos + fb] = id[k];
-      else plan.list_t[off0 + (lp - nf - fpos - fb)] = id[k] - n_fp8;
+      const int at = f ? off0 + nf + fpos + fb : off0 + (lp - nf - fpos - fb);
+      if (f) plan.list_f[at] = id[k];
+      else plan.list_t[at] = id[k] - n_fp8;
       fb += f;
       if (lp == n - 1) s_last = f ? 0 : 1;
+      if (lp == n - 2) { s_prev_fmt = f ? 0 : 1; s_prev_idx = at; }
     }
     nf += tot;
   }
@@ -144,6 +148,8 @@ __global__ void __launch_bounds__(kClassifyThreads) plan_classify(
     req_row(plan, R_TAIL)[b] = n ? sl - 16 * (n - 1) : 0;
     req_row(plan, R_LASTFMT)[b] = e ? -1 : s_last;
     req_row(plan, R_INVALID)[b] = e;
+    req_row(plan, R_PREVFMT)[b] = e ? -1 : s_prev_fmt;
+    req_row(plan, R_PREVIDX)[b] = e ? -1 : s_prev_idx;
   }
 }
 

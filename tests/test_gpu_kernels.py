@@ -380,3 +380,47 @@ def test_lifecycle_steps_match_the_oracle():
     M.mkv_lifecycle_step(layout, pd, offs_d, bt_d, sl_d, tier_d, ff_d, tf_d, tops_d, R, ws)
     assert M.mkv_workspace_status(ws) == LC.NO_FREE_PAGE
     same("after the failing step")
+
+
+@pytest.mark.parametrize("T,d,recent", [(2, 256, 64), (5, 256, 16), (16, 128, 16), (3, 128, 64)])
+def test_multi_query_decode_parity(T, d, recent):
+    """mkv_decode_attn_multi: each request's last T tokens as causal queries,
+    against the oracle; ragged lengths including a request shorter than T and
+    an empty one; recent = 16 tokens puts logical page n - 2 in TQ3, so the
+    causal mask runs on a TQ3 page too."""
+    M.set_partial_kind(1)
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=5, L=2, d=d,
+                 lengths=("list", (1500, 3, 0, 700, 33)), recent_tokens=recent)
+    st, dw, ref = _both(w)
+    layout = (w.Hq, w.Hkv, w.d)
+    L, B = 2, w.B
+    g = torch.Generator()
+    g.manual_seed(100 + T)
+    q = torch.randn((L, B, T, w.Hq, w.d), generator=g)
+    qd = q.to("cuda").contiguous()
+    wsb = M.mkv_decode_workspace_bytes_multi(layout, B, dw.bt.numel(), L, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((L, B, T, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((L, B, T, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn_multi(layout, dw.cache.pools, dw.batch(), qd, 1 / math.sqrt(w.d), out, lse, ws)
+    assert M.mkv_workspace_status(ws) == 0
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for li, (pool, bt, _, _) in enumerate(ref):
+        o_ref, l_ref = OA.decode_batch_multi(pool, q[li].numpy(), st.bt_offsets, bt, st.seq_lens)
+        compare(o[li].reshape(-1, w.d), o_ref.reshape(-1, w.d), l[li].reshape(-1), l_ref.reshape(-1),
+                f"T={T} d={d} layer {li}")
+    # a single query token through the same call is the single-query decode, bit for bit
+    if T == 2:
+        out1 = torch.full((L, B, 1, w.Hq, w.d), float("nan"), device="cuda")
+        lse1 = torch.full((L, B, 1, w.Hq), float("nan"), device="cuda")
+        M.mkv_decode_attn_multi(layout, dw.cache.pools, dw.batch(), qd[:, :, -1:].contiguous(), 1 / math.sqrt(w.d),
+                                out1, lse1, ws)
+        wsb1 = M.mkv_decode_workspace_bytes(layout, B, dw.bt.numel(), L)
+        ws1 = torch.empty(wsb1, dtype=torch.uint8, device="cuda")
+        out2 = torch.full((L, B, w.Hq, w.d), float("nan"), device="cuda")
+        lse2 = torch.full((L, B, w.Hq), float("nan"), device="cuda")
+        M.mkv_decode_attn_layers(layout, dw.cache.pools, dw.batch(), qd[:, :, -1].contiguous(), 1 / math.sqrt(w.d),
+                                 out2, lse2, ws1)
+        torch.cuda.synchronize()
+        assert np.array_equal(out1[:, :, 0].cpu().numpy(), out2.cpu().numpy())
+        assert np.array_equal(lse1[:, :, 0].cpu().numpy(), lse2.cpu().numpy())
