@@ -523,6 +523,7 @@ int check_lifecycle(const mkv_layout* layout, const mkv_pool* pools, int32_t n_l
     }
   }
   if (batch < 0 || bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", batch, bt_capacity);
+  if (batch == 0) return MKV_OK;                      // no request: nothing to do
   if (!bt_offsets || !bt_pages || !seq_lens || !tier || !fp8_free || !tq3_free || !free_tops || !ws)
     return fail(MKV_ERR_NULL, "tables, tier map, free stacks, free_tops and ws are required");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MKV_ERR_ALIGN, "ws must be 256-byte aligned");
@@ -540,7 +541,7 @@ int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t 
   LayerTable lt{};
   int rc = check_lifecycle(layout, pools, n_layers, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier,
                            fp8_free, tq3_free, free_tops, ws, ws_bytes, mkv_lifecycle_workspace_bytes(batch), &g, &lt);
-  if (rc) return rc;
+  if (rc || batch == 0) return rc;
   if (recent_pages < 1) return fail(MKV_ERR_RANGE, "recent_pages %d must be >= 1", recent_pages);
   if ((int64_t)n_layers * batch * g.hkv > 0x7fffffff) return fail(MKV_ERR_RANGE, "batch too large");
   hipError_t e = launch_lifecycle_step(g, lt, n_layers, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier,
@@ -556,7 +557,7 @@ int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool, const 
   Geometry g{};
   int rc = check_lifecycle(layout, pool, 1, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free,
                            tq3_free, free_tops, ws, ws_bytes, mkv_lifecycle_workspace_bytes(0), &g, nullptr);
-  if (rc) return rc;
+  if (rc || batch == 0) return rc;
   if (n_req < 0) return fail(MKV_ERR_RANGE, "n_req %d", n_req);
   if (n_req > 0 && !requests) return fail(MKV_ERR_NULL, "requests is required");
   hipError_t e = launch_lifecycle_release(g, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free,

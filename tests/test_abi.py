@@ -65,6 +65,19 @@ def test_host_validation_codes():
     assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 0, 0, 1, 8, 16, None) == -3   # misaligned
     assert L.mkv_materialize(lay, ctypes.byref(pool), None, 0, 0, 1, 16, 16, None) == -1
     assert L.mkv_materialize(lay, ctypes.byref(pool), ctypes.byref(batch), 0, 0, 0, None, None, None) == 0
+    # lifecycle: an empty batch is a no-op; a bad window or count is a range error
+    pool_t = M.PoolDesc(1 << 20, 1 << 21, 1 << 22, 10, 10, 1.0, 1.0)
+    assert L.mkv_lifecycle_step(lay, ctypes.byref(pool_t), 1, None, None, None, 0, 0, 1 << 22, None, None, None, 4,
+                                None, 0, None) == 0
+    args = (lay, ctypes.byref(pool_t), 1, 1 << 23, 1 << 24, 1 << 25, 2, 100, 1 << 22, 1 << 26, 1 << 27, 1 << 28)
+    assert L.mkv_lifecycle_step(*args, 0, 1 << 29, 4096, None) == -5                  # recent_pages < 1
+    assert L.mkv_lifecycle_step(*args, 4, 1 << 29, 16, None) == -4                    # workspace too small
+    assert L.mkv_lifecycle_step(*args, 4, 1 << 29 | 16, 4096, None) == -3             # misaligned workspace
+    assert L.mkv_lifecycle_step(lay, ctypes.byref(pool_t), 1, 1 << 23, 1 << 24, 1 << 25, 2, 100, 1 << 21, 1 << 26,
+                                1 << 27, 1 << 28, 4, 1 << 29, 4096, None) == -5       # tier is not the pools' map
+    # multi-query decode: n_query outside [1, 16]
+    assert L.mkv_decode_attn_multi(lay, ctypes.byref(pool), 1, ctypes.byref(batch), 17, 4096, 0.0625, 8192, None,
+                                   256, 1 << 30, None) == -5
     # zero-size work is a successful no-op that launches nothing
     assert L.mkv_demote_pages(lay, ctypes.byref(pool), None, None, 0, None) == 0
     empty = M.BatchDesc(None, None, None, 0, 0)
