@@ -84,11 +84,13 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   WsSizes s{};
   const int G = hq / hkv;
   const int R = n_query * G;                         // query rows per KV head
-  const int nblk = (R + kRowBlock - 1) / kRowBlock;
+  const int rowblk = (n_query > 1 && R > kRowBlock) ? 2 * kRowBlock : kRowBlock;
+  const int nblk = (R + rowblk - 1) / rowblk;
   const int Le = n_layers < kMaxLayers ? n_layers : kMaxLayers;
   const int per = Le * hkv * nblk;
   s.n_query = n_query;
   s.nblk = nblk;
+  s.rowblk = rowblk;
   s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
   // chunks per format <= min(pages / kMinChunkPages, max(target, pages / kMaxChunkPages)) + batch
@@ -142,6 +144,7 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
   p.chunks_target = s.chunks_target;
   p.n_query = s.n_query;
   p.nblk = s.nblk;
+  p.rowblk = s.rowblk;
   return p;
 }
 

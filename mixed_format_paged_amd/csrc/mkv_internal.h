@@ -81,6 +81,7 @@ struct Plan {
   // block).  Partial states hold R rows per KV head.
   int n_query;
   int nblk;
+  int rowblk;           // rows per block: 8, or 16 for multi-query with more than 8 rows
 };
 constexpr int kRowBlock = 8;          // query rows of one work item (MFMA rows 0..7, their remainders 8..15)
 constexpr int kMaxQuery = 16;         // query tokens per request
@@ -92,7 +93,7 @@ struct WsSizes {
   size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
   size_t off_part_ml, off_part_acc, total;
   int table_cap, np_cap, chunks_target;
-  int n_query, nblk;
+  int n_query, nblk, rowblk;
 };
 
 WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers, int n_query = 1);

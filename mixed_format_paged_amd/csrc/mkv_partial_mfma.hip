@@ -186,6 +186,11 @@ struct MergeLayout {
 template <int D>
 constexpr int kSmemBytes = Geo<D>::kLds > MergeLayout<D>::kBytes ? Geo<D>::kLds : MergeLayout<D>::kBytes;
 
+// 16-row blocks keep fp16(q) and its remainder as two fragment sets (2 kSq).
+template <int D>
+constexpr int kSmemBytes16 = Geo<D>::kLds + Geo<D>::kSq > MergeLayout<D>::kBytes + 256 ? Geo<D>::kLds + Geo<D>::kSq
+                                                                                      : MergeLayout<D>::kBytes + 256;
+
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
@@ -231,10 +236,17 @@ struct WaveState {
   // kNoMask: the page is wholly visible).  A row may then see nothing of a
   // page, even a wave's first, so a running max of -inf is taken as 0 in the
   // exponent.
-  template <bool MQ>
-  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first, int dist0 = 0, int lim = 0) {
+  //
+  // RB = 16 (16 real query rows, q's remainder already summed by a second
+  // MFMA): no row pairing, and P comes back as fp16(p) with its remainder in
+  // *p_lo, for two P V MFMAs.
+  template <bool MQ, int RB = 8>
+  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first, int dist0 = 0, int lim = 0,
+                               h4* p_lo = nullptr) {
+    if (RB == 8) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
+      for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
+    }
     if (MQ) {
       if (dist0 < kNoMask) {
 #pragma unroll
@@ -271,6 +283,10 @@ struct WaveState {
       p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);   // v_exp_f32; 0 for masked tokens
       l_run += p[r];
     }
+    if (RB == 16) {
+      *p_lo = split_rows(p, -1.0f);
+      return split_rows(p, 0.0f);
+    }
     return split_rows(p, lo_sel);
   }
 };
@@ -289,7 +305,7 @@ struct RowBlock {
 
 // Scores of one TQ3 page-head staged at pg: one 16x16x32 MFMA per 32-channel
 // scale group, its result scaled by the group's fp16 scale of each token.
-template <int D>
+template <int D, int RB = 8>
 __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j, uint32_t one024) {
   constexpr int NG = Geo<D>::NG, GB = 3 * NG;       // bytes of a lane's code chunk
   uint32_t kc[GB / 4];
@@ -307,14 +323,17 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
   f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
   h8 a = k_operand(0);
   h8 bq = sq[lane];
+  h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;          // 16 rows: q's remainder, a second MFMA
   u2 sk = k_scales(0);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    if (RB == 16) sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sg, 0, 0, 0);
     u2 sk_next = sk;
     if (g + 1 < NG) {                      // group g + 1 decodes and loads while the MFMA runs
       a = k_operand(g + 1);
       bq = sq[(g + 1) * 64 + lane];
+      if (RB == 16) bl = sq[NG * 64 + (g + 1) * 64 + lane];
       sk_next = k_scales(g + 1);
     }
     const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
@@ -327,7 +346,10 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
     // operands are live, before group g + 1's MFMA (instruction selection
     // would otherwise sink every scaling below all eight MFMAs and keep all
     // their results live)
-    asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(sk) :: "memory");
+    if (RB == 16)
+      asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(bl), "+v"(sk) :: "memory");
+    else
+      asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(sk) :: "memory");
   }
   return s;
 }
@@ -335,10 +357,12 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 // P V of one TQ3 page-head: V = (u - 4) s as an exact fp16 pair hi + lo; one
 // 16x16x32 MFMA per 16-channel tile takes both, its k index running over
 // (token 4j + (e & 3), part e >> 2) with P repeated for the two parts.
-template <int D>
-__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j, uint32_t one024) {
+template <int D, int RB = 8>
+__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j, uint32_t one024,
+                              h4 pl = h4{}) {
   constexpr int NG = Geo<D>::NG, GB = 3 * NG;
   const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
+  const h8 pl2 = __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3);   // RB 16: P's remainder
   uint32_t vc[GB / 4];
   const uint8_t* vp = pg + 6 * D + lane * GB;
 #pragma unroll
@@ -357,17 +381,21 @@ __device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int
     const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
     const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
     const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
-    O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-        pa2, __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)}), O[2 * pp], 0, 0, 0);
-    O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-        pa2, __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)}), O[2 * pp + 1], 0, 0, 0);
+    const h8 b0 = __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)});
+    const h8 b1 = __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)});
+    O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b0, O[2 * pp], 0, 0, 0);
+    O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b1, O[2 * pp + 1], 0, 0, 0);
+    if (RB == 16) {
+      O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b0, O[2 * pp], 0, 0, 0);
+      O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b1, O[2 * pp + 1], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // Scores of one FP8 K half staged at pg (16 tokens x d channels, E4M3):
 // codes convert exactly to fp16; lane (n, j) takes channels j d/4 + 8 g + e.
-template <int D>
+template <int D, int RB = 8>
 __device__ inline f4 fp8_scores(const uint8_t* pg, const h8* sq, int lane, int j) {
   const uint8_t* kp = pg + (lane & 15) * D + j * (D / 4);
   f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -380,6 +408,7 @@ __device__ inline f4 fp8_scores(const uint8_t* pg, const h8* sq, int lane, int j
     const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
     const h8 a = __builtin_bit_cast(h8, u4{h2u(p0), h2u(p1), h2u(p2), h2u(p3)});
     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[g * 64 + lane], s, 0, 0, 0);
+    if (RB == 16) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sq[Geo<D>::NG * 64 + g * 64 + lane], s, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s;
@@ -388,8 +417,8 @@ __device__ inline f4 fp8_scores(const uint8_t* pg, const h8* sq, int lane, int j
 // P V of one FP8 V half staged at pg: B = 16 tokens x 16 channels per tile
 // (FP8 values are exact in fp16); lane (n, j) holds tokens 4j..4j+3 of
 // channels n d/16 + T.
-template <int D>
-__device__ inline void fp8_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j) {
+template <int D, int RB = 8>
+__device__ inline void fp8_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j, h4 pl = h4{}) {
   constexpr int VW = D / 64;                 // dwords of one token row of the lane's channels
   const uint8_t* vp = pg + (4 * j) * D + (lane & 15) * (D / 16);
 #pragma unroll
@@ -408,8 +437,14 @@ __device__ inline void fp8_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int
       const h2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true);    // channel T+1
       const h2 a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false);
       const h2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true);
-      O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(a01), h2u(a23)}), O[T], 0, 0, 0);
-      O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(h4, u2{h2u(b01), h2u(b23)}), O[T + 1], 0, 0, 0);
+      const h4 va = __builtin_bit_cast(h4, u2{h2u(a01), h2u(a23)});
+      const h4 vb = __builtin_bit_cast(h4, u2{h2u(b01), h2u(b23)});
+      O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, va, O[T], 0, 0, 0);
+      O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, O[T + 1], 0, 0, 0);
+      if (RB == 16) {
+        O[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, va, O[T], 0, 0, 0);
+        O[T + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, O[T + 1], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -424,7 +459,7 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 // each format's code path gets its own register allocation, and each loop
 // body is straight-line code (no per-unit branch for the allocator to split
 // the accumulators at).
-template <int D, bool tq3, bool MQ>
+template <int D, bool tq3, bool MQ, int RB = 8>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
@@ -483,11 +518,13 @@ __device__ __forceinline__ void run_item(
   }
 
   // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
-  //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder ----
+  //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder; with
+  //      16-row blocks all 16 columns are rows, fp16(q) in the first fragment
+  //      set and the remainder in the second ----
   for (int e = threadIdx.x; e < NG * 64; e += kThreads) {
     const int g = e >> 6, ln = e & 63;
     const int nn = ln & 15, jj = ln >> 4;
-    const int row = nn < 8 ? nn : nn - 8;
+    const int row = RB == 16 ? nn : (nn < 8 ? nn : nn - 8);
     const bool use = row < rb.rows;
     const float* qrow;
     if (MQ) {
@@ -507,8 +544,13 @@ __device__ __forceinline__ void run_item(
       x0[k] = (use ? (tq3 ? v[kTq3SlotChannel[k]] : v[k]) : 0.0f) * sc;
       x1[k] = (use ? (tq3 ? v[kTq3SlotChannel[k + 4]] : v[k + 4]) : 0.0f) * sc;
     }
-    const float sel = nn < 8 ? 0.0f : -1.0f;
-    sq[e] = __builtin_shufflevector(split_rows(x0, sel), split_rows(x1, sel), 0, 1, 2, 3, 4, 5, 6, 7);
+    if (RB == 16) {
+      sq[e] = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
+      sq[NG * 64 + e] = __builtin_shufflevector(split_rows(x0, -1.0f), split_rows(x1, -1.0f), 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      const float sel = nn < 8 ? 0.0f : -1.0f;
+      sq[e] = __builtin_shufflevector(split_rows(x0, sel), split_rows(x1, sel), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   }
   __syncthreads();
 
@@ -517,7 +559,7 @@ __device__ __forceinline__ void run_item(
   // MQ: the lane's query row may see tokens at least `lim` before the end
   int lim = 0;
   if (MQ) {
-    const int row = n & 7;
+    const int row = RB == 16 ? n : (n & 7);
     lim = row < rb.rows ? rb.T - 1 - (rb.r0 + row) / G : 0;
   }
   auto dist0_of = [&](int e) {
@@ -540,9 +582,10 @@ __device__ __forceinline__ void run_item(
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
-      const f4 s = tq3_scores<D>(cur, sq, lane, j, one024);
-      const h4 pa = st.template softmax<MQ>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim);
-      tq3_pv<D>(cur, pa, st.O, lane, j, one024);
+      const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, one024);
+      h4 pl;
+      const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
+      tq3_pv<D, RB>(cur, pa, st.O, lane, j, one024, pl);
     }
   } else {
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
@@ -553,8 +596,9 @@ __device__ __forceinline__ void run_item(
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;
       const int ntok = (e == count - 1) ? last_tok : kPage;
-      const f4 s = fp8_scores<D>(slot0, sq, lane, j);
-      const h4 pa = st.template softmax<MQ>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim);
+      const f4 s = fp8_scores<D, RB>(slot0, sq, lane, j);
+      h4 pl;
+      const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
       const bool more = k + 1 < my_pages;     // wave-uniform
       const uint8_t* pn = page_src(id_next);
       id_next = page_id(k + 2);
@@ -565,7 +609,7 @@ __device__ __forceinline__ void run_item(
         wait_vmem<0>();
       }
       __builtin_amdgcn_sched_barrier(0);
-      fp8_pv<D>(slot1, pa, st.O, lane, j);
+      fp8_pv<D, RB>(slot1, pa, st.O, lane, j, pl);
       if (more) stage_issue<D>(pn + kPage * D, slot1, lane, kPage * D);
     }
   }
@@ -574,33 +618,64 @@ __device__ __forceinline__ void run_item(
 
   // ---- merge of the wave states: each wave rescales its rows to the common
   //      maximum, then the workgroup sums the states in a fixed order
+  constexpr int NR = RB == 16 ? 16 : kMaxG;              // rows of the wave states
   float* const so = reinterpret_cast<float*>(smem);
-  float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][kMaxG] maxima, then [kMaxG] their max
-  float* const sl = sm + kWaves * kMaxG;                 // [kWaves][kMaxG]
-  float* const sM = sl + kWaves * kMaxG;                 // [kMaxG]
+  float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][NR] maxima
+  float* const sl = sm + kWaves * NR;                    // [kWaves][NR]
+  float* const sM = sl + kWaves * NR;                    // [NR] their max
   const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
   if (j == 0 && n < rb.rows) {
-    sm[wave * kMaxG + n] = st.m_run;
-    sl[wave * kMaxG + n] = l_tot;
+    sm[wave * NR + n] = st.m_run;
+    sl[wave * NR + n] = l_tot;
   }
   __syncthreads();
-  if (threadIdx.x < kMaxG) {
+  if (threadIdx.x < NR) {
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * kMaxG + threadIdx.x]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * NR + threadIdx.x]);
     sM[threadIdx.x] = M;
   }
   __syncthreads();
+  const size_t pslot = (((size_t)layer * plan.np_cap + pidx) * hkv + h) * rb.R + rb.r0;
+  float* __restrict__ ml = plan.part_ml + pslot * 2;
+  float* __restrict__ pa_out = plan.part_acc + pslot * D;
+  const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
+  if constexpr (RB == 16) {
+    // 16 real rows, lane (n, j) holding rows 4j .. 4j + 3: rows 0..7 (j < 2),
+    // then rows 8..15 (j >= 2), through the 8-row LDS layout
+    for (int pass = 0; pass < 2 && 8 * pass < rb.rows; ++pass) {
+      if ((j >> 1) == pass) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * j + r;
+          const float mw = sm[wave * NR + row];
+          const float wr = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
+#pragma unroll
+          for (int T = 0; T < GD::NT; ++T) so[MergeLayout<D>::at(wave, 4 * (j & 1) + r, n, T)] = st.O[T][r] * wr;
+        }
+      }
+      __syncthreads();
+      const int rows_p = rb.rows - 8 * pass < 8 ? rb.rows - 8 * pass : 8;
+      for (int idx = threadIdx.x; idx < rows_p * D; idx += kThreads) {
+        const int i = idx / D, c = idx - (idx / D) * D;
+        const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
+        __builtin_nontemporal_store(acc, pa_out + (size_t)8 * pass * D + idx);
+      }
+      __syncthreads();                                  // the layout is rewritten by the next pass
+    }
+  } else {
   // O rows 4jj + r: after the swap below, lanes 0..31 (j < 2) hold the rows of
   // tile T, lanes 32..63 those of tile T + NT/2.  All kMaxG rows are stored
   // (rows >= G hold values nobody reads), so the stores need no lane mask and
   // take their row and tile from the instruction offset.
   const int jj = j & 1, thalf = j >> 1;
-  const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
   float wr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * jj + r;
-    const float mw = sm[wave * kMaxG + row];
+    const float mw = sm[wave * NR + row];
     wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
   }
 #pragma unroll
@@ -616,9 +691,6 @@ __device__ __forceinline__ void run_item(
   __syncthreads();
 
   // partial states [layer][partial][KV head][R rows]; this block's rows from r0
-  const size_t pslot = (((size_t)layer * plan.np_cap + pidx) * hkv + h) * rb.R + rb.r0;
-  float* __restrict__ ml = plan.part_ml + pslot * 2;
-  float* __restrict__ pa_out = plan.part_acc + pslot * D;
   for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
     const int i = idx / D, c = idx - (idx / D) * D;
     const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
@@ -627,13 +699,14 @@ __device__ __forceinline__ void run_item(
     for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
     __builtin_nontemporal_store(acc, pa_out + idx);   // streamed out: read once, by the merge
   }
+  }
   if (threadIdx.x < rb.rows) {
     const int i = threadIdx.x;
     const float M = sM[i];
     float L = 0.0f;
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm[w * kMaxG + i];
-      L += (mw == -INFINITY) ? 0.0f : sl[w * kMaxG + i] * __builtin_amdgcn_exp2f(mw - M);
+      const float mw = sm[w * NR + i];
+      L += (mw == -INFINITY) ? 0.0f : sl[w * NR + i] * __builtin_amdgcn_exp2f(mw - M);
     }
     ml[2 * i] = M;
     ml[2 * i + 1] = L;
@@ -650,11 +723,15 @@ __device__ __forceinline__ void run_item(
 // MQ: several query tokens per request (plan.n_query), their rows split in
 // plan.nblk blocks, one work item per (chunk, KV head, block); causal masks on
 // the request's last two logical pages.
-template <int D, int MODE, bool MQ>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MKV_OCC, MKV_OCC))) attend_kernel(
-    LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
-    float qscale, Plan plan, AppendIn ap) {
-  __shared__ __align__(16) uint8_t smem[kSmemBytes<D>];
+// RB: query rows per item, 8 (MFMA rows 0..7, remainders in 8..15) or, for
+// multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS, three
+// workgroups per CU).
+template <int D, int MODE, bool MQ, int RB>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(RB == 16 ? 3 : MKV_OCC, RB == 16 ? 3 : MKV_OCC))) attend_kernel(
+        LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
+        float qscale, Plan plan, AppendIn ap) {
+  __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
 
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
@@ -688,18 +765,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M
       const int prev_fmt = req[R_PREVFMT * rowlen + b], prev_idx = req[R_PREVIDX * rowlen + b];
       rb.T = plan.n_query;
       rb.R = rb.T * G;
-      rb.r0 = blk * kRowBlock;
-      rb.rows = rb.R - rb.r0 < kRowBlock ? rb.R - rb.r0 : kRowBlock;
+      rb.r0 = blk * RB;
+      rb.rows = rb.R - rb.r0 < RB ? rb.R - rb.r0 : RB;
       rb.tail_e = holds_tail ? count - 1 : -1;
       rb.prev_e = (prev_fmt == (tq3 ? 1 : 0) && prev_idx >= start && prev_idx < start + count) ? prev_idx - start : -1;
       rb.req_last = req[R_TAIL * rowlen + b];
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true, MQ>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
-                            one024, nullptr, rb);
+      run_item<D, true, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
+                                one024, nullptr, rb);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false, MQ>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
-                             one024, (!MQ && holds_tail) ? &ap : nullptr, rb);
+      run_item<D, false, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+                                 smem, one024, (!MQ && holds_tail) ? &ap : nullptr, rb);
     __syncthreads();
   }
 }
@@ -708,31 +785,33 @@ static dim3 attend_grid(long cap) {
   return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));
 }
 
-template <int MODE, bool MQ>
+template <int MODE, bool MQ, int RB>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
                             hipStream_t stream) {
   const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2) * (MQ ? plan.nblk : 1);
   const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(kThreads);
   if (g.d == 256)
-    hipLaunchKernelGGL((attend_kernel<256, MODE, MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+    hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan, ap);
   else
-    hipLaunchKernelGGL((attend_kernel<128, MODE, MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+    hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan, ap);
 }
 
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream) {
-  if (plan.n_query > 1)        // multi-query: both formats in one launch, no in-launch append
-    launch_attend_t<kBoth, true>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  if (plan.n_query > 1 && plan.rowblk == 16)   // multi-query: both formats in one launch, no in-launch append
+    launch_attend_t<kBoth, true, 16>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  else if (plan.n_query > 1)
+    launch_attend_t<kBoth, true, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else if (which == 0)
-    launch_attend_t<kFp8Only, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+    launch_attend_t<kFp8Only, false, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else if (which == 1)
-    launch_attend_t<kTq3Only, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+    launch_attend_t<kTq3Only, false, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else
-    launch_attend_t<kBoth, false>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+    launch_attend_t<kBoth, false, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   return hipGetLastError();
 }
 
