@@ -96,13 +96,19 @@ __global__ void __launch_bounds__(256) demote_kernel(
       u[c] = (__float_as_uint(x[c]) >> 31) ? 4u - m : 4u + m;
     }
     if (kv == 0) {
-      // K: channels 8j .. 8j + 7 of the group are triple (j, g) of row t, slot k = channel
+      // K: channel 8j + e of the group sits in row t, quarter j, triple
+      // 4 (g / 4) + 2 (gg % 2) + e / 4 at slot 2 (e % 4) + gg / 2 (gg = g % 4);
+      // groups gg and gg ^ 2 share those triples (even and odd slots), so OR them in
+      const int gg = g & 3, sh = 3 * (gg >> 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) w |= u[8 * j + k] << (3 * k);
-        tw[t * (D / 8) + j * G + g] = w;
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) w |= u[8 * j + 4 * hh + e4] << (6 * e4 + sh);
+          atomicOr(&tw[t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (gg & 1) + hh], w);
+        }
       }
     } else {
       // V: channels (a, a + 1) of token t sit in triple (t / 4, n, p) at slots

@@ -11,17 +11,25 @@
 //       s = fp16_RNE(fl32(absmax / 3)), codes u = q + 4 with q the nearest
 //       integer to x / s (ties to even) clamped to [-3, 3]; 8 codes per
 //       3 bytes, slot k at bits [3k, 3k+3) of the little-endian 24-bit word.
-//  TQ3 head block (14 * d bytes, G = d / 32):
-//       [0, 6d)    K codes: token row t at t * 3d/8; triple (j, g) at byte
-//                  3 * (j * G + g) holds channels 32 g + 8 j + slot.
+//  TQ3 head block (14 * d bytes, G = d / 32, a multiple of 4):
+//       [0, 6d)    K codes: token row t at t * 3d/8; in it, quarter j
+//                  (channels 8j .. 8j + 7 of every group) at 3 j G, in blocks
+//                  of 4 triples (12 bytes), block b for groups 4b .. 4b + 3.
+//                  Read as 16 six-bit fields, field f of a block holds
+//                  channel 8j + f % 8 of group 4b + f / 8 in its low 3 bits
+//                  and of group 4b + 2 + f / 8 in its high 3 bits: channel
+//                  32 g + 8 j + e, gg = g % 4, is triple 4 (g / 4) + 2 (gg % 2)
+//                  + e / 4 of the quarter, slot 2 (e % 4) + gg / 2.
 //       [6d, 12d)  V codes: triple at 3 * ((j * 16 + n) * G + p) holds tokens
-//                  4j..4j+3 of channels a = n * d/16 + 2p and a + 1 in slot order
-//                  (a,0) (a,2) (b,1) (b,0) (b,2) (b,3) (a,1) (a,3) for slots 0..7.
+//                  4j..4j+3 of channels a = n * d/16 + 2p and b = a + 1, slot
+//                  2r = (a, 4j + r), slot 2r + 1 = (b, 4j + r).
 //       [12d, 13d) K scales, [13d, 14d) V scales: fp16 of (t = 4j + r, g) at
 //                  element (j * G + g) * 4 + r.
-//  Why: one GPU lane's triples are adjacent (one aligned vector load) and a
-//  triple's slot order lets two codes become two fp16 halves with a single
-//  mask-and-or (see mkv_partial_mfma.hip).
+//  Why: one GPU lane's triples are adjacent (one aligned vector load), and a
+//  block of 4 triples read as 6-bit fields decodes in two FP6 conversions
+//  (low codes, then high codes) into operands the matrix cores take as they
+//  are: 8 channels of one K group per 4 registers, and V codes of one channel
+//  for 2 consecutive tokens per register (see mkv_partial_mfma.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -95,17 +103,13 @@ __device__ inline float half_bits_to_float(uint16_t b) { return __half2float(__u
 // Byte offset of the triple holding K (t, c) inside a head block, and its slot.
 __host__ __device__ inline int tq3_k_triple(int d, int t, int c, int* slot) {
   int G = d >> 5;
-  int g = c >> 5, j = (c >> 3) & 3;
-  *slot = c & 7;
-  return t * (3 * d / 8) + 3 * (j * G + g);
+  int g = c >> 5, j = (c >> 3) & 3, e = c & 7, gg = g & 3;
+  *slot = 2 * (e & 3) + (gg >> 1);
+  return t * (3 * d / 8) + 3 * (j * G + 4 * (g >> 2) + 2 * (gg & 1) + (e >> 2));
 }
 
 // V slot of (channel-in-pair ci, token-in-quarter r).
-__host__ __device__ inline int tq3_v_slot(int ci, int r) {
-  // (a,0)->0 (a,1)->6 (a,2)->1 (a,3)->7 (b,0)->3 (b,1)->2 (b,2)->4 (b,3)->5
-  const int tab = ci ? 0x5423 : 0x7160;                 // nibble r of the table
-  return (tab >> (4 * r)) & 0xf;
-}
+__host__ __device__ inline int tq3_v_slot(int ci, int r) { return 2 * r + ci; }
 
 __host__ __device__ inline int tq3_v_triple(int d, int t, int c, int* slot) {
   int G = d >> 5;

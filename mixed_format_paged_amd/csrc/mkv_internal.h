@@ -21,9 +21,11 @@ constexpr int kMaxLayers = 64;        // layers covered by one launch
 #define MKV_WAVES 4
 #endif
 constexpr int kItemWaves = MKV_WAVES;  // waves (of 64 lanes) that share one split-K work item
-// split-K work items aimed for per launch: one wave of workgroups at four
-// waves per SIMD on 256 CUs
-constexpr int kTargetItems = 4096 / kItemWaves;
+// partial-attention workgroups resident per CU (one wave per SIMD each; the
+// kernel's register budget is 512 / kAttendWgPerCu VGPRs per lane)
+constexpr int kAttendWgPerCu = 3;
+// split-K work items aimed for per launch: one wave of workgroups on 256 CUs
+constexpr int kTargetItems = 256 * kAttendWgPerCu;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk (a workgroup stages its page ids in LDS)
 constexpr int kMaxG = 8;              // query heads per KV head supported

@@ -79,18 +79,11 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
         const int c0 = 8 * c8;
         const float s = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + tq3_scale_off(D, kv, t, c0 >> 5)));
         float x[8];
-        if (kv == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
           int slot;
-          const int off = tq3_k_triple(D, t, c0, &slot);     // one triple: channels c0 .. c0 + 7 in slots 0..7
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] = (float)((int)tq3_code_at(blk, off, k) - 4) * s;
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            int slot;
-            const int off = tq3_v_triple(D, t, c0 + k, &slot);
-            x[k] = (float)((int)tq3_code_at(blk, off, slot) - 4) * s;
-          }
+          const int off = kv ? tq3_v_triple(D, t, c0 + k, &slot) : tq3_k_triple(D, t, c0 + k, &slot);
+          x[k] = (float)((int)tq3_code_at(blk, off, slot) - 4) * s;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = bf16_rne(x[2 * i]) | (bf16_rne(x[2 * i + 1]) << 16);

@@ -15,18 +15,22 @@
 //    fp16(q) and rows 8..8+G-1 the fp16 remainder q - fp16(q), so one DPP
 //    row-rotate by 8 adds the two halves (q carried to ~22 bits).  For TQ3
 //    each MFMA covers exactly one 32-channel scale group and the fp32 group
-//    scale multiplies its result; codes enter the MFMA as exact fp16 (u - 4).
+//    scale multiplies its result; codes enter the MFMA as exact fp16 u, and
+//    the -4 offset of every group arrives as one more MFMA per page (token
+//    scales x per-group sums of q) that seeds the scores.
 //  * Online softmax in log2 units with a lazy rescale: the running max moves
 //    only when a page's max exceeds it by more than 15 (p <= 2^15, finite in
 //    fp16).
 //  * P V: A = P (rows 0..G-1 fp16(p), rows 8..8+G-1 the remainder).  TQ3 V
-//    is (u - 4) * s split into an exact fp16 pair hi + lo; one
+//    is u * s split into an exact fp16 pair hi + lo; one
 //    v_mfma_f32_16x16x32_f16 per 16-channel tile takes both, its k index
-//    running over (token, part) with P repeated for the two parts.  FP8 V is
-//    exact in fp16 (v_mfma_f32_16x16x16_f16, k = the page's 16 tokens).
+//    running over (token, part) with P repeated for the two parts.  The -4
+//    offset is W = sum_t P s (one v_mfma_f32_16x16x16_f16 per page), taken
+//    off as O - 4 W when the item ends.  FP8 V is exact in fp16
+//    (v_mfma_f32_16x16x16_f16, k = the page's 16 tokens).
 //  Lane maps follow the byte layout in mkv_format.h: a TQ3 lane's triples
-//  arrive in one aligned chunk, and each triple becomes four fp16 pairs with
-//  one mask-and-or and one packed fma per pair.
+//  arrive in one aligned chunk, and each run of 4 triples becomes 32 fp16
+//  codes through one FP6 conversion (decode32 below).
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -47,13 +51,9 @@ constexpr int kThreads = 64 * kWaves;
 // kRescale (log2 units), so p <= 2^15 stays finite in fp16.
 constexpr float kRescale = 15.0f;
 constexpr int kNoMask = 1 << 20;
-// k-slot -> channel offset inside a TQ3 triple, in the order one triple
-// decodes into fp16 pairs: (0,6) (1,7) (3,2) (4,5)
-constexpr int kTq3SlotChannel[8] = {0, 6, 1, 7, 3, 2, 4, 5};
 
 __device__ inline h2 u2h(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ inline uint32_t h2u(h2 h) { return __builtin_bit_cast(uint32_t, h); }
-__device__ inline h2 mkh2(float a, float b) { return h2{(_Float16)a, (_Float16)b}; }
 
 // {x[l], x[l ^ 32]} and {x[l], x[l ^ 16]} (in either order) with one VALU
 // permute (gfx950 v_permlane32_swap / v_permlane16_swap): reductions over the
@@ -81,35 +81,29 @@ __device__ inline float dpp_ror8(float x) {             // lane l <- lane (l ^ 8
 
 // Byte `o` of a little-endian array of dwords, as the start of a triple: the
 // three dwords X = [b0 b1 b2 .], Y = [b1 b2 b0 b1], W = [b1 b2 b1 b2].
-template <int NW>
-__device__ inline void triple_words(const uint32_t (&c)[NW], int o, uint32_t& X, uint32_t& Y, uint32_t& W) {
-  const int i = o >> 2, s = o & 3;
-  const uint32_t lo = c[i];
-  const uint32_t hi = (s + 2 >= 4) ? c[i + 1] : lo;
-  const uint32_t b0 = s, b1 = s + 1, b2 = s + 2;
-  X = (s == 0) ? lo : __builtin_amdgcn_perm(hi, lo, b0 | (b1 << 8) | (b2 << 16) | (b2 << 24));
-  Y = __builtin_amdgcn_perm(hi, lo, b1 | (b2 << 8) | (b0 << 16) | (b1 << 24));
-  W = __builtin_amdgcn_perm(hi, lo, b1 | (b2 << 8) | (b1 << 16) | (b2 << 24));
-}
+typedef uint32_t u6 __attribute__((ext_vector_type(6)));
+typedef _Float16 h32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u16v __attribute__((ext_vector_type(16)));
 
-// (x & mask) | c in one VOP3 instruction.  Both constants come from
-// registers: gfx9-class VOP3 encodings take no literal operand and at most
-// one scalar, so the compiler would otherwise emit a separate AND and OR.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(c));
-  return r;
-}
-
-// One triple -> four fp16 pairs of (u - 4):
-//   r[0] = (slot0, slot6)  r[1] = (slot1, slot7)  r[2] = (slot3, slot2)  r[3] = (slot4, slot5)
-// Each code is dropped into the mantissa of fp16 1024.0 at bit offset j
-// (value 1024 + u 2^j) and one packed fma maps it exactly to u - 4.
-__device__ inline void decode_triple(uint32_t X, uint32_t Y, uint32_t W, uint32_t one024, h2 (&r)[4]) {
-  r[0] = __builtin_elementwise_fma(u2h(and_or(X, 0x001C0007u, one024)), mkh2(1.0f, 0.25f), mkh2(-1028.0f, -260.0f));
-  r[1] = __builtin_elementwise_fma(u2h(and_or(X, 0x00E00038u, one024)), mkh2(0.125f, 0.03125f), mkh2(-132.0f, -36.0f));
-  r[2] = __builtin_elementwise_fma(u2h(and_or(Y, 0x01C0000Eu, one024)), mkh2(0.5f, 0.015625f), mkh2(-516.0f, -20.0f));
-  r[3] = __builtin_elementwise_fma(u2h(and_or(W, 0x03800070u, one024)), mkh2(0.0625f, 0.0078125f), mkh2(-68.0f, -12.0f));
+// 4 triples = 32 codes = 3 words of a lane's code stream (code k of the
+// stream at bits [3k, 3k + 3), little endian) -> 32 fp16 codes u, exact.
+// Read as 6-bit fields, the stream holds two codes per field.  With the high
+// code masked away a field is an E2M3 value with zero exponent bits, i.e. the
+// subnormal u / 8, and gfx950 converts 32 such fields in one instruction
+// (scale 8 makes them u).  The high codes take a second pass over the stream
+// shifted down by 3 bits.  Element i < 16 is the low code of field i (slot
+// 2 (i % 4) of triple i / 4), element 16 + i the high code (slot 2 (i % 4) + 1).
+__device__ inline h32 decode32(uint32_t w0, uint32_t w1, uint32_t w2) {
+  // low 3 bits of every 6-bit field; the pattern repeats every 3 words
+  constexpr uint32_t M0 = 0xC71C71C7u, M1 = 0x71C71C71u, M2 = 0x1C71C71Cu;
+  u6 f;
+  f[0] = w0 & M0;
+  f[1] = w1 & M1;
+  f[2] = w2 & M2;
+  f[3] = __builtin_amdgcn_alignbit(w1, w0, 3) & M0;
+  f[4] = __builtin_amdgcn_alignbit(w2, w1, 3) & M1;
+  f[5] = (w2 >> 3) & M2;                  // M2 keeps bits <= 28: nothing comes from a next word
+  return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(f, 8.0f);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -123,7 +117,7 @@ typedef const __attribute__((address_space(4))) i4v* cptr_i4;
 
 // Per-head-dim constants and the LDS plan of a 4-wave workgroup:
 //   [ring: 4 waves x 2 slots x kSlot][sq: score-MFMA B operands, NG x 64 x 16 B]
-// (40 KB at d = 256, so four workgroups share a CU).  At the end of an item
+// (40 KB at d = 256; three workgroups share a CU).  At the end of an item
 // the whole block is reused for the merge of the 4 wave states.
 template <int D>
 struct Geo {
@@ -148,14 +142,19 @@ struct Geo {
 template <int D>
 __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slot, int lane, int bytes) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot));
+  // 16 * lane, recomputed at every call: kept out of loop-invariant code
+  // motion, which would hold one offset register per row across the page loop
+  uint32_t l16;
+  asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(l16) : "v"(lane));
 #pragma unroll
   for (int i = 0; i < Geo<D>::kRows; ++i) {
-    int off = 1024 * i + 16 * lane;
-    if (off >= bytes) off -= 1024 - (bytes & 1023);
-    // M0 holds the LDS row base; one wait state between the M0 write and the
-    // LDS-DMA load that reads it
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :: "v"(src + off), "s"(lds + 1024 * i) : "memory", "m0");
+    uint32_t off = 1024 * i + l16;
+    if (off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
+    // the (wave-uniform) unit address in an SGPR pair, the lane's 32-bit
+    // offset in a VGPR; M0 holds the LDS row base, with one wait state
+    // between the M0 write and the LDS-DMA load that reads it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
+                 :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
   }
 }
 
@@ -210,16 +209,19 @@ __device__ inline h4 split_rows(const float (&x)[4], float lo_sel) {
 }
 
 // Per-wave running state of the online softmax: O (16 query rows x d
-// channels, C layout of the P V MFMAs), the running max and denominator of the
-// query-row column n this lane holds in the score layout.
+// channels, C layout of the P V MFMAs), W (TQ3: sum of P s per query row and
+// the V scale group of the lane's column, same layout), the running max and
+// denominator of the query-row column n this lane holds in the score layout.
 template <int D>
 struct WaveState {
   f4 O[Geo<D>::NT];
+  f4 W;
   float m_run, l_run;
 
   __device__ inline void init() {
 #pragma unroll
     for (int T = 0; T < Geo<D>::NT; ++T) O[T] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    W = f4{0.0f, 0.0f, 0.0f, 0.0f};
     m_run = -INFINITY;
     l_run = 0.0f;
   }
@@ -274,6 +276,7 @@ struct WaveState {
         const float ar = __shfl(alpha, 4 * j + r);
 #pragma unroll
         for (int T = 0; T < Geo<D>::NT; ++T) O[T][r] *= ar;
+        W[r] *= ar;
       }
     }
     const float m_use = (MQ && m_run == -INFINITY) ? 0.0f : m_run;
@@ -304,92 +307,108 @@ struct RowBlock {
 };
 
 // Scores of one TQ3 page-head staged at pg: one 16x16x32 MFMA per 32-channel
-// scale group, its result scaled by the group's fp16 scale of each token.
+// scale group on the codes u, its result scaled by the group's fp16 scale of
+// each token.  The offset -4 s(t, g) sum_{c in g} q(c), summed over the
+// groups, is one 16x16x16 MFMA that seeds the scores: A = the token scales
+// (token n = lane & 15, k = 4 j + e -> group (4 j + e) % NG), B = kneg (the
+// lane's query row, minus the group sums of q as fp16 hi / lo parts, built
+// once per item).
 template <int D, int RB = 8>
-__device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j, uint32_t one024) {
+__device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j, h4 kneg) {
   constexpr int NG = Geo<D>::NG, GB = 3 * NG;       // bytes of a lane's code chunk
-  uint32_t kc[GB / 4];
-  const uint8_t* kp = pg + (4 * (lane & 15) + j) * GB;
+  const int n = lane & 15;
+  const uint8_t* kp = pg + (4 * n + j) * GB;
+  const uint8_t* sp = pg + 12 * D + 8 * ((n >> 2) * NG + (4 * j) % NG) + 2 * (n & 3);
+  h4 as;
 #pragma unroll
-  for (int i = 0; i < GB / 4; ++i) kc[i] = lds_load<uint32_t>(kp + 4 * i);
-  auto k_operand = [&](int g) {
-    uint32_t X, Y, W;
-    triple_words(kc, 3 * g, X, Y, W);
-    h2 r[4];
-    decode_triple(X, Y, W, one024, r);
-    return __builtin_bit_cast(h8, u4{h2u(r[0]), h2u(r[1]), h2u(r[2]), h2u(r[3])});
-  };
+  for (int e = 0; e < 4; ++e) as[e] = lds_load<_Float16>(sp + 8 * e);
+  f4 s = __builtin_amdgcn_mfma_f32_16x16x16f16(as, kneg, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] *= 4.0f;
   auto k_scales = [&](int g) { return lds_load<u2>(pg + 12 * D + 8 * (j * NG + g)); };  // tokens 4j..4j+3
-  f4 s = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  h8 a = k_operand(0);
   h8 bq = sq[lane];
-  h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;          // 16 rows: q's remainder, a second MFMA
+  h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;
   u2 sk = k_scales(0);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-    if (RB == 16) sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sg, 0, 0, 0);
-    u2 sk_next = sk;
-    if (g + 1 < NG) {                      // group g + 1 decodes and loads while the MFMA runs
-      a = k_operand(g + 1);
-      bq = sq[(g + 1) * 64 + lane];
-      if (RB == 16) bl = sq[NG * 64 + (g + 1) * 64 + lane];
-      sk_next = k_scales(g + 1);
+  for (int b = 0; b < NG / 4; ++b) {
+    // the block's 3 code words are read only now, so one block's codes are live at a time
+    const uint32_t w0 = lds_load<uint32_t>(kp + 12 * b), w1 = lds_load<uint32_t>(kp + 12 * b + 4),
+                   w2 = lds_load<uint32_t>(kp + 12 * b + 8);
+    const u16v u = __builtin_bit_cast(u16v, decode32(w0, w1, w2));
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int g = 4 * b + gg;
+      // group g: channels 8j .. 8j + 7 in words 4gg .. 4gg + 3 (low codes of
+      // fields 8 (gg % 2) .. + 7 for gg < 2, their high codes for gg >= 2)
+      const h8 a = __builtin_bit_cast(h8, u4{u[4 * gg], u[4 * gg + 1], u[4 * gg + 2], u[4 * gg + 3]});
+      f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if (RB == 16) sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sg, 0, 0, 0);
+      u2 sk_next = sk;
+      if (g + 1 < NG) {
+        bq = sq[(g + 1) * 64 + lane];
+        if (RB == 16) bl = sq[NG * 64 + (g + 1) * 64 + lane];
+        sk_next = k_scales(g + 1);
+      }
+      const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
+      s[0] = fmaf(sg[0], (float)s01[0], s[0]);
+      s[1] = fmaf(sg[1], (float)s01[1], s[1]);
+      s[2] = fmaf(sg[2], (float)s23[0], s[2]);
+      s[3] = fmaf(sg[3], (float)s23[1], s[3]);
+      sk = sk_next;
+      if (RB == 16)
+        asm volatile("" : "+v"(s), "+v"(bq), "+v"(bl), "+v"(sk) :: "memory");
+      else
+        asm volatile("" : "+v"(s), "+v"(bq), "+v"(sk) :: "memory");
     }
-    const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
-    s[0] = fmaf(sg[0], (float)s01[0], s[0]);
-    s[1] = fmaf(sg[1], (float)s01[1], s[1]);
-    s[2] = fmaf(sg[2], (float)s23[0], s[2]);
-    s[3] = fmaf(sg[3], (float)s23[1], s[3]);
-    sk = sk_next;
-    // pins the order: group g's scaling is done, and at most group g + 1's
-    // operands are live, before group g + 1's MFMA (instruction selection
-    // would otherwise sink every scaling below all eight MFMAs and keep all
-    // their results live)
-    if (RB == 16)
-      asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(bl), "+v"(sk) :: "memory");
-    else
-      asm volatile("" : "+v"(s), "+v"(a), "+v"(bq), "+v"(sk) :: "memory");
   }
   return s;
 }
 
-// P V of one TQ3 page-head: V = (u - 4) s as an exact fp16 pair hi + lo; one
+// P V of one TQ3 page-head: V = u s as an exact fp16 pair hi + lo; one
 // 16x16x32 MFMA per 16-channel tile takes both, its k index running over
-// (token 4j + (e & 3), part e >> 2) with P repeated for the two parts.
+// (token 4j + (e & 3), part e >> 2) with P repeated for the two parts.  The
+// lane's column keeps one V scale group in every tile, so W += P s (one
+// 16x16x16 MFMA, B = the group's scales of tokens 4j..4j+3) holds what the -4
+// offset takes off each of its tiles.
 template <int D, int RB = 8>
-__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], int lane, int j, uint32_t one024,
+__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], f4& W, int lane, int j,
                               h4 pl = h4{}) {
   constexpr int NG = Geo<D>::NG, GB = 3 * NG;
   const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
   const h8 pl2 = __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3);   // RB 16: P's remainder
-  uint32_t vc[GB / 4];
   const uint8_t* vp = pg + 6 * D + lane * GB;
-#pragma unroll
-  for (int i = 0; i < GB / 4; ++i) vc[i] = lds_load<uint32_t>(vp + 4 * i);
   const int gn = (lane & 15) * D / 512;      // the lane's V channel group
   const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
   const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
+  const h4 sv4 = __builtin_bit_cast(h4, svv);
+  W = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, sv4, W, 0, 0, 0);
+  if (RB == 16) W = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, sv4, W, 0, 0, 0);
 #pragma unroll
-  for (int pp = 0; pp < NG; ++pp) {
-    uint32_t X, Y, W;
-    triple_words(vc, 3 * pp, X, Y, W);
-    h2 r[4];
-    decode_triple(X, Y, W, one024, r);
-    const h2 hi0 = r[0] * sv01, hi1 = r[1] * sv23, hi2 = r[2] * sv01, hi3 = r[3] * sv23;
-    const h2 lo0 = __builtin_elementwise_fma(r[0], sv01, -hi0);
-    const h2 lo1 = __builtin_elementwise_fma(r[1], sv23, -hi1);
-    const h2 lo2 = __builtin_elementwise_fma(r[2], sv01, -hi2);
-    const h2 lo3 = __builtin_elementwise_fma(r[3], sv23, -hi3);
-    const h8 b0 = __builtin_bit_cast(h8, u4{h2u(hi0), h2u(hi1), h2u(lo0), h2u(lo1)});
-    const h8 b1 = __builtin_bit_cast(h8, u4{h2u(hi2), h2u(hi3), h2u(lo2), h2u(lo3)});
-    O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b0, O[2 * pp], 0, 0, 0);
-    O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b1, O[2 * pp + 1], 0, 0, 0);
-    if (RB == 16) {
-      O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b0, O[2 * pp], 0, 0, 0);
-      O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b1, O[2 * pp + 1], 0, 0, 0);
+  for (int b = 0; b < NG / 4; ++b) {
+    const uint32_t w0 = lds_load<uint32_t>(vp + 12 * b), w1 = lds_load<uint32_t>(vp + 12 * b + 4),
+                   w2 = lds_load<uint32_t>(vp + 12 * b + 8);
+    const u16v u = __builtin_bit_cast(u16v, decode32(w0, w1, w2));
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int pp = 4 * b + q4;
+      // field r of the triple holds (channel a, token 4j + r) low, (b, 4j + r) high
+      const h2 a01 = u2h(u[2 * q4]), a23 = u2h(u[2 * q4 + 1]);
+      const h2 b01 = u2h(u[8 + 2 * q4]), b23 = u2h(u[9 + 2 * q4]);
+      const h2 ha01 = a01 * sv01, ha23 = a23 * sv23, hb01 = b01 * sv01, hb23 = b23 * sv23;
+      const h2 la01 = __builtin_elementwise_fma(a01, sv01, -ha01);
+      const h2 la23 = __builtin_elementwise_fma(a23, sv23, -ha23);
+      const h2 lb01 = __builtin_elementwise_fma(b01, sv01, -hb01);
+      const h2 lb23 = __builtin_elementwise_fma(b23, sv23, -hb23);
+      const h8 b0 = __builtin_bit_cast(h8, u4{h2u(ha01), h2u(ha23), h2u(la01), h2u(la23)});
+      const h8 b1 = __builtin_bit_cast(h8, u4{h2u(hb01), h2u(hb23), h2u(lb01), h2u(lb23)});
+      O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b0, O[2 * pp], 0, 0, 0);
+      O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa2, b1, O[2 * pp + 1], 0, 0, 0);
+      if (RB == 16) {
+        O[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b0, O[2 * pp], 0, 0, 0);
+        O[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl2, b1, O[2 * pp + 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -463,7 +482,7 @@ template <int D, bool tq3, bool MQ, int RB = 8>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
     const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
-    uint8_t* smem, uint32_t one024, const AppendIn* ap, const RowBlock& rb) {
+    uint8_t* smem, const AppendIn* ap, const RowBlock& rb) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
   const int lane = threadIdx.x & 63;
@@ -541,8 +560,8 @@ __device__ __forceinline__ void run_item(
     float x0[4], x1[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      x0[k] = (use ? (tq3 ? v[kTq3SlotChannel[k]] : v[k]) : 0.0f) * sc;
-      x1[k] = (use ? (tq3 ? v[kTq3SlotChannel[k + 4]] : v[k + 4]) : 0.0f) * sc;
+      x0[k] = (use ? v[k] : 0.0f) * sc;
+      x1[k] = (use ? v[k + 4] : 0.0f) * sc;
     }
     if (RB == 16) {
       sq[e] = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -553,6 +572,32 @@ __device__ __forceinline__ void run_item(
     }
   }
   __syncthreads();
+
+  // TQ3: B operand of the offset MFMA.  Lane (n, j), k = 4 j + e: minus the
+  // sum of query row n's q over group (4 j + e) % NG, fp16 hi for k < NG, the
+  // remainder for NG <= k < 2 NG, 0 beyond.  The group sums come from MFMAs
+  // of the q fragments with a matrix of ones (every output row holds them).
+  h4 kneg = h4{};
+  if (tq3) {
+    constexpr h8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+    float qs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, sq[g * 64 + lane], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if (RB == 16) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, sq[NG * 64 + g * 64 + lane], c, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((4 * j + e) % NG == g) qs[e] = c[0];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * j + e;
+      const float x = -qs[e];
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)(x - (float)hi);
+      kneg[e] = k < NG ? hi : (k < 2 * NG ? lo : (_Float16)0.0f);
+    }
+  }
 
   WaveState<D> st;
   st.init();
@@ -582,10 +627,10 @@ __device__ __forceinline__ void run_item(
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
-      const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, one024);
+      const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, kneg);
       h4 pl;
       const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
-      tq3_pv<D, RB>(cur, pa, st.O, lane, j, one024, pl);
+      tq3_pv<D, RB>(cur, pa, st.O, st.W, lane, j, pl);
     }
   } else {
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
@@ -649,8 +694,10 @@ __device__ __forceinline__ void run_item(
           const int row = 4 * j + r;
           const float mw = sm[wave * NR + row];
           const float wr = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
+          const float cw = tq3 ? -4.0f * st.W[r] * wr : 0.0f;     // TQ3 V's -4 offset
 #pragma unroll
-          for (int T = 0; T < GD::NT; ++T) so[MergeLayout<D>::at(wave, 4 * (j & 1) + r, n, T)] = st.O[T][r] * wr;
+          for (int T = 0; T < GD::NT; ++T)
+            so[MergeLayout<D>::at(wave, 4 * (j & 1) + r, n, T)] = fmaf(st.O[T][r], wr, cw);
         }
       }
       __syncthreads();
@@ -671,12 +718,18 @@ __device__ __forceinline__ void run_item(
   // (rows >= G hold values nobody reads), so the stores need no lane mask and
   // take their row and tile from the instruction offset.
   const int jj = j & 1, thalf = j >> 1;
-  float wr[4];
+  float wr[4], cw[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * jj + r;
     const float mw = sm[wave * NR + row];
     wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
+    cw[r] = 0.0f;
+    if (tq3) {    // TQ3 V's -4 offset: W of the fp16 row and of its remainder row, like O below
+      const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.W[r]), __float_as_uint(st.W[r]), false,
+                                                       false);
+      cw[r] = -4.0f * (__uint_as_float(pw[0]) + __uint_as_float(pw[1])) * wr[r];
+    }
   }
 #pragma unroll
   for (int T = 0; T < GD::NT / 2; ++T) {
@@ -685,7 +738,7 @@ __device__ __forceinline__ void run_item(
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.O[T][r]),
                                                        __float_as_uint(st.O[T + GD::NT / 2][r]), false, false);
       const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-      so[MergeLayout<D>::at(wave, 4 * jj + r, n, T + thalf * (GD::NT / 2))] = tot * wr[r];
+      so[MergeLayout<D>::at(wave, 4 * jj + r, n, T + thalf * (GD::NT / 2))] = fmaf(tot, wr[r], cw[r]);
     }
   }
   __syncthreads();
@@ -716,19 +769,17 @@ __device__ __forceinline__ void run_item(
 // MODE selects which format's work items the launch takes (kBoth: the FP8
 // items first, then the TQ3 items, in one grid so the small FP8 share runs
 // alongside the TQ3 stream; each item runs its own format's code path).
-// 40 KB of LDS and at most 128 VGPRs per thread: four workgroups per CU.
-#ifndef MKV_OCC
-#define MKV_OCC 4
-#endif
+// 40 KB of LDS and at most 168 VGPRs per thread: kAttendWgPerCu = 3
+// workgroups per CU (the TQ3 page loop needs about 160 registers without
+// spills).
 // MQ: several query tokens per request (plan.n_query), their rows split in
 // plan.nblk blocks, one work item per (chunk, KV head, block); causal masks on
 // the request's last two logical pages.
 // RB: query rows per item, 8 (MFMA rows 0..7, remainders in 8..15) or, for
-// multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS, three
-// workgroups per CU).
+// multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS).
 template <int D, int MODE, bool MQ, int RB>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(RB == 16 ? 3 : MKV_OCC, RB == 16 ? 3 : MKV_OCC))) attend_kernel(
+    __attribute__((amdgpu_waves_per_eu(kAttendWgPerCu, kAttendWgPerCu))) attend_kernel(
         LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
         float qscale, Plan plan, AppendIn ap) {
   __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
@@ -739,8 +790,6 @@ __global__ void __launch_bounds__(kThreads)
   const long items_f = (long)n_layers * hkv * ncf * nblk;
   const long items_t = (long)n_layers * hkv * nct * nblk;
   const long items = items_f + items_t;
-  uint32_t one024 = 0x64006400u;             // fp16 1024.0 in both halves, kept in a VGPR
-  asm volatile("" : "+v"(one024));
 
   for (long item = blockIdx.x; item < items; item += gridDim.x) {
     const bool tq3 = item >= items_f;
@@ -773,10 +822,10 @@ __global__ void __launch_bounds__(kThreads)
     }
     if (MODE != kFp8Only && tq3)
       run_item<D, true, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
-                                one024, nullptr, rb);
+                                nullptr, rb);
     if (MODE != kTq3Only && !tq3)
       run_item<D, false, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
-                                 smem, one024, (!MQ && holds_tail) ? &ap : nullptr, rb);
+                                 smem, (!MQ && holds_tail) ? &ap : nullptr, rb);
     __syncthreads();
   }
 }

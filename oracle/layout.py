@@ -6,8 +6,8 @@ Abstract; page 2, "Technical Deep Dive", fourth bullet).  Everything below is
 this implementation's documented reading; the oracle writes it out with plain
 index loops so that a reader can check each position by eye.
 
-Page size is 16 tokens.  d = head_dim (multiple of 32, <= 512), G = d / 32
-scale groups per token, Hkv KV heads.
+Page size is 16 tokens.  d = head_dim (128 or 256), G = d / 32 scale groups
+per token (a multiple of 4), Hkv KV heads.
 
 FP8 page (physical id < n_fp8), Hkv * 2 * 16 * d bytes:
     byte ((h * 2 + kv) * 16 + t) * d + c  holds the E4M3 code of
@@ -22,22 +22,28 @@ TQ3 page, Hkv head blocks of 14 * d bytes each, block h at h * 14 * d:
 A triple is 3 bytes = 8 codes: code slot k sits at bits [3k, 3k + 3) of the
 little-endian 24-bit word b0 | b1 << 8 | b2 << 16 ("8 codes per 3 bytes").
 
-K codes: token row t starts at t * 3d/8; in it, the triple at byte
-3 * (j * G + g) (j = 0..3, g = 0..G-1) holds channels 32 g + 8 j + k in slot k.
+K codes: token row t starts at t * 3d/8; in it, channel quarter j (channels
+8 j .. 8 j + 7 of every group, j = 0..3) takes the G triples from byte 3 j G,
+in blocks of 4 triples, block b for groups 4 b .. 4 b + 3.  Channel
+c = 32 g + 8 j + e (e = 0..7), with gg = g % 4, sits in triple
+4 (g // 4) + 2 (gg % 2) + e // 4 of its quarter, slot 2 (e % 4) + gg // 2.
+(Read as 16 six-bit fields, field f of a block holds channel 8 j + f % 8 of
+group 4 b + f // 8 in its low three bits and of group 4 b + 2 + f // 8 in its
+high three bits.)
 
 V codes: the triple at byte 3 * ((j * 16 + n) * G + p) (token quarter j = 0..3,
 channel slice n = 0..15, p = 0..G-1) holds tokens 4 j .. 4 j + 3 of the two
-channels a = n * d/16 + 2 p and b = a + 1, in the slot order
-    slot 0: (a, 4j)   slot 6: (a, 4j+1)  slot 1: (a, 4j+2)  slot 7: (a, 4j+3)
-    slot 3: (b, 4j)   slot 2: (b, 4j+1)  slot 4: (b, 4j+2)  slot 5: (b, 4j+3)
+channels a = n * d/16 + 2 p and b = a + 1: slot 2 r holds (a, 4 j + r) and
+slot 2 r + 1 holds (b, 4 j + r), r = 0..3.
 
 Scales (K and V alike): the scale of token t = 4 j + r, group g is the fp16 at
 element (j * G + g) * 4 + r of the scale block.
 
-Why this arrangement: a triple is the unit one GPU lane decodes, and the order
-puts each lane's triples next to each other so they arrive in one aligned
-vector load; the slot order lets two codes become two fp16 halves with one
-mask-and-or.  The oracle does not depend on why; it only follows the map.
+Why this arrangement: each GPU lane's triples sit next to each other, so they
+arrive in one aligned vector load, and a block of 4 triples read as six-bit
+fields decodes with two FP6 conversions (low codes, then high codes) straight
+into matrix-core operands.  The oracle does not depend on why; it only
+follows the map.
 """
 import functools
 import numpy as np
@@ -62,7 +68,7 @@ def fp8_offset(d, h, kv, t, c):
 
 
 # V-triple slot -> (channel offset within the pair, token offset within the quarter)
-V_SLOT = {0: (0, 0), 6: (0, 1), 1: (0, 2), 7: (0, 3), 3: (1, 0), 2: (1, 1), 4: (1, 2), 5: (1, 3)}
+V_SLOT = {0: (0, 0), 1: (1, 0), 2: (0, 1), 3: (1, 1), 4: (0, 2), 5: (1, 2), 6: (0, 3), 7: (1, 3)}
 
 
 @functools.lru_cache(maxsize=None)
@@ -72,13 +78,16 @@ def k_code_map(d):
     row = 3 * d // 8
     tri = np.zeros((PAGE, d), dtype=np.int64)
     slot = np.zeros((PAGE, d), dtype=np.int64)
+    assert G % 4 == 0
     for t in range(PAGE):
         for g in range(G):
+            gg = g % 4
             for j in range(4):
-                for k in range(8):
-                    c = 32 * g + 8 * j + k
-                    tri[t, c] = t * row + 3 * (j * G + g)
-                    slot[t, c] = k
+                for e in range(8):
+                    c = 32 * g + 8 * j + e
+                    triple = 4 * (g // 4) + 2 * (gg % 2) + e // 4
+                    tri[t, c] = t * row + 3 * (j * G + triple)
+                    slot[t, c] = 2 * (e % 4) + gg // 2
     return tri, slot
 
 

@@ -25,7 +25,7 @@ def test_golden_positions_d128():
         else:
             t, g, byte = map(int, f[1:])
             assert sm[t, g] + (128 if f[0] == "SV" else 0) == byte, line
-    assert n == 15
+    assert n == 18
 
 
 def _check_bijection(d):
@@ -71,12 +71,33 @@ def test_head_block_roundtrip():
         assert np.array_equal(e.view(np.uint16), sV.view(np.uint16))
 
 
-def test_k_triple_is_eight_consecutive_channels():
-    # A K triple holds 8 consecutive channels of one token, slot k = channel % 8,
-    # and all 32 channels of a group lie in one token row.
+def test_k_block_read_as_six_bit_fields():
+    # The map's second description: a block of 4 K triples, read as a 96-bit
+    # little-endian stream of 16 six-bit fields, holds in field f channel
+    # 8 j + f % 8 of group 4 b + f // 8 (low three bits) and of group
+    # 4 b + 2 + f // 8 (high three bits).  Slot k of a triple is bits [3k, 3k+3).
+    for d in (128, 256):
+        G = d // 32
+        tri, slot = layout.k_code_map(d)
+        for t in (0, 7, 15):
+            for j in range(4):
+                for b in range(G // 4):
+                    base = t * 3 * d // 8 + 3 * (j * G + 4 * b)
+                    for f in range(16):
+                        for part, g in ((0, 4 * b + f // 8), (1, 4 * b + 2 + f // 8)):
+                            c = 32 * g + 8 * j + f % 8
+                            bit = 6 * f + 3 * part
+                            assert tri[t, c] == base + 3 * (bit // 24), (d, t, c)
+                            assert slot[t, c] == (bit % 24) // 3, (d, t, c)
+
+
+def test_v_slots_alternate_channels_token_major():
+    # slot 2 r: channel a (even) of token 4 j + r; slot 2 r + 1: channel b = a + 1
     d = 256
-    tri, slot = layout.k_code_map(d)
-    for t in (0, 7, 15):
-        for c0 in range(0, d, 8):
-            assert len(set(tri[t, c0:c0 + 8])) == 1
-            assert list(slot[t, c0:c0 + 8]) == list(range(8))
+    tri, slot = layout.v_code_map(d)
+    for start in np.unique(tri)[:64]:
+        t, c = np.nonzero(tri == start)
+        by_slot = {int(slot[ti, ci]): (int(ti), int(ci)) for ti, ci in zip(t, c)}
+        a, t0 = by_slot[0][1], by_slot[0][0]
+        for k in range(8):
+            assert by_slot[k] == (t0 + k // 2, a + k % 2)
