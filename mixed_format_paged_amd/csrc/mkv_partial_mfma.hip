@@ -329,6 +329,15 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
   h8 bq = sq[lane];
   h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;
   u2 sk = k_scales(0);
+  f4 sgp = f4{0.0f, 0.0f, 0.0f, 0.0f};                  // the previous group's result and scales:
+  u2 skp = u2{0u, 0u};                                  // scaled while the next group's MFMA runs
+  auto scale_into = [&](const f4& sg, const u2& sc) {
+    const h2 s01 = u2h(sc[0]), s23 = u2h(sc[1]);
+    s[0] = fmaf(sg[0], (float)s01[0], s[0]);
+    s[1] = fmaf(sg[1], (float)s01[1], s[1]);
+    s[2] = fmaf(sg[2], (float)s23[0], s[2]);
+    s[3] = fmaf(sg[3], (float)s23[1], s[3]);
+  };
 #pragma unroll
   for (int b = 0; b < NG / 4; ++b) {
     // the block's 3 code words are read only now, so one block's codes are live at a time
@@ -343,24 +352,26 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
       const h8 a = __builtin_bit_cast(h8, u4{u[4 * gg], u[4 * gg + 1], u[4 * gg + 2], u[4 * gg + 3]});
       f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
       if (RB == 16) sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sg, 0, 0, 0);
-      u2 sk_next = sk;
-      if (g + 1 < NG) {
+      const u2 sk_g = sk;
+      if (g + 1 < NG) {                    // group g + 1's operands load while the MFMA runs
         bq = sq[(g + 1) * 64 + lane];
         if (RB == 16) bl = sq[NG * 64 + (g + 1) * 64 + lane];
-        sk_next = k_scales(g + 1);
+        sk = k_scales(g + 1);
       }
-      const h2 s01 = u2h(sk[0]), s23 = u2h(sk[1]);
-      s[0] = fmaf(sg[0], (float)s01[0], s[0]);
-      s[1] = fmaf(sg[1], (float)s01[1], s[1]);
-      s[2] = fmaf(sg[2], (float)s23[0], s[2]);
-      s[3] = fmaf(sg[3], (float)s23[1], s[3]);
-      sk = sk_next;
+      if (g > 0) scale_into(sgp, skp);     // group g - 1, while group g's MFMA runs
+      sgp = sg;
+      skp = sk_g;
+      // pins the order: group g - 1 is scaled and only group g + 1's operands
+      // are loaded before group g + 1's MFMA (instruction selection would
+      // otherwise sink every scaling below all the MFMAs and keep all their
+      // results live)
       if (RB == 16)
-        asm volatile("" : "+v"(s), "+v"(bq), "+v"(bl), "+v"(sk) :: "memory");
+        asm volatile("" : "+v"(s), "+v"(bq), "+v"(bl), "+v"(sk), "+v"(sgp), "+v"(skp) :: "memory");
       else
-        asm volatile("" : "+v"(s), "+v"(bq), "+v"(sk) :: "memory");
+        asm volatile("" : "+v"(s), "+v"(bq), "+v"(sk), "+v"(sgp), "+v"(skp) :: "memory");
     }
   }
+  scale_into(sgp, skp);
   return s;
 }
 
