@@ -9,14 +9,15 @@
 // (layer, request, KV head, group of up to 8 query rows, slice of 32
 // channels), 512 threads (a KV head has R = T G rows: T query tokens per
 // request times G heads; row r = t G + g goes to out[b][t][h G + g]):
-//   1. each thread requests its share of the partial states (registers) and
-//      the workgroup the (m, l) pairs of the request (LDS), in one go;
-//   2. M per query head, then the weights w_p into LDS (one exp2 per partial
-//      and head, shared by every channel of the slice) and L: one wave per
-//      head, lanes strided over partials, DPP / permlane reductions;
-//   3. each (head, channel) pair of the slice is summed by several threads
-//      over interleaved partials, and their sums are added in a fixed order.
-// Every sum runs in a fixed order, so results are bitwise reproducible.
+//   1. each (row, 4-channel column) of the slice is shared by kSubs threads,
+//      each taking every kSubs-th partial: its (m, l) pairs and states are
+//      requested in one go, kReg at a time;
+//   2. the thread folds them with its own running maximum (the same merge,
+//      applied to its share): Mt, Lt and its weighted sum;
+//   3. the kSubs shares of a (row, column) are merged through LDS in a fixed
+//      order: M = max Mt, L = sum Lt 2^(Mt - M), o = sum at 2^(Mt - M) / L.
+// The order of every sum is fixed, so results are bitwise reproducible, and
+// there is one workgroup barrier per item.
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -32,35 +33,7 @@ constexpr int kThreads = 512;
 constexpr int kSliceC = 32;                      // channels per workgroup
 constexpr int kQuads = kSliceC / 4;              // float4 columns of a slice
 constexpr int kSubs = kThreads / (kMaxG * kQuads);   // threads sharing one (head, float4 column)
-constexpr int kTileP = 512;                      // partials whose weights sit in LDS at once
-constexpr int kReg = 16;                         // partial states (float4) a thread prefetches
-
-// Reductions over a wave without LDS: DPP row rotates inside each 16-lane
-// row, then the gfx950 permlane swaps across rows; every lane gets the result.
-template <int K>
-__device__ inline float ror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + K, 0xf, 0xf, false));
-}
-__device__ inline float wave_max(float x) {
-  x = fmaxf(x, ror<1>(x));
-  x = fmaxf(x, ror<2>(x));
-  x = fmaxf(x, ror<4>(x));
-  x = fmaxf(x, ror<8>(x));
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float wave_sum(float x) {
-  x += ror<1>(x);
-  x += ror<2>(x);
-  x += ror<4>(x);
-  x += ror<8>(x);
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+constexpr int kReg = 16;                         // partial states (float4) a thread requests at once
 
 }  // namespace
 
@@ -76,15 +49,13 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   const int T = plan.n_query;
   const int R = T * Gh;                                     // rows per KV head
   const int NRG = (R + kMaxG - 1) / kMaxG;                  // row groups
-  __shared__ float sw[kTileP * kMaxG];          // weights of the current tile, [p][i]
-  __shared__ float sml[kTileP * kMaxG * 2];     // (m, l) of the current tile, [p][i][2]
-  __shared__ f4v sred[kThreads];                // per-thread sums, [sub][i][q]
-  __shared__ float sM[kMaxG], sL[kMaxG];
+  __shared__ f4v sa[kThreads];                  // per-thread weighted sums, [sub][i][q]
+  __shared__ float sm[kThreads], sl[kThreads];  // per-thread maxima and denominators
   const int B = plan.batch;
   const int* poff = req_row(plan, R_POFF);
   const int* inval = req_row(plan, R_INVALID);
   const int hq = hkv * Gh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
   const long items = (long)n_layers * B * hkv * NRG * NS;
   // output element of row r of request b, KV head h
@@ -113,81 +84,66 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
     }
     const size_t sstride = (size_t)hkv * R;                 // states between consecutive partials
     const size_t st0 = ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * R + r0;
-    const float* ml = plan.part_ml + st0 * 2;
+    const float* ml = plan.part_ml + (st0 + (live ? pi : 0)) * 2;
     const float* acc = plan.part_acc + st0 * D + cs * kSliceC + (size_t)(live ? pi : 0) * D + 4 * qc;
-    f4v a = f4v{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int t0 = 0; t0 < np; t0 += kTileP) {
-      const int nt = np - t0 < kTileP ? np - t0 : kTileP;
-      const float* ap = acc + (size_t)t0 * sstride * D;
-      const int cnt = live ? (nt - sub + kSubs - 1) / kSubs : 0;   // this thread's partials
-      const bool in_regs = nt <= kSubs * kReg;                   // uniform
-      // 1. this thread's partial states to registers, the tile's (m, l) to LDS
+    // 1 + 2: this thread's share, partials sub, sub + kSubs, ..., kReg at a time
+    float Mt = -INFINITY, Lt = 0.0f;
+    f4v at = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+    const int mine = live ? (np - sub + kSubs - 1) / kSubs : 0;
+    for (int k0 = 0; k0 < mine; k0 += kReg) {
+      const int cnt = mine - k0 < kReg ? mine - k0 : kReg;
       f4v av[kReg];
-      if (in_regs) {
+      float mv[kReg], lv[kReg];
 #pragma unroll
-        for (int k = 0; k < kReg; ++k)
-          av[k] = k < cnt ? *reinterpret_cast<const f4v*>(ap + (size_t)(sub + k * kSubs) * sstride * D)
-                          : f4v{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-      for (int idx = tid; idx < nt * 2 * G; idx += kThreads) {      // (m, l) rows of 2G floats
-        const int p = idx / (2 * G), k = idx - p * (2 * G);
-        sml[idx] = ml[(t0 + p) * sstride * 2 + k];
-      }
-      __syncthreads();
-      // 2. M per query head (first tile), then the tile's weights and L
-      if (t0 == 0) {
-        for (int i = wave; i < G; i += kThreads / 64) {
-          float M = -INFINITY;
-          for (int p = lane; p < nt; p += 64) M = fmaxf(M, sml[p * 2 * G + 2 * i]);
-          M = wave_max(M);
-          if (lane == 0) { sM[i] = M; sL[i] = 0.0f; }
+      for (int k = 0; k < kReg; ++k) {
+        const size_t p = (size_t)(sub + (k0 + k) * kSubs);
+        if (k < cnt) {
+          av[k] = *reinterpret_cast<const f4v*>(acc + p * sstride * D);
+          const float2 m_l = *reinterpret_cast<const float2*>(ml + p * sstride * 2);
+          mv[k] = m_l.x;
+          lv[k] = m_l.y;
+        } else {
+          av[k] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+          mv[k] = -INFINITY;
+          lv[k] = 0.0f;
         }
-        if (nt < np) {                                              // the other tiles' maxima
-          __syncthreads();
-          for (int i = wave; i < G; i += kThreads / 64) {
-            float M = sM[i];
-            for (int p = nt + lane; p < np; p += 64) M = fmaxf(M, ml[(p * sstride + i) * 2]);
-            M = wave_max(M);
-            if (lane == 0) sM[i] = M;
-          }
-        }
-        __syncthreads();
       }
-      for (int i = wave; i < G; i += kThreads / 64) {
-        const float M = sM[i];
-        float l = 0.0f;
-        for (int p = lane; p < nt; p += 64) {
-          const float m = sml[p * 2 * G + 2 * i];
-          const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-          sw[p * G + i] = w;
-          l += sml[p * 2 * G + 2 * i + 1] * w;
-        }
-        l = wave_sum(l);
-        if (lane == 0) sL[i] += l;
-      }
-      __syncthreads();
-      // 3. this thread's interleaved partials, in index order
-      if (in_regs) {
+      float mx = Mt;
 #pragma unroll
-        for (int k = 0; k < kReg; ++k)
-          if (k < cnt) a += sw[(sub + k * kSubs) * G + pi] * av[k];
-      } else {
-        for (int k = 0; k < cnt; ++k)
-          a += sw[(sub + k * kSubs) * G + pi] * *reinterpret_cast<const f4v*>(ap + (size_t)(sub + k * kSubs) * sstride * D);
+      for (int k = 0; k < kReg; ++k) mx = fmaxf(mx, mv[k]);
+      if (mx > Mt) {                                        // Mt = -inf: nothing to rescale yet
+        const float sc = Mt == -INFINITY ? 0.0f : exp2f(Mt - mx);
+        at *= sc;
+        Lt *= sc;
+        Mt = mx;
       }
-      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kReg; ++k) {
+        const float w = mv[k] == -INFINITY ? 0.0f : exp2f(mv[k] - Mt);
+        at += w * av[k];
+        Lt += w * lv[k];
+      }
     }
-    sred[tid] = a;
+    // 3. the kSubs shares of (pi, qc), in sub order
+    sa[tid] = at;
+    sm[tid] = Mt;
+    sl[tid] = Lt;
     __syncthreads();
     if (sub == 0 && live) {
-      f4v o = a;
-      for (int s = 1; s < kSubs; ++s) o += sred[s * kQuads * kMaxG + tid];
-      const float L = sL[pi];
-      const f4v r = L > 0.0f ? o / L : f4v{0.0f, 0.0f, 0.0f, 0.0f};
-      *reinterpret_cast<f4v*>(out_row + 4 * qc) = r;
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < kSubs; ++s2) M = fmaxf(M, sm[s2 * kQuads * kMaxG + tid]);
+      f4v o = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+      float L = 0.0f;
+      for (int s2 = 0; s2 < kSubs; ++s2) {
+        const int t2 = s2 * kQuads * kMaxG + tid;
+        const float w = sm[t2] == -INFINITY ? 0.0f : exp2f(sm[t2] - M);
+        o += w * sa[t2];
+        L += w * sl[t2];
+      }
+      *reinterpret_cast<f4v*>(out_row + 4 * qc) = L > 0.0f ? o / L : f4v{0.0f, 0.0f, 0.0f, 0.0f};
+      if (cs == 0 && qc == 0 && lse_l)
+        lse_l[out_at(layer, b, h, r0 + pi)] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
     }
-    if (cs == 0 && lse_l && tid < G)
-      lse_l[out_at(layer, b, h, r0 + tid)] = sL[tid] > 0.0f ? (sM[tid] + log2f(sL[tid])) * 0.69314718055994531f : -INFINITY;
     __syncthreads();
   }
 }
