@@ -116,8 +116,8 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.off_req = take(sizeof(int32_t) * R_FIELDS * (size_t)(batch + 1));
   s.off_list_f = take(sizeof(int32_t) * (size_t)bt_capacity);
   s.off_list_t = take(sizeof(int32_t) * (size_t)bt_capacity);
-  s.off_chunks_f = take(sizeof(int4) * (size_t)s.table_cap);
-  s.off_chunks_t = take(sizeof(int4) * (size_t)s.table_cap);
+  s.off_chunks_f = take(sizeof(int32_t) * kChunkInts * (size_t)s.table_cap);
+  s.off_chunks_t = take(sizeof(int32_t) * kChunkInts * (size_t)s.table_cap);
   const size_t states = (size_t)Le * s.np_cap * hkv * R;
   s.off_part_ml = take(sizeof(float) * 2 * states);
   s.off_part_acc = take(sizeof(float) * d * states);

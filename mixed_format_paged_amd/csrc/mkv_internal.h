@@ -58,8 +58,12 @@ enum TotalField {
 // Chunk descriptor: x = request, y = first index into the format's page list
 // (absolute, in the request's CSR range), z = pages | (tokens on its last
 // page << 16) | (kChunkHoldsTail if its last page is the request's last
-// logical page), w = partial index within the layer.
+// logical page), w = partial index within the layer.  Each chunk-table entry
+// is two int4: the descriptor, then the chunk's page-list entries k = 0..3
+// (clamped to its last page), the first page of each of the kItemWaves waves
+// that share a work item, so a workgroup can start staging after one load.
 constexpr int kChunkHoldsTail = 1 << 30;
+constexpr int kChunkInts = 8;         // ints per chunk-table entry
 __host__ __device__ inline int chunk_pages(int z) { return z & 0xffff; }
 __host__ __device__ inline int chunk_last_tok(int z) { return (z >> 16) & 0x1f; }
 struct Plan {
@@ -68,8 +72,8 @@ struct Plan {
   int32_t* req;         // [R_FIELDS][batch + 1]
   int32_t* list_f;      // [bt_capacity] FP8 page ids, request-CSR order
   int32_t* list_t;      // [bt_capacity] TQ3 slot ids (id - n_fp8)
-  int4* chunks_f;       // [chunk_cap]
-  int4* chunks_t;       // [chunk_cap]
+  int4* chunks_f;       // [chunk_cap][2]: descriptor, first page ids
+  int4* chunks_t;       // [chunk_cap][2]
   float* part_ml;       // [L][np_cap][Hkv][G][2]  (m in log2 units, l)
   float* part_acc;      // [L][np_cap][Hkv][G][d]
   int batch;

@@ -112,8 +112,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // scalar unit and never count against the vector-memory counter that the
 // staging waits below rely on.
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
-typedef int i4v __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(4))) i4v* cptr_i4;
+typedef int i8v __attribute__((ext_vector_type(8)));
+typedef const __attribute__((address_space(4))) i8v* cptr_i8;
 
 // Per-head-dim constants and the LDS plan of a 4-wave workgroup:
 //   [ring: 4 waves x 2 slots x kSlot][sq: score-MFMA B operands, NG x 64 x 16 B]
@@ -492,7 +492,7 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 template <int D, bool tq3, bool MQ, int RB = 8>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
-    const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx,
+    const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx, int first_id,
     uint8_t* smem, const AppendIn* ap, const RowBlock& rb) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
@@ -539,9 +539,9 @@ __device__ __forceinline__ void run_item(
   // first unit(s) in flight before the query fragments are built
   if (my_pages > 0) {
     if (tq3) {
-      stage_issue<D>(page_src(page_id(0)), slot0, lane, tq3_head_bytes(D));
+      stage_issue<D>(page_src(first_id), slot0, lane, tq3_head_bytes(D));   // = page_id(0), from the chunk entry
     } else {
-      const uint8_t* p0 = page_src(page_id(0));
+      const uint8_t* p0 = page_src(first_id);
       stage_issue<D>(p0, slot0, lane, kPage * D);
       stage_issue<D>(p0 + kPage * D, slot1, lane, kPage * D);
     }
@@ -795,24 +795,36 @@ __global__ void __launch_bounds__(kThreads)
         float qscale, Plan plan, AppendIn ap) {
   __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
 
+  static_assert(kWaves <= 4, "a chunk-table entry holds the first page of 4 waves");
+  const int nblk = MQ ? plan.nblk : 1;
+  // Items: the TQ3 ones first, then the FP8 ones; within a format item
+  // ((chunk L + layer) Hkv + h) nblk + blk, so an item's chunk does not depend
+  // on the chunk counts and the TQ3 entry of the workgroup's first item is
+  // requested together with those counts (clamped into the table; used only if
+  // the item turns out to be a TQ3 one).
+  // (32-bit unsigned index arithmetic: items per launch stay far below 2^31)
+  const unsigned per_chunk = (unsigned)(n_layers * hkv * nblk);
+  const cptr_i8 tab_t = (cptr_i8)plan.chunks_t, tab_f = (cptr_i8)plan.chunks_f;
+  const int spec = (int)(blockIdx.x / per_chunk);
+  const i8v cd_spec = (MODE != kFp8Only && plan.table_cap > 0) ? tab_t[spec < plan.table_cap ? spec : plan.table_cap - 1]
+                                                                : i8v{};
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
-  const int nblk = MQ ? plan.nblk : 1;
-  const long items_f = (long)n_layers * hkv * ncf * nblk;
-  const long items_t = (long)n_layers * hkv * nct * nblk;
-  const long items = items_f + items_t;
+  const unsigned items_t = per_chunk * nct;
+  const unsigned items = per_chunk * ncf + items_t;
 
-  for (long item = blockIdx.x; item < items; item += gridDim.x) {
-    const bool tq3 = item >= items_f;
-    const long it = tq3 ? item - items_f : item;
-    const int nch = tq3 ? nct : ncf;
-    const int blk = MQ ? (int)(it % nblk) : 0;
-    const long itc = MQ ? it / nblk : it;
-    const int h = (int)(itc % hkv);
-    const int chunk = (int)((itc / hkv) % nch);
-    const int layer = (int)(itc / ((long)hkv * nch));
-    const i4v cd = ((cptr_i4)(tq3 ? plan.chunks_t : plan.chunks_f))[chunk];
+  for (unsigned item = blockIdx.x; item < items; item += gridDim.x) {
+    const bool tq3 = item < items_t;
+    const unsigned it = tq3 ? item : item - items_t;
+    const int blk = MQ ? (int)(it % (unsigned)nblk) : 0;
+    const unsigned itc = MQ ? it / (unsigned)nblk : it;
+    const int h = (int)(itc % (unsigned)hkv);
+    const int layer = (int)((itc / (unsigned)hkv) % (unsigned)n_layers);
+    const int chunk = (int)(itc / (unsigned)(hkv * n_layers));
+    const i8v cd = (tq3 && item == blockIdx.x) ? cd_spec : (tq3 ? tab_t : tab_f)[chunk];
     const int b = cd[0], start = cd[1], count = chunk_pages(cd[2]), last_tok = chunk_last_tok(cd[2]), pidx = cd[3];
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int first_id = wv == 0 ? cd[4] : (wv == 1 ? cd[5] : (wv == 2 ? cd[6] : cd[7]));
     const bool holds_tail = (cd[2] & kChunkHoldsTail) != 0;
     if (pidx >= plan.np_cap) {               // plan made for fewer layers than this call
       if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
@@ -832,10 +844,10 @@ __global__ void __launch_bounds__(kThreads)
       rb.req_last = req[R_TAIL * rowlen + b];
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, smem,
+      run_item<D, true, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id, smem,
                                 nullptr, rb);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx,
+      run_item<D, false, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
                                  smem, (!MQ && holds_tail) ? &ap : nullptr, rb);
     __syncthreads();
   }
@@ -849,8 +861,8 @@ template <int MODE, bool MQ, int RB>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
                             hipStream_t stream) {
-  const long per_fmt = (long)n_layers * g.hkv * (plan.np_cap / 2) * (MQ ? plan.nblk : 1);
-  const dim3 grid = attend_grid(MODE == kBoth ? 2 * per_fmt : per_fmt), block(kThreads);
+  // partials per layer bound the items of either format, or of both together
+  const dim3 grid = attend_grid((long)n_layers * g.hkv * plan.np_cap * (MQ ? plan.nblk : 1)), block(kThreads);
   if (g.d == 256)
     hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                        q_ls, qscale, plan, ap);

@@ -240,7 +240,11 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const bool holds_tail = local == nchunks - 1 && lastfmt[b] == fmt;
       const int last_tok = holds_tail ? tail[b] : 16;
       const int pidx = po[b] + (fmt ? (cf[b + 1] - cf[b]) : 0) + local;
-      out[c] = make_int4(b, bt_offsets[b] + start, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
+      const int first = bt_offsets[b] + start;
+      const int* lst = fmt ? plan.list_t : plan.list_f;
+      out[2 * c] = make_int4(b, first, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
+      out[2 * c + 1] = make_int4(lst[first], lst[first + min(1, count - 1)], lst[first + min(2, count - 1)],
+                                 lst[first + min(3, count - 1)]);
     }
   }
 }
