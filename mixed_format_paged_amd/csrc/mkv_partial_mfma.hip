@@ -149,13 +149,25 @@ __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slo
 #pragma unroll
   for (int i = 0; i < Geo<D>::kRows; ++i) {
     uint32_t off = 1024 * i + l16;
-    if (off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
+    if (1024 * (i + 1) > bytes && off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
     // the (wave-uniform) unit address in an SGPR pair, the lane's 32-bit
     // offset in a VGPR; M0 holds the LDS row base, with one wait state
     // between the M0 write and the LDS-DMA load that reads it
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
                  :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
   }
+}
+
+// Issue priority of the wave from its progress through the page loop: the
+// hardware issues from the oldest wave first, so workgroups dispatched later
+// to a CU would lag; raising the priority of the waves with the most pages
+// left keeps the workgroups sharing a CU finishing together.
+__device__ inline void progress_prio(int k, int n) {
+  const int left = 4 * (n - k) / (n > 0 ? n : 1);   // 4 .. 1
+  if (left >= 4) __builtin_amdgcn_s_setprio(3);
+  else if (left == 3) __builtin_amdgcn_s_setprio(2);
+  else if (left == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // Wait until at most N vector-memory instructions of this wave are in flight.
@@ -311,8 +323,8 @@ struct RowBlock {
 // each token.  The offset -4 s(t, g) sum_{c in g} q(c), summed over the
 // groups, is one 16x16x16 MFMA that seeds the scores: A = the token scales
 // (token n = lane & 15, k = 4 j + e -> group (4 j + e) % NG), B = kneg (the
-// lane's query row, minus the group sums of q as fp16 hi / lo parts, built
-// once per item).
+// lane's query row, minus four times the group sums of q as fp16 hi / lo
+// parts, built once per item; the power of two keeps both parts exact).
 template <int D, int RB = 8>
 __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j, h4 kneg) {
   constexpr int NG = Geo<D>::NG, GB = 3 * NG;       // bytes of a lane's code chunk
@@ -323,8 +335,6 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 #pragma unroll
   for (int e = 0; e < 4; ++e) as[e] = lds_load<_Float16>(sp + 8 * e);
   f4 s = __builtin_amdgcn_mfma_f32_16x16x16f16(as, kneg, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) s[r] *= 4.0f;
   auto k_scales = [&](int g) { return lds_load<u2>(pg + 12 * D + 8 * (j * NG + g)); };  // tokens 4j..4j+3
   h8 bq = sq[lane];
   h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;
@@ -584,8 +594,8 @@ __device__ __forceinline__ void run_item(
   }
   __syncthreads();
 
-  // TQ3: B operand of the offset MFMA.  Lane (n, j), k = 4 j + e: minus the
-  // sum of query row n's q over group (4 j + e) % NG, fp16 hi for k < NG, the
+  // TQ3: B operand of the offset MFMA.  Lane (n, j), k = 4 j + e: minus four
+  // times the sum of query row n's q over group (4 j + e) % NG, fp16 hi for k < NG, the
   // remainder for NG <= k < 2 NG, 0 beyond.  The group sums come from MFMAs
   // of the q fragments with a matrix of ones (every output row holds them).
   h4 kneg = h4{};
@@ -603,7 +613,7 @@ __device__ __forceinline__ void run_item(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int k = 4 * j + e;
-      const float x = -qs[e];
+      const float x = -4.0f * qs[e];       // the -4 code offset, times the group sum
       const _Float16 hi = (_Float16)x;
       const _Float16 lo = (_Float16)(x - (float)hi);
       kneg[e] = k < NG ? hi : (k < 2 * NG ? lo : (_Float16)0.0f);
@@ -625,6 +635,7 @@ __device__ __forceinline__ void run_item(
     // two slots: page k+1 travels while page k is computed
     int id_next = page_id(1);                 // page ids travel one page ahead of their loads
     for (int k = 0; k < my_pages; ++k) {
+      progress_prio(k, my_pages);
       uint8_t* const cur = (k & 1) ? slot1 : slot0;
       uint8_t* const nxt = (k & 1) ? slot0 : slot1;
       if (k + 1 < my_pages) {                 // wave-uniform
@@ -648,6 +659,7 @@ __device__ __forceinline__ void run_item(
     // page k is computed, and V of page k+1 while K of page k+1 is
     int id_next = page_id(1);
     for (int k = 0; k < my_pages; ++k) {
+      progress_prio(k, my_pages);
       wait_vmem<kRows>();                     // K of page k has landed
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;
@@ -669,6 +681,7 @@ __device__ __forceinline__ void run_item(
       if (more) stage_issue<D>(pn + kPage * D, slot1, lane, kPage * D);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   wait_vmem<0>();                               // no staging load may land after this point
   __syncthreads();                              // the staging block becomes the merge buffer
 
