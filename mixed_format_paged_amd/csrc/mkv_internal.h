@@ -74,8 +74,8 @@ struct Plan {
   int32_t* list_t;      // [bt_capacity] TQ3 slot ids (id - n_fp8)
   int4* chunks_f;       // [chunk_cap][2]: descriptor, first page ids
   int4* chunks_t;       // [chunk_cap][2]
-  float* part_ml;       // [L][np_cap][Hkv][G][2]  (m in log2 units, l)
-  float* part_acc;      // [L][np_cap][Hkv][G][d]
+  float* part_ml;       // [L][Hkv][np_cap][R][2]  (m in log2 units, l); part_ml_index
+  float* part_acc;      // [L][Hkv][d / 32][np_cap][R][32]; part_acc_index
   int batch;
   int bt_capacity;
   int table_cap;        // chunk-table entries per format (independent of the layer count)
@@ -89,6 +89,18 @@ struct Plan {
   int nblk;
   int rowblk;           // rows per block: 8, or 16 for multi-query with more than 8 rows
 };
+// Partial-state layout: the states one merge workgroup reads (one layer, KV
+// head and 32-channel slice; a request's consecutive partials; all R rows)
+// form one contiguous run, R * 32 floats per partial.
+constexpr int kStateSlice = 32;
+__host__ __device__ inline size_t part_acc_index(int np_cap, int hkv, int d, int R, int layer, int h, int pidx,
+                                                 int row, int c) {
+  return ((((size_t)layer * hkv + h) * (d / kStateSlice) + c / kStateSlice) * np_cap + pidx) * (size_t)R * kStateSlice +
+         (size_t)row * kStateSlice + c % kStateSlice;
+}
+__host__ __device__ inline size_t part_ml_index(int np_cap, int hkv, int R, int layer, int h, int pidx, int row) {
+  return ((((size_t)layer * hkv + h) * np_cap + pidx) * (size_t)R + row) * 2;
+}
 constexpr int kRowBlock = 8;          // query rows of one work item (MFMA rows 0..7, their remainders 8..15)
 constexpr int kMaxQuery = 16;         // query tokens per request
 

@@ -30,7 +30,7 @@ __device__ inline const int* req_row(const Plan& p, int field) { return p.req + 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
-constexpr int kSliceC = 32;                      // channels per workgroup
+constexpr int kSliceC = kStateSlice;             // channels per workgroup: one slice of the state layout
 constexpr int kQuads = kSliceC / 4;              // float4 columns of a slice
 constexpr int kSubs = kThreads / (kMaxG * kQuads);   // threads sharing one (head, float4 column)
 constexpr int kReg = 16;                         // partial states (float4) a thread requests at once
@@ -40,7 +40,9 @@ constexpr int kReg = 16;                         // partial states (float4) a th
 // Thread t takes float4 column q = t % kQuads of the slice, query row
 // i = (t / kQuads) % kMaxG of the row group (idle past its rows) and every kSubs-th partial from
 // sub = t / (kQuads kMaxG): its loads are 16-byte vectors, and the kQuads
-// threads of one (partial, head) read one contiguous 128-byte line.
+// threads of one (partial, row) read one contiguous 128-byte line; in the
+// state layout (part_acc_index) the rows and then the partials of a request
+// follow one another, so a workgroup's states are one contiguous run.
 template <int D>
 __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int Gh, Plan plan,
                                                          float* __restrict__ out, float* __restrict__ lse,
@@ -52,40 +54,49 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   __shared__ f4v sa[kThreads];                  // per-thread weighted sums, [sub][i][q]
   __shared__ float sm[kThreads], sl[kThreads];  // per-thread maxima and denominators
   const int B = plan.batch;
-  const int* poff = req_row(plan, R_POFF);
-  const int* inval = req_row(plan, R_INVALID);
+  // per-request plan fields through the constant address space: (uniform)
+  // scalar loads, requested together
+  typedef const __attribute__((address_space(4))) int* cptr;
+  const cptr poff = (cptr)req_row(plan, R_POFF);
+  const cptr inval = (cptr)req_row(plan, R_INVALID);
   const int hq = hkv * Gh;
   const int tid = threadIdx.x;
   const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
-  const long items = (long)n_layers * B * hkv * NRG * NS;
+  // 32-bit unsigned item arithmetic (far below 2^31 items per launch)
+  const unsigned items = (unsigned)(n_layers * B * hkv * NRG * NS);
   // output element of row r of request b, KV head h
   auto out_at = [&](int layer, int b, int h, int r) {
     const int t = r / Gh;
     return ((size_t)(b * T + t) * hq + (size_t)h * Gh + (r - t * Gh));
   };
-  for (long item = blockIdx.x; item < items; item += gridDim.x) {
+  for (unsigned item = blockIdx.x; item < items; item += gridDim.x) {
     const int cs = (int)(item % NS);
-    const int rg = (int)((item / NS) % NRG);
-    const int h = (int)((item / ((long)NS * NRG)) % hkv);
-    const int b = (int)((item / ((long)NS * NRG * hkv)) % B);
-    const int layer = (int)(item / ((long)NS * NRG * hkv * B));
+    const unsigned irg = item / NS;
+    const int rg = (int)(irg % (unsigned)NRG);
+    const unsigned ih = irg / (unsigned)NRG;
+    const int h = (int)(ih % (unsigned)hkv);
+    const unsigned ib = ih / (unsigned)hkv;
+    const int b = (int)(ib % (unsigned)B);
+    const int layer = (int)(ib / (unsigned)B);
     const int r0 = rg * kMaxG;
     const int G = R - r0 < kMaxG ? R - r0 : kMaxG;          // rows of this group
     const bool live = pi < G;
-    const int p0 = poff[b], np = poff[b + 1] - poff[b];
+    const int p0 = poff[b], np = poff[b + 1] - p0;
+    const int bad = inval[b];
     float* out_row = out + layer * out_ls + out_at(layer, b, h, r0 + (live ? pi : 0)) * D + cs * kSliceC;
     float* lse_l = lse ? lse + layer * lse_ls : nullptr;
-    if (inval[b] || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
-      const bool nan = inval[b] != 0 || np != 0;
+    if (bad || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
+      const bool nan = bad != 0 || np != 0;
       if (sub == 0 && live)
         *reinterpret_cast<f4v*>(out_row + 4 * qc) = nan ? f4v{NAN, NAN, NAN, NAN} : f4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (cs == 0 && lse_l && tid < G) lse_l[out_at(layer, b, h, r0 + tid)] = nan ? __int_as_float(0x7fc00000) : -INFINITY;
       continue;
     }
-    const size_t sstride = (size_t)hkv * R;                 // states between consecutive partials
-    const size_t st0 = ((size_t)layer * plan.np_cap * hkv + (size_t)p0 * hkv + h) * R + r0;
-    const float* ml = plan.part_ml + (st0 + (live ? pi : 0)) * 2;
-    const float* acc = plan.part_acc + st0 * D + cs * kSliceC + (size_t)(live ? pi : 0) * D + 4 * qc;
+    // a request's partials are consecutive: R rows of (m, l) and R * 32 floats of
+    // the slice's states per partial, one contiguous run
+    const int row = r0 + (live ? pi : 0);
+    const float* ml = plan.part_ml + part_ml_index(plan.np_cap, hkv, R, layer, h, p0, row);
+    const float* acc = plan.part_acc + part_acc_index(plan.np_cap, hkv, D, R, layer, h, p0, row, cs * kSliceC + 4 * qc);
     // 1 + 2: this thread's share, partials sub, sub + kSubs, ..., kReg at a time
     float Mt = -INFINITY, Lt = 0.0f;
     f4v at = f4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -98,8 +109,8 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
       for (int k = 0; k < kReg; ++k) {
         const size_t p = (size_t)(sub + (k0 + k) * kSubs);
         if (k < cnt) {
-          av[k] = *reinterpret_cast<const f4v*>(acc + p * sstride * D);
-          const float2 m_l = *reinterpret_cast<const float2*>(ml + p * sstride * 2);
+          av[k] = *reinterpret_cast<const f4v*>(acc + p * R * kSliceC);
+          const float2 m_l = *reinterpret_cast<const float2*>(ml + p * R * 2);
           mv[k] = m_l.x;
           lv[k] = m_l.y;
         } else {

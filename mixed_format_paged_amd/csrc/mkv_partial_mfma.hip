@@ -704,9 +704,11 @@ __device__ __forceinline__ void run_item(
     sM[threadIdx.x] = M;
   }
   __syncthreads();
-  const size_t pslot = (((size_t)layer * plan.np_cap + pidx) * hkv + h) * rb.R + rb.r0;
-  float* __restrict__ ml = plan.part_ml + pslot * 2;
-  float* __restrict__ pa_out = plan.part_acc + pslot * D;
+  // this block's rows from r0 (part_acc_index / part_ml_index layout)
+  float* __restrict__ ml = plan.part_ml + part_ml_index(plan.np_cap, hkv, rb.R, layer, h, pidx, rb.r0);
+  float* __restrict__ pa_out = plan.part_acc + part_acc_index(plan.np_cap, hkv, D, rb.R, layer, h, pidx, rb.r0, 0);
+  const size_t slice_stride = (size_t)plan.np_cap * rb.R * kStateSlice;   // between 32-channel slices
+  auto state_at = [&](int i, int c) { return (size_t)(c / kStateSlice) * slice_stride + i * kStateSlice + c % kStateSlice; };
   const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
   if constexpr (RB == 16) {
     // 16 real rows, lane (n, j) holding rows 4j .. 4j + 3: rows 0..7 (j < 2),
@@ -732,7 +734,7 @@ __device__ __forceinline__ void run_item(
         float acc = 0.0f;
 #pragma unroll 4
         for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-        __builtin_nontemporal_store(acc, pa_out + (size_t)8 * pass * D + idx);
+        __builtin_nontemporal_store(acc, pa_out + state_at(8 * pass + i, c));
       }
       __syncthreads();                                  // the layout is rewritten by the next pass
     }
@@ -767,14 +769,13 @@ __device__ __forceinline__ void run_item(
   }
   __syncthreads();
 
-  // partial states [layer][partial][KV head][R rows]; this block's rows from r0
   for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
     const int i = idx / D, c = idx - (idx / D) * D;
     const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
     float acc = 0.0f;
 #pragma unroll 4
     for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-    __builtin_nontemporal_store(acc, pa_out + idx);   // streamed out: read once, by the merge
+    __builtin_nontemporal_store(acc, pa_out + state_at(i, c));   // streamed out: read once, by the merge
   }
   }
   if (threadIdx.x < rb.rows) {

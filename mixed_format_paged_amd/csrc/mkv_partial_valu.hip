@@ -117,14 +117,12 @@ __global__ void __launch_bounds__(256) partial_valu_kernel(
       }
       __syncthreads();
     }
-    const size_t slot = ((size_t)layer * plan.np_cap + pidx) * hkv + h;
-    float* ml = plan.part_ml + slot * G * 2;
-    float* pa = plan.part_acc + slot * G * D;
+    float* ml = plan.part_ml + part_ml_index(plan.np_cap, hkv, G, layer, h, pidx, 0);
     if (tid < G) { ml[2 * tid] = m_s[tid]; ml[2 * tid + 1] = l_s[tid]; }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int idx = tid + 256 * k;
-      if (idx < G * D) pa[idx] = acc[k];
+      if (idx < G * D) plan.part_acc[part_acc_index(plan.np_cap, hkv, D, G, layer, h, pidx, idx / D, idx % D)] = acc[k];
     }
     __syncthreads();
   }
