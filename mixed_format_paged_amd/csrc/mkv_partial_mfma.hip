@@ -272,8 +272,12 @@ struct WaveState {
       for (int r = 0; r < 4; ++r)
         if (4 * j + r >= ntok) s[r] = -INFINITY;
     }
-    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    pm = max_xor32(max_xor16(pm));
+    // the lane's own maximum decides whether any row must move its running
+    // max (a row's max exceeds m_run + kRescale iff one of its lanes' does);
+    // the row maximum itself, over the four lanes of the column, is needed
+    // only on a wave's first page and when some row moves
+    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const float pm = (first || __any(lm > m_run + kRescale)) ? max_xor32(max_xor16(lm)) : lm;
     const bool need = pm > m_run + kRescale;
     if (first) {
       m_run = pm;
