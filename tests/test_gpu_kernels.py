@@ -101,6 +101,38 @@ def test_demote_bitexact_random_bytes(d):
         assert np.array_equal(got, pool.tq3), (ks, vs, np.argwhere(got != pool.tq3)[:5])
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_demote_layers_many_items(d):
+    # several thousand (layer, page, head) items, more than the workgroups the
+    # GPU holds at once, so each workgroup takes several items and prefetches;
+    # three layers with their own scales in one launch, ids permuted
+    hq, hkv, n, L = 24, 4, 700, 3
+    rng = np.random.default_rng(100 + d)
+    pb = OL.fp8_page_bytes(hkv, d)
+    scales = [(1.0, 1.0), (0.25, 3.0), (7.0, 0.5)]
+    raws, pools, ref = [], [], []
+    src = rng.permutation(n)[: n - 50]                   # not every FP8 slot, in random order
+    dst = n + rng.permutation(n)[: n - 50]
+    for l in range(L):
+        raw = rng.integers(0, 256, (n, pb)).astype(np.uint8)
+        raw[(raw & 0x7F) == 0x7F] = 0x7E
+        pool = OP.Pool(hkv, d, n, n, *scales[l])
+        pool.fp8[:] = raw
+        OP.demote(pool, src, dst)
+        ref.append(pool.tq3)
+        fp8 = torch.as_tensor(raw, device="cuda")
+        tq3 = torch.zeros((n, OL.tq3_page_bytes(hkv, d)), dtype=torch.uint8, device="cuda")
+        tier = torch.zeros(2 * n, dtype=torch.uint8, device="cuda")
+        raws.append((fp8, tq3, tier))
+        pools.append(M.make_pool(fp8, tq3, tier, n, n, *scales[l]))
+    M.mkv_demote_pages_layers((hq, hkv, d), pools, torch.as_tensor(src, dtype=torch.int32, device="cuda"),
+                              torch.as_tensor(dst, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for l in range(L):
+        got = raws[l][1].cpu().numpy()
+        assert np.array_equal(got, ref[l]), (l, np.argwhere(got != ref[l])[:5])
+
+
 def test_build_gather_and_decode_tiny(kind):
     w = W.WORKLOADS["tiny-1x1024-d128"]
     st, dw, ref = _both(w)
