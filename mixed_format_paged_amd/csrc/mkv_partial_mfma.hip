@@ -394,14 +394,14 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 // (token 4j + (e & 3), part e >> 2) with P repeated for the two parts.  The
 // lane's column keeps one V scale group in every tile, so W += P s (one
 // 16x16x16 MFMA, B = the group's scales of tokens 4j..4j+3) holds what the -4
-// offset takes off each of its tiles.
+// offset takes off each of its tiles.  vw: the lane's V code words, block b
+// in vw[b] (read from the staged page by the caller, ahead of the scores).
 template <int D, int RB = 8>
 __device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], f4& W, int lane, int j,
-                              h4 pl = h4{}) {
-  constexpr int NG = Geo<D>::NG, GB = 3 * NG;
+                              const uint32_t (&vw)[Geo<D>::NG / 4][3], h4 pl = h4{}) {
+  constexpr int NG = Geo<D>::NG;
   const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
   const h8 pl2 = __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3);   // RB 16: P's remainder
-  const uint8_t* vp = pg + 6 * D + lane * GB;
   const int gn = (lane & 15) * D / 512;      // the lane's V channel group
   const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
   const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
@@ -410,9 +410,7 @@ __device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], f4&
   if (RB == 16) W = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, sv4, W, 0, 0, 0);
 #pragma unroll
   for (int b = 0; b < NG / 4; ++b) {
-    const uint32_t w0 = lds_load<uint32_t>(vp + 12 * b), w1 = lds_load<uint32_t>(vp + 12 * b + 4),
-                   w2 = lds_load<uint32_t>(vp + 12 * b + 8);
-    const u16v u = __builtin_bit_cast(u16v, decode32(w0, w1, w2));
+    const u16v u = __builtin_bit_cast(u16v, decode32(vw[b][0], vw[b][1], vw[b][2]));
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int pp = 4 * b + q4;
@@ -653,10 +651,17 @@ __device__ __forceinline__ void run_item(
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
+      // this lane's V code words (its 3 NG bytes of the V code stream),
+      // requested before the scores so they have landed by the P V step
+      uint32_t vw[NG / 4][3];
+#pragma unroll
+      for (int b = 0; b < NG / 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) vw[b][i] = lds_load<uint32_t>(cur + 6 * D + lane * 3 * NG + 12 * b + 4 * i);
       const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, kneg);
       h4 pl;
       const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
-      tq3_pv<D, RB>(cur, pa, st.O, st.W, lane, j, pl);
+      tq3_pv<D, RB>(cur, pa, st.O, st.W, lane, j, vw, pl);
     }
   } else {
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
