@@ -395,15 +395,14 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 // lane's column keeps one V scale group in every tile, so W += P s (one
 // 16x16x16 MFMA, B = the group's scales of tokens 4j..4j+3) holds what the -4
 // offset takes off each of its tiles.  vw: the lane's V code words, block b
-// in vw[b] (read from the staged page by the caller, ahead of the scores).
+// in vw[b]; svv: the lane's V scales (its column's group, tokens 4j..4j+3);
+// both read from the staged page by the caller, ahead of the scores.
 template <int D, int RB = 8>
-__device__ inline void tq3_pv(const uint8_t* pg, h4 pa, f4 (&O)[Geo<D>::NT], f4& W, int lane, int j,
-                              const uint32_t (&vw)[Geo<D>::NG / 4][3], h4 pl = h4{}) {
+__device__ inline void tq3_pv(h4 pa, f4 (&O)[Geo<D>::NT], f4& W, int lane, int j,
+                              const uint32_t (&vw)[Geo<D>::NG / 4][3], u2 svv, h4 pl = h4{}) {
   constexpr int NG = Geo<D>::NG;
   const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
   const h8 pl2 = __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3);   // RB 16: P's remainder
-  const int gn = (lane & 15) * D / 512;      // the lane's V channel group
-  const u2 svv = lds_load<u2>(pg + 13 * D + 8 * (j * NG + gn));
   const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
   const h4 sv4 = __builtin_bit_cast(h4, svv);
   W = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, sv4, W, 0, 0, 0);
@@ -658,10 +657,11 @@ __device__ __forceinline__ void run_item(
       for (int b = 0; b < NG / 4; ++b)
 #pragma unroll
         for (int i = 0; i < 3; ++i) vw[b][i] = lds_load<uint32_t>(cur + 6 * D + lane * 3 * NG + 12 * b + 4 * i);
+      const u2 svv = lds_load<u2>(cur + 13 * D + 8 * (j * NG + (lane & 15) * D / 512));   // V scales of the lane's group
       const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, kneg);
       h4 pl;
       const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
-      tq3_pv<D, RB>(cur, pa, st.O, st.W, lane, j, vw, pl);
+      tq3_pv<D, RB>(pa, st.O, st.W, lane, j, vw, svv, pl);
     }
   } else {
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
