@@ -262,9 +262,10 @@ int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n
  *  lse (nullable): [n_layers][batch][n_query][num_q_heads].
  *  ws_bytes >= mkv_decode_workspace_bytes_multi(layout, batch->batch,
  *  batch->bt_capacity, n_layers, n_query).  The query rows of a KV head
- *  (n_query * G) are taken 8 at a time: one split-K work item per chunk, KV
- *  head and 8 rows, so a page is read ceil(n_query * G / 8) times, not
- *  n_query times.  n_query == 1 is mkv_decode_attn_layers.  Needs the
+ *  (n_query * G) are taken 8 at a time when there are at most 8 of them,
+ *  else 16 at a time: one split-K work item per chunk, KV head and row
+ *  block, so a page is read ceil(n_query * G / 16) times (once for up to 8
+ *  rows), not n_query times.  n_query == 1 is mkv_decode_attn_layers.  Needs the
  *  matrix-core kernels for n_query > 1 (MKV_ERR_RANGE otherwise). */
 size_t mkv_decode_workspace_bytes_multi(const mkv_layout* layout, int32_t batch,
                                         int32_t bt_capacity, int32_t n_layers, int32_t n_query);
