@@ -463,10 +463,10 @@ def main():
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
     result = {
-        "metric": "decode-attn KV GB/s at 2x59,008 ctx, 16 layers (tokens/s and % of MI355X HBM peak alongside)",
+        "metric": "decode-attn KV GB/s + tokens/s at 2x59,008 ctx, 16 layers; % MI355X HBM peak",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32 accumulate over fp8-e4m3 / 3-bit TQ3 cache", "data": "synthetic",
+        "dtype": "f16 mfma operands, f32 accumulate", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq_len": int(st.seq_lens[0]), "layers": w.L,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "page": 16,
                    "fp8_pages_per_request": int(st.n_pages[0] - (st.tiers[:st.n_pages[0]] == 2).sum()),
