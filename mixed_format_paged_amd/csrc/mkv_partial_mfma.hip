@@ -650,17 +650,24 @@ __device__ __forceinline__ void run_item(
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
-      // this lane's V code words (its 3 NG bytes of the V code stream),
-      // requested before the scores so they have landed by the P V step
+      // this lane's V code words (its 3 NG bytes of the V code stream) and the
+      // V scales of its column's group: with 8-row blocks they are requested
+      // before the scores, so they have landed by the P V step; the 16-row
+      // instance has no registers to spare and reads them after the softmax
       uint32_t vw[NG / 4][3];
+      u2 svv;
+      auto read_v = [&]() {
 #pragma unroll
-      for (int b = 0; b < NG / 4; ++b)
+        for (int b = 0; b < NG / 4; ++b)
 #pragma unroll
-        for (int i = 0; i < 3; ++i) vw[b][i] = lds_load<uint32_t>(cur + 6 * D + lane * 3 * NG + 12 * b + 4 * i);
-      const u2 svv = lds_load<u2>(cur + 13 * D + 8 * (j * NG + (lane & 15) * D / 512));   // V scales of the lane's group
+          for (int i = 0; i < 3; ++i) vw[b][i] = lds_load<uint32_t>(cur + 6 * D + lane * 3 * NG + 12 * b + 4 * i);
+        svv = lds_load<u2>(cur + 13 * D + 8 * (j * NG + (lane & 15) * D / 512));
+      };
+      if constexpr (RB == 8) read_v();
       const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, kneg);
       h4 pl;
       const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
+      if constexpr (RB == 16) read_v();
       tq3_pv<D, RB>(pa, st.O, st.W, lane, j, vw, svv, pl);
     }
   } else {
