@@ -12,6 +12,8 @@ import torch
 from . import (Layout, TIER_FREE, TIER_STALE, make_pool, mkv_append, mkv_demote_pages,
                mkv_fp8_page_bytes, mkv_tq3_page_bytes, _layout)
 
+APPEND_MAX = 65520        # tokens per mkv_append call when filling a request (a whole number of pages)
+
 
 class PagedCache:
     def __init__(self, layout, n_layers, n_fp8, n_tq3, device="cuda", k_scale=1.0, v_scale=1.0):
@@ -37,13 +39,17 @@ class PagedCache:
 
     def fill_request(self, layer, k, v, fp8_pages):
         """Write one request's tokens k, v [T][Hkv][d] (fp32, device) from
-        position 0 onward onto the FP8 pages `fp8_pages` (int32, device)."""
+        position 0 onward onto the FP8 pages `fp8_pages` (int32, device), in
+        appends of at most APPEND_MAX tokens (mkv_append takes up to 65535)."""
         n_pages = fp8_pages.numel()
         dev = k.device
         offs = torch.tensor([0, n_pages], dtype=torch.int32, device=dev)
-        pos = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.append(layer, k.unsqueeze(0).contiguous(), v.unsqueeze(0).contiguous(), offs,
-                    fp8_pages.contiguous(), pos)
+        pages = fp8_pages.contiguous()
+        for t0 in range(0, k.shape[0], APPEND_MAX):
+            t1 = min(k.shape[0], t0 + APPEND_MAX)
+            pos = torch.tensor([t0], dtype=torch.int32, device=dev)
+            self.append(layer, k[t0:t1].unsqueeze(0).contiguous(), v[t0:t1].unsqueeze(0).contiguous(), offs,
+                        pages, pos)
 
     def retier_demoted(self, src_fp8, dst_tq3):
         """After demotion on every layer: dst pages become Stale, src slots free."""

@@ -1,0 +1,110 @@
+"""Parity at the full workload sizes, on sampled outputs.
+
+The workloads are built on the GPU at their real sizes and decoded through the
+C ABI; a few (layer, request, KV head) units, drawn with a fixed seed, are
+checked one by one against the oracle's value path (quantise -> dequantise,
+pinned against the byte path in the oracle's own tests) and its fp64 dense
+attention.  The canary runs exactly the step bench.py times: the plan, then
+for each of its 16 layers the step's new token appended inside the attention
+launch followed by the merge, then the demotion of the pages leaving the
+recent window.  Bar: max-abs 2e-3 and rel-L2 1e-3 on out, 1e-3 on lse.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_format_paged_amd as M
+import workloads as W
+from workloads.device_cache import DeviceWorkload
+from oracle import attention as OA, pool as OP
+
+from gpu_util import compare
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _picks(w, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({(int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(n)})
+
+
+def _check_units(w, st, picks, out, lse, new_kv=None, what=""):
+    """out [L][B][Hq][d], lse [L][B][Hq] (numpy); new_kv(l, b, h) -> (k, v) of a
+    token appended at position seq_len - 1, or None."""
+    G = w.Hq // w.Hkv
+    by_layer = {}
+    for l, b, h in picks:
+        by_layer.setdefault(l, []).append((b, h))
+    for l, items in by_layer.items():
+        vals = W.layer_values(w, st, l, device="cuda", requests={b for b, _ in items})
+        for b, h in items:
+            T = int(st.seq_lens[b])
+            k = vals["k"][b][:, h].clone()
+            v = vals["v"][b][:, h].clone()
+            if new_kv is not None and T > 0:
+                k[T - 1], v[T - 1] = new_kv(l, b, h)
+            tiers = st.tiers[st.bt_offsets[b]:st.bt_offsets[b + 1]]
+            is_tq3 = tiers == W.TIER_S
+            K = OP.quantized_values(k.cpu().numpy(), is_tq3, 1.0)
+            V = OP.quantized_values(v.cpu().numpy(), is_tq3, 1.0)
+            q = vals["q"][b, h * G:(h + 1) * G].cpu().numpy()
+            o_ref, lse_ref = OA.decode_attention(q, K[:, None, :], V[:, None, :])
+            compare(out[l, b, h * G:(h + 1) * G], o_ref, lse[l, b, h * G:(h + 1) * G], lse_ref,
+                    f"{what} layer {l} request {b} head {h}")
+        del vals
+        torch.cuda.empty_cache()
+
+
+def test_canary_full_size_bench_step():
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    w = W.WORKLOADS["canary-2x59008-16L"]
+    st = W.make_structure(w)
+    print(f"[fullsize] {w.name}: building", flush=True)
+    r = bench.Runner(w, st)
+    r.out.fill_(float("nan"))
+    r.lse.fill_(float("nan"))
+    r.step()
+    torch.cuda.synchronize()
+    assert M.mkv_workspace_status(r.ws) == 0
+    out, lse = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    picks = _picks(w, 4, 11)
+    print(f"[fullsize] {w.name}: checking {picks}", flush=True)
+    _check_units(w, st, picks, out, lse,
+                 new_kv=lambda l, b, h: (r.k_new[l, b, 0, h], r.v_new[l, b, 0, h]), what=w.name)
+    del r
+    torch.cuda.empty_cache()
+
+
+FULL = ["batch-8x16384", "ragged-32x4096-65536", "demote-64x32768", "long-1x131072"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_decode(name):
+    w = W.WORKLOADS[name]
+    st = W.make_structure(w)
+    print(f"[fullsize] {name}: building", flush=True)
+    dw = DeviceWorkload(w, st, "cuda")
+    dw.step_demote()                       # the aging pages of the demotion workload (none elsewhere)
+    layout = (w.Hq, w.Hkv, w.d)
+    ws = torch.empty(M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((w.B, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((w.B, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn(layout, dw.cache.pools[0], dw.batch(), dw.q[0].contiguous(), 1 / math.sqrt(w.d), out, lse, ws)
+    torch.cuda.synchronize()
+    assert M.mkv_workspace_status(ws) == 0
+    o, l = out.cpu().numpy()[None], lse.cpu().numpy()[None]
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    picks = _picks(w, 3, 12)
+    print(f"[fullsize] {name}: checking {picks}", flush=True)
+    _check_units(w, st, picks, o, l, what=name)
+    del dw, ws, out, lse
+    torch.cuda.empty_cache()
