@@ -10,9 +10,11 @@
 // Element values: FP8 page bf16_RNE(fl32(decode(e) * scale)); TQ3 page
 // bf16_RNE((u - 4) * s), where (u - 4) * s is exact in fp32 (11 + 3 bits).
 // One workgroup per (logical page, KV head): an FP8 page-head converts from
-// global memory directly; a TQ3 head block (14 d bytes) is first staged in
-// LDS, then each thread writes whole 16-byte chunks of 8 channels of one
-// token, so the stores of a workgroup are contiguous rows.
+// global memory directly (hardware E4M3 decode, exact); a TQ3 head block
+// (14 d bytes) is first staged in LDS, each thread decodes whole triples (8
+// codes, one 3-byte read) into a bf16 tile of the page-head in LDS, and then
+// every thread writes whole 16-byte chunks of 8 channels of one token, so the
+// stores of a workgroup are contiguous rows.
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -28,11 +30,6 @@ __device__ inline uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ inline uint32_t tq3_code_at(const uint8_t* blk, int off, int slot) {
-  const uint32_t w = blk[off] | ((uint32_t)blk[off + 1] << 8) | ((uint32_t)blk[off + 2] << 16);
-  return (w >> (3 * slot)) & 7u;
-}
-
 }  // namespace
 
 template <int D>
@@ -43,7 +40,10 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
     uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
   constexpr int C8 = D / 8;                          // 16-byte output chunks per token row
   constexpr int kChunks = 2 * kPage * C8;            // K and V chunks of a page-head
+  constexpr int G = D / 32;                          // 32-channel scale groups
+  constexpr int NTRI = 2 * D;                        // triples of K (and of V) in a head block
   __shared__ __align__(16) uint8_t blk[14 * D];
+  __shared__ __align__(16) uint16_t tile[2][kPage][D];   // bf16 bits of a TQ3 page-head, [K/V][token][channel]
   const int off0 = bt_offsets[b], off1 = bt_offsets[b + 1];
   const long units = (long)n_pages * hkv;
   for (long unit = blockIdx.x; unit < units; unit += gridDim.x) {
@@ -59,42 +59,66 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
                                                         (size_t)h * tq3_head_bytes(D));
       for (int e = threadIdx.x; e < 14 * D / 16; e += kThreads) reinterpret_cast<uint4*>(blk)[e] = src[e];
       __syncthreads();
+      // one triple (8 codes) per step: K triple x of row t holds channels
+      // 32 g + 8 j + e of token t (two scale groups), V triple x holds two
+      // channels of one group for the 4 tokens of a quarter (four scales);
+      // each value (u - 4) s (exact in fp32) goes to the bf16 tile
+      for (int tau = threadIdx.x; tau < 2 * NTRI; tau += kThreads) {
+        const bool isv = tau >= NTRI;
+        const int x = isv ? tau - NTRI : tau;
+        const int o = (isv ? 6 * D : 0) + 3 * x;
+        const uint32_t w = blk[o] | ((uint32_t)blk[o + 1] << 8) | ((uint32_t)blk[o + 2] << 16);
+        if (!isv) {
+          const int t = x / (D / 8), xr = x % (D / 8), j = xr / G, r = xr % G;
+          const int g0 = 4 * (r >> 2) + ((r >> 1) & 1), g1 = g0 + 2;     // slots s: group g0 + 2 (s & 1)
+          const float s0 = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + tq3_scale_off(D, 0, t, g0)));
+          const float s1 = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + tq3_scale_off(D, 0, t, g1)));
+          const int cb = 8 * j + 4 * (r & 1);
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            const float v = (float)((int)((w >> (3 * sl)) & 7u) - 4) * ((sl & 1) ? s1 : s0);
+            tile[0][t][32 * ((sl & 1) ? g1 : g0) + cb + (sl >> 1)] = (uint16_t)bf16_rne(v);
+          }
+        } else {
+          const int jq = x / (16 * G), rem = x % (16 * G), n = rem / G, p = rem % G;
+          const int c0 = n * (D / 16) + 2 * p, g = c0 / 32;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * jq + r;
+            const float sc = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + tq3_scale_off(D, 1, t, g)));
+#pragma unroll
+            for (int ci = 0; ci < 2; ++ci) {
+              const int sl = tq3_v_slot(ci, r);
+              tile[1][t][c0 + ci] = (uint16_t)bf16_rne((float)((int)((w >> (3 * sl)) & 7u) - 4) * sc);
+            }
+          }
+        }
+      }
+      __syncthreads();
     }
     for (int q = threadIdx.x; q < kChunks; q += kThreads) {
       const int kv = q / (kPage * C8), t = (q / C8) % kPage, c8 = q % C8;
-      uint32_t w[4];
+      uint4 o4;
       if (fp8) {
+        // exact E4M3 -> fp32 through the hardware conversion, then the scale
         const uint8_t* src = fp8_slab + (size_t)id * fp8_page_bytes(hkv, D) + ((size_t)(h * 2 + kv) * kPage + t) * D + 8 * c8;
         const uint2 e = *reinterpret_cast<const uint2*>(src);
         const float sc = kv ? v_scale : k_scale;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t word = i < 2 ? e.x : e.y;
-          const int sh = 16 * (i & 1);
-          const float lo = __fmul_rn(e4m3_decode((word >> sh) & 0xffu), sc);
-          const float hi = __fmul_rn(e4m3_decode((word >> (sh + 8)) & 0xffu), sc);
-          w[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
-        }
+        const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e.x, 1.0f, false);   // bytes 0, 1
+        const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e.x, 1.0f, true);    // bytes 2, 3
+        const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e.y, 1.0f, false);
+        const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e.y, 1.0f, true);
+        auto pk = [&](float a, float b2) { return bf16_rne(__fmul_rn(a, sc)) | (bf16_rne(__fmul_rn(b2, sc)) << 16); };
+        o4 = make_uint4(pk(f0[0], f0[1]), pk(f1[0], f1[1]), pk(f2[0], f2[1]), pk(f3[0], f3[1]));
       } else if (tq3) {
-        const int c0 = 8 * c8;
-        const float s = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + tq3_scale_off(D, kv, t, c0 >> 5)));
-        float x[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          int slot;
-          const int off = kv ? tq3_v_triple(D, t, c0 + k, &slot) : tq3_k_triple(D, t, c0 + k, &slot);
-          x[k] = (float)((int)tq3_code_at(blk, off, slot) - 4) * s;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = bf16_rne(x[2 * i]) | (bf16_rne(x[2 * i + 1]) << 16);
+        o4 = *reinterpret_cast<const uint4*>(&tile[kv][t][8 * c8]);
       } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = 0x7fc07fc0u;   // bf16 NaN: no page in the pool
+        o4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);   // bf16 NaN: no page in the pool
       }
       uint16_t* dst = (kv ? v_out : k_out) + ((size_t)(lp * kPage + t) * hkv + h) * D + 8 * c8;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst) = o4;
     }
-    if (tq3) __syncthreads();                        // blk is rewritten by the next unit
+    if (tq3) __syncthreads();                        // blk and tile are rewritten by the next unit
   }
 }
 
