@@ -15,6 +15,7 @@ written from the Minima-KV pages (arXiv 2608.23834, abstract on page 1; the
 * ``pool``      -- a byte-level page pool: append, FP8->TQ3 demotion, page-table gather
 * ``attention`` -- dense fp64 softmax decode attention and the log-sum-exp merge
 * ``dense``     -- bf16 rounding and the dense materialisation of pages
+* ``rotation``  -- the rotated TQ3 variant: sign flip and Walsh-Hadamard rotation
 
 Every floating-point step of attention is carried out in fp64 on the
 dequantised values; quantisation steps are done exactly (integer / exact

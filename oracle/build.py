@@ -11,9 +11,10 @@ import numpy as np
 from .pool import Pool, append, demote, TIER_R, TIER_S, TIER_FREE
 
 
-def build_layer(w, st, k_list, v_list, k_scale=1.0, v_scale=1.0):
-    """Returns (pool, bt_pages) for the state before the step's own demotion."""
-    pool = Pool(w.Hkv, w.d, st.n_fp8, st.n_tq3, k_scale, v_scale)
+def build_layer(w, st, k_list, v_list, k_scale=1.0, v_scale=1.0, signs=None):
+    """Returns (pool, bt_pages) for the state before the step's own demotion.
+    signs: rotated TQ3 pages (oracle/rotation.py) with this sign vector."""
+    pool = Pool(w.Hkv, w.d, st.n_fp8, st.n_tq3, k_scale, v_scale, signs=signs)
     bt = st.staging_ids.astype(np.int64).copy()
     pool.tier[bt] = TIER_R
     for b in range(w.B):

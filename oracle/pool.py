@@ -16,7 +16,7 @@ fp32 k_scale and one v_scale per layer.
 """
 import numpy as np
 
-from . import fp8, tq3
+from . import fp8, rotation, tq3
 from .layout import (PAGE, fp8_page_bytes, tq3_page_bytes, tq3_head_bytes, fp8_offset,
                      encode_tq3_head, decode_tq3_head)
 
@@ -26,8 +26,11 @@ TIER_R, TIER_A, TIER_S, TIER_FREE = 0, 1, 2, 0xFF
 class Pool:
     """One layer's pool: an FP8 slab, a TQ3 slab, and (shared) tier map."""
 
-    def __init__(self, num_kv_heads, d, n_fp8, n_tq3, k_scale=1.0, v_scale=1.0, tier=None):
+    def __init__(self, num_kv_heads, d, n_fp8, n_tq3, k_scale=1.0, v_scale=1.0, tier=None, signs=None):
+        """signs: None, or the layer's +-1 vector [d]: its TQ3 pages are rotated
+        (oracle/rotation.py)."""
         self.Hkv, self.d = num_kv_heads, d
+        self.signs = None if signs is None else np.asarray(signs, dtype=np.int8)
         self.n_fp8, self.n_tq3 = n_fp8, n_tq3
         self.fp8 = np.zeros((n_fp8, fp8_page_bytes(num_kv_heads, d)), dtype=np.uint8)
         self.tq3 = np.zeros((n_tq3, tq3_page_bytes(num_kv_heads, d)), dtype=np.uint8)
@@ -74,7 +77,9 @@ def demote(pool, src_fp8, dst_tq3):
 
     For every head, K and V, token and 32-channel group: quantise the FP8
     page's dequantised values with the TQ3 rule and write the head blocks.
-    The caller updates the block table and the tier map afterwards.
+    With pool.signs set, each (head, K/V, token) row of d values is rotated
+    first (rotation.rotate_f32).  The caller updates the block table and the
+    tier map afterwards.
     """
     d = pool.d
     G = d // tq3.GROUP
@@ -82,6 +87,8 @@ def demote(pool, src_fp8, dst_tq3):
         s, t = int(s), int(t)
         assert 0 <= s < pool.n_fp8 and pool.n_fp8 <= t < pool.n_fp8 + pool.n_tq3
         x = fp8_page_values(pool, s)                                # [Hkv][2][16][d]
+        if pool.signs is not None:
+            x = rotation.rotate_f32(x, pool.signs)
         u, sc = tq3.quantize_groups(x.reshape(pool.Hkv, 2, PAGE, G, tq3.GROUP))
         u = u.reshape(pool.Hkv, 2, PAGE, d)
         hb = tq3_head_bytes(d)
@@ -106,6 +113,8 @@ def page_values(pool, pid):
         G = pool.d // tq3.GROUP
         out[h, 0] = tq3.dequantize_groups(uK.reshape(PAGE, G, tq3.GROUP), sK).reshape(PAGE, pool.d)
         out[h, 1] = tq3.dequantize_groups(uV.reshape(PAGE, G, tq3.GROUP), sV).reshape(PAGE, pool.d)
+    if pool.signs is not None:
+        out = rotation.unrotate_f64(out, pool.signs)             # back to the channels of the cache
     return out
 
 
@@ -140,7 +149,7 @@ def gather_raw(pool, bt_offsets, bt_pages, b, n_pages):
     return out
 
 
-def quantized_values(x, page_is_tq3, scale):
+def quantized_values(x, page_is_tq3, scale, signs=None):
     """Value path without bytes: what one head's tokens dequantise to.
 
     x: fp32 [T][d] source values of one KV head (K or V) of one request;
@@ -148,7 +157,8 @@ def quantized_values(x, page_is_tq3, scale):
     decode(encode(x / scale)) * scale; TQ3 tokens quantise fl32(that FP8 value)
     with the TQ3 rule and give (u - 4) * s.  Float64 [T][d].  Used for samples
     of workloads too large to build as byte pools on the CPU; tests show it
-    equals the byte path.
+    equals the byte path.  signs: rotated TQ3 (rotate, quantise, dequantise,
+    rotate back in fp64).
     """
     x = np.asarray(x, dtype=np.float32)
     T, d = x.shape
@@ -158,6 +168,8 @@ def quantized_values(x, page_is_tq3, scale):
     tq = np.repeat(np.asarray(page_is_tq3, dtype=bool), PAGE)[:T]
     if tq.any():
         G = d // tq3.GROUP
-        u, s = tq3.quantize_groups(f32[tq].reshape(-1, G, tq3.GROUP))
-        out[tq] = tq3.dequantize_groups(u, s).reshape(-1, d)
+        y = f32[tq] if signs is None else rotation.rotate_f32(f32[tq], signs)
+        u, s = tq3.quantize_groups(y.reshape(-1, G, tq3.GROUP))
+        deq = tq3.dequantize_groups(u, s).reshape(-1, d)
+        out[tq] = deq if signs is None else rotation.unrotate_f64(deq, signs)
     return out
