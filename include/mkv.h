@@ -85,7 +85,21 @@ typedef struct {
  *  tier:     device, n_fp8 + n_tq3 bytes, shared by all layers.
  *  Physical ids [0, n_fp8) are FP8 slots, [n_fp8, n_fp8 + n_tq3) TQ3 slots;
  *  a page with tier R or A must have an FP8 id, tier S a TQ3 id.
- *  k_scale / v_scale: per-layer fp32 FP8 scales (value = decode(byte) * scale). */
+ *  k_scale / v_scale: per-layer fp32 FP8 scales (value = decode(byte) * scale).
+ *  tq3_signs: NULL, or device int8[head_dim] of +1 / -1 (16-byte aligned): the layer's TQ3
+ *            pages are "rotated TQ3".  The pages cite TurboQuant, which
+ *            rotates before scalar quantisation (page 1, Abstract and its
+ *            references); the rotated variant reads TQ3 that way.  Each
+ *            (token, KV head, K or V) row x of head_dim values is stored as the
+ *            TQ3 codes of y = c H (signs . x), H the Sylvester-Hadamard matrix
+ *            applied by the fast transform in fp32, stage s pairing channels i
+ *            and i + 2^s as (a + b, a - b) for s = 0, 1, ..., and c = 1/16 at
+ *            head_dim 256, 1/8 at 128 (oracle/rotation.py).  Demotion rotates;
+ *            single-query decode with the matrix-core kernels rotates the
+ *            queries of TQ3 pages and rotates their partial states back.
+ *            Multi-query decode (n_query > 1), materialisation and the VALU
+ *            baseline kernels return MKV_ERR_RANGE for such a pool.  FP8
+ *            pages are never rotated. */
 typedef struct {
   uint8_t* fp8_slab;
   uint8_t* tq3_slab;
@@ -94,6 +108,7 @@ typedef struct {
   int32_t n_tq3;
   float k_scale;
   float v_scale;
+  const int8_t* tq3_signs;
 } mkv_pool;
 
 /* A decode batch: ragged CSR block tables shared by all layers.

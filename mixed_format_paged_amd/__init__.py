@@ -40,7 +40,7 @@ class Layout(ctypes.Structure):
 
 class PoolDesc(ctypes.Structure):
     _fields_ = [("fp8_slab", c_vp), ("tq3_slab", c_vp), ("tier", c_vp), ("n_fp8", c_i32),
-                ("n_tq3", c_i32), ("k_scale", c_f32), ("v_scale", c_f32)]
+                ("n_tq3", c_i32), ("k_scale", c_f32), ("v_scale", c_f32), ("tq3_signs", c_vp)]
 
 
 class BatchDesc(ctypes.Structure):
@@ -133,12 +133,14 @@ def _layout(layout):
     return Layout(hq, hkv, d, layout[3] if len(layout) > 3 else 16)
 
 
-def make_pool(fp8_slab, tq3_slab, tier, n_fp8, n_tq3, k_scale=1.0, v_scale=1.0):
-    """PoolDesc over device tensors (uint8 slabs and the uint8 tier map)."""
+def make_pool(fp8_slab, tq3_slab, tier, n_fp8, n_tq3, k_scale=1.0, v_scale=1.0, tq3_signs=None):
+    """PoolDesc over device tensors (uint8 slabs and the uint8 tier map);
+    tq3_signs: None, or a device int8 [head_dim] tensor of +-1 (rotated TQ3)."""
     import torch
+    signs = None if tq3_signs is None else _ptr(tq3_signs, torch.int8, "tq3_signs")
     p = PoolDesc(_ptr(fp8_slab, torch.uint8, "fp8_slab"), _ptr(tq3_slab, torch.uint8, "tq3_slab"),
-                 _ptr(tier, torch.uint8, "tier"), int(n_fp8), int(n_tq3), float(k_scale), float(v_scale))
-    p._keep = (fp8_slab, tq3_slab, tier)
+                 _ptr(tier, torch.uint8, "tier"), int(n_fp8), int(n_tq3), float(k_scale), float(v_scale), signs)
+    p._keep = (fp8_slab, tq3_slab, tier, tq3_signs)
     return p
 
 

@@ -16,7 +16,9 @@ APPEND_MAX = 65520        # tokens per mkv_append call when filling a request (a
 
 
 class PagedCache:
-    def __init__(self, layout, n_layers, n_fp8, n_tq3, device="cuda", k_scale=1.0, v_scale=1.0):
+    def __init__(self, layout, n_layers, n_fp8, n_tq3, device="cuda", k_scale=1.0, v_scale=1.0, tq3_signs=None):
+        """tq3_signs: None, or one device int8 [head_dim] tensor per layer
+        (rotated TQ3 pages in that layer; None entries: plain TQ3)."""
         self.layout = _layout(layout)
         self.n_layers, self.n_fp8, self.n_tq3 = int(n_layers), int(n_fp8), int(n_tq3)
         fb, tb = mkv_fp8_page_bytes(self.layout), mkv_tq3_page_bytes(self.layout)
@@ -24,7 +26,8 @@ class PagedCache:
         self.tq3 = [torch.zeros((max(1, n_tq3), tb), dtype=torch.uint8, device=device) for _ in range(n_layers)]
         self.tier = torch.full((n_fp8 + n_tq3,), TIER_FREE, dtype=torch.uint8, device=device)
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
-        self.pools = [make_pool(self.fp8[l], self.tq3[l], self.tier, n_fp8, n_tq3, k_scale, v_scale)
+        self.signs = list(tq3_signs) if tq3_signs is not None else [None] * n_layers
+        self.pools = [make_pool(self.fp8[l], self.tq3[l], self.tier, n_fp8, n_tq3, k_scale, v_scale, self.signs[l])
                       for l in range(n_layers)]
 
     @property

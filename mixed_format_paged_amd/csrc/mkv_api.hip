@@ -69,6 +69,7 @@ int check_pool(const mkv_pool* p, Geometry* g, bool need_fp8, bool need_tq3, boo
   if (need_tq3 && !p->tq3_slab && p->n_tq3 > 0) return fail(MKV_ERR_NULL, "tq3_slab is NULL");
   if (need_tier && !p->tier) return fail(MKV_ERR_NULL, "tier is NULL");
   if (!aligned16(p->fp8_slab) || !aligned16(p->tq3_slab)) return fail(MKV_ERR_ALIGN, "slabs must be 16-byte aligned");
+  if (!aligned16(p->tq3_signs)) return fail(MKV_ERR_ALIGN, "tq3_signs must be 16-byte aligned");
   if (!(p->k_scale > 0.0f) || !(p->v_scale > 0.0f) || std::isinf(p->k_scale) || std::isinf(p->v_scale))
     return fail(MKV_ERR_RANGE, "k_scale and v_scale must be finite and > 0");
   g->n_fp8 = p->n_fp8;
@@ -119,6 +120,7 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.off_chunks_f = take(sizeof(int32_t) * kChunkInts * (size_t)s.table_cap);
   s.off_chunks_t = take(sizeof(int32_t) * kChunkInts * (size_t)s.table_cap);
   const size_t states = (size_t)Le * s.np_cap * hkv * R;
+  s.off_q_rot = take(sizeof(float) * (size_t)Le * batch * n_query * hq * d);
   s.off_part_ml = take(sizeof(float) * 2 * states);
   s.off_part_acc = take(sizeof(float) * d * states);
   s.total = o;
@@ -135,6 +137,7 @@ Plan plan_from_ws(void* ws, const WsSizes& s, int batch, int bt_capacity) {
   p.list_t = reinterpret_cast<int32_t*>(base + s.off_list_t);
   p.chunks_f = reinterpret_cast<int4*>(base + s.off_chunks_f);
   p.chunks_t = reinterpret_cast<int4*>(base + s.off_chunks_t);
+  p.q_rot = reinterpret_cast<float*>(base + s.off_q_rot);
   p.part_ml = reinterpret_cast<float*>(base + s.off_part_ml);
   p.part_acc = reinterpret_cast<float*>(base + s.off_part_acc);
   p.batch = batch;
@@ -199,6 +202,8 @@ int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools, int
     lt.tq3[l] = pools[l].tq3_slab;
     lt.k_scale[l] = pools[l].k_scale;
     lt.v_scale[l] = pools[l].v_scale;
+    lt.signs[l] = pools[l].tq3_signs;
+    lt.any_signs |= pools[l].tq3_signs != nullptr;
   }
   if (n < 0) return fail(MKV_ERR_RANGE, "n = %d", n);
   if ((int64_t)n * g.hkv * n_layers > 0x7fffffff) return fail(MKV_ERR_RANGE, "n too large");
@@ -236,11 +241,15 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
       if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
       if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
         return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
+      if (pools[l].tq3_signs && (n_query > 1 || !g_partial_kind))
+        return fail(MKV_ERR_RANGE, "layer %d: rotated TQ3 pages need single-query decode with the matrix-core kernels", l);
       if (lt) {
         lt->fp8[l] = pools[l].fp8_slab;
         lt->tq3[l] = pools[l].tq3_slab;
         lt->k_scale[l] = pools[l].k_scale;
         lt->v_scale[l] = pools[l].v_scale;
+        lt->signs[l] = pools[l].tq3_signs;
+        lt->any_signs |= pools[l].tq3_signs != nullptr;
       }
     }
   }
@@ -483,6 +492,7 @@ int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_ba
   int rc = check_layout(layout, &g);
   if (rc) return rc;
   if ((rc = check_pool(pool, &g, true, true, false))) return rc;
+  if (pool->tq3_signs) return fail(MKV_ERR_RANGE, "materialisation of rotated TQ3 pages is not supported");
   if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
   if (b < 0 || b >= batch->batch || page_lo < 0 || n_pages < 0)
     return fail(MKV_ERR_RANGE, "b %d (batch %d) / page_lo %d / n_pages %d", b, batch->batch, page_lo, n_pages);
@@ -523,6 +533,8 @@ int check_lifecycle(const mkv_layout* layout, const mkv_pool* pools, int32_t n_l
       lt->tq3[l] = pools[l].tq3_slab;
       lt->k_scale[l] = pools[l].k_scale;
       lt->v_scale[l] = pools[l].v_scale;
+      lt->signs[l] = pools[l].tq3_signs;
+      lt->any_signs |= pools[l].tq3_signs != nullptr;
     }
   }
   if (batch < 0 || bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", batch, bt_capacity);

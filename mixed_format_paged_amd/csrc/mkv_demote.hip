@@ -25,7 +25,7 @@ namespace mkv {
 
 typedef uint32_t u3v __attribute__((ext_vector_type(3)));
 
-template <int D>
+template <int D, bool ROT = false>
 __global__ void __launch_bounds__(256) demote_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
     const int32_t* __restrict__ dst, const int32_t* __restrict__ n_dev, TableUpdate upd) {
@@ -78,6 +78,39 @@ __global__ void __launch_bounds__(256) demote_kernel(
     if (scl != 1.0f) {                               // uniform; x * 1 is x exactly
 #pragma unroll
       for (int c = 0; c < 32; ++c) x[c] = __fmul_rn(x[c], scl);
+    }
+    const int8_t* const sg = ROT ? lt.signs[layer] : nullptr;
+    if (ROT && sg) {                                   // rotated TQ3 (uniform per launch item)
+      // y = c H (signs . x) over the row's d channels, in the stage order of
+      // the format: channel bits 0..4 within the thread's group, then the
+      // group bits across the threads of the row (lanes differing in g)
+      const uint4 s0 = *reinterpret_cast<const uint4*>(sg + 32 * g), s1 = *reinterpret_cast<const uint4*>(sg + 32 * g + 16);
+      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if ((int8_t)((sw[c >> 2] >> (8 * (c & 3))) & 0xffu) < 0) x[c] = -x[c];
+#pragma unroll
+      for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          if (c & hs) continue;
+          const float a = x[c], b2 = x[c + hs];
+          x[c] = a + b2;
+          x[c + hs] = a - b2;
+        }
+      }
+#pragma unroll
+      for (int gb = 1; gb < G; gb <<= 1) {             // group bit: partner thread = lane ^ gb
+        const bool hi = (g & gb) != 0;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          const float p = __shfl_xor(x[c], gb);
+          x[c] = hi ? p - x[c] : x[c] + p;             // (a + b, a - b) with a from the lower channel
+        }
+      }
+      const float cs = D == 256 ? 0.0625f : 0.125f;    // c = 2^-floor(log2(d) / 2), exact
+#pragma unroll
+      for (int c = 0; c < 32; ++c) x[c] *= cs;
     }
 #pragma unroll
     for (int c = 0; c < 32; ++c) a = fmaxf(a, fabsf(x[c]));
@@ -141,12 +174,22 @@ hipError_t launch_demote_listed(const Geometry& g, const LayerTable& lt, int n_l
   if (n == 0 || n_layers == 0) return hipSuccess;
   dim3 grid(n_layers * n * g.hkv);
   const TableUpdate u = upd ? *upd : TableUpdate{nullptr, nullptr, nullptr, nullptr, nullptr};
-  if (g.d == 256)
-    hipLaunchKernelGGL(demote_kernel<256>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
-                       g.hkv, src, dst, n_dev, u);
-  else
-    hipLaunchKernelGGL(demote_kernel<128>, grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3,
-                       g.hkv, src, dst, n_dev, u);
+  // layers with rotated TQ3 pages take the instance with the rotation
+  if (g.d == 256) {
+    if (lt.any_signs)
+      hipLaunchKernelGGL((demote_kernel<256, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
+                         n_dev, u);
+    else
+      hipLaunchKernelGGL((demote_kernel<256, false>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src,
+                         dst, n_dev, u);
+  } else {
+    if (lt.any_signs)
+      hipLaunchKernelGGL((demote_kernel<128, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
+                         n_dev, u);
+    else
+      hipLaunchKernelGGL((demote_kernel<128, false>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src,
+                         dst, n_dev, u);
+  }
   return hipGetLastError();
 }
 

@@ -74,6 +74,7 @@ struct Plan {
   int32_t* list_t;      // [bt_capacity] TQ3 slot ids (id - n_fp8)
   int4* chunks_f;       // [chunk_cap][2]: descriptor, first page ids
   int4* chunks_t;       // [chunk_cap][2]
+  float* q_rot;         // [L][batch][Hq][d]: queries of rotated TQ3 pages (rotated pools only)
   float* part_ml;       // [L][Hkv][np_cap][R][2]  (m in log2 units, l); part_ml_index
   float* part_acc;      // [L][Hkv][d / 32][np_cap][R][32]; part_acc_index
   int batch;
@@ -109,7 +110,7 @@ constexpr int kMaxQuery = 16;         // query tokens per request
 // by calls for <= L layers; the state part scales with the layer count.
 struct WsSizes {
   size_t off_status, off_totals, off_req, off_list_f, off_list_t, off_chunks_f, off_chunks_t;
-  size_t off_part_ml, off_part_acc, total;
+  size_t off_q_rot, off_part_ml, off_part_acc, total;
   int table_cap, np_cap, chunks_target;
   int n_query, nblk, rowblk;
 };
@@ -123,6 +124,8 @@ struct LayerTable {
   uint8_t* tq3[kMaxLayers];
   float k_scale[kMaxLayers];
   float v_scale[kMaxLayers];
+  const int8_t* signs[kMaxLayers];    // rotated TQ3 pages (NULL: plain TQ3)
+  int any_signs;                      // some layer of the table is rotated
 };
 
 struct Geometry {

@@ -195,7 +195,9 @@ struct MergeLayout {
   __device__ static inline int at(int w, int i, int n, int T) { return w * kWave + i * kRow + n * kSlice + T; }
 };
 template <int D>
-constexpr int kSmemBytes = Geo<D>::kLds > MergeLayout<D>::kBytes ? Geo<D>::kLds : MergeLayout<D>::kBytes;
+constexpr int kRotBytes = MergeLayout<D>::kBytes + kMaxG * D * 4;   // the merge layout, then rows for the back-rotation
+template <int D>
+constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotBytes<D>;
 
 // 16-row blocks keep fp16(q) and its remainder as two fragment sets (2 kSq).
 template <int D>
@@ -500,10 +502,10 @@ enum AttendMode { kFp8Only = 0, kTq3Only = 1, kBoth = 2 };
 // each format's code path gets its own register allocation, and each loop
 // body is straight-line code (no per-unit branch for the allocator to split
 // the accumulators at).
-template <int D, bool tq3, bool MQ, int RB = 8>
+template <int D, bool tq3, bool MQ, int RB = 8, bool ROT = false>
 __device__ __forceinline__ void run_item(
-    const LayerTable& lt, int hkv, int G, const float* __restrict__ q, size_t q_ls, float qscale,
-    const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx, int first_id,
+    const LayerTable& lt, int hkv, int G, const float* __restrict__ q, const float* __restrict__ q_t, size_t q_ls,
+    float qscale, const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx, int first_id,
     uint8_t* smem, const AppendIn* ap, const RowBlock& rb) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
@@ -570,9 +572,9 @@ __device__ __forceinline__ void run_item(
     const float* qrow;
     if (MQ) {
       const int r = rb.r0 + (use ? row : 0), t = r / G;
-      qrow = q + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
+      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
     } else {
-      qrow = q + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
+      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
     }
     const float sc = qscale * ks_layer;
     const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
@@ -785,13 +787,42 @@ __device__ __forceinline__ void run_item(
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
-    const int i = idx / D, c = idx - (idx / D) * D;
-    const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
-    float acc = 0.0f;
+  const int8_t* const sgn = (ROT && tq3) ? lt.signs[layer] : nullptr;
+  if (ROT && sgn) {                                     // rotated TQ3 (uniform): acc = signs . (H acc') / (c d)
+    float* const rbuf = so + MergeLayout<D>::kBytes / 4;   // [rows][D], after the merge layout
+    for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
+      const int i = idx / D, c = idx - (idx / D) * D;
+      const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+      float acc = 0.0f;
 #pragma unroll 4
-    for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-    __builtin_nontemporal_store(acc, pa_out + state_at(i, c));   // streamed out: read once, by the merge
+      for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
+      rbuf[idx] = acc;
+    }
+    for (int hs = 1; hs < D; hs <<= 1) {
+      __syncthreads();
+      for (int pp = threadIdx.x; pp < rb.rows * D / 2; pp += kThreads) {
+        const int i = pp / (D / 2), r = pp - i * (D / 2);
+        float* const rr = rbuf + i * D + (r / hs) * 2 * hs + r % hs;
+        const float a = rr[0], b2 = rr[hs];
+        rr[0] = a + b2;
+        rr[hs] = a - b2;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
+      const int c = idx % D;
+      const float v = rbuf[idx] * 0.0625f;       // 1 / (c d) = 1/16 at d = 128 and 256
+      __builtin_nontemporal_store(sgn[c] < 0 ? -v : v, pa_out + state_at(idx / D, c));
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
+      const int i = idx / D, c = idx - (idx / D) * D;
+      const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
+      __builtin_nontemporal_store(acc, pa_out + state_at(i, c));   // streamed out: read once, by the merge
+    }
   }
   }
   if (threadIdx.x < rb.rows) {
@@ -818,11 +849,11 @@ __device__ __forceinline__ void run_item(
 // the request's last two logical pages.
 // RB: query rows per item, 8 (MFMA rows 0..7, remainders in 8..15) or, for
 // multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS).
-template <int D, int MODE, bool MQ, int RB>
+template <int D, int MODE, bool MQ, int RB, bool ROT = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(kAttendWgPerCu, kAttendWgPerCu))) attend_kernel(
-        LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, size_t q_ls,
-        float qscale, Plan plan, AppendIn ap) {
+        LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, const float* __restrict__ q_t,
+        size_t q_ls, float qscale, Plan plan, AppendIn ap) {
   __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
 
   static_assert(kWaves <= 4, "a chunk-table entry holds the first page of 4 waves");
@@ -874,10 +905,10 @@ __global__ void __launch_bounds__(kThreads)
       rb.req_last = req[R_TAIL * rowlen + b];
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id, smem,
+      run_item<D, true, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id, smem,
                                 nullptr, rb);
     if (MODE != kTq3Only && !tq3)
-      run_item<D, false, MQ, RB>(lt, hkv, G, q, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
+      run_item<D, false, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
                                  smem, (!MQ && holds_tail) ? &ap : nullptr, rb);
     __syncthreads();
   }
@@ -887,18 +918,66 @@ static dim3 attend_grid(long cap) {
   return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));
 }
 
+// Queries of rotated TQ3 pages: q' = H (signs . q) / (c d) per row of D
+// channels (1 / (c d) = 1/16 at d = 128 and 256), one workgroup of D threads
+// per row, the butterflies in LDS; rows of layers without signs are copied.
+template <int D>
+__global__ void __launch_bounds__(256) rotate_q_kernel(const float* __restrict__ q, float* __restrict__ qr,
+                                                      int rows_per_layer, LayerTable lt) {
+  __shared__ float buf[D];
+  const int row = blockIdx.x, c = threadIdx.x;
+  const int8_t* const sg = lt.signs[row / rows_per_layer];
+  const float x = q[(size_t)row * D + c];
+  if (!sg) {                                         // uniform
+    qr[(size_t)row * D + c] = x;
+    return;
+  }
+  buf[c] = sg[c] < 0 ? -x : x;
+  for (int hs = 1; hs < D; hs <<= 1) {
+    __syncthreads();
+    const float a = buf[c & ~hs], b = buf[c | hs];
+    __syncthreads();
+    buf[c] = (c & hs) ? a - b : a + b;
+  }
+  __syncthreads();
+  qr[(size_t)row * D + c] = buf[c] * 0.0625f;
+}
+
 template <int MODE, bool MQ, int RB>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
                             hipStream_t stream) {
+  // rotated TQ3 pages read rotated queries (single-query decode only; the
+  // host rejects rotated pools for several query tokens)
+  const float* q_t = q;
+  if (lt.any_signs && !MQ) {
+    const int rows = plan.batch * g.hq;
+    if (rows > 0) {
+      if (g.d == 256)
+        hipLaunchKernelGGL(rotate_q_kernel<256>, dim3(n_layers * rows), dim3(256), 0, stream, q, plan.q_rot, rows, lt);
+      else
+        hipLaunchKernelGGL(rotate_q_kernel<128>, dim3(n_layers * rows), dim3(128), 0, stream, q, plan.q_rot, rows, lt);
+    }
+    q_t = plan.q_rot;
+  }
   // partials per layer bound the items of either format, or of both together
   const dim3 grid = attend_grid((long)n_layers * g.hkv * plan.np_cap * (MQ ? plan.nblk : 1)), block(kThreads);
-  if (g.d == 256)
-    hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                       q_ls, qscale, plan, ap);
-  else
-    hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                       q_ls, qscale, plan, ap);
+  const bool rot = lt.any_signs && !MQ;
+  if (g.d == 256) {
+    if (rot)
+      hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB, !MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                         q_t, q_ls, qscale, plan, ap);
+    else
+      hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                         q_t, q_ls, qscale, plan, ap);
+  } else {
+    if (rot)
+      hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB, !MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                         q_t, q_ls, qscale, plan, ap);
+    else
+      hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
+                         q_t, q_ls, qscale, plan, ap);
+  }
 }
 
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,

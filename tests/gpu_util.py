@@ -23,13 +23,14 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def oracle_side(w, st, layer_vals):
-    """Oracle pools, block tables and decode outputs for every layer."""
+def oracle_side(w, st, layer_vals, signs=None):
+    """Oracle pools, block tables and decode outputs for every layer
+    (signs: per layer None or the sign vector of rotated TQ3 pages)."""
     res = []
-    for vals in layer_vals:
+    for li, vals in enumerate(layer_vals):
         k = [None if x is None else x.cpu().numpy() for x in vals["k"]]
         v = [None if x is None else x.cpu().numpy() for x in vals["v"]]
-        pool, bt = OB.build_layer(w, st, k, v)
+        pool, bt = OB.build_layer(w, st, k, v, signs=None if signs is None else signs[li])
         OB.step_demote(pool, st, bt)
         o, lse = OA.decode_batch(pool, vals["q"].cpu().numpy(), st.bt_offsets, bt, st.seq_lens)
         res.append((pool, bt, o, lse))
