@@ -325,6 +325,75 @@ def time_lifecycle(runner, reps=8):
     return sum(ms[1:]) / (reps - 1), demoted
 
 
+def time_rotated(runner, reps=16):
+    """Rotated TQ3 pages: layer 0 of the workload built again with a sign
+    vector (its TQ3 pages rotated), and the attention of one layer (plan, the
+    query rotation, partials with the back-rotation, merge: mkv_attend after
+    mkv_decode_plan) timed against the same call on the plain layer 0, with HIP
+    events, alternating; plus mkv_demote_pages of 8,192 random E4M3 pages with
+    the rotation.  Returns a dict of ms."""
+    import numpy as np
+    torch, M = runner.torch, runner.M
+    import workloads as W
+    from workloads.device_cache import DeviceWorkload
+    w, st = runner.w, runner.st
+    signs = np.where(np.random.default_rng(5).integers(0, 2, w.d) == 0, 1, -1).astype(np.int8)
+    dwr = DeviceWorkload(w, st, "cuda", layers=[0], tq3_signs=[signs])
+    lay, bat = runner.layout, runner.batch
+    ws = torch.empty(M.mkv_decode_workspace_bytes(lay, w.B, runner.dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.d), device="cuda")
+    lse = torch.empty((w.B, w.Hq), device="cuda")
+    q = runner.q[0]
+    M.mkv_decode_plan(lay, runner.dw.cache.pools[0], bat, 1, ws)
+
+    def run(pool):
+        M.mkv_attend(lay, [pool], bat, q, runner.sm_scale, out, lse, ws)
+
+    for pool in (dwr.cache.pools[0], runner.dw.cache.pools[0]):
+        run(pool)
+    torch.cuda.synchronize()
+    res = {"rot": [], "plain": []}
+    for i in range(2 * reps):
+        pool, key = (dwr.cache.pools[0], "rot") if i % 2 == 0 else (runner.dw.cache.pools[0], "plain")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run(pool)
+        b.record()
+        torch.cuda.synchronize()
+        res[key].append(a.elapsed_time(b))
+    status = M.mkv_workspace_status(ws)
+    # the rotated pack
+    n_pages = 8192
+    fb, tb = M.mkv_fp8_page_bytes(lay), M.mkv_tq3_page_bytes(lay)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    fp8 = torch.randint(0, 254, (n_pages, fb), dtype=torch.uint8, generator=g, device="cuda")
+    fp8 += (fp8 >= 0x7F).to(torch.uint8)
+    tq3 = torch.empty((n_pages, tb), dtype=torch.uint8, device="cuda")
+    tier = torch.full((2 * n_pages,), M.TIER_FREE, dtype=torch.uint8, device="cuda")
+    sg = torch.as_tensor(signs, device="cuda")
+    pool = M.make_pool(fp8, tq3, tier, n_pages, n_pages, tq3_signs=sg)
+    src = torch.arange(n_pages, dtype=torch.int32, device="cuda")
+    dst = src + n_pages
+    M.mkv_demote_pages(lay, pool, src, dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        M.mkv_demote_pages(lay, pool, src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    dem = a.elapsed_time(b) / 5
+    del dwr, fp8, tq3
+    torch.cuda.empty_cache()
+    if status != 0:
+        raise RuntimeError(f"rotated attend status {status}")
+    rot, plain = sum(res["rot"]) / reps, sum(res["plain"]) / reps
+    return {"attend_merge_ms_per_layer": round(rot, 5), "plain_attend_merge_ms_per_layer": round(plain, 5),
+            "vs_plain": round(rot / plain, 3), "demote_8192_pages_ms": round(dem, 5),
+            "demote_gbs": round(n_pages * (fb + tb) / (dem * 1e-3) / 1e9, 2)}
+
+
 def kernel_source_hash():
     """Hash of the sources the partial-attention kernel is compiled from."""
     import hashlib
@@ -459,6 +528,7 @@ def main():
     dem_ms, dem_bytes = time_demote_pack(r)
     lc_ms, lc_demoted = time_lifecycle(r)
     mq_ms = time_multi_query(r, T=4)
+    rot = time_rotated(r)
     traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
@@ -501,6 +571,7 @@ def main():
                                  "query_tokens_per_s": round(w.B * 4 / (mq_ms * 1e-3), 1),
                                  "kv_gbs_per_query_token": round(4 * layer_bytes / (mq_ms * 1e-3) / 1e9, 2),
                                  "vs_single_query_launch": round(mq_ms / k_avg, 3)},
+        "rotated_tq3_one_layer": rot,
     }
     if not a.no_control:
         del r

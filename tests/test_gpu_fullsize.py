@@ -34,9 +34,9 @@ def _picks(w, n, seed):
     return sorted({(int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(n)})
 
 
-def _check_units(w, st, picks, out, lse, new_kv=None, what=""):
+def _check_units(w, st, picks, out, lse, new_kv=None, what="", signs=None):
     """out [L][B][Hq][d], lse [L][B][Hq] (numpy); new_kv(l, b, h) -> (k, v) of a
-    token appended at position seq_len - 1, or None."""
+    token appended at position seq_len - 1, or None; signs: rotated TQ3 pages."""
     G = w.Hq // w.Hkv
     by_layer = {}
     for l, b, h in picks:
@@ -51,8 +51,8 @@ def _check_units(w, st, picks, out, lse, new_kv=None, what=""):
                 k[T - 1], v[T - 1] = new_kv(l, b, h)
             tiers = st.tiers[st.bt_offsets[b]:st.bt_offsets[b + 1]]
             is_tq3 = tiers == W.TIER_S
-            K = OP.quantized_values(k.cpu().numpy(), is_tq3, 1.0)
-            V = OP.quantized_values(v.cpu().numpy(), is_tq3, 1.0)
+            K = OP.quantized_values(k.cpu().numpy(), is_tq3, 1.0, signs)
+            V = OP.quantized_values(v.cpu().numpy(), is_tq3, 1.0, signs)
             q = vals["q"][b, h * G:(h + 1) * G].cpu().numpy()
             o_ref, lse_ref = OA.decode_attention(q, K[:, None, :], V[:, None, :])
             compare(out[l, b, h * G:(h + 1) * G], o_ref, lse[l, b, h * G:(h + 1) * G], lse_ref,
@@ -106,5 +106,26 @@ def test_full_size_decode(name):
     picks = _picks(w, 3, 12)
     print(f"[fullsize] {name}: checking {picks}", flush=True)
     _check_units(w, st, picks, o, l, what=name)
+    del dw, ws, out, lse
+    torch.cuda.empty_cache()
+
+
+def test_rotated_canary_layer_full_size():
+    # one layer of the canary at its full size with rotated TQ3 pages
+    from oracle import rotation as OR
+    w = W.WORKLOADS["canary-2x59008-16L"]
+    st = W.make_structure(w)
+    signs = OR.random_signs(w.d, 21)
+    print(f"[fullsize] {w.name} layer 0, rotated TQ3: building", flush=True)
+    dw = DeviceWorkload(w, st, "cuda", layers=[0], tq3_signs=[signs])
+    layout = (w.Hq, w.Hkv, w.d)
+    ws = torch.empty(M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((w.B, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((w.B, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn(layout, dw.cache.pools[0], dw.batch(), dw.q[0].contiguous(), 1 / math.sqrt(w.d), out, lse, ws)
+    torch.cuda.synchronize()
+    assert M.mkv_workspace_status(ws) == 0
+    picks = [(0, b, h) for b, h in ((0, 1), (1, 2), (1, 0))]
+    _check_units(w, st, picks, out.cpu().numpy()[None], lse.cpu().numpy()[None], what="canary rotated", signs=signs)
     del dw, ws, out, lse
     torch.cuda.empty_cache()
