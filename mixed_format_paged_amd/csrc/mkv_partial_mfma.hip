@@ -31,6 +31,12 @@
 //  Lane maps follow the byte layout in mkv_format.h: a TQ3 lane's triples
 //  arrive in one aligned chunk, and each run of 4 triples becomes 32 fp16
 //  codes through one FP6 conversion (decode32 below).
+//  Rotated TQ3 pages (a layer with a sign vector: the stale pages hold the
+//  codes of c H (signs . x), H the Sylvester-Hadamard matrix) run in their
+//  own kernel instance (ROT): its TQ3 items read queries rotated by
+//  rotate_q_kernel, q' = H (signs . q) / (c d), so the scores are unchanged,
+//  and rotate each partial state back, signs . (H acc) / (c d), before
+//  storing it.  Plain layers run the ROT = false instances, compiled as before.
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
@@ -849,6 +855,8 @@ __device__ __forceinline__ void run_item(
 // the request's last two logical pages.
 // RB: query rows per item, 8 (MFMA rows 0..7, remainders in 8..15) or, for
 // multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS).
+// ROT: some layer has rotated TQ3 pages (single-query only): TQ3 items read
+// q_t (the rotated queries) and rotate their partial states back.
 template <int D, int MODE, bool MQ, int RB, bool ROT = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(kAttendWgPerCu, kAttendWgPerCu))) attend_kernel(
