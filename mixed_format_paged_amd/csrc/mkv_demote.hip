@@ -18,12 +18,26 @@
 // rewrites each demoted page's block-table entry, tier bytes and free-stack
 // slot (one workgroup per page does it; nothing else in the launch reads
 // them, and the FP8 slot it frees is only reused by a later launch).
+#include <type_traits>
+
 #include "mkv_format.h"
 #include "mkv_internal.h"
 
 namespace mkv {
 
 typedef uint32_t u3v __attribute__((ext_vector_type(3)));
+
+// x of the lane whose index differs in bit gb (1, 2 or 4) within its group of
+// 8 lanes, by DPP moves (no LDS): quad permutes for xor 1 and 2; xor 4 is a
+// quad permute (xor 3) then a half-row mirror (xor 7).
+template <int GB>
+__device__ inline float lane_xor(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  if constexpr (GB == 1) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+  if constexpr (GB == 2) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  const int t = __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xf, 0xf, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, t, 0x141, 0xf, 0xf, false));
+}
 
 template <int D, bool ROT = false>
 __global__ void __launch_bounds__(256) demote_kernel(
@@ -99,15 +113,21 @@ __global__ void __launch_bounds__(256) demote_kernel(
           x[c + hs] = a - b2;
         }
       }
-#pragma unroll
-      for (int gb = 1; gb < G; gb <<= 1) {             // group bit: partner thread = lane ^ gb
+      // group bits: the partner thread is lane ^ gb (the row's G threads are
+      // consecutive lanes, G = 4 or 8)
+      auto cross = [&](auto gbc) {
+        constexpr int gb = decltype(gbc)::value;
         const bool hi = (g & gb) != 0;
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
-          const float p = __shfl_xor(x[c], gb);
+          const float p = lane_xor<gb>(x[c]);
           x[c] = hi ? p - x[c] : x[c] + p;             // (a + b, a - b) with a from the lower channel
         }
-      }
+      };
+      cross(std::integral_constant<int, 1>{});
+      cross(std::integral_constant<int, 2>{});
+      if constexpr (G == 8) cross(std::integral_constant<int, 4>{});
+      static_assert(G == 4 || G == 8, "row of 4 or 8 groups");
       const float cs = D == 256 ? 0.0625f : 0.125f;    // c = 2^-floor(log2(d) / 2), exact
 #pragma unroll
       for (int c = 0; c < 32; ++c) x[c] *= cs;
