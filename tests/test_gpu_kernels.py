@@ -337,18 +337,21 @@ def test_materialize_bitexact(d, scales):
         M.mkv_materialize(layout, pd, batch, 3, 0, 1, K, V)                  # b outside the batch
 
 
-def test_lifecycle_steps_match_the_oracle():
+@pytest.mark.parametrize("rotated", [False, True])
+def test_lifecycle_steps_match_the_oracle(rotated):
     """mkv_lifecycle_step (+ the step's mkv_append) from the same start state as
     the oracle: block table, seq_lens, tier map, free stacks, tops and every
     slab byte agree bit for bit at every checkpoint; an anchor set by the
     caller stays FP8; a request released mid-way regrows from zero (ragged
-    lengths); a step that cannot get free pages changes nothing."""
-    from oracle import lifecycle as LC
+    lengths); a step that cannot get free pages changes nothing.  rotated:
+    layer 0 demotes to rotated TQ3, layer 1 to plain TQ3, in the same launch."""
+    from oracle import lifecycle as LC, rotation as ORot
     hq, hkv, d, R, L, B, cap, n_fp8, n_tq3 = 4, 2, 128, 3, 2, 3, 12, 14, 30
     layout = (hq, hkv, d)
     rng = np.random.default_rng(7)
     tier = np.full(n_fp8 + n_tq3, OP.TIER_FREE, dtype=np.uint8)
-    pools = [OP.Pool(hkv, d, n_fp8, n_tq3, tier=tier) for _ in range(L)]
+    signs = [ORot.random_signs(d, 31) if rotated else None, None]
+    pools = [OP.Pool(hkv, d, n_fp8, n_tq3, tier=tier, signs=signs[l]) for l in range(L)]
     t = LC.Tables(np.arange(B + 1) * cap, np.full(B * cap, -1), np.zeros(B, dtype=np.int64), tier,
                   rng.permutation(n_fp8), n_fp8 + rng.permutation(n_tq3), [n_fp8, n_tq3])
     dev = "cuda"
@@ -356,7 +359,8 @@ def test_lifecycle_steps_match_the_oracle():
     fp8_d = [torch.from_numpy(p.fp8).to(dev) for p in pools]
     tq3_d = [torch.from_numpy(p.tq3).to(dev) for p in pools]
     tier_d = torch.from_numpy(tier).to(dev)
-    pd = [M.make_pool(fp8_d[l], tq3_d[l], tier_d, n_fp8, n_tq3) for l in range(L)]
+    signs_d = [None if sg is None else torch.from_numpy(sg).to(dev) for sg in signs]
+    pd = [M.make_pool(fp8_d[l], tq3_d[l], tier_d, n_fp8, n_tq3, tq3_signs=signs_d[l]) for l in range(L)]
     offs_d, bt_d, sl_d = i32(t.bt_offsets), i32(t.bt_pages), i32(t.seq_lens)
     ff_d, tf_d, tops_d = i32(t.fp8_free), i32(t.tq3_free), i32(t.tops)
     ws = torch.zeros(M.mkv_lifecycle_workspace_bytes(B), dtype=torch.uint8, device=dev)
