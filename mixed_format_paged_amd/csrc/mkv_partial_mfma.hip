@@ -122,9 +122,13 @@ typedef int i8v __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(4))) i8v* cptr_i8;
 
 // Per-head-dim constants and the LDS plan of a 4-wave workgroup:
-//   [ring: 4 waves x 2 slots x kSlot][sq: score-MFMA B operands, NG x 64 x 16 B]
-// (40 KB at d = 256; three workgroups share a CU).  At the end of an item
-// the whole block is reused for the merge of the 4 wave states.
+//   [ring: 4 waves x kWaveRing3 bytes][sq: score-MFMA B operands, NG x 64 x 16 B]
+// (50 KB at d = 256; three workgroups share a CU).  A wave's ring holds
+// three TQ3 page-heads back to back (kTq3Unit bytes each) or two FP8 halves
+// (kSlot each).  The 16-row instance keeps two slots of kSlot per wave
+// (kRing), as its second fragment set leaves no room for the third.  At the
+// end of an item the whole block is reused for the merge of the 4 wave
+// states.
 template <int D>
 struct Geo {
   static constexpr int NG = D / 32;                 // 32-channel MFMA k-chunks (TQ3: scale groups)
@@ -132,8 +136,11 @@ struct Geo {
   static constexpr int kRows = D / 64;              // 1 KB rows of a staging slot
   static constexpr int kSlot = kRows * 1024;
   static constexpr int kRing = kWaves * 2 * kSlot;
+  static constexpr int kTq3Unit = 14 * D;           // one TQ3 page-head
+  static constexpr int kWaveRing3 = 3 * kTq3Unit > 2 * kSlot ? 3 * kTq3Unit : 2 * kSlot;
+  static constexpr int kRing3 = kWaves * kWaveRing3;
   static constexpr int kSq = NG * 64 * 16;
-  static constexpr int kLds = kRing + kSq;
+  static constexpr int kLds = kRing3 + kSq;
 };
 
 // Staging unit: the bytes a wave moves to one LDS slot.  For TQ3 a unit is
@@ -145,7 +152,7 @@ struct Geo {
 // partial last row the lanes past the end re-read an in-range address and
 // fill the slot's padding, so every load is issued unconditionally and the
 // wave's count of outstanding loads is static.
-template <int D>
+template <int D, bool kMaskTail = false>
 __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slot, int lane, int bytes) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot));
   // 16 * lane, recomputed at every call: kept out of loop-invariant code
@@ -155,10 +162,18 @@ __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slo
 #pragma unroll
   for (int i = 0; i < Geo<D>::kRows; ++i) {
     uint32_t off = 1024 * i + l16;
-    if (1024 * (i + 1) > bytes && off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
     // the (wave-uniform) unit address in an SGPR pair, the lane's 32-bit
     // offset in a VGPR; M0 holds the LDS row base, with one wait state
     // between the M0 write and the LDS-DMA load that reads it
+    if (kMaskTail && 1024 * (i + 1) > bytes) {
+      // slots packed back to back: the lanes past the end stay inactive (the
+      // load is still one instruction, so the count of loads is unchanged)
+      if (off < (uint32_t)bytes)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
+                     :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
+      continue;
+    }
+    if (1024 * (i + 1) > bytes && off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
                  :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
   }
@@ -207,8 +222,9 @@ constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotByte
 
 // 16-row blocks keep fp16(q) and its remainder as two fragment sets (2 kSq).
 template <int D>
-constexpr int kSmemBytes16 = Geo<D>::kLds + Geo<D>::kSq > MergeLayout<D>::kBytes + 256 ? Geo<D>::kLds + Geo<D>::kSq
-                                                                                      : MergeLayout<D>::kBytes + 256;
+constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq;
+template <int D>
+constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::kBytes + 256 ? kLds16<D> : MergeLayout<D>::kBytes + 256;
 
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
@@ -520,9 +536,11 @@ __device__ __forceinline__ void run_item(
   const int n = lane & 15, j = lane >> 4;   // C/B column (query row or channel slice), row group
   const float lo_sel = n < 8 ? 0.0f : -1.0f;  // MFMA rows 8..15 carry the fp16 remainders
   const int hq = hkv * G;
-  uint8_t* const slot0 = smem + wave * 2 * kSlot;
-  uint8_t* const slot1 = slot0 + kSlot;
-  h8* const sq = reinterpret_cast<h8*>(smem + GD::kRing);
+  constexpr int NS = RB == 8 ? 3 : 2;        // TQ3 staging slots of a wave
+  constexpr int kTs = NS == 3 ? GD::kTq3Unit : kSlot;
+  uint8_t* const slot0 = smem + wave * (NS == 3 ? GD::kWaveRing3 : 2 * kSlot);
+  uint8_t* const slot1 = slot0 + kSlot;      // FP8: K halves in slot0, V halves in slot1
+  h8* const sq = reinterpret_cast<h8*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing));
   const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
   const cptr_i32 list = (cptr_i32)(tq3 ? plan.list_t : plan.list_f);
   const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
@@ -558,7 +576,7 @@ __device__ __forceinline__ void run_item(
   // first unit(s) in flight before the query fragments are built
   if (my_pages > 0) {
     if (tq3) {
-      stage_issue<D>(page_src(first_id), slot0, lane, tq3_head_bytes(D));   // = page_id(0), from the chunk entry
+      stage_issue<D, NS == 3>(page_src(first_id), slot0, lane, tq3_head_bytes(D));   // = page_id(0), from the chunk entry
     } else {
       const uint8_t* p0 = page_src(first_id);
       stage_issue<D>(p0, slot0, lane, kPage * D);
@@ -629,6 +647,11 @@ __device__ __forceinline__ void run_item(
     }
   }
 
+  // three slots: page 1 goes out once the query fragments are built (its id,
+  // a scalar load, has landed by then)
+  if (tq3 && NS == 3 && my_pages > 1)
+    stage_issue<D, true>(page_src(page_id(1)), slot0 + kTs, lane, tq3_head_bytes(D));
+
   WaveState<D> st;
   st.init();
   // MQ: the lane's query row may see tokens at least `lim` before the end
@@ -641,20 +664,25 @@ __device__ __forceinline__ void run_item(
     return e == rb.tail_e ? last_tok - 1 : (e == rb.prev_e ? rb.req_last + kPage - 1 : kNoMask);
   };
   if (tq3) {
-    // two slots: page k+1 travels while page k is computed
-    int id_next = page_id(1);                 // page ids travel one page ahead of their loads
+    // NS slots: pages k+1 .. k+NS-1 travel while page k is computed; page
+    // k+NS-1 goes to the slot page k-1 left
+    int id_next = page_id(NS - 1);            // page ids travel one page ahead of their loads
+    int s_cur = 0;                            // slot of page k (wave-uniform)
     for (int k = 0; k < my_pages; ++k) {
       progress_prio(k, my_pages);
-      uint8_t* const cur = (k & 1) ? slot1 : slot0;
-      uint8_t* const nxt = (k & 1) ? slot0 : slot1;
-      if (k + 1 < my_pages) {                 // wave-uniform
+      uint8_t* const cur = slot0 + s_cur * kTs;
+      if (k + NS - 1 < my_pages) {            // wave-uniform
+        const int s_new = s_cur == 0 ? NS - 1 : s_cur - 1;
         const uint8_t* const nsrc = page_src(id_next);
-        id_next = page_id(k + 2);
-        stage_issue<D>(nsrc, nxt, lane, tq3_head_bytes(D));
-        wait_vmem<kRows>();                   // page k has landed, page k+1 in flight
+        id_next = page_id(k + NS);
+        stage_issue<D, NS == 3>(nsrc, slot0 + s_new * kTs, lane, tq3_head_bytes(D));
+        wait_vmem<(NS - 1) * kRows>();        // page k has landed, the next NS - 1 in flight
+      } else if (NS == 3 && k + 1 < my_pages) {
+        wait_vmem<kRows>();                   // page k has landed, the last one in flight
       } else {
         wait_vmem<0>();                       // the last page has landed
       }
+      s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
       __builtin_amdgcn_sched_barrier(0);
       const int e = wave + kWaves * k;        // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
