@@ -160,6 +160,16 @@ SMALL = [
     ("long-1x8192", W.scaled(W.WORKLOADS["long-1x131072"], lengths=("fixed", 8192))),
     ("canary-3L", W.scaled(W.WORKLOADS["canary-2x59008-16L"], L=3, lengths=("fixed", 1500), recent_tokens=256)),
     ("demote-4x2048", W.scaled(W.WORKLOADS["demote-64x32768"], B=4, lengths=("fixed", 2048), aging_pages=16)),
+    # other head layouts: a full 8-row group (no padding rows), one query head
+    # per KV head, a single KV head
+    ("heads-32q-4kv", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=3, Hq=32, Hkv=4,
+                               lengths=("list", (500, 0, 1025)), recent_tokens=64)),
+    ("heads-8q-8kv-d128", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, Hq=8, Hkv=8,
+                                   lengths=("list", (700, 33)), recent_tokens=64)),
+    ("heads-16q-2kv-d128", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, Hq=16, Hkv=2,
+                                    lengths=("list", (257, 1200)), recent_tokens=32)),
+    ("heads-3q-1kv", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=2, Hq=3, Hkv=1,
+                              lengths=("list", (64, 800)), recent_tokens=32)),
 ]
 
 

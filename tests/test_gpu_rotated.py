@@ -59,6 +59,10 @@ ROT = [
     ("ragged-7", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=7,
                           lengths=("list", (1, 17, 0, 300, 1031, 2000, 16)), recent_tokens=64)),
     ("demote-4x2048", W.scaled(W.WORKLOADS["demote-64x32768"], B=4, lengths=("fixed", 2048), aging_pages=16)),
+    ("heads-32q-4kv", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=3, Hq=32, Hkv=4,
+                               lengths=("list", (500, 0, 1025)), recent_tokens=64)),
+    ("heads-16q-2kv-d128", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, Hq=16, Hkv=2,
+                                    lengths=("list", (257, 1200)), recent_tokens=32)),
 ]
 
 
