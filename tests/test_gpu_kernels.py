@@ -428,14 +428,18 @@ def test_lifecycle_steps_match_the_oracle(rotated):
     same("after the failing step")
 
 
-@pytest.mark.parametrize("T,d,recent", [(2, 256, 64), (5, 256, 16), (16, 128, 16), (3, 128, 64)])
-def test_multi_query_decode_parity(T, d, recent):
+@pytest.mark.parametrize("T,d,recent,hq,hkv", [(2, 256, 64, 24, 4), (5, 256, 16, 24, 4), (16, 128, 16, 24, 4),
+                                               (3, 128, 64, 24, 4), (4, 256, 16, 4, 2), (2, 128, 16, 16, 2),
+                                               (3, 256, 64, 8, 8)])
+def test_multi_query_decode_parity(T, d, recent, hq, hkv):
     """mkv_decode_attn_multi: each request's last T tokens as causal queries,
     against the oracle; ragged lengths including a request shorter than T and
     an empty one; recent = 16 tokens puts logical page n - 2 in TQ3, so the
-    causal mask runs on a TQ3 page too."""
+    causal mask runs on a TQ3 page too.  Rows per KV head T G: 12, 30, 96
+    and 18 (16-row blocks, the last one part-filled), 8 (one 8-row block,
+    full), 16 (one 16-row block, full) and 3."""
     M.set_partial_kind(1)
-    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=5, L=2, d=d,
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=5, L=2, d=d, Hq=hq, Hkv=hkv,
                  lengths=("list", (1500, 3, 0, 700, 33)), recent_tokens=recent)
     st, dw, ref = _both(w)
     layout = (w.Hq, w.Hkv, w.d)
