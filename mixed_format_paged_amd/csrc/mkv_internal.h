@@ -27,7 +27,7 @@ constexpr int kAttendWgPerCu = 3;
 // split-K work items aimed for per launch: one wave of workgroups on 256 CUs
 constexpr int kTargetItems = 256 * kAttendWgPerCu;
 constexpr int kMinChunkPages = 4;     // smallest chunk
-constexpr int kMaxChunkPages = 512;   // largest chunk (a workgroup stages its page ids in LDS)
+constexpr int kMaxChunkPages = 512;   // largest chunk: longer contexts get more chunks than the target
 constexpr int kMaxG = 8;              // query heads per KV head supported
 constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8;
 

@@ -129,3 +129,28 @@ def test_rotated_canary_layer_full_size():
     _check_units(w, st, picks, out.cpu().numpy()[None], lse.cpu().numpy()[None], what="canary rotated", signs=signs)
     del dw, ws, out, lse
     torch.cuda.empty_cache()
+
+
+def test_largest_chunks_sixteen_layers():
+    # sixteen layers in one call over one request of 90,000 tokens (5,625
+    # pages): the chunk target per layer drops to 10, so the plan's chunk size
+    # reaches its cap of 512 pages (128 per wave) and the TQ3 pages of a layer
+    # split into 11 chunks, one of them part-filled
+    w = W.scaled(W.WORKLOADS["long-1x131072"], name="long-16L-1x90000", L=16, lengths=("fixed", 90_000))
+    st = W.make_structure(w)
+    print(f"[fullsize] {w.name}: building", flush=True)
+    dw = DeviceWorkload(w, st, "cuda")
+    layout = (w.Hq, w.Hkv, w.d)
+    ws = torch.empty(M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), w.L), dtype=torch.uint8, device="cuda")
+    out = torch.full((w.L, w.B, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((w.L, w.B, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn_layers(layout, dw.cache.pools, dw.batch(), dw.q.contiguous(), 1 / math.sqrt(w.d), out, lse, ws)
+    torch.cuda.synchronize()
+    assert M.mkv_workspace_status(ws) == 0
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    picks = _picks(w, 3, 14)
+    print(f"[fullsize] {w.name}: checking {picks}", flush=True)
+    _check_units(w, st, picks, o, l, what=w.name)
+    del dw, ws, out, lse
+    torch.cuda.empty_cache()
