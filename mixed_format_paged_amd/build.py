@@ -34,15 +34,16 @@ def _compile(src):
     return src, obj, r.returncode, err
 
 
-def build(jobs=None, verbose=False):
+def build(jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(8, len(srcs))
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_compile, srcs))
     bad = [r for r in results if r[2] != 0]
+    # every compiler diagnostic of the HIP sources is shown, not only on failure
     for src, _, rc, err in results:
-        if err.strip() and (verbose or rc):
+        if err.strip():
             print(f"== {os.path.basename(src)}\n{err}", file=sys.stderr)
     if bad:
         raise RuntimeError("HIP compile failed: " + ", ".join(os.path.basename(b[0]) for b in bad))
@@ -58,6 +59,5 @@ def build(jobs=None, verbose=False):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
-    ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs))

@@ -163,19 +163,20 @@ __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slo
   for (int i = 0; i < Geo<D>::kRows; ++i) {
     uint32_t off = 1024 * i + l16;
     // the (wave-uniform) unit address in an SGPR pair, the lane's 32-bit
-    // offset in a VGPR; M0 holds the LDS row base, with one wait state
-    // between the M0 write and the LDS-DMA load that reads it
+    // offset in a VGPR; M0 holds the LDS row base.  M0 is an input operand
+    // of the asm, so the compiler writes it (and knows it is written); the
+    // s_nop gives the one wait state an LDS-DMA load needs after an M0 write
     if (kMaskTail && 1024 * (i + 1) > bytes) {
       // slots packed back to back: the lanes past the end stay inactive (the
       // load is still one instruction, so the count of loads is unchanged)
       if (off < (uint32_t)bytes)
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
-                     :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :: "v"(off), "s"(src), "{m0}"(lds + 1024 * i) : "memory");
       continue;
     }
     if (1024 * (i + 1) > bytes && off >= (uint32_t)bytes) off -= 1024 - (bytes & 1023);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt"
-                 :: "v"(off), "s"(lds + 1024 * i), "s"(src) : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(off), "s"(src), "{m0}"(lds + 1024 * i) : "memory");
   }
 }
 
