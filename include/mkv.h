@@ -65,8 +65,10 @@ enum {
 enum { MKV_TIER_RECENT = 0, MKV_TIER_ANCHOR = 1, MKV_TIER_STALE = 2, MKV_TIER_FREE = 0xFF };
 
 /* Head geometry.  Supported: head_dim in {128, 256}, page_size == 16,
- * num_q_heads % num_kv_heads == 0 and G = num_q_heads / num_kv_heads <= 8.
- * Query head i reads KV head i / G (grouped-query attention). */
+ * num_q_heads % num_kv_heads == 0 and G = num_q_heads / num_kv_heads <= 16.
+ * Query head i reads KV head i / G (grouped-query attention).  Each KV page
+ * is read once per KV head for all G query heads (up to 8 query rows in one
+ * matrix-core tile with their fp16 remainders, 9..16 rows in a 16-row tile). */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -85,7 +87,13 @@ typedef struct {
  *  tier:     device, n_fp8 + n_tq3 bytes, shared by all layers.
  *  Physical ids [0, n_fp8) are FP8 slots, [n_fp8, n_fp8 + n_tq3) TQ3 slots;
  *  a page with tier R or A must have an FP8 id, tier S a TQ3 id.
- *  k_scale / v_scale: per-layer fp32 FP8 scales (value = decode(byte) * scale).
+ *  k_scale / v_scale: per-layer fp32 FP8 scales (value = decode(byte) * scale),
+ *           any finite value > 0.  TQ3 pages demoted from this pool carry
+ *           the scale in their fp16 group scales; decode keeps every TQ3 V
+ *           product exact and finite for any v_scale, provided the TQ3 pages
+ *           were demoted with the same v_scale (their scales are then at most
+ *           fp16(448 * v_scale / 3)).  FP8 K scores are (q . code) * k_scale
+ *           in fp32.
  *  tq3_signs: NULL, or device int8[head_dim] of +1 / -1 (16-byte aligned): the layer's TQ3
  *            pages are "rotated TQ3".  The pages cite TurboQuant, which
  *            rotates before scalar quantisation (page 1, Abstract and its
@@ -97,8 +105,8 @@ typedef struct {
  *            head_dim 256, 1/8 at 128 (oracle/rotation.py).  Demotion rotates;
  *            single-query decode with the matrix-core kernels rotates the
  *            queries of TQ3 pages and rotates their partial states back.
- *            Multi-query decode (n_query > 1), materialisation and the VALU
- *            baseline kernels return MKV_ERR_RANGE for such a pool.  FP8
+ *            Multi-query decode (n_query > 1), G > 8, materialisation and the
+ *            VALU baseline kernels return MKV_ERR_RANGE for such a pool.  FP8
  *            pages are never rotated. */
 typedef struct {
   uint8_t* fp8_slab;
@@ -182,7 +190,10 @@ size_t mkv_decode_workspace_bytes(const mkv_layout* layout, int32_t batch,
 /* Decode attention for one layer: q fp32 [batch][num_q_heads][head_dim]
  * (device) -> out fp32 [batch][num_q_heads][head_dim] (device) and, if lse is
  * not NULL, lse fp32 [batch][num_q_heads] (natural log of the softmax
- * denominator including its max).  Scores are (q . k) * sm_scale.
+ * denominator including its max).  Scores are (q . k) * sm_scale.  The
+ * matrix-core kernels carry q * sm_scale * log2(e) as an fp16 pair (about 22
+ * significant bits, absolute resolution 2^-25), so |q * sm_scale| must stay
+ * below 40000.
  * The FP8 pages of each request are attended by the FP8 partial kernel, the
  * TQ3 pages by the TQ3 partial kernel (split-K over pages, each KV page read
  * once per GQA group), and a log-sum-exp merge combines the partial states
@@ -256,6 +267,8 @@ int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers
  *    aligned: K and V of the token at position seq_lens[b] - 1 of request b.
  *    That token's logical page (the request's last) must be an FP8 page of
  *    the pool (tier Recent); it is written exactly as mkv_append writes it.
+ *    A request whose last logical page is TQ3 gets NaN outputs and the
+ *    status bit MKV_DEV_BAD_TIER (the token is not written).
  *  The other arguments and the plan requirements are those of mkv_attend
  *  (the plan counts the new token: seq_lens include it).  Results, and the
  *  cache bytes written, are identical to mkv_append + mkv_attend.  Needs the

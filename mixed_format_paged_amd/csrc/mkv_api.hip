@@ -53,7 +53,7 @@ int check_layout(const mkv_layout* L, Geometry* g) {
     return fail(MKV_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                 L->num_q_heads, L->num_kv_heads);
   const int G = L->num_q_heads / L->num_kv_heads;
-  if (G > kMaxG) return fail(MKV_ERR_SHAPE, "GQA group %d > %d unsupported", G, kMaxG);
+  if (G > kMaxGroup) return fail(MKV_ERR_SHAPE, "GQA group %d > %d unsupported", G, kMaxGroup);
   g->hq = L->num_q_heads;
   g->hkv = L->num_kv_heads;
   g->d = L->head_dim;
@@ -79,13 +79,23 @@ int check_pool(const mkv_pool* p, Geometry* g, bool need_fp8, bool need_tq3, boo
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+void set_layer(LayerTable* lt, int l, const mkv_pool& p) {
+  lt->fp8[l] = p.fp8_slab;
+  lt->tq3[l] = p.tq3_slab;
+  lt->k_scale[l] = p.k_scale;
+  lt->v_scale[l] = p.v_scale;
+  lt->tq3_v_up[l] = (float)(1 << tq3_v_exponent(p.v_scale));
+  lt->signs[l] = p.tq3_signs;
+  lt->any_signs |= p.tq3_signs != nullptr;
+}
+
 }  // namespace
 
 WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int n_layers, int n_query) {
   WsSizes s{};
   const int G = hq / hkv;
   const int R = n_query * G;                         // query rows per KV head
-  const int rowblk = (n_query > 1 && R > kRowBlock) ? 2 * kRowBlock : kRowBlock;
+  const int rowblk = R > kRowBlock ? 2 * kRowBlock : kRowBlock;   // 16-row blocks past 8 rows
   const int nblk = (R + rowblk - 1) / rowblk;
   const int Le = n_layers < kMaxLayers ? n_layers : kMaxLayers;
   const int per = Le * hkv * nblk;
@@ -198,12 +208,7 @@ int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools, int
     if ((rc = check_pool(&pools[l], &g, true, true, false))) return rc;
     if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3)
       return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8 and n_tq3", l);
-    lt.fp8[l] = pools[l].fp8_slab;
-    lt.tq3[l] = pools[l].tq3_slab;
-    lt.k_scale[l] = pools[l].k_scale;
-    lt.v_scale[l] = pools[l].v_scale;
-    lt.signs[l] = pools[l].tq3_signs;
-    lt.any_signs |= pools[l].tq3_signs != nullptr;
+    set_layer(&lt, l, pools[l]);
   }
   if (n < 0) return fail(MKV_ERR_RANGE, "n = %d", n);
   if ((int64_t)n * g.hkv * n_layers > 0x7fffffff) return fail(MKV_ERR_RANGE, "n too large");
@@ -241,16 +246,11 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
       if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
       if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
         return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
-      if (pools[l].tq3_signs && (n_query > 1 || !g_partial_kind))
-        return fail(MKV_ERR_RANGE, "layer %d: rotated TQ3 pages need single-query decode with the matrix-core kernels", l);
-      if (lt) {
-        lt->fp8[l] = pools[l].fp8_slab;
-        lt->tq3[l] = pools[l].tq3_slab;
-        lt->k_scale[l] = pools[l].k_scale;
-        lt->v_scale[l] = pools[l].v_scale;
-        lt->signs[l] = pools[l].tq3_signs;
-        lt->any_signs |= pools[l].tq3_signs != nullptr;
-      }
+      if (pools[l].tq3_signs && (n_query > 1 || g->G > kRowBlock || !g_partial_kind))
+        return fail(MKV_ERR_RANGE,
+                    "layer %d: rotated TQ3 pages need single-query decode, at most 8 query heads per KV head and "
+                    "the matrix-core kernels", l);
+      if (lt) set_layer(lt, l, pools[l]);
     }
   }
   const int B = batch->batch;
@@ -296,9 +296,9 @@ int run_attend(int which, const Geometry& g, const LayerTable& lt, int n_layers,
 }
 
 int run_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse, int batch,
-              hipStream_t st) {
+              hipStream_t st, bool appended = false) {
   hipError_t e = launch_merge(g, n_layers, plan, out, lse, (size_t)batch * g.hq * g.d,
-                              (size_t)batch * g.hq, st);
+                              (size_t)batch * g.hq, st, appended);
   return e == hipSuccess ? MKV_OK : hip_fail(e, "merge launch");
 }
 
@@ -409,7 +409,7 @@ int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n
   const AppendIn ap{k_new, v_new, (size_t)B * g.hkv * g.d};
   hipError_t e = launch_partial_mfma(2, g, lt, n_layers, q, q_ls, qscale, plan, ap, st);
   if (e != hipSuccess) return hip_fail(e, "partial-attention launch");
-  return run_merge(g, n_layers, plan, out, lse, B, st);
+  return run_merge(g, n_layers, plan, out, lse, B, st, true);
 }
 
 int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
@@ -528,14 +528,7 @@ int check_lifecycle(const mkv_layout* layout, const mkv_pool* pools, int32_t n_l
     if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
     if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != tier)
       return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map passed in", l);
-    if (lt) {
-      lt->fp8[l] = pools[l].fp8_slab;
-      lt->tq3[l] = pools[l].tq3_slab;
-      lt->k_scale[l] = pools[l].k_scale;
-      lt->v_scale[l] = pools[l].v_scale;
-      lt->signs[l] = pools[l].tq3_signs;
-      lt->any_signs |= pools[l].tq3_signs != nullptr;
-    }
+    if (lt) set_layer(lt, l, pools[l]);
   }
   if (batch < 0 || bt_capacity < 0) return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", batch, bt_capacity);
   if (batch == 0) return MKV_OK;                      // no request: nothing to do

@@ -28,7 +28,8 @@ constexpr int kAttendWgPerCu = 3;
 constexpr int kTargetItems = 256 * kAttendWgPerCu;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk: longer contexts get more chunks than the target
-constexpr int kMaxG = 8;              // query heads per KV head supported
+constexpr int kMaxG = 8;              // query rows of an 8-row block (attend wave states, merge row groups)
+constexpr int kMaxGroup = 16;         // query heads per KV head supported (more than 8: 16-row blocks)
 constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8;
 
 // Per-request plan fields, each an int32[batch + 1] row of req[].
@@ -124,9 +125,27 @@ struct LayerTable {
   uint8_t* tq3[kMaxLayers];
   float k_scale[kMaxLayers];
   float v_scale[kMaxLayers];
+  // TQ3 V values u s, with u <= 7, reach 7 * 149.375 v_scale, past the fp16
+  // range once v_scale > 62.7.  The P V products then take s 2^-E, exact
+  // (see tq3_v_exponent), and the partial state is scaled back by
+  // tq3_v_up = 2^E in fp32.
+  float tq3_v_up[kMaxLayers];
   const int8_t* signs[kMaxLayers];    // rotated TQ3 pages (NULL: plain TQ3)
   int any_signs;                      // some layer of the table is rotated
 };
+
+// Smallest E >= 0 with 7 s 2^-E <= 65504 for every TQ3 V scale s a layer
+// with this v_scale can hold (s <= fp16(fl32(448 v_scale) / 3), saturated at
+// 65504), so the products u s 2^-E of P V stay finite in fp16; E <= 3.  The
+// shift is exact: E > 0 only when v_scale > 62.6, and then every nonzero s is
+// at least fp16(2^-9 v_scale / 3) > 0.04, so s 2^-E stays a normal fp16.
+inline int tq3_v_exponent(float v_scale) {
+  double smax = 448.0 * (double)v_scale / 3.0 * (1.0 + 1.0 / 1024.0);
+  if (smax > 65504.0) smax = 65504.0;
+  int e = 0;
+  while (7.0 * smax > 65504.0 * (double)(1 << e)) ++e;
+  return e;
+}
 
 struct Geometry {
   int hq, hkv, d, G;
@@ -189,8 +208,10 @@ struct AppendIn {
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream);
+// appended: the partials come from a launch with the in-launch append
+// (requests whose last logical page is TQ3 then get NaN outputs).
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out,
                         float* lse, size_t out_layer_stride, size_t lse_layer_stride,
-                        hipStream_t stream);
+                        hipStream_t stream, bool appended = false);
 
 }  // namespace mkv

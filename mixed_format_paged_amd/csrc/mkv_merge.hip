@@ -43,10 +43,14 @@ constexpr int kReg = 16;                         // partial states (float4) a th
 // threads of one (partial, row) read one contiguous 128-byte line; in the
 // state layout (part_acc_index) the rows and then the partials of a request
 // follow one another, so a workgroup's states are one contiguous run.
+// appended: the partial states come from a launch that appended each
+// request's new token to its last logical page (mkv_append_attend).  That page
+// must be FP8; a request whose last page is TQ3 could not take the token, so
+// its outputs are NaN and the status gets MKV_DEV_BAD_TIER.
 template <int D>
 __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, int Gh, Plan plan,
                                                          float* __restrict__ out, float* __restrict__ lse,
-                                                         size_t out_ls, size_t lse_ls) {
+                                                         size_t out_ls, size_t lse_ls, int appended) {
   constexpr int NS = D / kSliceC;
   const int T = plan.n_query;
   const int R = T * Gh;                                     // rows per KV head
@@ -59,6 +63,7 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   typedef const __attribute__((address_space(4))) int* cptr;
   const cptr poff = (cptr)req_row(plan, R_POFF);
   const cptr inval = (cptr)req_row(plan, R_INVALID);
+  const cptr lastfmt = (cptr)req_row(plan, R_LASTFMT);
   const int hq = hkv * Gh;
   const int tid = threadIdx.x;
   const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
@@ -82,7 +87,9 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
     const int G = R - r0 < kMaxG ? R - r0 : kMaxG;          // rows of this group
     const bool live = pi < G;
     const int p0 = poff[b], np = poff[b + 1] - p0;
-    const int bad = inval[b];
+    const int bad_append = (appended && lastfmt[b] == 1) ? kDevBadTier : 0;
+    const int bad = inval[b] | bad_append;
+    if (bad_append && layer == 0 && h == 0 && rg == 0 && cs == 0 && tid == 0) atomicOr(plan.status, bad_append);
     float* out_row = out + layer * out_ls + out_at(layer, b, h, r0 + (live ? pi : 0)) * D + cs * kSliceC;
     float* lse_l = lse ? lse + layer * lse_ls : nullptr;
     if (bad || np == 0 || p0 + np > plan.np_cap) {   // uniform per workgroup
@@ -160,14 +167,16 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
 }
 
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, float* lse,
-                        size_t out_ls, size_t lse_ls, hipStream_t stream) {
+                        size_t out_ls, size_t lse_ls, hipStream_t stream, bool appended) {
   const int R = plan.n_query * g.G;
   const long cap = (long)n_layers * plan.batch * g.hkv * ((R + kMaxG - 1) / kMaxG) * (g.d / kSliceC);
   const dim3 grid((unsigned)(cap < 4096 ? (cap > 0 ? cap : 1) : 4096));
   if (g.d == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls,
+                       appended ? 1 : 0);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, n_layers, g.hkv, g.G, plan, out, lse, out_ls, lse_ls,
+                       appended ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -140,7 +140,8 @@ struct Geo {
   static constexpr int kWaveRing3 = 3 * kTq3Unit > 2 * kSlot ? 3 * kTq3Unit : 2 * kSlot;
   static constexpr int kRing3 = kWaves * kWaveRing3;
   static constexpr int kSq = NG * 64 * 16;
-  static constexpr int kLds = kRing3 + kSq;
+  static constexpr int kRowMax = kWaves * 16 * 4;     // per-wave query-row maxima (prologue)
+  static constexpr int kLds = kRing3 + kSq + kRowMax;
 };
 
 // Staging unit: the bytes a wave moves to one LDS slot.  For TQ3 a unit is
@@ -223,7 +224,7 @@ constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotByte
 
 // 16-row blocks keep fp16(q) and its remainder as two fragment sets (2 kSq).
 template <int D>
-constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq;
+constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq + Geo<D>::kRowMax;
 template <int D>
 constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::kBytes + 256 ? kLds16<D> : MergeLayout<D>::kBytes + 256;
 
@@ -264,7 +265,9 @@ struct WaveState {
   }
 
   // Online-softmax update for a page's scores s (tokens 4j..4j+3 of query-row
-  // column n, log2 units, hi and lo query rows not yet added); returns the A
+  // column n, hi and lo query rows not yet added; times sc they are in log2
+  // units: sc undoes the power-of-two row scaling of the query fragments and,
+  // for FP8 pages, applies the layer's k_scale); returns the A
   // operand of P V: rows 0..7 fp16(p), rows 8..15 the remainder.  On a wave's
   // first page (wave-uniform `first`) O and l are still zero: the max is
   // taken as is and nothing is rescaled.
@@ -280,11 +283,14 @@ struct WaveState {
   // MFMA): no row pairing, and P comes back as fp16(p) with its remainder in
   // *p_lo, for two P V MFMAs.
   template <bool MQ, int RB = 8>
-  __device__ inline h4 softmax(f4 s, int ntok, float lo_sel, int j, bool first, int dist0 = 0, int lim = 0,
-                               h4* p_lo = nullptr) {
+  __device__ inline h4 softmax(f4 s, float sc, int ntok, float lo_sel, int j, bool first, int dist0 = 0,
+                               int lim = 0, h4* p_lo = nullptr) {
     if (RB == 8) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] += dpp_ror8(s[r]);   // hi + lo query rows
+      for (int r = 0; r < 4; ++r) s[r] = (s[r] + dpp_ror8(s[r])) * sc;   // hi + lo query rows, in score units
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] *= sc;
     }
     if (MQ) {
       if (dist0 < kNoMask) {
@@ -422,14 +428,16 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 // offset takes off each of its tiles.  vw: the lane's V code words, block b
 // in vw[b]; svv: the lane's V scales (its column's group, tokens 4j..4j+3);
 // both read from the staged page by the caller, ahead of the scores.
+// vdn = 2^-E (the layer's V shift, tq3_v_exponent): the scales enter as s 2^-E
+// (exact), so u s 2^-E stays finite in fp16; the epilogue multiplies by 2^E.
 template <int D, int RB = 8>
 __device__ inline void tq3_pv(h4 pa, f4 (&O)[Geo<D>::NT], f4& W, int lane, int j,
-                              const uint32_t (&vw)[Geo<D>::NG / 4][3], u2 svv, h4 pl = h4{}) {
+                              const uint32_t (&vw)[Geo<D>::NG / 4][3], u2 svv, h2 vdn, h4 pl = h4{}) {
   constexpr int NG = Geo<D>::NG;
   const h8 pa2 = __builtin_shufflevector(pa, pa, 0, 1, 2, 3, 0, 1, 2, 3);
   const h8 pl2 = __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3);   // RB 16: P's remainder
-  const h2 sv01 = u2h(svv[0]), sv23 = u2h(svv[1]);
-  const h4 sv4 = __builtin_bit_cast(h4, svv);
+  const h2 sv01 = u2h(svv[0]) * vdn, sv23 = u2h(svv[1]) * vdn;
+  const h4 sv4 = __builtin_shufflevector(sv01, sv23, 0, 1, 2, 3);
   W = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, sv4, W, 0, 0, 0);
   if (RB == 16) W = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, sv4, W, 0, 0, 0);
 #pragma unroll
@@ -542,7 +550,12 @@ __device__ __forceinline__ void run_item(
   uint8_t* const slot0 = smem + wave * (NS == 3 ? GD::kWaveRing3 : 2 * kSlot);
   uint8_t* const slot1 = slot0 + kSlot;      // FP8: K halves in slot0, V halves in slot1
   h8* const sq = reinterpret_cast<h8*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing));
+  // FP8 K codes enter the score MFMAs as they are; the layer's k_scale
+  // multiplies the fp32 scores (TQ3 K scales are in the group scales)
   const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
+  const float vup = tq3 ? lt.tq3_v_up[layer] : lt.v_scale[layer];   // fp32 factor of the wave states
+  const _Float16 vdn1 = (_Float16)(1.0f / lt.tq3_v_up[layer]);        // 2^-E, exact in fp16
+  const h2 vdn = h2{vdn1, vdn1};
   const cptr_i32 list = (cptr_i32)(tq3 ? plan.list_t : plan.list_f);
   const uint8_t* __restrict__ slab = tq3 ? lt.tq3[layer] : lt.fp8[layer];
   const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
@@ -586,38 +599,71 @@ __device__ __forceinline__ void run_item(
   }
 
   // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
-  //      query rows 0..G-1 carry fp16(q), rows 8..8+G-1 the remainder; with
-  //      16-row blocks all 16 columns are rows, fp16(q) in the first fragment
-  //      set and the remainder in the second ----
-  for (int e = threadIdx.x; e < NG * 64; e += kThreads) {
-    const int g = e >> 6, ln = e & 63;
-    const int nn = ln & 15, jj = ln >> 4;
-    const int row = RB == 16 ? nn : (nn < 8 ? nn : nn - 8);
-    const bool use = row < rb.rows;
+  //      query rows 0..G-1 carry fp16(x), rows 8..8+G-1 the remainder; with
+  //      16-row blocks all 16 columns are rows, fp16(x) in the first fragment
+  //      set and the remainder in the second.  x = q qscale 2^F, with F a
+  //      power of two per query row that puts the row's largest |x| in
+  //      [128, 256): the fp16 pair then holds x to about 22 bits of the row's
+  //      maximum whatever the size of q (and of the layer scales), and four
+  //      times a group sum (the TQ3 offset operand, at most 4 * 32 * 256)
+  //      stays inside fp16.  Scores are multiplied by 2^-F in fp32.
+  //      A thread's row is that of its lane's MFMA column (lane & 15), so the
+  //      same F scales its fragments and, later, its column of scores.
+  constexpr int IT = NG * 64 / kThreads;     // fragment entries per thread
+  static_assert(IT * kThreads == NG * 64, "whole fragment sets per workgroup");
+  float xq[IT][8];
+  float lmax = 0.0f;
+  const int qrow_i = RB == 16 ? n : (n & 7);  // this thread's query row (MFMA column n)
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int e = threadIdx.x + kThreads * it;
+    const int g = e >> 6, jj = (e & 63) >> 4;
+    const bool use = qrow_i < rb.rows;
     const float* qrow;
     if (MQ) {
-      const int r = rb.r0 + (use ? row : 0), t = r / G;
+      const int r = rb.r0 + (use ? qrow_i : 0), t = r / G;
       qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
     } else {
-      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? row : 0)) * D;
+      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? qrow_i : 0)) * D;
     }
-    const float sc = qscale * ks_layer;
     const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
     const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
     const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
     const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xq[it][k] = (use ? v[k] : 0.0f) * qscale;
+      lmax = fmaxf(lmax, fabsf(xq[it][k]));
+    }
+  }
+  // the row's maximum: over the lanes of the row in this wave (RB 8: lanes
+  // n and n ^ 8 hold the same row), then over the 4 waves through LDS
+  if (RB == 8) lmax = fmaxf(lmax, dpp_ror8(lmax));
+  lmax = max_xor32(max_xor16(lmax));
+  float* const srm = reinterpret_cast<float*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing) + (RB == 16 ? 2 : 1) * GD::kSq);
+  if (lane < (RB == 16 ? 16 : 8)) srm[wave * 16 + lane] = lmax;
+  __syncthreads();
+  float rmax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) rmax = fmaxf(rmax, srm[w * 16 + qrow_i]);
+  int F = rmax > 0.0f ? 8 - __builtin_amdgcn_frexp_expf(rmax) : 0;
+  F = F < -100 ? -100 : (F > 100 ? 100 : F);
+  const float up = __builtin_amdgcn_ldexpf(1.0f, F);
+  const float qsc = __builtin_amdgcn_ldexpf(1.0f, -F);   // score factor of this lane's column
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int e = threadIdx.x + kThreads * it;
     float x0[4], x1[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      x0[k] = (use ? v[k] : 0.0f) * sc;
-      x1[k] = (use ? v[k + 4] : 0.0f) * sc;
+      x0[k] = xq[it][k] * up;
+      x1[k] = xq[it][k + 4] * up;
     }
     if (RB == 16) {
       sq[e] = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
       sq[NG * 64 + e] = __builtin_shufflevector(split_rows(x0, -1.0f), split_rows(x1, -1.0f), 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
-      const float sel = nn < 8 ? 0.0f : -1.0f;
-      sq[e] = __builtin_shufflevector(split_rows(x0, sel), split_rows(x1, sel), 0, 1, 2, 3, 4, 5, 6, 7);
+      sq[e] = __builtin_shufflevector(split_rows(x0, lo_sel), split_rows(x1, lo_sel), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
   __syncthreads();
@@ -703,11 +749,12 @@ __device__ __forceinline__ void run_item(
       if constexpr (RB == 8) read_v();
       const f4 s = tq3_scores<D, RB>(cur, sq, lane, j, kneg);
       h4 pl;
-      const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
+      const h4 pa = st.template softmax<MQ, RB>(s, qsc, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
       if constexpr (RB == 16) read_v();
-      tq3_pv<D, RB>(pa, st.O, st.W, lane, j, vw, svv, pl);
+      tq3_pv<D, RB>(pa, st.O, st.W, lane, j, vw, svv, vdn, pl);
     }
   } else {
+    const float qsc_k = qsc * ks_layer;
     // slot 0 holds K halves, slot 1 V halves: K of page k+1 travels while V of
     // page k is computed, and V of page k+1 while K of page k+1 is
     int id_next = page_id(1);
@@ -719,7 +766,7 @@ __device__ __forceinline__ void run_item(
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D, RB>(slot0, sq, lane, j);
       h4 pl;
-      const h4 pa = st.template softmax<MQ, RB>(s, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
+      const h4 pa = st.template softmax<MQ, RB>(s, qsc_k, ntok, lo_sel, j, k == 0, MQ ? dist0_of(e) : 0, lim, &pl);
       const bool more = k + 1 < my_pages;     // wave-uniform
       const uint8_t* pn = page_src(id_next);
       id_next = page_id(k + 2);
@@ -762,7 +809,7 @@ __device__ __forceinline__ void run_item(
   float* __restrict__ pa_out = plan.part_acc + part_acc_index(plan.np_cap, hkv, D, rb.R, layer, h, pidx, rb.r0, 0);
   const size_t slice_stride = (size_t)plan.np_cap * rb.R * kStateSlice;   // between 32-channel slices
   auto state_at = [&](int i, int c) { return (size_t)(c / kStateSlice) * slice_stride + i * kStateSlice + c % kStateSlice; };
-  const float vscale = tq3 ? 1.0f : lt.v_scale[layer];
+  const float vscale = vup;
   if constexpr (RB == 16) {
     // 16 real rows, lane (n, j) holding rows 4j .. 4j + 3: rows 0..7 (j < 2),
     // then rows 8..15 (j >= 2), through the 8-row LDS layout
@@ -946,7 +993,7 @@ __global__ void __launch_bounds__(kThreads)
                                 nullptr, rb);
     if (MODE != kTq3Only && !tq3)
       run_item<D, false, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
-                                 smem, (!MQ && holds_tail) ? &ap : nullptr, rb);
+                                 smem, (holds_tail && (!MQ || plan.n_query == 1)) ? &ap : nullptr, rb);
     __syncthreads();
   }
 }
@@ -1020,7 +1067,14 @@ static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layer
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream) {
-  if (plan.n_query > 1 && plan.rowblk == 16)   // multi-query: both formats in one launch, no in-launch append
+  // 16-row blocks: multi-query with more than 8 rows per KV head, or one
+  // query token with 9..16 heads per KV head (then the in-launch append and
+  // the format-only launches apply as in the 8-row instance)
+  if (plan.rowblk == 16 && which == 0)
+    launch_attend_t<kFp8Only, true, 16>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  else if (plan.rowblk == 16 && which == 1)
+    launch_attend_t<kTq3Only, true, 16>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
+  else if (plan.rowblk == 16)
     launch_attend_t<kBoth, true, 16>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   else if (plan.n_query > 1)
     launch_attend_t<kBoth, true, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);

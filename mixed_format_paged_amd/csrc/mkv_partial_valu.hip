@@ -34,10 +34,10 @@ __global__ void __launch_bounds__(256) partial_valu_kernel(
     size_t q_layer_stride, float qscale, Plan plan) {
   __shared__ float Ks[kPage][D];
   __shared__ float Vs[kPage][D];
-  __shared__ float Qs[kMaxG][D];
-  __shared__ float S[kMaxG][kPage];
-  __shared__ float alpha_s[kMaxG], m_s[kMaxG], l_s[kMaxG];
-  constexpr int kPer = kMaxG * D / 256;
+  __shared__ float Qs[kMaxGroup][D];
+  __shared__ float S[kMaxGroup][kPage];
+  __shared__ float alpha_s[kMaxGroup], m_s[kMaxGroup], l_s[kMaxGroup];
+  constexpr int kPer = kMaxGroup * D / 256;
   const int tid = threadIdx.x;
   const int n_chunks = plan.totals[TQ3 ? T_NCT : T_NCF];
   const int4* chunks = TQ3 ? plan.chunks_t : plan.chunks_f;

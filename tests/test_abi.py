@@ -30,7 +30,8 @@ def test_page_sizes_and_shape_checks():
     assert M.mkv_fp8_page_bytes((24, 4, 256)) == 32768
     assert M.mkv_tq3_page_bytes((24, 4, 256)) == 14336
     assert M.mkv_tq3_page_bytes((24, 4, 128)) == 7168
-    for bad in [(24, 4, 64), (24, 5, 256), (36, 4, 256), (24, 4, 256, 32)]:
+    assert M.mkv_fp8_page_bytes((64, 4, 256)) == 32768     # 16 query heads per KV head
+    for bad in [(24, 4, 64), (24, 5, 256), (68, 4, 256), (17, 1, 128), (24, 4, 256, 32)]:
         assert M.mkv_fp8_page_bytes(bad) == 0
 
 

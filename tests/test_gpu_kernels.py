@@ -474,3 +474,30 @@ def test_multi_query_decode_parity(T, d, recent, hq, hkv):
         torch.cuda.synchronize()
         assert np.array_equal(out1[:, :, 0].cpu().numpy(), out2.cpu().numpy())
         assert np.array_equal(lse1[:, :, 0].cpu().numpy(), lse2.cpu().numpy())
+
+
+def test_append_attend_refuses_a_tq3_last_page():
+    """mkv_append_attend needs each request's last logical page to be FP8
+    (Recent).  With no recent window the last pages are TQ3 (unless drawn as
+    anchors): those requests get NaN outputs and MKV_DEV_BAD_TIER, the others
+    decode normally, and a plain decode of the same plan is unaffected."""
+    M.set_partial_kind(1)
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=4, L=1, lengths=("list", (900, 33, 1, 500)),
+                 recent_tokens=0, random_anchor_frac=0.0, fixed_anchor_pages=2)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    layout = (w.Hq, w.Hkv, w.d)
+    B = w.B
+    last_is_tq3 = np.array([st.tiers[st.bt_offsets[b + 1] - 1] == W.TIER_S for b in range(B)])
+    assert last_is_tq3.any() and not last_is_tq3.all()
+    ws = torch.empty(M.mkv_decode_workspace_bytes(layout, B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((1, B, w.Hq, w.d), 0.0, device="cuda")
+    lse = torch.full((1, B, w.Hq), 0.0, device="cuda")
+    k_new = torch.zeros((1, B, w.Hkv, w.d), device="cuda")
+    M.mkv_decode_plan(layout, dw.cache.pools[0], dw.batch(), 1, ws)
+    M.mkv_append_attend(layout, dw.cache.pools[:1], dw.batch(), k_new, k_new, dw.q, 1 / math.sqrt(w.d), out, lse, ws)
+    assert M.mkv_workspace_status(ws) == M.MKV_DEV_BAD_TIER
+    o = out.cpu().numpy()[0]
+    for b in range(B):
+        assert np.isnan(o[b]).all() == last_is_tq3[b], b
+        assert np.isfinite(o[b]).all() != last_is_tq3[b], b

@@ -15,18 +15,22 @@ from mixed_format_paged_amd.cache import PagedCache
 
 class DeviceWorkload:
     def __init__(self, w, st, device="cuda", layers=None, keep_values=False, gen_device=None, spare_tq3=0,
-                 tq3_signs=None):
+                 tq3_signs=None, k_scale=1.0, v_scale=1.0, value_fn=None):
         """gen_device: where the fp32 values are drawn (default: `device`); tests
         draw on the CPU so the oracle can consume the very same tensors.
         spare_tq3: extra TQ3 slots after the workload's own (ids n_fp8 + n_tq3 ...).
         tq3_signs: None, or per built layer an int8 [d] sign vector (numpy or
-        None): that layer's TQ3 pages are rotated TQ3."""
+        None): that layer's TQ3 pages are rotated TQ3.
+        k_scale, v_scale: the pools' FP8 scales (every layer).
+        value_fn(vals, layer) -> vals: applied to each layer's drawn values
+        before they are written (tests use it to put values in other units)."""
         self.w, self.st = w, st
         n_layers = w.L if layers is None else len(layers)
         self.layers = list(range(w.L)) if layers is None else list(layers)
         signs = None if tq3_signs is None else [
             None if s is None else torch.as_tensor(np.asarray(s, dtype=np.int8), device=device) for s in tq3_signs]
-        self.cache = PagedCache((w.Hq, w.Hkv, w.d), n_layers, st.n_fp8, st.n_tq3 + spare_tq3, device, tq3_signs=signs)
+        self.cache = PagedCache((w.Hq, w.Hkv, w.d), n_layers, st.n_fp8, st.n_tq3 + spare_tq3, device,
+                                k_scale=k_scale, v_scale=v_scale, tq3_signs=signs)
         dev = device
         self.bt = torch.as_tensor(st.staging_ids, dtype=torch.int32, device=dev).clone()
         self.bt_offsets = torch.as_tensor(st.bt_offsets, dtype=torch.int32, device=dev)
@@ -38,6 +42,8 @@ class DeviceWorkload:
         b_dst = torch.as_tensor(st.final_ids[st.build_entries], dtype=torch.int32, device=dev)
         for li, layer in enumerate(self.layers):
             vals = layer_values(w, st, layer, device=gen_device or dev)
+            if value_fn is not None:
+                vals = value_fn(vals, layer)
             self.q[li] = vals["q"].to(dev)
             for b in range(w.B):
                 pages = self.bt[int(st.bt_offsets[b]):int(st.bt_offsets[b + 1])]
