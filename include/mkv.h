@@ -205,6 +205,24 @@ int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool,
                     float* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* mkv_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same decode, the same kernels and bit-identical results, with the
+ * workspace in a static device array of the library (32 MiB on each GPU the
+ * library runs on, held until the process ends) instead of a caller buffer.
+ * The call allocates nothing.  The array belongs to the current device
+ * (hipGetDevice); `stream` must be a stream of that device.  Every call on a
+ * GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * Returns MKV_ERR_WORKSPACE when the batch needs more workspace than the
+ * array holds (mkv_decode_workspace_bytes(layout, batch->batch,
+ * batch->bt_capacity, 1) > 32 MiB).  Device-data errors give NaN outputs as
+ * in mkv_decode_attn; their status word sits in the array and is not
+ * exported. */
+int mkv_decode_attn_noalloc(const mkv_layout* layout, const mkv_pool* pool,
+                            const mkv_batch* batch, const float* q, float sm_scale,
+                            float* out, float* lse, void* stream);
+
 /* Decode attention for n_layers (1..64) layers that share one tier map and one set
  * of block tables (the pages' canary decodes 16 full-attention layers per
  * step).  pools: host array of n_layers descriptors with equal n_fp8, n_tq3

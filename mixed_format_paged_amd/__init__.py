@@ -12,7 +12,7 @@ import os
 __all__ = [
     "MkvError", "Layout", "PoolDesc", "BatchDesc", "lib", "make_pool", "make_batch",
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
-    "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_layers",
+    "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_noalloc", "mkv_decode_attn_layers",
     "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
     "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
     "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
@@ -78,6 +78,7 @@ def lib():
                                       c_vp, c_sz, c_vp]),
         "mkv_decode_workspace_bytes": (c_sz, [P(Layout), c_i32, c_i32, c_i32]),
         "mkv_decode_attn": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "mkv_decode_attn_noalloc": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp]),
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_debug_gather": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
         "mkv_materialize": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
@@ -260,6 +261,14 @@ def mkv_decode_attn(layout, pool, batch, q, sm_scale, out, lse, ws, stream=None)
                                         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
                                         _ptr(ws, None, "ws"), int(ws.numel() * ws.element_size()),
                                         _stream(stream)))
+
+
+def mkv_decode_attn_noalloc(layout, pool, batch, q, sm_scale, out, lse, stream=None):
+    import torch
+    return _check(lib().mkv_decode_attn_noalloc(ctypes.byref(_layout(layout)), ctypes.byref(pool), ctypes.byref(batch),
+                                                _ptr(q, torch.float32, "q"), float(sm_scale),
+                                                _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+                                                _stream(stream)))
 
 
 def mkv_decode_attn_layers(layout, pools, batch, q, sm_scale, out, lse, ws, stream=None):

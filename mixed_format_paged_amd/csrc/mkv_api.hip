@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "mkv.h"
 #include "mkv_format.h"
@@ -469,6 +470,62 @@ int mkv_decode_attn(const mkv_layout* layout, const mkv_pool* pool, const mkv_ba
                     const float* q, float sm_scale, float* out, float* lse, void* ws,
                     size_t ws_bytes, void* stream) {
   return mkv_decode_attn_layers(layout, pool, 1, batch, q, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- decode for callers that cannot allocate -----------------------------
+// mkv_decode_attn_noalloc runs mkv_decode_attn with its workspace in `scratch`,
+// a file-scope device array: each GPU the library runs on holds one copy of
+// kNoAllocScratchBytes for the life of the process.  In host code `scratch`
+// names a host-side stand-in, not the device copy, so its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever handed to kernels.
+namespace mkv {
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];        // device address of `scratch`, per device
+
+int scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MKV_ERR_RANGE, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MKV_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MKV_OK;
+}
+}  // namespace
+}  // namespace mkv
+
+extern "C" {
+
+int mkv_decode_attn_noalloc(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                            const float* q, float sm_scale, float* out, float* lse, void* stream) {
+  Geometry g{};
+  int rc = check_layout(layout, &g);
+  if (rc) return rc;
+  if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
+  if (batch->batch < 0 || batch->bt_capacity < 0)
+    return fail(MKV_ERR_RANGE, "batch %d / bt_capacity %d", batch->batch, batch->bt_capacity);
+  const size_t need = workspace_sizes(g.hq, g.hkv, g.d, batch->batch, batch->bt_capacity, 1).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(MKV_ERR_WORKSPACE, "this batch needs %zu bytes of workspace, more than the %zu-byte static scratch of "
+                "mkv_decode_attn_noalloc (use mkv_decode_attn with a caller workspace)", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws))) return rc;
+  return mkv_decode_attn(layout, pool, batch, q, sm_scale, out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
 int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
