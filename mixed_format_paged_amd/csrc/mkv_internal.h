@@ -17,15 +17,13 @@
 namespace mkv {
 
 constexpr int kMaxLayers = 64;        // layers covered by one launch
-#ifndef MKV_WAVES
-#define MKV_WAVES 4
-#endif
-constexpr int kItemWaves = MKV_WAVES;  // waves (of 64 lanes) that share one split-K work item
-// partial-attention workgroups resident per CU (one wave per SIMD each; the
-// kernel's register budget is 512 / kAttendWgPerCu VGPRs per lane)
-constexpr int kAttendWgPerCu = 3;
-// split-K work items aimed for per launch: one wave of workgroups on 256 CUs
-constexpr int kTargetItems = 256 * kAttendWgPerCu;
+// Waves (of 64 lanes) that share one split-K work item: the partial-attention
+// workgroup is 12 waves, three per SIMD, one workgroup per CU (the kernel's
+// register budget is 512 / kAttendWavesPerSimd VGPRs per lane).
+constexpr int kAttendWavesPerSimd = 3;
+constexpr int kItemWaves = 4 * kAttendWavesPerSimd;
+// split-K work items aimed for per launch: one per CU of the 256
+constexpr int kTargetItems = 256;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk: longer contexts get more chunks than the target
 constexpr int kMaxG = 8;              // query rows of an 8-row block (attend wave states, merge row groups)
@@ -60,11 +58,20 @@ enum TotalField {
 // (absolute, in the request's CSR range), z = pages | (tokens on its last
 // page << 16) | (kChunkHoldsTail if its last page is the request's last
 // logical page), w = partial index within the layer.  Each chunk-table entry
-// is two int4: the descriptor, then the chunk's page-list entries k = 0..3
-// (clamped to its last page), the first page of each of the kItemWaves waves
-// that share a work item, so a workgroup can start staging after one load.
+// is four int4: the descriptor, then the first page of each of the
+// kItemWaves waves that share a work item (chunk_order(k) for k = 0..11,
+// clamped to the chunk's last page), so a workgroup can start staging after
+// one load.
 constexpr int kChunkHoldsTail = 1 << 30;
-constexpr int kChunkInts = 8;         // ints per chunk-table entry
+constexpr int kChunkInts = 16;        // ints per chunk-table entry
+static_assert(kChunkInts == 4 + kItemWaves, "a chunk-table entry holds the first page of every wave");
+// Order in which a work item takes its chunk's pages: k-th page taken = page
+// (k + count - 1) % count of the chunk when the chunk holds the request's last
+// logical page (so that page, the one the in-launch append writes, is the
+// first page of wave 0), else page k.  Wave w takes the pages k = w, w + 12, ...
+__host__ __device__ inline int chunk_order(int k, int count, bool holds_tail) {
+  return holds_tail ? (k == 0 ? count - 1 : k - 1) : k;
+}
 __host__ __device__ inline int chunk_pages(int z) { return z & 0xffff; }
 __host__ __device__ inline int chunk_last_tok(int z) { return (z >> 16) & 0x1f; }
 struct Plan {

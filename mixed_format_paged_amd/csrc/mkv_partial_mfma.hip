@@ -118,17 +118,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // scalar unit and never count against the vector-memory counter that the
 // staging waits below rely on.
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
-typedef int i8v __attribute__((ext_vector_type(8)));
-typedef const __attribute__((address_space(4))) i8v* cptr_i8;
+typedef int i16v __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(4))) i16v* cptr_i16;
 
-// Per-head-dim constants and the LDS plan of a 4-wave workgroup:
-//   [ring: 4 waves x kWaveRing3 bytes][sq: score-MFMA B operands, NG x 64 x 16 B]
-// (50 KB at d = 256; three workgroups share a CU).  A wave's ring holds
-// three TQ3 page-heads back to back (kTq3Unit bytes each) or two FP8 halves
-// (kSlot each).  The 16-row instance keeps two slots of kSlot per wave
-// (kRing), as its second fragment set leaves no room for the third.  At the
-// end of an item the whole block is reused for the merge of the 4 wave
-// states.
+// Per-head-dim constants and the LDS plan of a 12-wave workgroup (one per CU):
+//   [ring: 12 waves x kWaveRing3 bytes][sq: score-MFMA B operands, NG x 64 x 16 B]
+//   [per-wave query-row maxima]
+// (135 KB at d = 256).  A wave's ring holds three TQ3 page-heads back to back
+// (kTq3Unit bytes each) or two FP8 halves (kSlot each).  The 16-row instance
+// keeps two slots of kSlot per wave (kRing) and a second fragment set.  At the
+// end of an item the ring is reused for the merge of the 12 wave states.
 template <int D>
 struct Geo {
   static constexpr int NG = D / 32;                 // 32-channel MFMA k-chunks (TQ3: scale groups)
@@ -140,7 +139,8 @@ struct Geo {
   static constexpr int kWaveRing3 = 3 * kTq3Unit > 2 * kSlot ? 3 * kTq3Unit : 2 * kSlot;
   static constexpr int kRing3 = kWaves * kWaveRing3;
   static constexpr int kSq = NG * 64 * 16;
-  static constexpr int kRowMax = kWaves * 16 * 4;     // per-wave query-row maxima (prologue)
+  static constexpr int kRowMax = kWaves * 16 * 4 + 64; // per-wave query-row maxima (prologue), then the
+                                                        // waves' pages left (page loops)
   static constexpr int kLds = kRing3 + kSq + kRowMax;
 };
 
@@ -181,16 +181,33 @@ __device__ inline void stage_issue(const uint8_t* __restrict__ src, uint8_t* slo
   }
 }
 
+// One row of `bytes` (a multiple of 16, at most 1 KB) copied HBM -> LDS by
+// LDS-DMA: lane l moves bytes [16 l, 16 l + 16); lanes past the end are inactive.
+__device__ inline void stage_row(const void* __restrict__ src, void* dst, int lane, int bytes) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
+  uint32_t l16;
+  asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(l16) : "v"(lane));
+  if (l16 < (uint32_t)bytes)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(l16), "s"(src), "{m0}"(lds) : "memory");
+}
+
 // Issue priority of the wave from its progress through the page loop: the
-// hardware issues from the oldest wave first, so workgroups dispatched later
-// to a CU would lag; raising the priority of the waves with the most pages
-// left keeps the workgroups sharing a CU finishing together.
-__device__ inline void progress_prio(int k, int n) {
-  const int left = 4 * (n - k) / (n > 0 ? n : 1);   // 4 .. 1
-  if (left >= 4) __builtin_amdgcn_s_setprio(3);
-  else if (left == 3) __builtin_amdgcn_s_setprio(2);
-  else if (left == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
+// SIMD issues from the oldest wave first, so of the three waves of a workgroup
+// that share a SIMD (waves w, w + 4, w + 8) the oldest would run ahead and the
+// youngest would finish last, alone on its SIMD.  Each wave publishes the
+// pages it has left (left[], LDS) and, against its two siblings, takes the
+// highest priority when it has the most left and the lowest when it has the
+// fewest, so the three finish together.
+__device__ inline void progress_prio(volatile int* left, int wave, int pages_left) {
+  if (__builtin_amdgcn_mbcnt_lo(~0u, 0) == 0) left[wave] = pages_left;
+  const int a = __builtin_amdgcn_readfirstlane(left[wave < 8 ? wave + 4 : wave - 8]);
+  const int b = __builtin_amdgcn_readfirstlane(left[wave < 4 ? wave + 8 : wave - 4]);
+  const int behind = (a < pages_left) + (b < pages_left);     // siblings with fewer pages left
+  const int ahead = (a > pages_left) + (b > pages_left);
+  if (behind == 2) __builtin_amdgcn_s_setprio(3);
+  else if (ahead == 2) __builtin_amdgcn_s_setprio(0);
+  else if (behind == 1) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(1);
 }
 
 // Wait until at most N vector-memory instructions of this wave are in flight.
@@ -214,11 +231,30 @@ struct MergeLayout {
   static constexpr int kRow = 16 * kSlice + 8;
   static constexpr int kWave = kMaxG * kRow;
   static constexpr int kStates = kWaves * kWave;                 // floats
-  static constexpr int kBytes = (kStates + (2 * kWaves + 1) * kMaxG) * 4;
+  // the states, then per-wave maxima and denominators of NR rows and their max
+  static constexpr int bytes(int NR) { return (kStates + (2 * kWaves + 1) * NR) * 4; }
   __device__ static inline int at(int w, int i, int n, int T) { return w * kWave + i * kRow + n * kSlice + T; }
 };
+// 8-row blocks: each wave leaves its state in its own staging ring as soon as
+// its page loop ends (no wave waits for another to write): O minus 4 W (the
+// TQ3 offset) of its 8 rows, unscaled, at o(i, n, T) (channel n D/16 + T),
+// then its running maxima and denominators.
 template <int D>
-constexpr int kRotBytes = MergeLayout<D>::kBytes + kMaxG * D * 4;   // the merge layout, then rows for the back-rotation
+struct OwnLayout {
+  static constexpr int kSlice = D / 16 + 1;
+  static constexpr int kRow = 16 * kSlice + (D == 256 ? 8 : 0);
+  static constexpr int kO = kMaxG * kRow;
+  static constexpr int kM = kO, kL = kO + kMaxG;         // maxima, denominators
+  static constexpr int kFloats = kO + 2 * kMaxG;
+  static constexpr int kStride = Geo<D>::kWaveRing3 / 4;  // floats between the waves' regions
+  __device__ static inline int o(int i, int n, int T) { return i * kRow + n * kSlice + T; }
+};
+static_assert(OwnLayout<256>::kFloats <= OwnLayout<256>::kStride && OwnLayout<128>::kFloats <= OwnLayout<128>::kStride,
+              "a wave's state fits its staging ring");
+template <int D>
+constexpr int kOwnBytes = kWaves * Geo<D>::kWaveRing3 + kWaves * kMaxG * 4;   // the regions, then weights
+template <int D>
+constexpr int kRotBytes = kOwnBytes<D> + kMaxG * D * 4;   // then rows for the back-rotation
 template <int D>
 constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotBytes<D>;
 
@@ -226,7 +262,8 @@ constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotByte
 template <int D>
 constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq + Geo<D>::kRowMax;
 template <int D>
-constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::kBytes + 256 ? kLds16<D> : MergeLayout<D>::kBytes + 256;
+constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::bytes(16) ? kLds16<D> : MergeLayout<D>::bytes(16);
+static_assert(kSmemBytes<256> <= 160 * 1024 && kSmemBytes16<256> <= 160 * 1024, "LDS of one workgroup");
 
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
@@ -537,7 +574,7 @@ template <int D, bool tq3, bool MQ, int RB = 8, bool ROT = false>
 __device__ __forceinline__ void run_item(
     const LayerTable& lt, int hkv, int G, const float* __restrict__ q, const float* __restrict__ q_t, size_t q_ls,
     float qscale, const Plan& plan, int layer, int h, int b, int start, int count, int last_tok, int pidx, int first_id,
-    uint8_t* smem, const AppendIn* ap, const RowBlock& rb) {
+    bool holds_tail, uint8_t* smem, const AppendIn* ap, const RowBlock& rb) {
   using GD = Geo<D>;
   constexpr int NG = GD::NG, kSlot = GD::kSlot, kRows = GD::kRows;
   const int lane = threadIdx.x & 63;
@@ -550,6 +587,8 @@ __device__ __forceinline__ void run_item(
   uint8_t* const slot0 = smem + wave * (NS == 3 ? GD::kWaveRing3 : 2 * kSlot);
   uint8_t* const slot1 = slot0 + kSlot;      // FP8: K halves in slot0, V halves in slot1
   h8* const sq = reinterpret_cast<h8*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing));
+  volatile int* const s_left = reinterpret_cast<volatile int*>(
+      smem + (NS == 3 ? GD::kRing3 : GD::kRing) + (RB == 16 ? 2 : 1) * GD::kSq + kWaves * 16 * 4);
   // FP8 K codes enter the score MFMAs as they are; the layer's k_scale
   // multiplies the fp32 scores (TQ3 K scales are in the group scales)
   const float ks_layer = tq3 ? 1.0f : lt.k_scale[layer];
@@ -561,17 +600,20 @@ __device__ __forceinline__ void run_item(
   const size_t page_bytes = tq3 ? (size_t)tq3_page_bytes(hkv, D) : (size_t)fp8_page_bytes(hkv, D);
   const uint8_t* __restrict__ head = slab + (tq3 ? (size_t)h * tq3_head_bytes(D) : (size_t)h * 2 * kPage * D);
   const int my_pages = count > wave ? (count - wave + kWaves - 1) / kWaves : 0;
-  // page k of this wave (clamped, so reading one id past the end stays in range)
-  auto page_id = [&](int k) { return list[start + wave + kWaves * (k < my_pages ? k : my_pages - 1)]; };
+  // page of the chunk that this wave takes k-th (chunk_order: with the
+  // request's last page in the chunk, that page comes first, to wave 0)
+  auto chunk_page = [&](int k) { return chunk_order(wave + kWaves * k, count, holds_tail); };
+  // its id (clamped, so reading one id past the end stays in range)
+  auto page_id = [&](int k) { return list[start + chunk_page(k < my_pages ? k : my_pages - 1)]; };
   auto page_src = [&](int id) { return head + (size_t)id * page_bytes; };
 
   // The step's new token, appended in the same launch: the FP8 chunk that
   // holds a request's last logical page (always FP8: it is Recent) writes
   // head h's K and V rows of the token into it, E4M3 round-to-nearest-even
   // saturating like mkv_append, before anything of that page is staged; the
-  // wave that stages the page is the one that writes it, so its own loads
-  // come after its stores.
-  if (!tq3 && ap && ap->k && wave == (count - 1) % kWaves) {
+  // wave that stages the page (wave 0, which takes it first) is the one that
+  // writes it, so its own loads come after its stores.
+  if (!tq3 && ap && ap->k && holds_tail && wave == 0) {
     uint8_t* page = lt.fp8[layer] + (size_t)list[start + count - 1] * page_bytes;
     const int slot = last_tok - 1;
     const size_t row = layer * ap->ls + ((size_t)b * hkv + h) * D;
@@ -587,16 +629,39 @@ __device__ __forceinline__ void run_item(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stores done before the page is staged
   }
 
-  // first unit(s) in flight before the query fragments are built
+  // The item's query rows go to LDS first (LDS-DMA into the fragment area,
+  // which they leave before the fragments are written), then the first unit(s)
+  // of each wave: a wave waits for its query rows alone (the copies complete
+  // in order), so the fragments are built while the first pages travel.
+  const float* const qsrc = (ROT && tq3) ? q_t : q;
+  float* const qbuf = reinterpret_cast<float*>(sq);      // [RB][D] fp32 rows
+  auto q_row_ptr = [&](int row) {
+    if (MQ) {
+      const int r = rb.r0 + row, t = r / G;
+      return qsrc + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
+    }
+    return qsrc + layer * q_ls + ((size_t)b * hq + (size_t)h * G + row) * D;
+  };
+  int q_loads = 0;                                          // wave-uniform
+  for (int row = wave; row < rb.rows; row += kWaves) {
+    stage_row(q_row_ptr(row), qbuf + row * D, lane, D * 4);
+    ++q_loads;
+  }
   if (my_pages > 0) {
     if (tq3) {
       stage_issue<D, NS == 3>(page_src(first_id), slot0, lane, tq3_head_bytes(D));   // = page_id(0), from the chunk entry
+      wait_vmem<kRows>();                                  // the query rows have landed
     } else {
       const uint8_t* p0 = page_src(first_id);
       stage_issue<D>(p0, slot0, lane, kPage * D);
       stage_issue<D>(p0 + kPage * D, slot1, lane, kPage * D);
+      wait_vmem<2 * kRows>();
     }
+  } else {
+    wait_vmem<0>();
   }
+  (void)q_loads;
+  __syncthreads();                                          // every wave's query rows
 
   // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
   //      query rows 0..G-1 carry fp16(x), rows 8..8+G-1 the remainder; with
@@ -609,8 +674,9 @@ __device__ __forceinline__ void run_item(
   //      stays inside fp16.  Scores are multiplied by 2^-F in fp32.
   //      A thread's row is that of its lane's MFMA column (lane & 15), so the
   //      same F scales its fragments and, later, its column of scores.
-  constexpr int IT = NG * 64 / kThreads;     // fragment entries per thread
-  static_assert(IT * kThreads == NG * 64, "whole fragment sets per workgroup");
+  static_assert(NG * 64 <= kThreads, "one fragment entry per thread");
+  constexpr int IT = 1;
+  const bool builds = threadIdx.x < NG * 64;  // this thread builds fragment entry threadIdx.x
   float xq[IT][8];
   float lmax = 0.0f;
   const int qrow_i = RB == 16 ? n : (n & 7);  // this thread's query row (MFMA column n)
@@ -618,15 +684,9 @@ __device__ __forceinline__ void run_item(
   for (int it = 0; it < IT; ++it) {
     const int e = threadIdx.x + kThreads * it;
     const int g = e >> 6, jj = (e & 63) >> 4;
-    const bool use = qrow_i < rb.rows;
-    const float* qrow;
-    if (MQ) {
-      const int r = rb.r0 + (use ? qrow_i : 0), t = r / G;
-      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)(b * rb.T + t) * hq + (size_t)h * G + (r - t * G)) * D;
-    } else {
-      qrow = ((ROT && tq3) ? q_t : q) + layer * q_ls + ((size_t)b * hq + (size_t)h * G + (use ? qrow_i : 0)) * D;
-    }
-    const int c0 = tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g;
+    const bool use = qrow_i < rb.rows && builds;
+    const float* qrow = qbuf + (use ? qrow_i : 0) * D;
+    const int c0 = builds ? (tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g) : 0;
     const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
     const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
     const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
@@ -638,6 +698,7 @@ __device__ __forceinline__ void run_item(
   }
   // the row's maximum: over the lanes of the row in this wave (RB 8: lanes
   // n and n ^ 8 hold the same row), then over the 4 waves through LDS
+  if (lane == 0) s_left[wave] = my_pages;     // pages left, read by the page loops' priorities
   if (RB == 8) lmax = fmaxf(lmax, dpp_ror8(lmax));
   lmax = max_xor32(max_xor16(lmax));
   float* const srm = reinterpret_cast<float*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing) + (RB == 16 ? 2 : 1) * GD::kSq);
@@ -651,7 +712,7 @@ __device__ __forceinline__ void run_item(
   const float up = __builtin_amdgcn_ldexpf(1.0f, F);
   const float qsc = __builtin_amdgcn_ldexpf(1.0f, -F);   // score factor of this lane's column
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
+  for (int it = 0; it < IT && builds; ++it) {
     const int e = threadIdx.x + kThreads * it;
     float x0[4], x1[4];
 #pragma unroll
@@ -716,7 +777,7 @@ __device__ __forceinline__ void run_item(
     int id_next = page_id(NS - 1);            // page ids travel one page ahead of their loads
     int s_cur = 0;                            // slot of page k (wave-uniform)
     for (int k = 0; k < my_pages; ++k) {
-      progress_prio(k, my_pages);
+      progress_prio(s_left, wave, my_pages - k);
       uint8_t* const cur = slot0 + s_cur * kTs;
       if (k + NS - 1 < my_pages) {            // wave-uniform
         const int s_new = s_cur == 0 ? NS - 1 : s_cur - 1;
@@ -731,7 +792,7 @@ __device__ __forceinline__ void run_item(
       }
       s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
       __builtin_amdgcn_sched_barrier(0);
-      const int e = wave + kWaves * k;        // page of the chunk
+      const int e = chunk_page(k);            // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
       // this lane's V code words (its 3 NG bytes of the V code stream) and the
       // V scales of its column's group: with 8-row blocks they are requested
@@ -759,10 +820,10 @@ __device__ __forceinline__ void run_item(
     // page k is computed, and V of page k+1 while K of page k+1 is
     int id_next = page_id(1);
     for (int k = 0; k < my_pages; ++k) {
-      progress_prio(k, my_pages);
+      progress_prio(s_left, wave, my_pages - k);
       wait_vmem<kRows>();                     // K of page k has landed
       __builtin_amdgcn_sched_barrier(0);
-      const int e = wave + kWaves * k;
+      const int e = chunk_page(k);
       const int ntok = (e == count - 1) ? last_tok : kPage;
       const f4 s = fp8_scores<D, RB>(slot0, sq, lane, j);
       h4 pl;
@@ -783,16 +844,27 @@ __device__ __forceinline__ void run_item(
   }
   __builtin_amdgcn_s_setprio(0);
   wait_vmem<0>();                               // no staging load may land after this point
+  const float vscale = vup;
+  // this block's rows from r0 (part_acc_index / part_ml_index layout)
+  float* __restrict__ ml = plan.part_ml + part_ml_index(plan.np_cap, hkv, rb.R, layer, h, pidx, rb.r0);
+  float* __restrict__ pa_out = plan.part_acc + part_acc_index(plan.np_cap, hkv, D, rb.R, layer, h, pidx, rb.r0, 0);
+  const size_t slice_stride = (size_t)plan.np_cap * rb.R * kStateSlice;   // between 32-channel slices
+  auto state_at = [&](int i, int c) { return (size_t)(c / kStateSlice) * slice_stride + i * kStateSlice + c % kStateSlice; };
+  const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
+  uint32_t opq = 0;
+  if constexpr (RB == 16) {
   __syncthreads();                              // the staging block becomes the merge buffer
-
+  // an opaque zero offset for the merge-buffer addresses below: it keeps the
+  // compiler from computing the address of every wave's state before the page
+  // loops (and spilling them) instead of here
+  asm volatile("" : "+v"(opq));
   // ---- merge of the wave states: each wave rescales its rows to the common
   //      maximum, then the workgroup sums the states in a fixed order
-  constexpr int NR = RB == 16 ? 16 : kMaxG;              // rows of the wave states
+  constexpr int NR = 16;                                 // rows of the wave states
   float* const so = reinterpret_cast<float*>(smem);
   float* const sm = so + MergeLayout<D>::kStates;        // [kWaves][NR] maxima
   float* const sl = sm + kWaves * NR;                    // [kWaves][NR]
   float* const sM = sl + kWaves * NR;                    // [NR] their max
-  const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
   if (j == 0 && n < rb.rows) {
     sm[wave * NR + n] = st.m_run;
     sl[wave * NR + n] = l_tot;
@@ -800,17 +872,11 @@ __device__ __forceinline__ void run_item(
   __syncthreads();
   if (threadIdx.x < NR) {
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * NR + threadIdx.x]);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * NR + threadIdx.x + opq]);
     sM[threadIdx.x] = M;
   }
   __syncthreads();
-  // this block's rows from r0 (part_acc_index / part_ml_index layout)
-  float* __restrict__ ml = plan.part_ml + part_ml_index(plan.np_cap, hkv, rb.R, layer, h, pidx, rb.r0);
-  float* __restrict__ pa_out = plan.part_acc + part_acc_index(plan.np_cap, hkv, D, rb.R, layer, h, pidx, rb.r0, 0);
-  const size_t slice_stride = (size_t)plan.np_cap * rb.R * kStateSlice;   // between 32-channel slices
-  auto state_at = [&](int i, int c) { return (size_t)(c / kStateSlice) * slice_stride + i * kStateSlice + c % kStateSlice; };
-  const float vscale = vup;
-  if constexpr (RB == 16) {
     // 16 real rows, lane (n, j) holding rows 4j .. 4j + 3: rows 0..7 (j < 2),
     // then rows 8..15 (j >= 2), through the 8-row LDS layout
     for (int pass = 0; pass < 2 && 8 * pass < rb.rows; ++pass) {
@@ -830,7 +896,7 @@ __device__ __forceinline__ void run_item(
       const int rows_p = rb.rows - 8 * pass < 8 ? rb.rows - 8 * pass : 8;
       for (int idx = threadIdx.x; idx < rows_p * D; idx += kThreads) {
         const int i = idx / D, c = idx - (idx / D) * D;
-        const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
+        const float* src = so + opq + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
         float acc = 0.0f;
 #pragma unroll 4
         for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
@@ -838,47 +904,91 @@ __device__ __forceinline__ void run_item(
       }
       __syncthreads();                                  // the layout is rewritten by the next pass
     }
+  if (threadIdx.x < rb.rows) {
+    const int i = threadIdx.x + opq;
+    const float M = sM[i];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm[w * NR + i];
+      const float lw = sl[w * NR + i] * __builtin_amdgcn_exp2f(mw - M);
+      L += (mw == -INFINITY) ? 0.0f : lw;
+    }
+    ml[2 * i] = M;
+    ml[2 * i + 1] = L;
+  }
   } else {
-  // O rows 4jj + r: after the swap below, lanes 0..31 (j < 2) hold the rows of
-  // tile T, lanes 32..63 those of tile T + NT/2.  All kMaxG rows are stored
-  // (rows >= G hold values nobody reads), so the stores need no lane mask and
-  // take their row and tile from the instruction offset.
+  // ---- merge of the wave states (8-row blocks).  Each wave writes its state
+  //      into its own staging ring (OwnLayout) right away: O rows 4jj + r,
+  //      after the swap below lanes 0..31 (j < 2) hold the rows of tile T and
+  //      lanes 32..63 those of tile T + NT/2, combined with their fp16
+  //      remainder rows, minus 4 W (TQ3 V's offset, whose lane column keeps
+  //      one scale group in every tile); all kMaxG rows are stored (rows >= G
+  //      hold values nobody reads).  After one barrier, 96 threads turn the
+  //      maxima into per-(wave, row) weights, and after a second the
+  //      workgroup sums the states in a fixed order.
+  using OL = OwnLayout<D>;
+  float* const own = reinterpret_cast<float*>(slot0);
   const int jj = j & 1, thalf = j >> 1;
-  float wr[4], cw[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = 4 * jj + r;
-    const float mw = sm[wave * NR + row];
-    wr[r] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - sM[row]) * vscale;
-    cw[r] = 0.0f;
-    if (tq3) {    // TQ3 V's -4 offset: W of the fp16 row and of its remainder row, like O below
+    float wc = 0.0f;
+    if (tq3) {
       const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.W[r]), __float_as_uint(st.W[r]), false,
                                                        false);
-      cw[r] = -4.0f * (__uint_as_float(pw[0]) + __uint_as_float(pw[1])) * wr[r];
+      wc = -4.0f * (__uint_as_float(pw[0]) + __uint_as_float(pw[1]));
     }
-  }
 #pragma unroll
-  for (int T = 0; T < GD::NT / 2; ++T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int T = 0; T < GD::NT / 2; ++T) {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.O[T][r]),
                                                        __float_as_uint(st.O[T + GD::NT / 2][r]), false, false);
       const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-      so[MergeLayout<D>::at(wave, 4 * jj + r, n, T + thalf * (GD::NT / 2))] = fmaf(tot, wr[r], cw[r]);
+      own[OL::o(4 * jj + r, n, T + thalf * (GD::NT / 2))] = tot + wc;
+    }
+  }
+  if (j == 0 && n < kMaxG) {
+    own[OL::kM + n] = st.m_run;
+    own[OL::kL + n] = l_tot;
+  }
+  __syncthreads();                              // every wave's state is in place
+  asm volatile("" : "+v"(opq));                 // (as above: addresses computed here)
+  float* const so = reinterpret_cast<float*>(smem);
+  float* const wgt = so + kWaves * OL::kStride;           // [kWaves][kMaxG] weights
+  if (threadIdx.x < kWaves * kMaxG) {
+    const int w = threadIdx.x / kMaxG, i = threadIdx.x % kMaxG;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, so[v * OL::kStride + OL::kM + i + opq]);
+    const float mw = so[w * OL::kStride + OL::kM + i];
+    wgt[w * kMaxG + i] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * vscale;
+    if (w == 0 && i < rb.rows) {                // the partial's (m, l)
+      float L = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float mv = so[v * OL::kStride + OL::kM + i + opq];
+        const float lv = so[v * OL::kStride + OL::kL + i] * __builtin_amdgcn_exp2f(mv - M);
+        L += (mv == -INFINITY) ? 0.0f : lv;
+      }
+      ml[2 * i] = M;
+      ml[2 * i + 1] = L;
     }
   }
   __syncthreads();
+  auto sum_at = [&](int i, int c) {
+    const float* src = so + opq + OL::o(i, c / (D / 16), c % (D / 16));
+    const float* wi = wgt + opq + i;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc = fmaf(src[w * OL::kStride], wi[w * kMaxG], acc);
+    return acc;
+  };
 
   const int8_t* const sgn = (ROT && tq3) ? lt.signs[layer] : nullptr;
   if (ROT && sgn) {                                     // rotated TQ3 (uniform): acc = signs . (H acc') / (c d)
-    float* const rbuf = so + MergeLayout<D>::kBytes / 4;   // [rows][D], after the merge layout
+    float* const rbuf = so + kOwnBytes<D> / 4;          // [rows][D], after the regions and weights
     for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
       const int i = idx / D, c = idx - (idx / D) * D;
-      const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
-      float acc = 0.0f;
-#pragma unroll 4
-      for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-      rbuf[idx] = acc;
+      rbuf[idx] = sum_at(i, c);
     }
     for (int hs = 1; hs < D; hs <<= 1) {
       __syncthreads();
@@ -899,26 +1009,12 @@ __device__ __forceinline__ void run_item(
   } else {
     for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
       const int i = idx / D, c = idx - (idx / D) * D;
-      const float* src = so + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
-      float acc = 0.0f;
-#pragma unroll 4
-      for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-      __builtin_nontemporal_store(acc, pa_out + state_at(i, c));   // streamed out: read once, by the merge
+      __builtin_nontemporal_store(sum_at(i, c), pa_out + state_at(i, c));   // streamed out: read once, by the merge
     }
   }
-  }
-  if (threadIdx.x < rb.rows) {
-    const int i = threadIdx.x;
-    const float M = sM[i];
-    float L = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm[w * NR + i];
-      L += (mw == -INFINITY) ? 0.0f : sl[w * NR + i] * __builtin_amdgcn_exp2f(mw - M);
-    }
-    ml[2 * i] = M;
-    ml[2 * i + 1] = L;
   }
 }
+
 
 // MODE selects which format's work items the launch takes (kBoth: the FP8
 // items first, then the TQ3 items, in one grid so the small FP8 share runs
@@ -935,12 +1031,12 @@ __device__ __forceinline__ void run_item(
 // q_t (the rotated queries) and rotate their partial states back.
 template <int D, int MODE, bool MQ, int RB, bool ROT = false>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(kAttendWgPerCu, kAttendWgPerCu))) attend_kernel(
+    __attribute__((amdgpu_waves_per_eu(kAttendWavesPerSimd, kAttendWavesPerSimd))) attend_kernel(
         LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, const float* __restrict__ q_t,
         size_t q_ls, float qscale, Plan plan, AppendIn ap) {
   __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
 
-  static_assert(kWaves <= 4, "a chunk-table entry holds the first page of 4 waves");
+  static_assert(kWaves == kItemWaves, "a chunk-table entry holds the first page of every wave");
   const int nblk = MQ ? plan.nblk : 1;
   // Items: the TQ3 ones first, then the FP8 ones; within a format item
   // ((chunk L + layer) Hkv + h) nblk + blk, so an item's chunk does not depend
@@ -949,10 +1045,10 @@ __global__ void __launch_bounds__(kThreads)
   // the item turns out to be a TQ3 one).
   // (32-bit unsigned index arithmetic: items per launch stay far below 2^31)
   const unsigned per_chunk = (unsigned)(n_layers * hkv * nblk);
-  const cptr_i8 tab_t = (cptr_i8)plan.chunks_t, tab_f = (cptr_i8)plan.chunks_f;
+  const cptr_i16 tab_t = (cptr_i16)plan.chunks_t, tab_f = (cptr_i16)plan.chunks_f;
   const int spec = (int)(blockIdx.x / per_chunk);
-  const i8v cd_spec = (MODE != kFp8Only && plan.table_cap > 0) ? tab_t[spec < plan.table_cap ? spec : plan.table_cap - 1]
-                                                                : i8v{};
+  const i16v cd_spec = (MODE != kFp8Only && plan.table_cap > 0) ? tab_t[spec < plan.table_cap ? spec : plan.table_cap - 1]
+                                                                 : i16v{};
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
   const unsigned items_t = per_chunk * nct;
@@ -966,10 +1062,12 @@ __global__ void __launch_bounds__(kThreads)
     const int h = (int)(itc % (unsigned)hkv);
     const int layer = (int)((itc / (unsigned)hkv) % (unsigned)n_layers);
     const int chunk = (int)(itc / (unsigned)(hkv * n_layers));
-    const i8v cd = (tq3 && item == blockIdx.x) ? cd_spec : (tq3 ? tab_t : tab_f)[chunk];
+    const i16v cd = (tq3 && item == blockIdx.x) ? cd_spec : (tq3 ? tab_t : tab_f)[chunk];
     const int b = cd[0], start = cd[1], count = chunk_pages(cd[2]), last_tok = chunk_last_tok(cd[2]), pidx = cd[3];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int first_id = wv == 0 ? cd[4] : (wv == 1 ? cd[5] : (wv == 2 ? cd[6] : cd[7]));
+    int first_id = cd[4];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) first_id = wv == w ? cd[4 + w] : first_id;
     const bool holds_tail = (cd[2] & kChunkHoldsTail) != 0;
     if (pidx >= plan.np_cap) {               // plan made for fewer layers than this call
       if (threadIdx.x == 0) atomicOr(plan.status, kDevBadSeqLen);
@@ -989,17 +1087,33 @@ __global__ void __launch_bounds__(kThreads)
       rb.req_last = req[R_TAIL * rowlen + b];
     }
     if (MODE != kFp8Only && tq3)
-      run_item<D, true, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id, smem,
-                                nullptr, rb);
+      run_item<D, true, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
+                                holds_tail, smem, nullptr, rb);
     if (MODE != kTq3Only && !tq3)
       run_item<D, false, MQ, RB, ROT>(lt, hkv, G, q, q_t, q_ls, qscale, plan, layer, h, b, start, count, last_tok, pidx, first_id,
-                                 smem, (holds_tail && (!MQ || plan.n_query == 1)) ? &ap : nullptr, rb);
+                                 holds_tail, smem, (holds_tail && (!MQ || plan.n_query == 1)) ? &ap : nullptr, rb);
     __syncthreads();
   }
 }
 
+// One workgroup per CU (a workgroup fills its CU's registers), each taking
+// work items blockIdx.x, blockIdx.x + gridDim.x, ...: a grid larger than the
+// CU count would only add workgroups that wait for a CU to free up.
+static int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 static dim3 attend_grid(long cap) {
-  return dim3((unsigned)(cap < 2048 ? (cap > 0 ? cap : 1) : 2048));
+  const long cus = cu_count();
+  return dim3((unsigned)(cap < cus ? (cap > 0 ? cap : 1) : cus));
 }
 
 // Queries of rotated TQ3 pages: q' = H (signs . q) / (c d) per row of D

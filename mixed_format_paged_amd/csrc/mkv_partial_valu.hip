@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(256) partial_valu_kernel(
     const int h = (int)(item % hkv);
     const int chunk = (int)((item / hkv) % n_chunks);
     const int layer = (int)(item / ((long)hkv * n_chunks));
-    const int4 cd = chunks[2 * chunk];
+    const int4 cd = chunks[(kChunkInts / 4) * chunk];
     const int b = cd.x, start = cd.y, count = chunk_pages(cd.z), last_tok = chunk_last_tok(cd.z), pidx = cd.w;
     if (pidx >= plan.np_cap) {                 // plan made for more layers than this call
       if (tid == 0) atomicOr(plan.status, kDevBadSeqLen);

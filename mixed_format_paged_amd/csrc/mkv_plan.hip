@@ -170,12 +170,27 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   block_exclusive_scan<1024>(pack2(sf, st), &tot2, sh);
   const int TF = lo32(tot2), TT = hi32(tot2);
   const int status = block_or_bits(serr);
-  // One chunk size for both formats, so the work items of a launch are of
-  // equal size whatever the mix: about chunks_target chunks in all, less one
-  // tail chunk per request and format, so the items fill one wave of
-  // workgroups.
-  const int tgt = max(1, plan.chunks_target - 2 * B);
-  const int ppf = min(kMaxChunkPages, max(kMinChunkPages, (TF + TT + tgt - 1) / tgt));
+  // Chunk size: every (request, format) segment of n pages is cut into
+  // ceil(n / P) chunks of balanced size (floor or ceil of n / chunks), with P
+  // the smallest size (at least kMinChunkPages) that keeps the chunk count
+  // within chunks_target, so the items fill the CUs once with the least work
+  // per item.  P = ceil(total / (target - 2 B)) always fits (each segment adds
+  // at most one part-filled chunk); a binary search below it finds the
+  // smallest.  Past kMaxChunkPages pages per chunk, longer contexts get more
+  // chunks than the target instead.
+  const int target = plan.chunks_target;
+  const int tgt = max(1, target - 2 * B);
+  int p_hi = min(kMaxChunkPages, max(kMinChunkPages, (TF + TT + tgt - 1) / tgt));
+  int p_lo = min(p_hi, max(kMinChunkPages, (TF + TT + target - 1) / max(1, target)));
+  while (p_lo < p_hi) {                                   // uniform over the block
+    const int mid = (p_lo + p_hi) >> 1;
+    int c = 0;
+    for (int b = tid; b < B; b += 1024) c += (nf_row[b] + mid - 1) / mid + (nt_row[b] + mid - 1) / mid;
+    int tot;
+    block_exclusive_scan<1024>(c, &tot, reinterpret_cast<int*>(sh));
+    if (tot <= target) p_hi = mid; else p_lo = mid + 1;
+  }
+  const int ppf = p_hi;
   const int ppt = ppf;
   // per-request counts and their prefix sums
   int carry_f = 0, carry_t = 0, carry_p = 0;
@@ -235,16 +250,23 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const int b = lo;
       const int local = c - co[b];
       const int nchunks = co[b + 1] - co[b];
-      const int start = local * pp;
-      const int count = min(pp, cnt[b] - start);
+      (void)pp;
+      // balanced cut of the segment's n pages into nchunks chunks
+      const int n_seg = cnt[b];
+      const int start = (int)((int64_t)local * n_seg / nchunks);
+      const int count = (int)((int64_t)(local + 1) * n_seg / nchunks) - start;
       const bool holds_tail = local == nchunks - 1 && lastfmt[b] == fmt;
       const int last_tok = holds_tail ? tail[b] : 16;
       const int pidx = po[b] + (fmt ? (cf[b + 1] - cf[b]) : 0) + local;
       const int first = bt_offsets[b] + start;
       const int* lst = fmt ? plan.list_t : plan.list_f;
-      out[2 * c] = make_int4(b, first, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
-      out[2 * c + 1] = make_int4(lst[first], lst[first + min(1, count - 1)], lst[first + min(2, count - 1)],
-                                 lst[first + min(3, count - 1)]);
+      int4* const ent = out + (kChunkInts / 4) * c;
+      ent[0] = make_int4(b, first, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
+      int fid[kItemWaves];
+#pragma unroll
+      for (int w = 0; w < kItemWaves; ++w) fid[w] = lst[first + chunk_order(min(w, count - 1), count, holds_tail)];
+#pragma unroll
+      for (int q = 0; q < kItemWaves / 4; ++q) ent[1 + q] = make_int4(fid[4 * q], fid[4 * q + 1], fid[4 * q + 2], fid[4 * q + 3]);
     }
   }
 }
