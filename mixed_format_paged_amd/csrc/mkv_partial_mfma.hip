@@ -198,7 +198,11 @@ __device__ inline void stage_row(const void* __restrict__ src, void* dst, int la
 // pages it has left (left[], LDS) and, against its two siblings, takes the
 // highest priority when it has the most left and the lowest when it has the
 // fewest, so the three finish together.
-__device__ inline void progress_prio(volatile int* left, int wave, int pages_left) {
+// left[] is read through a plain LDS pointer: the page loops' asm statements
+// clobber memory, so it is read again on every page (a volatile generic
+// pointer would compile to flat loads, which count against the vector-memory
+// counter the staging waits rely on).
+__device__ inline void progress_prio(int* left, int wave, int pages_left) {
   if (__builtin_amdgcn_mbcnt_lo(~0u, 0) == 0) left[wave] = pages_left;
   const int a = __builtin_amdgcn_readfirstlane(left[wave < 8 ? wave + 4 : wave - 8]);
   const int b = __builtin_amdgcn_readfirstlane(left[wave < 4 ? wave + 8 : wave - 4]);
@@ -587,7 +591,7 @@ __device__ __forceinline__ void run_item(
   uint8_t* const slot0 = smem + wave * (NS == 3 ? GD::kWaveRing3 : 2 * kSlot);
   uint8_t* const slot1 = slot0 + kSlot;      // FP8: K halves in slot0, V halves in slot1
   h8* const sq = reinterpret_cast<h8*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing));
-  volatile int* const s_left = reinterpret_cast<volatile int*>(
+  int* const s_left = reinterpret_cast<int*>(
       smem + (NS == 3 ? GD::kRing3 : GD::kRing) + (RB == 16 ? 2 : 1) * GD::kSq + kWaves * 16 * 4);
   // FP8 K codes enter the score MFMAs as they are; the layer's k_scale
   // multiplies the fp32 scores (TQ3 K scales are in the group scales)
