@@ -105,9 +105,10 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.rowblk = rowblk;
   s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
-  // chunks per format <= min(pages / kMinChunkPages, max(target, pages / kMaxChunkPages)) + batch
+  // chunks per format <= min(pages / kMinChunkPages, max(target, weighted
+  // pages / kMaxChunkPages)) + batch (an FP8 page weighs 16/7 TQ3 pages)
   const int by_pages = (bt_capacity + kMinChunkPages - 1) / kMinChunkPages;
-  const int by_max = (bt_capacity + kMaxChunkPages - 1) / kMaxChunkPages;
+  const int by_max = max_size_chunks(bt_capacity);
   auto chunk_bound = [&](int target) {
     const int t = target > by_max ? target : by_max;
     return (t < by_pages ? t : by_pages) + batch;
@@ -115,10 +116,11 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   // chunk tables: sized for the largest chunk count any layer count can plan
   s.table_cap = chunk_bound((kTargetItems + hkv - 1) / hkv);
   // partial states per layer of a plan made for this layer count.  The planner
-  // takes pp >= pages / max(1, target - 2 batch) pages per chunk (or pp =
+  // takes pp >= weighted pages / max(1, target - 2 batch) per chunk (or pp =
   // kMaxChunkPages) and each request adds at most one part-filled chunk per
-  // format, so NP < max(target, pages / kMaxChunkPages) + 2 batch; and never
-  // more than one chunk per kMinChunkPages pages plus one per request and format.
+  // format, so NP < max(target, weighted pages / kMaxChunkPages) + 2 batch; and
+  // never more than one chunk per kMinChunkPages pages plus one per request
+  // and format.
   const int t = s.chunks_target > by_max ? s.chunks_target : by_max;
   s.np_cap = t + 2 * batch < 2 * (by_pages + batch) ? t + 2 * batch : 2 * (by_pages + batch);
   size_t o = 0;

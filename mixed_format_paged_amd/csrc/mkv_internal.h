@@ -26,6 +26,22 @@ constexpr int kItemWaves = 4 * kAttendWavesPerSimd;
 constexpr int kTargetItems = 256;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk: longer contexts get more chunks than the target
+// An FP8 page-head carries 32 d bytes against 14 d for TQ3, and a split-K
+// item's time follows its bytes, so an FP8 page counts kFp8Weight = 16 / 7 TQ3
+// pages when chunks are cut: an FP8 segment of nf pages at chunk size P (in
+// TQ3 pages) takes ceil(16 nf / (7 P)) chunks, never fewer than kMinChunkPages
+// pages each.
+__host__ __device__ inline int fp8_chunk_count(int nf, int P) {
+  if (nf <= 0) return 0;
+  const int by_weight = (int)(((long long)nf * 16 + 7LL * P - 1) / (7LL * P));
+  const int by_min = (nf + kMinChunkPages - 1) / kMinChunkPages;
+  return by_weight < by_min ? by_weight : by_min;
+}
+// Upper bound of the chunks of any plan for bt_capacity pages at chunk size
+// kMaxChunkPages, in weighted pages (the FP8 weight applied to every page).
+__host__ __device__ inline int max_size_chunks(int bt_capacity) {
+  return (int)(((long long)bt_capacity * 16 + 7LL * kMaxChunkPages - 1) / (7LL * kMaxChunkPages));
+}
 constexpr int kMaxG = 8;              // query rows of an 8-row block (attend wave states, merge row groups)
 constexpr int kMaxGroup = 16;         // query heads per KV head supported (more than 8: 16-row blocks)
 constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8;
@@ -49,7 +65,7 @@ enum TotalField {
   T_NCF = 0,     // FP8 chunks in total
   T_NCT,         // TQ3 chunks in total
   T_NP,          // partials per layer
-  T_PPF,         // pages per FP8 chunk
+  T_PPF,         // FP8 chunk size in TQ3 pages (each FP8 page weighs 16/7)
   T_PPT,         // pages per TQ3 chunk
   T_FIELDS = 16
 };

@@ -72,6 +72,13 @@ __device__ inline float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// max of four scores (finite or -inf: arithmetic results, so no signalling
+// NaN to quiet and no canonicalising moves)
+__device__ inline float max4(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return r;
+}
 __device__ inline float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -85,20 +92,19 @@ __device__ inline float dpp_ror8(float x) {             // lane l <- lane (l ^ 8
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
 }
 
-// Byte `o` of a little-endian array of dwords, as the start of a triple: the
-// three dwords X = [b0 b1 b2 .], Y = [b1 b2 b0 b1], W = [b1 b2 b1 b2].
 typedef uint32_t u6 __attribute__((ext_vector_type(6)));
 typedef _Float16 h32 __attribute__((ext_vector_type(32)));
 typedef uint32_t u16v __attribute__((ext_vector_type(16)));
 
-// 4 triples = 32 codes = 3 words of a lane's code stream (code k of the
-// stream at bits [3k, 3k + 3), little endian) -> 32 fp16 codes u, exact.
-// Read as 6-bit fields, the stream holds two codes per field.  With the high
-// code masked away a field is an E2M3 value with zero exponent bits, i.e. the
-// subnormal u / 8, and gfx950 converts 32 such fields in one instruction
-// (scale 8 makes them u).  The high codes take a second pass over the stream
-// shifted down by 3 bits.  Element i < 16 is the low code of field i (slot
-// 2 (i % 4) of triple i / 4), element 16 + i the high code (slot 2 (i % 4) + 1).
+// V codes of a 12-byte block (4 triples = 32 codes, code k of the stream at
+// bits [3k, 3k + 3), little endian) -> 32 fp16 codes u, exact (normal fp16,
+// which the V scales multiply exactly into hi + lo pairs).  Read as 6-bit
+// fields, the stream holds two codes per field.  With the high code masked
+// away a field is an E2M3 value with zero exponent bits, i.e. the subnormal
+// u / 8, and gfx950 converts 32 such fields in one instruction (scale 8 makes
+// them u).  The high codes take a second pass over the stream shifted down by
+// 3 bits.  Element i < 16 is the low code of field i (slot 2 (i % 4) of triple
+// i / 4), element 16 + i the high code (slot 2 (i % 4) + 1).
 __device__ inline h32 decode32(uint32_t w0, uint32_t w1, uint32_t w2) {
   // low 3 bits of every 6-bit field; the pattern repeats every 3 words
   constexpr uint32_t M0 = 0xC71C71C7u, M1 = 0x71C71C71u, M2 = 0x1C71C71Cu;
@@ -111,6 +117,38 @@ __device__ inline h32 decode32(uint32_t w0, uint32_t w1, uint32_t w2) {
   f[5] = (w2 >> 3) & M2;                  // M2 keeps bits <= 28: nothing comes from a next word
   return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(f, 8.0f);
 }
+
+// K codes of a 12-byte block (w0..w2, 16 six-bit fields, mkv_format.h)
+// straight into MFMA operands, with shifts and masks only.  Window q of the
+// block is the block shifted right by 6 f0 - 4 bits, f0 the first field of
+// fields f0 and f0 + 2, f0 = 0, 1, 4, 5, 8, 9, 12, 13 for q = 0..7; in it the
+// low code of field f0 sits at bits 4..6, that of f0 + 2 at 16..18, and their
+// high codes at 7..9 and 19..21.  Masked (kLoCodes, kHiCodes), a window is
+// two fp16 values of one scale group: u 2^(s - 24) with s the code's bit
+// position in its half (subnormals, which the matrix cores take exactly).
+// Windows 0..3 with kLoCodes hold group 4b of the block, 4..7 group 4b + 1;
+// with kHiCodes, 4b + 2 and 4b + 3.  An operand of 4 windows lists the
+// group's channels (of the lane's 8) in the order tq3_channel gives.
+constexpr uint32_t kLoCodes = 0x00070070u;
+constexpr uint32_t kHiCodes = 0x00380380u;
+__device__ inline void code_windows(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t (&x)[8]) {
+  x[0] = w0 << 4;                                   // fields 0, 2
+  x[1] = w0 >> 2;                                   // 1, 3
+  x[2] = __builtin_amdgcn_alignbit(w1, w0, 20);     // 4, 6
+  x[3] = __builtin_amdgcn_alignbit(w1, w0, 26);     // 5, 7
+  x[4] = __builtin_amdgcn_alignbit(w2, w1, 12);     // 8, 10
+  x[5] = __builtin_amdgcn_alignbit(w2, w1, 18);     // 9, 11
+  x[6] = w2 >> 4;                                   // 12, 14
+  x[7] = w2 >> 10;                                  // 13, 15
+}
+// fp16 element k (0..7) of a 4-window operand: channel of the lane's 8
+// (field f0 + (k & 1) * 2 of window k / 2) and the bit position of its code
+// (low codes at 4 / 0 in the low / high half, high codes at 7 / 3)
+__host__ __device__ constexpr int tq3_channel(int k) { return (k & ~3) + ((k >> 1) & 1) + 2 * (k & 1); }
+__host__ __device__ constexpr int tq3_code_shift(bool hi_codes, int k) { return (hi_codes ? 3 : 0) + ((k & 1) ? 0 : 4); }
+static_assert(tq3_channel(0) == 0 && tq3_channel(1) == 2 && tq3_channel(2) == 1 && tq3_channel(3) == 3 &&
+              tq3_channel(4) == 4 && tq3_channel(5) == 6 && tq3_channel(6) == 5 && tq3_channel(7) == 7,
+              "windows hold fields (0, 2), (1, 3), (4, 6), (5, 7)");
 
 typedef __attribute__((address_space(3))) void lds_void;
 // Page lists and chunk tables are read-only during the launch: read them
@@ -141,7 +179,8 @@ struct Geo {
   static constexpr int kSq = NG * 64 * 16;
   static constexpr int kRowMax = kWaves * 16 * 4 + 64; // per-wave query-row maxima (prologue), then the
                                                         // waves' pages left (page loops)
-  static constexpr int kLds = kRing3 + kSq + kRowMax;
+  static constexpr int kKsum = NG * 16 * 4;         // TQ3 offset sums per group and column (prologue)
+  static constexpr int kLds = kRing3 + kSq + kRowMax + kKsum;
 };
 
 // Staging unit: the bytes a wave moves to one LDS slot.  For TQ3 a unit is
@@ -264,7 +303,7 @@ constexpr int kSmemBytes = Geo<D>::kLds > kRotBytes<D> ? Geo<D>::kLds : kRotByte
 
 // 16-row blocks keep fp16(q) and its remainder as two fragment sets (2 kSq).
 template <int D>
-constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq + Geo<D>::kRowMax;
+constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq + Geo<D>::kRowMax + Geo<D>::kKsum;
 template <int D>
 constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::bytes(16) ? kLds16<D> : MergeLayout<D>::bytes(16);
 static_assert(kSmemBytes<256> <= 160 * 1024 && kSmemBytes16<256> <= 160 * 1024, "LDS of one workgroup");
@@ -326,12 +365,11 @@ struct WaveState {
   template <bool MQ, int RB = 8>
   __device__ inline h4 softmax(f4 s, float sc, int ntok, float lo_sel, int j, bool first, int dist0 = 0,
                                int lim = 0, h4* p_lo = nullptr) {
+    // scores stay in fragment units (score = s sc, sc a power of two, so the
+    // product is exact and the exponent below takes it in one fma)
     if (RB == 8) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] = (s[r] + dpp_ror8(s[r])) * sc;   // hi + lo query rows, in score units
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] *= sc;
+      for (int r = 0; r < 4; ++r) s[r] = s[r] + dpp_ror8(s[r]);   // hi + lo query rows
     }
     if (MQ) {
       if (dist0 < kNoMask) {
@@ -348,7 +386,7 @@ struct WaveState {
     // max (a row's max exceeds m_run + kRescale iff one of its lanes' does);
     // the row maximum itself, over the four lanes of the column, is needed
     // only on a wave's first page and when some row moves
-    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const float lm = max4(s[0], s[1], s[2], s[3]) * sc;
     const float pm = (first || __any(lm > m_run + kRescale)) ? max_xor32(max_xor16(lm)) : lm;
     const bool need = pm > m_run + kRescale;
     if (first) {
@@ -371,7 +409,7 @@ struct WaveState {
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);   // v_exp_f32; 0 for masked tokens
+      p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -m_use));   // v_exp_f32; 0 for masked tokens
       l_run += p[r];
     }
     if (RB == 16) {
@@ -394,9 +432,15 @@ struct RowBlock {
   int req_last;  // tokens on the request's last page
 };
 
+// The TQ3 offset operand (kneg) is built 2^17 above the query units of the
+// fragments, so its fp16 parts keep about 22 bits whatever the group sums
+// (|x| < 2^-9 in those units puts 4 times a group sum below 2^15).
+constexpr float kKnegUp = 131072.0f, kKnegDown = 1.0f / 131072.0f;
+
 // Scores of one TQ3 page-head staged at pg: one 16x16x32 MFMA per 32-channel
-// scale group on the codes u, its result scaled by the group's fp16 scale of
-// each token.  The offset -4 s(t, g) sum_{c in g} q(c), summed over the
+// scale group on the codes u (masked windows of the code stream, fp16
+// subnormals u 2^(shift - 24), against fragments that carry 2^(24 - shift)),
+// its result scaled by the group's fp16 scale of each token.  The offset -4 s(t, g) sum_{c in g} q(c), summed over the
 // groups, is one 16x16x16 MFMA that seeds the scores: A = the token scales
 // (token n = lane & 15, k = 4 j + e -> group (4 j + e) % NG), B = kneg (the
 // lane's query row, minus four times the group sums of q as fp16 hi / lo
@@ -411,6 +455,7 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
 #pragma unroll
   for (int e = 0; e < 4; ++e) as[e] = lds_load<_Float16>(sp + 8 * e);
   f4 s = __builtin_amdgcn_mfma_f32_16x16x16f16(as, kneg, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+  s *= kKnegDown;                                       // kneg carries 2^17 (fp16 range of its parts)
   auto k_scales = [&](int g) { return lds_load<u2>(pg + 12 * D + 8 * (j * NG + g)); };  // tokens 4j..4j+3
   h8 bq = sq[lane];
   h8 bl = RB == 16 ? sq[NG * 64 + lane] : bq;
@@ -429,13 +474,16 @@ __device__ inline f4 tq3_scores(const uint8_t* pg, const h8* sq, int lane, int j
     // the block's 3 code words are read only now, so one block's codes are live at a time
     const uint32_t w0 = lds_load<uint32_t>(kp + 12 * b), w1 = lds_load<uint32_t>(kp + 12 * b + 4),
                    w2 = lds_load<uint32_t>(kp + 12 * b + 8);
-    const u16v u = __builtin_bit_cast(u16v, decode32(w0, w1, w2));
+    uint32_t x[8];
+    code_windows(w0, w1, w2, x);
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
       const int g = 4 * b + gg;
-      // group g: channels 8j .. 8j + 7 in words 4gg .. 4gg + 3 (low codes of
-      // fields 8 (gg % 2) .. + 7 for gg < 2, their high codes for gg >= 2)
-      const h8 a = __builtin_bit_cast(h8, u4{u[4 * gg], u[4 * gg + 1], u[4 * gg + 2], u[4 * gg + 3]});
+      // group g: the lane's 8 channels as fp16 subnormals u 2^(shift - 24),
+      // in tq3_channel order (the B fragments carry the matching 2^(24 - shift))
+      const int w = 4 * (gg & 1);
+      const uint32_t m = gg < 2 ? kLoCodes : kHiCodes;
+      const h8 a = __builtin_bit_cast(h8, u4{x[w] & m, x[w + 1] & m, x[w + 2] & m, x[w + 3] & m});
       f4 sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
       if (RB == 16) sg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sg, 0, 0, 0);
       const u2 sk_g = sk;
@@ -667,92 +715,100 @@ __device__ __forceinline__ void run_item(
   (void)q_loads;
   __syncthreads();                                          // every wave's query rows
 
-  // ---- B operand of the score MFMAs, shared by the 4 waves through LDS:
-  //      query rows 0..G-1 carry fp16(x), rows 8..8+G-1 the remainder; with
-  //      16-row blocks all 16 columns are rows, fp16(x) in the first fragment
+  // ---- B operand of the score MFMAs, shared by the waves through LDS:
+  //      query rows 0..G-1 carry fp16(y), rows 8..8+G-1 the remainder; with
+  //      16-row blocks all 16 columns are rows, fp16(y) in the first fragment
   //      set and the remainder in the second.  x = q qscale 2^F, with F a
   //      power of two per query row that puts the row's largest |x| in
-  //      [128, 256): the fp16 pair then holds x to about 22 bits of the row's
-  //      maximum whatever the size of q (and of the layer scales), and four
-  //      times a group sum (the TQ3 offset operand, at most 4 * 32 * 256)
-  //      stays inside fp16.  Scores are multiplied by 2^-F in fp32.
+  //      [128, 256) for FP8 items and in [2^-10, 2^-9) for TQ3 items, and
+  //      y = x for FP8.  For TQ3, entry k of a fragment is channel
+  //      tq3_channel(k) of the lane's quarter (the order in which tq3_scores
+  //      extracts the codes) and y = x 2^(24 - tq3_code_shift(g, k)): the codes
+  //      enter the MFMA as fp16 subnormals u 2^(shift - 24), so each product
+  //      is u x, and y stays below 2^15.  The fp16 pair holds y to about 22
+  //      bits of the row's maximum whatever the size of q (and of the layer
+  //      scales).  Scores are multiplied by 2^-F in fp32.
   //      A thread's row is that of its lane's MFMA column (lane & 15), so the
   //      same F scales its fragments and, later, its column of scores.
   static_assert(NG * 64 <= kThreads, "one fragment entry per thread");
-  constexpr int IT = 1;
   const bool builds = threadIdx.x < NG * 64;  // this thread builds fragment entry threadIdx.x
-  float xq[IT][8];
+  const int fe = threadIdx.x;
+  const int fg = fe >> 6, fjj = (fe & 63) >> 4;
+  float xq[8];
   float lmax = 0.0f;
   const int qrow_i = RB == 16 ? n : (n & 7);  // this thread's query row (MFMA column n)
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = threadIdx.x + kThreads * it;
-    const int g = e >> 6, jj = (e & 63) >> 4;
+  {
     const bool use = qrow_i < rb.rows && builds;
     const float* qrow = qbuf + (use ? qrow_i : 0) * D;
-    const int c0 = builds ? (tq3 ? 32 * g + 8 * jj : jj * (D / 4) + 8 * g) : 0;
+    const int c0 = builds ? (tq3 ? 32 * fg + 8 * fjj : fjj * (D / 4) + 8 * fg) : 0;
     const float4 a = *reinterpret_cast<const float4*>(qrow + c0);
     const float4 c = *reinterpret_cast<const float4*>(qrow + c0 + 4);
     const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      xq[it][k] = (use ? v[k] : 0.0f) * qscale;
-      lmax = fmaxf(lmax, fabsf(xq[it][k]));
+      xq[k] = (use ? v[tq3 ? tq3_channel(k) : k] : 0.0f) * qscale;
+      lmax = fmaxf(lmax, fabsf(xq[k]));
     }
   }
   // the row's maximum: over the lanes of the row in this wave (RB 8: lanes
-  // n and n ^ 8 hold the same row), then over the 4 waves through LDS
+  // n and n ^ 8 hold the same row), then over the waves through LDS
   if (lane == 0) s_left[wave] = my_pages;     // pages left, read by the page loops' priorities
   if (RB == 8) lmax = fmaxf(lmax, dpp_ror8(lmax));
   lmax = max_xor32(max_xor16(lmax));
   float* const srm = reinterpret_cast<float*>(smem + (NS == 3 ? GD::kRing3 : GD::kRing) + (RB == 16 ? 2 : 1) * GD::kSq);
+  float* const ksum = srm + GD::kRowMax / 4;  // TQ3: per group and column, the sum its offset takes
   if (lane < (RB == 16 ? 16 : 8)) srm[wave * 16 + lane] = lmax;
   __syncthreads();
   float rmax = 0.0f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) rmax = fmaxf(rmax, srm[w * 16 + qrow_i]);
-  int F = rmax > 0.0f ? 8 - __builtin_amdgcn_frexp_expf(rmax) : 0;
+  int F = rmax > 0.0f ? (tq3 ? -9 : 8) - __builtin_amdgcn_frexp_expf(rmax) : 0;
   F = F < -100 ? -100 : (F > 100 ? 100 : F);
-  const float up = __builtin_amdgcn_ldexpf(1.0f, F);
   const float qsc = __builtin_amdgcn_ldexpf(1.0f, -F);   // score factor of this lane's column
-#pragma unroll
-  for (int it = 0; it < IT && builds; ++it) {
-    const int e = threadIdx.x + kThreads * it;
+  if (builds) {
+    const bool hi_codes = (fg & 3) >= 2;      // groups 4b + 2, 4b + 3 take the blocks' high codes
     float x0[4], x1[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      x0[k] = xq[it][k] * up;
-      x1[k] = xq[it][k + 4] * up;
+      x0[k] = __builtin_amdgcn_ldexpf(xq[k], F + (tq3 ? 24 - tq3_code_shift(hi_codes, k) : 0));
+      x1[k] = __builtin_amdgcn_ldexpf(xq[k + 4], F + (tq3 ? 24 - tq3_code_shift(hi_codes, k + 4) : 0));
     }
+    h8 f0, f1;
     if (RB == 16) {
-      sq[e] = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
-      sq[NG * 64 + e] = __builtin_shufflevector(split_rows(x0, -1.0f), split_rows(x1, -1.0f), 0, 1, 2, 3, 4, 5, 6, 7);
+      f0 = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
+      f1 = __builtin_shufflevector(split_rows(x0, -1.0f), split_rows(x1, -1.0f), 0, 1, 2, 3, 4, 5, 6, 7);
+      sq[fe] = f0;
+      sq[NG * 64 + fe] = f1;
     } else {
-      sq[e] = __builtin_shufflevector(split_rows(x0, lo_sel), split_rows(x1, lo_sel), 0, 1, 2, 3, 4, 5, 6, 7);
+      f0 = __builtin_shufflevector(split_rows(x0, lo_sel), split_rows(x1, lo_sel), 0, 1, 2, 3, 4, 5, 6, 7);
+      f1 = h8{};
+      sq[fe] = f0;
+    }
+    if (tq3) {
+      // the column's share of the offset: its fragment values taken back to
+      // x units (exact: fp16 times a power of two), summed over the quarter
+      // lanes of the group in this wave
+      float t = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float back = __builtin_amdgcn_ldexpf(1.0f, tq3_code_shift(hi_codes, k) - 24);
+        t = fmaf((float)f0[k] + (RB == 16 ? (float)f1[k] : 0.0f), back, t);
+      }
+      t = sum_xor32(sum_xor16(t));
+      if (lane < 16) ksum[fg * 16 + lane] = t;
     }
   }
   __syncthreads();
 
   // TQ3: B operand of the offset MFMA.  Lane (n, j), k = 4 j + e: minus four
-  // times the sum of query row n's q over group (4 j + e) % NG, fp16 hi for k < NG, the
-  // remainder for NG <= k < 2 NG, 0 beyond.  The group sums come from MFMAs
-  // of the q fragments with a matrix of ones (every output row holds them).
+  // times column n's sum over group (4 j + e) % NG, fp16 hi for k < NG, the
+  // remainder for NG <= k < 2 NG, 0 beyond.
   h4 kneg = h4{};
   if (tq3) {
-    constexpr h8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
-    float qs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, sq[g * 64 + lane], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      if (RB == 16) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, sq[NG * 64 + g * 64 + lane], c, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((4 * j + e) % NG == g) qs[e] = c[0];
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int k = 4 * j + e;
-      const float x = -4.0f * qs[e];       // the -4 code offset, times the group sum
+      const float x = -4.0f * kKnegUp * ksum[(k % NG) * 16 + n];   // the -4 code offset, times the group sum
       const _Float16 hi = (_Float16)x;
       const _Float16 lo = (_Float16)(x - (float)hi);
       kneg[e] = k < NG ? hi : (k < 2 * NG ? lo : (_Float16)0.0f);

@@ -170,35 +170,40 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   block_exclusive_scan<1024>(pack2(sf, st), &tot2, sh);
   const int TF = lo32(tot2), TT = hi32(tot2);
   const int status = block_or_bits(serr);
-  // Chunk size: every (request, format) segment of n pages is cut into
-  // ceil(n / P) chunks of balanced size (floor or ceil of n / chunks), with P
-  // the smallest size (at least kMinChunkPages) that keeps the chunk count
-  // within chunks_target, so the items fill the CUs once with the least work
-  // per item.  P = ceil(total / (target - 2 B)) always fits (each segment adds
-  // at most one part-filled chunk); a binary search below it finds the
-  // smallest.  Past kMaxChunkPages pages per chunk, longer contexts get more
-  // chunks than the target instead.
+  // Chunk size: every (request, format) segment is cut into chunks of
+  // balanced size (floor or ceil of n / chunks): a TQ3 segment of n pages
+  // into ceil(n / P), an FP8 one into fp8_chunk_count(n, P) (its pages weigh
+  // 16/7), with P the smallest size (at least kMinChunkPages) that keeps the
+  // chunk count within chunks_target, so the items fill the CUs once with the
+  // least work per item.  P = ceil(W / (target - 2 B)), W the weighted page
+  // total, always fits (each segment adds at most one part-filled chunk); a
+  // binary search below it finds the smallest.  Past kMaxChunkPages pages per
+  // chunk, longer contexts get more chunks than the target instead.
   const int target = plan.chunks_target;
   const int tgt = max(1, target - 2 * B);
-  int p_hi = min(kMaxChunkPages, max(kMinChunkPages, (TF + TT + tgt - 1) / tgt));
-  int p_lo = min(p_hi, max(kMinChunkPages, (TF + TT + target - 1) / max(1, target)));
+  const long long W = (long long)TT + ((long long)TF * 16 + 6) / 7;
+  auto size_for = [&](long long div) {
+    const long long p = (W + div - 1) / div;
+    return (int)(p < kMinChunkPages ? kMinChunkPages : (p > kMaxChunkPages ? kMaxChunkPages : p));
+  };
+  int p_hi = size_for(tgt);
+  int p_lo = min(p_hi, size_for(max(1, target)));
   while (p_lo < p_hi) {                                   // uniform over the block
     const int mid = (p_lo + p_hi) >> 1;
     int c = 0;
-    for (int b = tid; b < B; b += 1024) c += (nf_row[b] + mid - 1) / mid + (nt_row[b] + mid - 1) / mid;
+    for (int b = tid; b < B; b += 1024) c += fp8_chunk_count(nf_row[b], mid) + (nt_row[b] + mid - 1) / mid;
     int tot;
     block_exclusive_scan<1024>(c, &tot, reinterpret_cast<int*>(sh));
     if (tot <= target) p_hi = mid; else p_lo = mid + 1;
   }
-  const int ppf = p_hi;
-  const int ppt = ppf;
+  const int ppt = p_hi;
   // per-request counts and their prefix sums
   int carry_f = 0, carry_t = 0, carry_p = 0;
   for (int base = 0; base < B; base += 1024) {
     const int b = base + tid;
     int nfc = 0, ntc = 0, np = 0;
     if (b < B) {
-      nfc = (nf_row[b] + ppf - 1) / ppf;
+      nfc = fp8_chunk_count(nf_row[b], ppt);
       ntc = (nt_row[b] + ppt - 1) / ppt;
       np = nfc + ntc;
     }
@@ -225,7 +230,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     plan.totals[T_NCF] = carry_f;
     plan.totals[T_NCT] = carry_t;
     plan.totals[T_NP] = carry_p;
-    plan.totals[T_PPF] = ppf;
+    plan.totals[T_PPF] = ppt;
     plan.totals[T_PPT] = ppt;
   }
   __syncthreads();
@@ -238,7 +243,6 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   for (int fmt = 0; fmt < 2; ++fmt) {
     const int* co = fmt ? ct : cf;
     const int total = co[B];
-    const int pp = fmt ? ppt : ppf;
     const int* cnt = fmt ? nt_row : nf_row;
     int4* out = fmt ? plan.chunks_t : plan.chunks_f;
     for (int c = tid; c < total && c < plan.table_cap; c += 1024) {
@@ -250,7 +254,6 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const int b = lo;
       const int local = c - co[b];
       const int nchunks = co[b + 1] - co[b];
-      (void)pp;
       // balanced cut of the segment's n pages into nchunks chunks
       const int n_seg = cnt[b];
       const int start = (int)((int64_t)local * n_seg / nchunks);
