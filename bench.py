@@ -48,6 +48,7 @@ def parse():
                     help="append with its own launch (mkv_append) instead of inside the attend launch")
     ap.add_argument("--no-control", action="store_true", help="skip the same-run all-FP8 control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-units", type=int, default=6, help="(layer, request, KV head) units the oracle is timed on")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (counter calibration)")
@@ -145,13 +146,18 @@ class Runner:
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+        # an event between consecutive steps: the mean is first to last, and
+        # each step's own time gives the spread
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
+        for i in range(steps):
             run()
-        e1.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        self.step_p10 = per[int(0.1 * (steps - 1))]
+        self.step_p90 = per[int(0.9 * (steps - 1))]
+        return evs[0].elapsed_time(evs[-1]) / steps
 
     def time_kernels(self, reps=32):
         """Average and median duration of the partial-attention launch (both
@@ -433,35 +439,33 @@ def copy_calibration(nbytes, reps):
     print(f"[bench] copy calibration: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(runner, units):
-    """Time the CPU oracle on a bounded sample of the same step, and check the
-    GPU's outputs for the sampled (layer, request, KV head) units against it."""
+def oracle_units(w, st, picks, out, new_kv=None):
+    """The CPU oracle on sampled (layer, request, KV head) units: its value
+    path (quantise -> dequantise) and fp64 dense attention for the unit's G
+    query heads, compared with the GPU's out [L][B][Hq][d] (numpy).  new_kv(l,
+    b, h) -> (k, v) of the step's appended token, or None.  Returns (oracle
+    seconds, KV bytes the units cover, worst max-abs, worst rel-L2)."""
     import numpy as np
     import torch
     import workloads as W
     from oracle import attention as OA, pool as OP
-    w, st = runner.w, runner.st
-    rng = np.random.default_rng(7)
-    picks = [(int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(units)]
     G = w.Hq // w.Hkv
+    import mixed_format_paged_amd as M
+    layout = (w.Hq, w.Hkv, w.d)
+    tb = M.mkv_tq3_page_bytes(layout) // w.Hkv
+    fb = M.mkv_fp8_page_bytes(layout) // w.Hkv
     by_layer = {}
     for l, b, h in picks:
         by_layer.setdefault(l, []).append((b, h))
-    t_oracle = 0.0
-    worst = 0.0
-    worst_rel = 0.0
-    bytes_done = 0
-    tb = runner.M.mkv_tq3_page_bytes(runner.layout) // w.Hkv
-    fb = runner.M.mkv_fp8_page_bytes(runner.layout) // w.Hkv
-    out = runner.out.cpu().numpy()
+    t_oracle, bytes_done, worst, worst_rel = 0.0, 0, 0.0, 0.0
     for l, items in by_layer.items():
         vals = W.layer_values(w, st, l, device="cuda", requests={b for b, _ in items})
         for b, h in items:
             T = int(st.seq_lens[b])
             k = vals["k"][b][:, h].clone()
             v = vals["v"][b][:, h].clone()
-            k[T - 1] = runner.k_new[l, b, 0, h]          # the step's appended token
-            v[T - 1] = runner.v_new[l, b, 0, h]
+            if new_kv is not None and T > 0:
+                k[T - 1], v[T - 1] = new_kv(l, b, h)
             k, v = k.cpu().numpy(), v.cpu().numpy()
             q = vals["q"][b, h * G:(h + 1) * G].cpu().numpy()
             tiers = st.tiers[st.bt_offsets[b]:st.bt_offsets[b + 1]]
@@ -474,19 +478,199 @@ def cpu_baseline(runner, units):
             bytes_done += int(is_tq3.sum()) * tb + int((~is_tq3).sum()) * fb
             got = out[l, b, h * G:(h + 1) * G].astype(np.float64)
             worst = max(worst, float(np.abs(got - o).max()))
-            worst_rel = max(worst_rel, float(np.linalg.norm(got - o) / np.linalg.norm(o)))
+            worst_rel = max(worst_rel, float(np.linalg.norm(got - o) / max(np.linalg.norm(o), 1e-30)))
         del vals
         torch.cuda.empty_cache()
+    return t_oracle, bytes_done, worst, worst_rel
+
+
+def time_config(name, copies=1, passes=8, units=2):
+    """One of the other workloads, single layer: the whole decode of one layer
+    per pass (mkv_decode_attn: plan, partials, merge; for the demotion
+    workload mkv_demote_pages of its aging pages first), captured in a HIP
+    graph of `copies` passes, one per cache copy (a layer small enough for the
+    last-level cache is held `copies` times over and the passes rotate through
+    the copies, so no pass finds its pages cached), replayed `passes` times.
+    Sampled outputs of copy 0 are checked against the oracle; for the
+    demotion workload a sample of the demoted pages is compared byte for byte
+    with the oracle's pack."""
+    import numpy as np
+    import torch
+    import mixed_format_paged_amd as M
+    import workloads as W
+    from workloads.device_cache import DeviceWorkload
+    from oracle import pool as OP
+    w0 = W.WORKLOADS[name]
+    w = W.scaled(w0, name=f"{name}-{copies}copies", L=copies) if copies > 1 else w0
+    st = W.make_structure(w)
+    t0 = time.time()
+    dw = DeviceWorkload(w, st, "cuda")
+    dw.step_demote()                     # the aging pages of the demotion workload (none elsewhere)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    lay = (w.Hq, w.Hkv, w.d)
+    bat = dw.batch()
+    sm = 1.0 / math.sqrt(w.d)
+    ws = torch.empty(M.mkv_decode_workspace_bytes(lay, w.B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.L, w.B, w.Hq, w.d), device="cuda")
+    lse = torch.empty((w.L, w.B, w.Hq), device="cuda")
+    q = [dw.q[l].contiguous() for l in range(w.L)]
+    demote = dw.d_idx.numel() > 0
+
+    def one(l):
+        if demote:                        # rewrites the same TQ3 bytes every pass
+            dw.cache.demote(l, dw.d_src, dw.d_dst)
+        M.mkv_decode_attn(lay, dw.cache.pools[l], bat, q[l], sm, out[l], lse[l], ws)
+
+    def replay_all():
+        for l in range(w.L):
+            one(l)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        replay_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        replay_all()
+    graph.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
+    evs[0].record()
+    for i in range(passes):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) / w.L for i in range(passes))
+    ms = evs[0].elapsed_time(evs[-1]) / passes / w.L
+    status = M.mkv_workspace_status(ws)
+    # the demotion alone, same launch sizes
+    dem = None
+    if demote:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            dw.cache.demote(0, dw.d_src, dw.d_dst)
+        b.record()
+        torch.cuda.synchronize()
+        dem_ms = a.elapsed_time(b) / 5
+        n_dem = dw.d_src.numel()
+        fb, tb = M.mkv_fp8_page_bytes(lay), M.mkv_tq3_page_bytes(lay)
+        # a sample of the demoted pages against the oracle's pack, byte for byte
+        pick = np.random.default_rng(9).choice(n_dem, 16, replace=False)
+        src = dw.d_src[torch.as_tensor(pick, device="cuda")].cpu().numpy()
+        dst = dw.d_dst[torch.as_tensor(pick, device="cuda")].cpu().numpy() - st.n_fp8
+        pool = OP.Pool(w.Hkv, w.d, 16, 16, 1.0, 1.0)
+        pool.fp8[:] = dw.cache.fp8[0][torch.as_tensor(src, dtype=torch.long, device="cuda")].cpu().numpy()
+        OP.demote(pool, np.arange(16), 16 + np.arange(16))
+        got = dw.cache.tq3[0][torch.as_tensor(dst, dtype=torch.long, device="cuda")].cpu().numpy()
+        dem = {"pages": n_dem, "avg_ms": round(dem_ms, 5), "gbs": round(n_dem * (fb + tb) / (dem_ms * 1e-3) / 1e9, 2),
+               "sample_bitexact_vs_oracle": bool(np.array_equal(got, pool.tq3))}
+    n_t = int((st.tiers == W.TIER_S).sum())
+    n_f = int(st.total_pages - n_t)
+    layer_bytes = n_f * M.mkv_fp8_page_bytes(lay) + n_t * M.mkv_tq3_page_bytes(lay)
+    picks = sorted({(0, int(b), int(h)) for b, h in zip(np.random.default_rng(21).integers(0, w.B, units),
+                                                        np.random.default_rng(22).integers(0, w.Hkv, units))})
+    _, _, worst, worst_rel = oracle_units(w, st, picks, out.cpu().numpy())
+    res = {"workload": name, "batch": w0.B, "tokens": int(st.seq_lens.sum()), "layer_kv_bytes": layer_bytes,
+           "cache_copies": w.L, "ms_per_layer": round(ms, 5), "p10_ms": round(per[int(0.1 * (passes - 1))], 5),
+           "p90_ms": round(per[int(0.9 * (passes - 1))], 5),
+           "kv_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 2),
+           "pct_hbm_peak": round(100 * layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "tokens_per_s": round(w0.B / (ms * 1e-3), 2),
+           "sampled_parity": {"units": len(picks), "max_abs": worst, "rel_l2": worst_rel,
+                              "pass": bool(worst <= 2e-3 and worst_rel <= 1e-3)},
+           "device_status": status, "build_s": round(build_s, 1)}
+    if dem is not None:
+        res["demote_then_decode"] = dict(dem, note="each pass demotes the aging pages, then decodes the layer")
+    del dw, ws, out, lse, q, graph
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_ceiling(nbytes=2 << 30, reps=10):
+    """Streaming HBM rates measured in the same run: a device copy (bytes read
+    + written) and a sum over the buffer (bytes read), each over nbytes."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    x.sum()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, moved in (("copy", lambda: y.copy_(x), 2 * nbytes), ("sum", lambda: x.sum(), nbytes)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"{name}_gbs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    res["bytes"] = nbytes
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(runner, units):
+    """Time the CPU oracle on a bounded sample of the same step, and check the
+    GPU's outputs for the sampled (layer, request, KV head) units against it;
+    then one unit again with the oracle's numeric libraries held to one thread,
+    and the oracle's FP8 -> TQ3 pack on a sample of pages."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import pool as OP
+    w, st = runner.w, runner.st
+    rng = np.random.default_rng(7)
+    picks = [(int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(units)]
+    G = w.Hq // w.Hkv
+    out = runner.out.cpu().numpy()
+    new_kv = lambda l, b, h: (runner.k_new[l, b, 0, h], runner.v_new[l, b, 0, h])   # the step's appended token
+    t_oracle, bytes_done, worst, worst_rel = oracle_units(w, st, picks, out, new_kv)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        t1, bytes1, _, _ = oracle_units(w, st, picks[:1], out, new_kv)
+    # the pack, on 64 pages of random E4M3 bytes (no NaN codes)
+    lay = runner.layout
+    n = 64
+    pool = OP.Pool(w.Hkv, w.d, n, n, 1.0, 1.0)
+    raw = np.random.default_rng(3).integers(0, 254, pool.fp8.shape).astype(np.uint8)
+    raw += (raw >= 0x7F).astype(np.uint8)
+    pool.fp8[:] = raw
+    t0 = time.perf_counter()
+    OP.demote(pool, np.arange(n), n + np.arange(n))
+    t_pack = time.perf_counter() - t0
+    fb, tb = runner.M.mkv_fp8_page_bytes(lay), runner.M.mkv_tq3_page_bytes(lay)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     return {
-        "value": round(bytes_done / t_oracle / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "value": round(bytes_done / t_oracle / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model(), "cores_available": cores,
         "sample": (f"{units} (layer, request, KV head) units of the same step, each the oracle's "
                    f"quantise -> dequantise value path and fp64 attention for its {G} query heads over "
                    f"all {int(st.seq_lens[0])} tokens; {t_oracle:.1f} s of CPU time"),
         "tokens_per_s": round(w.B / (t_oracle / units * w.L * w.B * w.Hkv), 6),
+        "kv_token_layers_per_s": round(units * int(st.seq_lens[0]) / t_oracle, 1),
+        "one_thread": {"value": round(bytes1 / t1 / 1e9, 4), "unit": "GB/s", "sample": "the first unit above", "s": round(t1, 2)},
+        "pack_fp8_to_tq3": {"pages": n, "s": round(t_pack, 3), "pages_per_s": round(n / t_pack, 1),
+                            "gbs": round(n * (fb + tb) / t_pack / 1e9, 5),
+                            "sample": "the oracle's pack of 64 pages of random E4M3 bytes (one layer)"},
         "parity_max_abs": worst, "parity_rel_l2": worst_rel,
     }
 
@@ -544,6 +728,8 @@ def main():
                    "kernel": a.kernel, "graph": not a.no_graph,
                    "append": "separate launch" if a.separate_append else "inside the attend launch"},
         "tokens_per_s": round(w.B / (ms * 1e-3), 2),
+        "kv_token_layers_per_s": round(int(st.seq_lens.sum()) * w.L / (ms * 1e-3), 1),
+        "ms_per_step_p10": round(r.step_p10, 5), "ms_per_step_p90": round(r.step_p90, 5),
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "device_status": status,
@@ -572,7 +758,20 @@ def main():
                                  "kv_gbs_per_query_token": round(4 * layer_bytes / (mq_ms * 1e-3) / 1e9, 2),
                                  "vs_single_query_launch": round(mq_ms / k_avg, 3)},
         "rotated_tq3_one_layer": rot,
+        "stream_ceiling": stream_ceiling(),
     }
+    result["roofline"]["frac_of_measured_copy_ceiling"] = round(
+        result["roofline"]["achieved"] / result["stream_ceiling"]["copy_gbs"], 4)
+    if not a.no_configs:
+        # the other workloads of the benchmark set, one layer each: 8 requests
+        # x 16,384 and one request of 131,072 tokens fit the last-level cache,
+        # so they rotate through 8 cache copies
+        others = []
+        for name, copies in (("batch-8x16384", 8), ("ragged-32x4096-65536", 1), ("demote-64x32768", 1),
+                             ("long-1x131072", 8)):
+            print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+            others.append(time_config(name, copies))
+        result["other_workloads"] = others
     if not a.no_control:
         del r
         torch.cuda.empty_cache()

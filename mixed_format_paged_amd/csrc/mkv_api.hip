@@ -106,7 +106,7 @@ WsSizes workspace_sizes(int hq, int hkv, int d, int batch, int bt_capacity, int 
   s.chunks_target = (kTargetItems + per - 1) / per;
   if (s.chunks_target < 1) s.chunks_target = 1;
   // chunks per format <= min(pages / kMinChunkPages, max(target, weighted
-  // pages / kMaxChunkPages)) + batch (an FP8 page weighs 16/7 TQ3 pages)
+  // pages / kMaxChunkPages)) + batch (an FP8 page weighs 4/3 TQ3 pages)
   const int by_pages = (bt_capacity + kMinChunkPages - 1) / kMinChunkPages;
   const int by_max = max_size_chunks(bt_capacity);
   auto chunk_bound = [&](int target) {

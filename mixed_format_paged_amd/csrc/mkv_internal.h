@@ -26,21 +26,23 @@ constexpr int kItemWaves = 4 * kAttendWavesPerSimd;
 constexpr int kTargetItems = 256;
 constexpr int kMinChunkPages = 4;     // smallest chunk
 constexpr int kMaxChunkPages = 512;   // largest chunk: longer contexts get more chunks than the target
-// An FP8 page-head carries 32 d bytes against 14 d for TQ3, and a split-K
-// item's time follows its bytes, so an FP8 page counts kFp8Weight = 16 / 7 TQ3
-// pages when chunks are cut: an FP8 segment of nf pages at chunk size P (in
-// TQ3 pages) takes ceil(16 nf / (7 P)) chunks, never fewer than kMinChunkPages
-// pages each.
+// Chunks are cut by cost: in the partial-attention kernel an FP8 page-head
+// takes about 4/3 the time of a TQ3 page-head (2.3 times the bytes, a third of
+// the arithmetic), so an FP8 segment of nf pages at chunk size P (in TQ3 pages)
+// takes ceil(4 nf / (3 P)) chunks, never fewer than kMinChunkPages pages each.
+constexpr int kFp8WeightNum = 4, kFp8WeightDen = 3;
 __host__ __device__ inline int fp8_chunk_count(int nf, int P) {
   if (nf <= 0) return 0;
-  const int by_weight = (int)(((long long)nf * 16 + 7LL * P - 1) / (7LL * P));
+  const long long den = (long long)kFp8WeightDen * P;
+  const int by_weight = (int)(((long long)nf * kFp8WeightNum + den - 1) / den);
   const int by_min = (nf + kMinChunkPages - 1) / kMinChunkPages;
   return by_weight < by_min ? by_weight : by_min;
 }
 // Upper bound of the chunks of any plan for bt_capacity pages at chunk size
 // kMaxChunkPages, in weighted pages (the FP8 weight applied to every page).
 __host__ __device__ inline int max_size_chunks(int bt_capacity) {
-  return (int)(((long long)bt_capacity * 16 + 7LL * kMaxChunkPages - 1) / (7LL * kMaxChunkPages));
+  const long long den = (long long)kFp8WeightDen * kMaxChunkPages;
+  return (int)(((long long)bt_capacity * kFp8WeightNum + den - 1) / den);
 }
 constexpr int kMaxG = 8;              // query rows of an 8-row block (attend wave states, merge row groups)
 constexpr int kMaxGroup = 16;         // query heads per KV head supported (more than 8: 16-row blocks)
@@ -65,7 +67,7 @@ enum TotalField {
   T_NCF = 0,     // FP8 chunks in total
   T_NCT,         // TQ3 chunks in total
   T_NP,          // partials per layer
-  T_PPF,         // FP8 chunk size in TQ3 pages (each FP8 page weighs 16/7)
+  T_PPF,         // FP8 chunk size in TQ3 pages (each FP8 page weighs 4/3)
   T_PPT,         // pages per TQ3 chunk
   T_FIELDS = 16
 };

@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   // Chunk size: every (request, format) segment is cut into chunks of
   // balanced size (floor or ceil of n / chunks): a TQ3 segment of n pages
   // into ceil(n / P), an FP8 one into fp8_chunk_count(n, P) (its pages weigh
-  // 16/7), with P the smallest size (at least kMinChunkPages) that keeps the
+  // 4/3), with P the smallest size (at least kMinChunkPages) that keeps the
   // chunk count within chunks_target, so the items fill the CUs once with the
   // least work per item.  P = ceil(W / (target - 2 B)), W the weighted page
   // total, always fits (each segment adds at most one part-filled chunk); a
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   // chunk, longer contexts get more chunks than the target instead.
   const int target = plan.chunks_target;
   const int tgt = max(1, target - 2 * B);
-  const long long W = (long long)TT + ((long long)TF * 16 + 6) / 7;
+  const long long W = (long long)TT + ((long long)TF * kFp8WeightNum + kFp8WeightDen - 1) / kFp8WeightDen;
   auto size_for = [&](long long div) {
     const long long p = (W + div - 1) / div;
     return (int)(p < kMinChunkPages ? kMinChunkPages : (p > kMaxChunkPages ? kMaxChunkPages : p));
