@@ -329,6 +329,18 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool,
                      const int32_t* bt_offsets, const int32_t* bt_pages,
                      int32_t b, int32_t n_pages, uint8_t* out, void* stream);
 
+/* Streaming-read probe (measurement support): read the first
+ * floor(bytes / 3584) * 3584 bytes at src (device, 16-byte aligned) once, in
+ * units of 3584 bytes (one TQ3 page-head at head_dim 256) with the loads the
+ * decode kernels stage pages with (HBM -> LDS, 16 bytes per lane,
+ * non-temporal, three units in flight per wave, one 12-wave workgroup per CU),
+ * computing nothing; its rate is the streaming ceiling of those loads.  Wave
+ * w of the launch XORs the first 32-bit word of each unit it reads into
+ * sink[w] (device, sink_words >= 12 words; the launch uses
+ * 12 * min(CUs, sink_words / 12) of them), so the XOR of those words is the
+ * XOR of every unit's first word. */
+int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+
 /* Materialise: dequantise logical pages [page_lo, page_lo + n_pages) of
  * request b to dense bfloat16 K and V.  The pages' quality profile runs on
  * materialised pages while their decode path reads the mixed pages in place

@@ -13,7 +13,7 @@ __all__ = [
     "MkvError", "Layout", "PoolDesc", "BatchDesc", "lib", "make_pool", "make_batch",
     "mkv_fp8_page_bytes", "mkv_tq3_page_bytes", "mkv_append", "mkv_demote_pages",
     "mkv_decode_workspace_bytes", "mkv_decode_attn", "mkv_decode_attn_noalloc", "mkv_decode_attn_layers",
-    "mkv_debug_gather", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
+    "mkv_debug_gather", "mkv_stream_read", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
     "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
     "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
     "mkv_last_error",
@@ -81,6 +81,7 @@ def lib():
         "mkv_decode_attn_noalloc": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp]),
         "mkv_decode_attn_layers": (c_i32, [P(Layout), P(PoolDesc), c_i32, P(BatchDesc), c_vp, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "mkv_debug_gather": (c_i32, [P(Layout), P(PoolDesc), c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
+        "mkv_stream_read": (c_i32, [c_vp, c_sz, c_vp, c_sz, c_vp]),
         "mkv_materialize": (c_i32, [P(Layout), P(PoolDesc), P(BatchDesc), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
         "mkv_lifecycle_workspace_bytes": (c_sz, [c_i32]),
         "mkv_decode_workspace_bytes_multi": (c_sz, [P(Layout), c_i32, c_i32, c_i32, c_i32]),
@@ -287,6 +288,18 @@ def mkv_debug_gather(layout, pool, bt_offsets, bt_pages, b, n_pages, out, stream
                                          _ptr(bt_offsets, torch.int32, "bt_offsets"),
                                          _ptr(bt_pages, torch.int32, "bt_pages"), int(b), int(n_pages),
                                          _ptr(out, torch.uint8, "out"), _stream(stream)))
+
+
+def mkv_stream_read(src, sink, nbytes=None, stream=None):
+    """Read the first floor(nbytes / 3584) * 3584 bytes of device tensor src
+    (all of it by default) with the page-staging loads; sink: int32 device
+    tensor of at least 12 words, per-wave XORs of the units' first words."""
+    import torch
+    nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if nb > src.numel() * src.element_size():
+        raise MkvError(-101, "nbytes exceeds src")
+    return _check(lib().mkv_stream_read(_ptr(src, name="src"), nb, _ptr(sink, torch.int32, "sink"), sink.numel(),
+                                        _stream(stream)))
 
 
 def mkv_materialize(layout, pool, batch, b, page_lo, n_pages, k_out, v_out, stream=None):

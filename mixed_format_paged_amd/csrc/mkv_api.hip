@@ -545,6 +545,15 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32
   return e == hipSuccess ? MKV_OK : hip_fail(e, "gather launch");
 }
 
+int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  if (!src || !sink) return fail(MKV_ERR_NULL, "src and sink are required");
+  if (!aligned16(src)) return fail(MKV_ERR_ALIGN, "src must be 16-byte aligned");
+  if (sink_words < (size_t)kItemWaves) return fail(MKV_ERR_RANGE, "sink_words %zu < %d", sink_words, kItemWaves);
+  if (bytes / stream_read_unit() > 0x7fffffffu) return fail(MKV_ERR_RANGE, "bytes too large");
+  hipError_t e = launch_stream_read(src, bytes, sink, sink_words, as_stream(stream));
+  return e == hipSuccess ? MKV_OK : hip_fail(e, "stream-read launch");
+}
+
 int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
                     int32_t page_lo, int32_t n_pages, uint16_t* k_out, uint16_t* v_out, void* stream) {
   Geometry g{};

@@ -233,6 +233,9 @@ struct AppendIn {
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream);
+// Streaming-read probe (mkv_stream_read): sink_words >= kItemWaves.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
+size_t stream_read_unit();
 // appended: the partials come from a launch with the in-launch append
 // (requests whose last logical page is TQ3 then get NaN outputs).
 hipError_t launch_merge(const Geometry& g, int n_layers, const Plan& plan, float* out,

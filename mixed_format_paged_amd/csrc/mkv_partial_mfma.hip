@@ -1238,6 +1238,52 @@ static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layer
   }
 }
 
+// Streaming-read probe: units of kProbeUnit bytes (one TQ3 page-head at
+// d = 256) copied HBM -> LDS by the page-staging loads (stage_issue: LDS-DMA,
+// 16 bytes per lane, non-temporal), three units in flight per wave as in the
+// TQ3 page loop, one 12-wave workgroup per CU, nothing computed but an XOR of
+// each unit's first word, which lane 0 of each wave leaves in sink.
+constexpr int kProbeUnit = 14 * 256;
+__global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint8_t* __restrict__ src, unsigned n_units,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ __align__(16) uint8_t ring[kWaves * Geo<256>::kWaveRing3];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned gw = blockIdx.x * kWaves + wave, nw = gridDim.x * kWaves;
+  const int mine = gw < n_units ? (int)((n_units - 1 - gw) / nw + 1) : 0;   // units gw, gw + nw, ...
+  uint8_t* const slot0 = ring + wave * Geo<256>::kWaveRing3;
+  auto unit = [&](int k) { return src + (size_t)(gw + (unsigned)k * nw) * kProbeUnit; };
+  uint32_t x = 0;
+  if (mine > 0) stage_issue<256, true>(unit(0), slot0, lane, kProbeUnit);
+  if (mine > 1) stage_issue<256, true>(unit(1), slot0 + kProbeUnit, lane, kProbeUnit);
+  int s_cur = 0;
+  for (int k = 0; k < mine; ++k) {
+    if (k + 2 < mine) {
+      stage_issue<256, true>(unit(k + 2), slot0 + (s_cur == 0 ? 2 : s_cur - 1) * kProbeUnit, lane, kProbeUnit);
+      wait_vmem<2 * Geo<256>::kRows>();
+    } else if (k + 1 < mine) {
+      wait_vmem<Geo<256>::kRows>();
+    } else {
+      wait_vmem<0>();
+    }
+    x ^= lds_load<uint32_t>(slot0 + s_cur * kProbeUnit);
+    s_cur = s_cur == 2 ? 0 : s_cur + 1;
+  }
+  if (lane == 0) sink[gw] = x;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  const size_t units = bytes / kProbeUnit;
+  size_t groups = (size_t)cu_count();
+  if (groups > sink_words / kWaves) groups = sink_words / kWaves;
+  if (groups < 1) groups = 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(src), (unsigned)units, sink);
+  return hipGetLastError();
+}
+
+size_t stream_read_unit() { return kProbeUnit; }
+
 hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& lt, int n_layers,
                                const float* q, size_t q_layer_stride, float qscale,
                                const Plan& plan, const AppendIn& ap, hipStream_t stream) {

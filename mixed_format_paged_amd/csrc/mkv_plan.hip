@@ -69,6 +69,7 @@ __device__ inline int hi32(uint64_t x) { return (int)(uint32_t)(x >> 32); }
 __device__ inline int* req_row(const Plan& p, int field) { return p.req + (size_t)field * (p.batch + 1); }
 
 constexpr int kClassifyThreads = 1024;
+constexpr int kPlanLdsRows = 1025;                  // per-request rows of batches up to 1024 go to LDS
 constexpr int kClassifyPages = 8;
 
 }  // namespace
@@ -239,11 +240,41 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   const int* po = req_row(plan, R_POFF);
   const int* tail = req_row(plan, R_TAIL);
   const int* lastfmt = req_row(plan, R_LASTFMT);
+  const int* nf_b = nf_row;
+  const int* nt_b = nt_row;
+  const int* bto = bt_offsets;
+  // With a batch that fits, the per-request rows the chunk tables read are
+  // copied to LDS in one round of loads (the owning request's binary search
+  // and its row reads then stay on chip).
+  __shared__ int s_rows[8][kPlanLdsRows];
+  if (B + 1 <= kPlanLdsRows) {                            // uniform
+    for (int i = tid; i <= B; i += 1024) {
+      s_rows[0][i] = cf[i];
+      s_rows[1][i] = ct[i];
+      s_rows[2][i] = po[i];
+      if (i < B) {
+        s_rows[3][i] = tail[i];
+        s_rows[4][i] = lastfmt[i];
+        s_rows[5][i] = nf_row[i];
+        s_rows[6][i] = nt_row[i];
+        s_rows[7][i] = bt_offsets[i];
+      }
+    }
+    __syncthreads();
+    cf = s_rows[0];
+    ct = s_rows[1];
+    po = s_rows[2];
+    tail = s_rows[3];
+    lastfmt = s_rows[4];
+    nf_b = s_rows[5];
+    nt_b = s_rows[6];
+    bto = s_rows[7];
+  }
   // chunk tables, one thread per chunk; the owning request by binary search
   for (int fmt = 0; fmt < 2; ++fmt) {
     const int* co = fmt ? ct : cf;
     const int total = co[B];
-    const int* cnt = fmt ? nt_row : nf_row;
+    const int* cnt = fmt ? nt_b : nf_b;
     int4* out = fmt ? plan.chunks_t : plan.chunks_f;
     for (int c = tid; c < total && c < plan.table_cap; c += 1024) {
       int lo = 0, hi = B - 1;                 // last b with co[b] <= c
@@ -261,7 +292,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const bool holds_tail = local == nchunks - 1 && lastfmt[b] == fmt;
       const int last_tok = holds_tail ? tail[b] : 16;
       const int pidx = po[b] + (fmt ? (cf[b + 1] - cf[b]) : 0) + local;
-      const int first = bt_offsets[b] + start;
+      const int first = bto[b] + start;
       const int* lst = fmt ? plan.list_t : plan.list_f;
       int4* const ent = out + (kChunkInts / 4) * c;
       ent[0] = make_int4(b, first, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);

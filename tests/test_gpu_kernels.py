@@ -501,3 +501,24 @@ def test_append_attend_refuses_a_tq3_last_page():
     for b in range(B):
         assert np.isnan(o[b]).all() == last_is_tq3[b], b
         assert np.isfinite(o[b]).all() != last_is_tq3[b], b
+
+
+def test_stream_read_probe_reads_every_unit():
+    # the streaming-read probe reads each 3584-byte unit once: the XOR of its
+    # per-wave words is the XOR of every unit's first word (a partial unit at
+    # the end is not read)
+    g = torch.Generator()
+    g.manual_seed(11)
+    n_units = 20000
+    words = torch.randint(-2**31, 2**31 - 1, (n_units * 896 + 200,), dtype=torch.int32, generator=g)
+    src = words.cuda()
+    sink = torch.zeros(12 * 300, dtype=torch.int32, device="cuda")
+    M.mkv_stream_read(src, sink)
+    torch.cuda.synchronize()
+    expect = np.bitwise_xor.reduce(words[0:n_units * 896:896].numpy())
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == expect
+    # a small sink (12 words: one workgroup) covers every unit too
+    sink1 = torch.zeros(12, dtype=torch.int32, device="cuda")
+    M.mkv_stream_read(src, sink1, nbytes=1000 * 3584 + 17)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink1.cpu().numpy()) == np.bitwise_xor.reduce(words[0:1000 * 896:896].numpy())
