@@ -410,6 +410,14 @@ int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool,
                           int32_t* tq3_free, int32_t* free_tops, const int32_t* requests,
                           int32_t n_req, void* ws, size_t ws_bytes, void* stream);
 
+/* Partial-kernel family of the decode calls (measurement support): 1 (the
+ * default) selects the matrix-core kernels, 0 the plain VALU kernels kept as
+ * the measured baseline.  Process-wide; a call reads the setting once, when
+ * it starts, so calls running on other threads are not affected mid-way.
+ * Under 0, mkv_append_attend, multi-query decode and rotated TQ3 pools
+ * return MKV_ERR_RANGE.  Returns MKV_OK, or MKV_ERR_RANGE for another kind. */
+int mkv_set_partial_kind(int32_t kind);
+
 /* Synchronise `stream` and return the device status bits (MKV_DEV_*) left in
  * the workspace by the last decode or lifecycle call on it (0 = no device-data error);
  * negative MKV_ERR_* on failure. */

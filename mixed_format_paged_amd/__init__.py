@@ -16,13 +16,15 @@ __all__ = [
     "mkv_debug_gather", "mkv_stream_read", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
     "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
     "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
-    "mkv_last_error",
+    "mkv_last_error", "mkv_set_partial_kind", "set_partial_kind",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
     "MKV_DEV_BAD_PAGE_ID", "MKV_DEV_BAD_TIER", "MKV_DEV_BAD_SEQ_LEN", "MKV_DEV_NO_FREE_PAGE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmkv.so")
+# MKV_LIB_PATH selects another build of the library (e.g. one with host-side
+# sanitizers); by default the in-tree libmkv.so
+LIB_PATH = os.environ.get("MKV_LIB_PATH") or os.path.join(_HERE, "libmkv.so")
 
 TIER_RECENT, TIER_ANCHOR, TIER_STALE, TIER_FREE = 0, 1, 2, 0xFF
 MKV_DEV_BAD_PAGE_ID, MKV_DEV_BAD_TIER, MKV_DEV_BAD_SEQ_LEN, MKV_DEV_NO_FREE_PAGE = 1, 2, 4, 8
@@ -94,7 +96,7 @@ def lib():
         "mkv_workspace_status": (c_i32, [c_vp, c_vp]),
         "mkv_status_string": (ctypes.c_char_p, [c_i32]),
         "mkv_last_error": (ctypes.c_char_p, []),
-        "mkv_internal_set_partial_kind": (c_i32, [c_i32]),
+        "mkv_set_partial_kind": (c_i32, [c_i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -381,6 +383,9 @@ def mkv_last_error():
     return lib().mkv_last_error().decode()
 
 
-def set_partial_kind(kind):
+def mkv_set_partial_kind(kind):
     """Measurement hook: 1 = matrix-core partial kernels, 0 = VALU kernels."""
-    return _check(lib().mkv_internal_set_partial_kind(int(kind)))
+    return _check(lib().mkv_set_partial_kind(int(kind)))
+
+
+set_partial_kind = mkv_set_partial_kind

@@ -11,7 +11,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "mkv.h"
@@ -20,9 +22,11 @@
 
 namespace mkv {
 
-// Which partial-kernel family the decode uses: 1 = matrix cores,
-// 0 = the plain VALU kernels (kept as the measured baseline).
-static int g_partial_kind = 1;
+// Which partial-kernel family decode calls use: 1 = matrix cores, 0 = the
+// plain VALU kernels (kept as the measured baseline).  Set by
+// mkv_set_partial_kind from any thread; each call reads it once, when it
+// starts (Geometry::partial_kind), and uses that value throughout.
+static std::atomic<int> g_partial_kind{1};
 
 namespace {
 
@@ -79,6 +83,31 @@ int check_pool(const mkv_pool* p, Geometry* g, bool need_fp8, bool need_tq3, boo
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// MKV_DEBUG_SYNC=1 in the environment (read at every call): after a call
+// has enqueued its work, synchronise the stream and check it, so a failing
+// launch is reported by the call that made it (MKV_ERR_HIP) rather than by a
+// later one; device-data status bits left in the call's workspace are
+// printed to stderr (the call still returns MKV_OK for them, as without the
+// flag: they are read with mkv_workspace_status).
+bool debug_sync() {
+  const char* v = std::getenv("MKV_DEBUG_SYNC");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+int debug_finish(int rc, void* stream, const void* ws, const char* what) {
+  if (rc != MKV_OK || !debug_sync()) return rc;
+  hipError_t e = hipStreamSynchronize(as_stream(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (ws) {
+    int32_t status = 0;
+    e = hipMemcpy(&status, ws, sizeof status, hipMemcpyDeviceToHost);   // status is the first field
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (status) std::fprintf(stderr, "[mkv] %s: device status bits 0x%x\n", what, (unsigned)status);
+  }
+  return MKV_OK;
+}
 
 void set_layer(LayerTable* lt, int l, const mkv_pool& p) {
   lt->fp8[l] = p.fp8_slab;
@@ -182,7 +211,7 @@ size_t mkv_tq3_page_bytes(const mkv_layout* layout) {
   return (size_t)tq3_page_bytes(g.hkv, g.d);
 }
 
-int mkv_append(const mkv_layout* layout, const mkv_pool* pool, const float* k, const float* v,
+static int mkv_append_impl(const mkv_layout* layout, const mkv_pool* pool, const float* k, const float* v,
                int32_t n_new, const int32_t* bt_offsets, const int32_t* bt_pages,
                const int32_t* pos, const int32_t* counts, int32_t batch, void* stream) {
   Geometry g{};
@@ -199,7 +228,7 @@ int mkv_append(const mkv_layout* layout, const mkv_pool* pool, const float* k, c
   return e == hipSuccess ? MKV_OK : hip_fail(e, "append launch");
 }
 
-int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_demote_pages_layers_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                             const int32_t* src_fp8, const int32_t* dst_tq3, int32_t n, void* stream) {
   Geometry g{};
   int rc = check_layout(layout, &g);
@@ -242,6 +271,7 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
                    LayerTable* lt, int n_query = 1) {
   int rc = check_layout(layout, g);
   if (rc) return rc;
+  g->partial_kind = g_partial_kind.load(std::memory_order_relaxed);
   if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
   if (n_layers < 1 || n_layers > kMaxLayers) return fail(MKV_ERR_RANGE, "n_layers %d not in [1, %d]", n_layers, kMaxLayers);
   if (pools) {
@@ -249,7 +279,7 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
       if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
       if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
         return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
-      if (pools[l].tq3_signs && (n_query > 1 || g->G > kRowBlock || !g_partial_kind))
+      if (pools[l].tq3_signs && (n_query > 1 || g->G > kRowBlock || !g->partial_kind))
         return fail(MKV_ERR_RANGE,
                     "layer %d: rotated TQ3 pages need single-query decode, at most 8 query heads per KV head and "
                     "the matrix-core kernels", l);
@@ -288,7 +318,7 @@ int run_attend(int which, const Geometry& g, const LayerTable& lt, int n_layers,
   const float qscale = sm_scale * 1.4426950408889634f;   // scores in log2 units
   const size_t q_ls = (size_t)batch * g.hq * g.d;
   hipError_t e;
-  if (g_partial_kind) {
+  if (g.partial_kind) {
     e = launch_partial_mfma(which, g, lt, n_layers, q, q_ls, qscale, plan, AppendIn{nullptr, nullptr, 0}, st);
   } else {
     e = hipSuccess;
@@ -307,7 +337,7 @@ int run_merge(const Geometry& g, int n_layers, const Plan& plan, float* out, flo
 
 }  // namespace
 
-int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+static int mkv_decode_plan_impl(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
                     int32_t n_layers, void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
   Plan plan{};
@@ -337,25 +367,25 @@ static int attend_entry(int which, const mkv_layout* layout, const mkv_pool* poo
   return run_attend(which, g, lt, n_layers, plan, q, sm_scale, batch->batch, as_stream(stream));
 }
 
-int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_attend_fp8_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                    const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                    size_t ws_bytes, void* stream) {
   return attend_entry(0, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
 }
 
-int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_attend_tq3_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                    const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                    size_t ws_bytes, void* stream) {
   return attend_entry(1, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
 }
 
-int mkv_attend_partials(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_attend_partials_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                         const mkv_batch* batch, const float* q, float sm_scale, void* ws,
                         size_t ws_bytes, void* stream) {
   return attend_entry(2, layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream);
 }
 
-int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
+static int mkv_merge_impl(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
               float* lse, void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
   Plan plan{};
@@ -376,7 +406,7 @@ int run_fused(const Geometry& g, const LayerTable& lt, int n_layers, const Plan&
 
 }  // namespace
 
-int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_attend_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                const mkv_batch* batch, const float* q, float sm_scale, float* out, float* lse,
                void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
@@ -390,7 +420,7 @@ int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers
   return run_fused(g, lt, n_layers, plan, q, sm_scale, out, lse, batch->batch, as_stream(stream));
 }
 
-int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_append_attend_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                       const mkv_batch* batch, const float* k_new, const float* v_new,
                       const float* q, float sm_scale, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream) {
@@ -403,7 +433,7 @@ int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n
   if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
   if (!k_new || !v_new) return fail(MKV_ERR_NULL, "k_new and v_new are required");
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(MKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
-  if (!g_partial_kind) return fail(MKV_ERR_RANGE, "mkv_append_attend needs the matrix-core partial kernels");
+  if (!g.partial_kind) return fail(MKV_ERR_RANGE, "mkv_append_attend needs the matrix-core partial kernels");
   if (batch->batch == 0) return MKV_OK;
   const int B = batch->batch;
   hipStream_t st = as_stream(stream);
@@ -415,7 +445,7 @@ int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n
   return run_merge(g, n_layers, plan, out, lse, B, st, true);
 }
 
-int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_decode_attn_layers_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                            const mkv_batch* batch, const float* q, float sm_scale, float* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
@@ -442,7 +472,7 @@ size_t mkv_decode_workspace_bytes_multi(const mkv_layout* layout, int32_t batch,
   return workspace_sizes(g.hq, g.hkv, g.d, batch, bt_capacity, n_layers, n_query).total;
 }
 
-int mkv_decode_attn_multi(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_decode_attn_multi_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                           const mkv_batch* batch, int32_t n_query, const float* q, float sm_scale,
                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   Geometry g{};
@@ -453,7 +483,7 @@ int mkv_decode_attn_multi(const mkv_layout* layout, const mkv_pool* pools, int32
   int rc = prepare_decode(layout, pools, n_layers, batch, ws, ws_bytes, &g, &plan, &lt, n_query);
   if (rc) return rc;
   if ((rc = check_qo(q, out, lse, sm_scale, true, true))) return rc;
-  if (n_query > 1 && !g_partial_kind) return fail(MKV_ERR_RANGE, "multi-query decode needs the matrix-core kernels");
+  if (n_query > 1 && !g.partial_kind) return fail(MKV_ERR_RANGE, "multi-query decode needs the matrix-core kernels");
   const int B = batch->batch;
   if (B == 0) return MKV_OK;
   hipStream_t st = as_stream(stream);
@@ -530,7 +560,7 @@ int mkv_decode_attn_noalloc(const mkv_layout* layout, const mkv_pool* pool, cons
   return mkv_decode_attn(layout, pool, batch, q, sm_scale, out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
-int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+static int mkv_debug_gather_impl(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
                      const int32_t* bt_pages, int32_t b, int32_t n_pages, uint8_t* out, void* stream) {
   Geometry g{};
   int rc = check_layout(layout, &g);
@@ -545,7 +575,7 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32
   return e == hipSuccess ? MKV_OK : hip_fail(e, "gather launch");
 }
 
-int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+static int mkv_stream_read_impl(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
   if (!src || !sink) return fail(MKV_ERR_NULL, "src and sink are required");
   if (!aligned16(src)) return fail(MKV_ERR_ALIGN, "src must be 16-byte aligned");
   if (sink_words < (size_t)kItemWaves) return fail(MKV_ERR_RANGE, "sink_words %zu < %d", sink_words, kItemWaves);
@@ -554,7 +584,7 @@ int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_w
   return e == hipSuccess ? MKV_OK : hip_fail(e, "stream-read launch");
 }
 
-int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
+static int mkv_materialize_impl(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
                     int32_t page_lo, int32_t n_pages, uint16_t* k_out, uint16_t* v_out, void* stream) {
   Geometry g{};
   int rc = check_layout(layout, &g);
@@ -609,7 +639,7 @@ int check_lifecycle(const mkv_layout* layout, const mkv_pool* pools, int32_t n_l
 
 }  // namespace
 
-int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+static int mkv_lifecycle_step_impl(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
                        const int32_t* bt_offsets, int32_t* bt_pages, int32_t* seq_lens, int32_t batch,
                        int32_t bt_capacity, uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free,
                        int32_t* free_tops, int32_t recent_pages, void* ws, size_t ws_bytes, void* stream) {
@@ -626,7 +656,7 @@ int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t 
   return e == hipSuccess ? MKV_OK : hip_fail(e, "lifecycle launch");
 }
 
-int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+static int mkv_lifecycle_release_impl(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
                           const int32_t* bt_pages, int32_t* seq_lens, int32_t batch, int32_t bt_capacity,
                           uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free, int32_t* free_tops,
                           const int32_t* requests, int32_t n_req, void* ws, size_t ws_bytes, void* stream) {
@@ -667,13 +697,105 @@ const char* mkv_status_string(int status) {
 
 const char* mkv_last_error(void) { return g_err; }
 
-// Selects the partial-kernel family for later decode calls in this process:
-// 1 = matrix-core kernels (default), 0 = plain VALU kernels.  Not part of
-// include/mkv.h: a measurement hook for comparing the two families.
-int mkv_internal_set_partial_kind(int kind) {
+int mkv_set_partial_kind(int32_t kind) {
   if (kind != 0 && kind != 1) return fail(MKV_ERR_RANGE, "kind %d", kind);
-  g_partial_kind = kind;
+  g_partial_kind.store(kind, std::memory_order_relaxed);
   return MKV_OK;
+}
+
+
+// MKV_DEBUG_SYNC=1: every call that enqueues work synchronises its stream and
+// checks it before returning (debug_finish).
+int mkv_append(const mkv_layout* layout, const mkv_pool* pool, const float* k, const float* v,
+               int32_t n_new, const int32_t* bt_offsets, const int32_t* bt_pages,
+               const int32_t* pos, const int32_t* counts, int32_t batch, void* stream) {
+  return debug_finish(mkv_append_impl(layout, pool, k, v, n_new, bt_offsets, bt_pages, pos, counts, batch, stream), stream, nullptr, "mkv_append");
+}
+
+int mkv_demote_pages_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                            const int32_t* src_fp8, const int32_t* dst_tq3, int32_t n, void* stream) {
+  return debug_finish(mkv_demote_pages_layers_impl(layout, pools, n_layers, src_fp8, dst_tq3, n, stream), stream, nullptr, "mkv_demote_pages_layers");
+}
+
+int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
+                    int32_t n_layers, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_decode_plan_impl(layout, pool, batch, n_layers, ws, ws_bytes, stream), stream, ws, "mkv_decode_plan");
+}
+
+int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_attend_fp8_impl(layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream), stream, ws, "mkv_attend_fp8");
+}
+
+int mkv_attend_tq3(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                   const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_attend_tq3_impl(layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream), stream, ws, "mkv_attend_tq3");
+}
+
+int mkv_attend_partials(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                        const mkv_batch* batch, const float* q, float sm_scale, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_attend_partials_impl(layout, pools, n_layers, batch, q, sm_scale, ws, ws_bytes, stream), stream, ws, "mkv_attend_partials");
+}
+
+int mkv_merge(const mkv_layout* layout, int32_t n_layers, const mkv_batch* batch, float* out,
+              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_merge_impl(layout, n_layers, batch, out, lse, ws, ws_bytes, stream), stream, ws, "mkv_merge");
+}
+
+int mkv_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+               const mkv_batch* batch, const float* q, float sm_scale, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_attend_impl(layout, pools, n_layers, batch, q, sm_scale, out, lse, ws, ws_bytes, stream), stream, ws, "mkv_attend");
+}
+
+int mkv_append_attend(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                      const mkv_batch* batch, const float* k_new, const float* v_new,
+                      const float* q, float sm_scale, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_append_attend_impl(layout, pools, n_layers, batch, k_new, v_new, q, sm_scale, out, lse, ws, ws_bytes, stream), stream, ws, "mkv_append_attend");
+}
+
+int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                           const mkv_batch* batch, const float* q, float sm_scale, float* out,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_decode_attn_layers_impl(layout, pools, n_layers, batch, q, sm_scale, out, lse, ws, ws_bytes, stream), stream, ws, "mkv_decode_attn_layers");
+}
+
+int mkv_decode_attn_multi(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                          const mkv_batch* batch, int32_t n_query, const float* q, float sm_scale,
+                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_decode_attn_multi_impl(layout, pools, n_layers, batch, n_query, q, sm_scale, out, lse, ws, ws_bytes, stream), stream, ws, "mkv_decode_attn_multi");
+}
+
+int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+                     const int32_t* bt_pages, int32_t b, int32_t n_pages, uint8_t* out, void* stream) {
+  return debug_finish(mkv_debug_gather_impl(layout, pool, bt_offsets, bt_pages, b, n_pages, out, stream), stream, nullptr, "mkv_debug_gather");
+}
+
+int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  return debug_finish(mkv_stream_read_impl(src, bytes, sink, sink_words, stream), stream, nullptr, "mkv_stream_read");
+}
+
+int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
+                    int32_t page_lo, int32_t n_pages, uint16_t* k_out, uint16_t* v_out, void* stream) {
+  return debug_finish(mkv_materialize_impl(layout, pool, batch, b, page_lo, n_pages, k_out, v_out, stream), stream, nullptr, "mkv_materialize");
+}
+
+int mkv_lifecycle_step(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,
+                       const int32_t* bt_offsets, int32_t* bt_pages, int32_t* seq_lens, int32_t batch,
+                       int32_t bt_capacity, uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free,
+                       int32_t* free_tops, int32_t recent_pages, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_lifecycle_step_impl(layout, pools, n_layers, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free, tq3_free, free_tops, recent_pages, ws, ws_bytes, stream), stream, ws, "mkv_lifecycle_step");
+}
+
+int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool, const int32_t* bt_offsets,
+                          const int32_t* bt_pages, int32_t* seq_lens, int32_t batch, int32_t bt_capacity,
+                          uint8_t* tier, int32_t* fp8_free, int32_t* tq3_free, int32_t* free_tops,
+                          const int32_t* requests, int32_t n_req, void* ws, size_t ws_bytes, void* stream) {
+  return debug_finish(mkv_lifecycle_release_impl(layout, pool, bt_offsets, bt_pages, seq_lens, batch, bt_capacity, tier, fp8_free, tq3_free, free_tops, requests, n_req, ws, ws_bytes, stream), stream, ws, "mkv_lifecycle_release");
 }
 
 }  // extern "C"

@@ -175,6 +175,7 @@ inline int tq3_v_exponent(float v_scale) {
 struct Geometry {
   int hq, hkv, d, G;
   int n_fp8, n_tq3;
+  int partial_kind;     // the call's partial-kernel family (1 matrix cores, 0 VALU), read once per call
 };
 
 // ---- launchers (each returns hipGetLastError() of its launch) --------------

@@ -522,3 +522,27 @@ def test_stream_read_probe_reads_every_unit():
     M.mkv_stream_read(src, sink1, nbytes=1000 * 3584 + 17)
     torch.cuda.synchronize()
     assert np.bitwise_xor.reduce(sink1.cpu().numpy()) == np.bitwise_xor.reduce(words[0:1000 * 896:896].numpy())
+
+
+def test_debug_sync_reports_device_status(capfd, monkeypatch):
+    """MKV_DEBUG_SYNC=1: each call synchronises its stream before returning
+    and prints the device status bits its workspace holds; the call itself
+    still returns MKV_OK and the outputs are the same as without the flag."""
+    M.set_partial_kind(1)
+    w = W.scaled(W.WORKLOADS["batch-8x16384"], B=2, lengths=("fixed", 300), recent_tokens=64)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    out0, lse0, status = _decode(dw)
+    assert status == 0
+    dw.bt[int(st.bt_offsets[1]) + 3] = st.n_fp8 + st.n_tq3 + 5        # request 1: an id outside the pool
+    monkeypatch.setenv("MKV_DEBUG_SYNC", "1")
+    capfd.readouterr()
+    out, lse, status = _decode(dw)
+    err = capfd.readouterr().err
+    assert status == M.MKV_DEV_BAD_PAGE_ID
+    assert "[mkv] mkv_decode_attn_layers: device status bits 0x1" in err, err
+    assert np.all(np.isnan(out[0, 1])) and np.array_equal(out[0, 0], out0[0, 0])
+    monkeypatch.delenv("MKV_DEBUG_SYNC")
+    capfd.readouterr()
+    _decode(dw)
+    assert "[mkv]" not in capfd.readouterr().err
