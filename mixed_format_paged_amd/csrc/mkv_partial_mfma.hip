@@ -725,9 +725,16 @@ __device__ __forceinline__ void run_item(
   //      tq3_channel(k) of the lane's quarter (the order in which tq3_scores
   //      extracts the codes) and y = x 2^(24 - tq3_code_shift(g, k)): the codes
   //      enter the MFMA as fp16 subnormals u 2^(shift - 24), so each product
-  //      is u x, and y stays below 2^15.  The fp16 pair holds y to about 22
-  //      bits of the row's maximum whatever the size of q (and of the layer
-  //      scales).  Scores are multiplied by 2^-F in fp32.
+  //      is u x, and y stays below 2^15.  The matrix cores align a dot
+  //      product's terms on their operands' exponent fields, and a subnormal
+  //      code counts at exponent -14 however small it is, so terms whose code
+  //      sits low in its half would lose their low bits.  TQ3 fp16(y) is
+  //      therefore x rounded to the uniform grid 2^-20 (an integer below 2^11
+  //      times 2^(4 - shift), exact in fp16): every hi term is a multiple of
+  //      2^-20, which the alignment keeps whole; the remainder (below 2^-21)
+  //      follows in fp16.  FP8 fp16(x) rounds toward zero.  Either pair holds
+  //      x to about 22 bits of the row's maximum whatever the size of q (and
+  //      of the layer scales).  Scores are multiplied by 2^-F in fp32.
   //      A thread's row is that of its lane's MFMA column (lane & 15), so the
   //      same F scales its fragments and, later, its column of scores.
   static_assert(NG * 64 <= kThreads, "one fragment entry per thread");
@@ -767,19 +774,45 @@ __device__ __forceinline__ void run_item(
   const float qsc = __builtin_amdgcn_ldexpf(1.0f, -F);   // score factor of this lane's column
   if (builds) {
     const bool hi_codes = (fg & 3) >= 2;      // groups 4b + 2, 4b + 3 take the blocks' high codes
-    float x0[4], x1[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x0[k] = __builtin_amdgcn_ldexpf(xq[k], F + (tq3 ? 24 - tq3_code_shift(hi_codes, k) : 0));
-      x1[k] = __builtin_amdgcn_ldexpf(xq[k + 4], F + (tq3 ? 24 - tq3_code_shift(hi_codes, k + 4) : 0));
-    }
     h8 f0, f1;
-    if (RB == 16) {
+    if (tq3) {
+      h8 hi, lo;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = __builtin_amdgcn_ldexpf(xq[k], F);
+        const float hx = __builtin_rintf(__builtin_amdgcn_ldexpf(x, 20));   // |hx| <= 2^11
+        const int sh = tq3_code_shift(hi_codes, k);
+        hi[k] = (_Float16)__builtin_amdgcn_ldexpf(hx, 4 - sh);             // exact
+        lo[k] = (_Float16)__builtin_amdgcn_ldexpf(x - __builtin_amdgcn_ldexpf(hx, -20), 24 - sh);
+      }
+      if (RB == 16) {
+        f0 = hi;
+        f1 = lo;
+        sq[fe] = f0;
+        sq[NG * 64 + fe] = f1;
+      } else {
+        f0 = lo_sel < 0.0f ? lo : hi;
+        f1 = h8{};
+        sq[fe] = f0;
+      }
+    } else if (RB == 16) {
+      float x0[4], x1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x0[k] = __builtin_amdgcn_ldexpf(xq[k], F);
+        x1[k] = __builtin_amdgcn_ldexpf(xq[k + 4], F);
+      }
       f0 = __builtin_shufflevector(split_rows(x0, 0.0f), split_rows(x1, 0.0f), 0, 1, 2, 3, 4, 5, 6, 7);
       f1 = __builtin_shufflevector(split_rows(x0, -1.0f), split_rows(x1, -1.0f), 0, 1, 2, 3, 4, 5, 6, 7);
       sq[fe] = f0;
       sq[NG * 64 + fe] = f1;
     } else {
+      float x0[4], x1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x0[k] = __builtin_amdgcn_ldexpf(xq[k], F);
+        x1[k] = __builtin_amdgcn_ldexpf(xq[k + 4], F);
+      }
       f0 = __builtin_shufflevector(split_rows(x0, lo_sel), split_rows(x1, lo_sel), 0, 1, 2, 3, 4, 5, 6, 7);
       f1 = h8{};
       sq[fe] = f0;
