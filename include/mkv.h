@@ -76,14 +76,48 @@ typedef struct {
   int32_t page_size;
 } mkv_layout;
 
+/* Page formats (frozen: the demote kernel writes them, the decode,
+ * materialise and gather kernels read them, and the golden rows in
+ * tests/golden/ pin them; any change is a new format).  The pages name the
+ * formats but fix none of these details (arXiv 2608.23834, page 1,
+ * Abstract: FP8 Recent / Anchor pages, packed TQ3 stale pages); this is the
+ * reading this library implements.
+ *
+ * FP8 page: [kv head][K = 0, V = 1][16 tokens][head_dim] OCP E4M3FN bytes
+ *   (round to nearest even, saturating to +-448); value = decode(byte) * the
+ *   pool's k_scale or v_scale.
+ *
+ * TQ3 page: one block of 14 * head_dim bytes per KV head, head h at
+ *   h * 14 * head_dim.  Per token, K or V and group of 32 channels: an fp16
+ *   scale s = fp16_RNE(fl32(absmax / 3)) (saturating to 65504) of the group's
+ *   fp32 values x, and per channel a 3-bit code u = q + 4, q in [-3, 3] the
+ *   integer nearest x / s with ties to even (exact fp32 thresholds 0.5 s,
+ *   1.5 s, 2.5 s; s = 0 gives q = 0); the value is (u - 4) * s.  Codes go 8
+ *   to 3 bytes: a "triple" is a little-endian 24-bit word, slot k at bits
+ *   [3k, 3k + 3).  With d = head_dim and G = d / 32 groups, a block is:
+ *   [0, 6d)    K codes.  Token t's row starts at byte 3 d t / 8; in it,
+ *              quarter j in [0, 4) (channels 8 j .. 8 j + 7 of every group)
+ *              starts at byte 3 j G and is G / 4 blocks of 4 triples.
+ *              Channel c = 32 g + 8 j + e (e in [0, 8)), with gg = g mod 4,
+ *              is in triple 4 floor(g / 4) + 2 (gg mod 2) + floor(e / 4) of
+ *              its quarter, at slot 2 (e mod 4) + floor(gg / 2).
+ *   [6d, 12d)  V codes.  The triple at byte 6 d + 3 ((16 j + n) G + p), for
+ *              j in [0, 4), n in [0, 16), p in [0, G), holds tokens
+ *              4 j .. 4 j + 3 of channels a = n d / 16 + 2 p and a + 1:
+ *              slot 2 r is (a, token 4 j + r), slot 2 r + 1 is (a + 1,
+ *              token 4 j + r).
+ *   [12d, 13d) K scales, [13d, 14d) V scales: fp16, the scale of token
+ *              t = 4 j + r and group g at element (j G + g) * 4 + r.
+ *   Read as 6-bit fields, a block of 4 K triples holds in field f the codes
+ *   of channel 8 j + (f mod 8) of groups 4 b + floor(f / 8) (low 3 bits) and
+ *   4 b + 2 + floor(f / 8) (high 3 bits); each GPU lane's codes of one token
+ *   quarter, or of 4 tokens of 2 V channels, are contiguous. */
+
 /* One layer's page pool.
- *  fp8_slab: device, n_fp8 FP8 pages of mkv_fp8_page_bytes() bytes each.
- *            Page layout [kv head][K=0,V=1][16 tokens][head_dim] E4M3FN bytes.
- *  tq3_slab: device, n_tq3 TQ3 pages of mkv_tq3_page_bytes() bytes each.
- *            Per KV head a block of 14*head_dim bytes: K codes, V codes,
- *            K scales, V scales (layout in oracle/layout.py and the
- *            kernels' headers: 8 3-bit codes per 3 bytes, one fp16 scale per
- *            32 channels per token per KV head).
+ *  fp8_slab: device, n_fp8 FP8 pages of mkv_fp8_page_bytes() bytes each
+ *            (the FP8 page format above).
+ *  tq3_slab: device, n_tq3 TQ3 pages of mkv_tq3_page_bytes() bytes each
+ *            (the TQ3 page format above).
  *  tier:     device, n_fp8 + n_tq3 bytes, shared by all layers.
  *  Physical ids [0, n_fp8) are FP8 slots, [n_fp8, n_fp8 + n_tq3) TQ3 slots;
  *  a page with tier R or A must have an FP8 id, tier S a TQ3 id.
@@ -102,7 +136,7 @@ typedef struct {
  *            TQ3 codes of y = c H (signs . x), H the Sylvester-Hadamard matrix
  *            applied by the fast transform in fp32, stage s pairing channels i
  *            and i + 2^s as (a + b, a - b) for s = 0, 1, ..., and c = 1/16 at
- *            head_dim 256, 1/8 at 128 (oracle/rotation.py).  Demotion rotates;
+ *            head_dim 256, 1/8 at 128.  Demotion rotates;
  *            single-query decode with the matrix-core kernels rotates the
  *            queries of TQ3 pages and rotates their partial states back.
  *            Multi-query decode (n_query > 1), G > 8, materialisation and the
