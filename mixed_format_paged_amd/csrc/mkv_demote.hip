@@ -188,27 +188,284 @@ __global__ void __launch_bounds__(256) demote_kernel(
     reinterpret_cast<uint4*>(out + 12 * D)[e] = reinterpret_cast<const uint4*>(sc)[e];
 }
 
+// ---- plain pages: codes from lane masks -----------------------------------
+//
+// The code of x against its group's scale s is decided by three compares,
+// each a lane mask of the wave, the second against a threshold the first
+// selects: B = [|x| >= 3s/2], D = [|x| > (B ? 5s/2 : s/2)] and N = [x < -s/2].
+// The magnitude m = [|x| > s/2] + [|x| >= 3s/2] + [|x| > 5s/2] is then 2 B + D,
+// and the code u = 4 + m (x >= 0) or 4 - m (x < 0; N is then m > 0) has
+//   u0 = D (4 + m and 4 - m are odd together),
+//   u1 = B ^ (N & D) (4 - m is 3 or 2 for m = 1, 2; 4 + m is 6 or 7 for m >= 2),
+//   u2 = !N,
+// so the scalar unit spends two ops on a code, and each bit goes into its
+// triple word with one carry-in add (w = 2 w + bit of this lane).  A thread
+// builds whole triples: a K thread takes one token row of the groups g and
+// g + 2 that share K triples, a V thread the four tokens of one token
+// quarter in half of a group (its partner lane holds the other half for the
+// group's maxima).
+
+// w <- 2 w + (this lane's bit of mask)
+__device__ inline uint32_t push_bit(uint32_t w, uint64_t mask) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(mask));
+  return r;
+}
+
+struct Thresholds {
+  float t1, t2, t3;   // s/2, 3s/2, 5s/2 (exact); +inf for s = 0
+};
+
+__device__ inline Thresholds thresholds(float s) {
+  const float z = s == 0.0f ? INFINITY : s;
+  return {0.5f * z, 1.5f * z, 2.5f * z};
+}
+
+constexpr uint32_t kFlipHigh = 0x924924u;   // bit 3k + 2 of each of the 8 slots
+
+// The masks of one code
+struct CodeMasks {
+  uint64_t B, D, N;
+};
+
+__device__ inline CodeMasks code_masks(float x, const Thresholds& th) {
+  const float ax = fabsf(x);
+  const bool b = ax >= th.t2;
+  return {__builtin_amdgcn_ballot_w64(b), __builtin_amdgcn_ballot_w64(ax > (b ? th.t3 : th.t1)),
+          __builtin_amdgcn_ballot_w64(x < -th.t1)};
+}
+
+// Push 4 codes (3 bits each, high bit first) from their masks.  The masks
+// of the 4 are formed before the first push, so the compares of the others
+// fill the wait between a compare and the select that reads its mask.
+__device__ inline uint32_t push4(uint32_t w, const CodeMasks (&m)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w = push_bit(w, m[i].N);                          // !u2, flipped by kFlipHigh
+    w = push_bit(w, m[i].B ^ (m[i].N & m[i].D));
+    w = push_bit(w, m[i].D);
+  }
+  return w;
+}
+
+// Two FP8 bytes (bytes 0, 1 or 2, 3 of w) -> fp32 (exact), times scl when
+// SCALED (the fp32 product the format defines x as; unscaled, x * 1 is x)
+template <bool HI, bool SCALED>
+__device__ inline float2 fp8x2(uint32_t w, float scl) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
+  return SCALED ? make_float2(__fmul_rn(v[0], scl), __fmul_rn(v[1], scl)) : make_float2(v[0], v[1]);
+}
+
+// Largest |decode| of 16 FP8 bytes.  With the layer scale: the largest
+// fl32(|d| scl) is fl32(max |d| scl), fp32 rounding being monotone.
+__device__ inline float absmax_fp8x16(const uint4 q) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, true);
+    a = fmaxf(fmaxf(a, fabsf(lo[0])), fabsf(lo[1]));
+    a = fmaxf(fmaxf(a, fabsf(hi[0])), fabsf(hi[1]));
+  }
+  return a;
+}
+
+__device__ inline uint32_t word_of(const uint4& q, int i) { return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w; }
+
+// The bytes again for the code pass: opaque to the compiler, so it converts
+// them anew instead of keeping the first pass's 64 values live
+__device__ inline uint4 reread(uint4 q) {
+  asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+  return q;
+}
+
+// Workgroup of 128 threads: wave 0 builds the K triples, wave 1 the V
+// triples, of PH (layer, page, KV head) items (8 G threads each per wave).
+// SCALED: some layer of the launch has a k_scale or v_scale other than 1
+// (every value is then multiplied by its layer's scale; by 1 it is exact).
+// A thread codes 64 FP8 bytes: K, token row t of groups g (gg = g mod 4 in
+// {0, 1}) and g + 2; V, tokens 4 j .. 4 j + 3 of channels 32 g + 16 hh .. + 15.
+// It keeps them as bytes and converts each value twice (once for the
+// group's maximum, once, 8 at a time, for its triple), which keeps the
+// registers few and the waves per SIMD many.
+template <int D, bool SCALED>
+__global__ void __launch_bounds__(128) demote_plain_kernel(
+    LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ dst, const int32_t* __restrict__ n_dev, TableUpdate upd, int n_items) {
+  constexpr int G = D / 32;
+  constexpr int PH = 64 / (8 * G);                   // items per workgroup: 1 at d = 256, 2 at d = 128
+  constexpr int NTRI = 4 * D;
+  __shared__ __align__(16) uint32_t tw[PH][NTRI];    // one word per triple (24 bits used)
+  __shared__ __align__(16) uint16_t sc[PH][D];       // the 2D scale bytes, in block order
+  __shared__ uint8_t* outp[PH];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ph = lane / (8 * G), r8 = lane % (8 * G);
+
+  const int item = blockIdx.x * PH + ph;
+  bool valid = item < n_items;
+  int layer = 0, page = 0, h = 0, s_id = -1, d_id = -1;
+  if (valid) {
+    layer = item / (n * hkv);
+    const int rest = item - layer * n * hkv;
+    page = rest / hkv;
+    h = rest - page * hkv;
+    if (n_dev && page >= *n_dev) valid = false;
+  }
+  if (valid) {
+    s_id = src[page];
+    d_id = dst[page];
+    valid = !(s_id < 0 || s_id >= n_fp8 || d_id < n_fp8 || d_id >= n_fp8 + n_tq3);
+  }
+  uint8_t* out = nullptr;
+  const uint8_t* in = nullptr;
+  if (valid) {
+    in = lt.fp8[layer] + (size_t)s_id * fp8_page_bytes(hkv, D) + (size_t)h * 2 * kPage * D;
+    out = lt.tq3[layer] + (size_t)(d_id - n_fp8) * tq3_page_bytes(hkv, D) + (size_t)h * tq3_head_bytes(D);
+  }
+  if (wave == 0 && r8 == 0) {
+    outp[ph] = out;
+    if (valid && upd.bt_pages && layer == 0 && h == 0) {
+      upd.bt_pages[upd.entry[page]] = d_id;
+      upd.tier[d_id] = kTierStale;
+      upd.tier[s_id] = kTierFree;
+      upd.fp8_free[*upd.push_base + page] = s_id;
+    }
+  }
+
+  if (valid && wave == 0) {
+    const int t = r8 / (G / 2), pr = r8 % (G / 2);
+    const int g = 4 * (pr >> 1) + (pr & 1);
+    const float scl = lt.k_scale[layer];
+    const uint4* row = reinterpret_cast<const uint4*>(in + t * D);
+    const uint4 q[4] = {row[2 * g], row[2 * g + 1], row[2 * g + 4], row[2 * g + 5]};   // groups g, g + 2
+    const float al = fmaxf(absmax_fp8x16(q[0]), absmax_fp8x16(q[1]));
+    const float ah = fmaxf(absmax_fp8x16(q[2]), absmax_fp8x16(q[3]));
+    const uint16_t sbl = tq3_scale_bits(SCALED ? __fmul_rn(al, scl) : al);
+    const uint16_t sbh = tq3_scale_bits(SCALED ? __fmul_rn(ah, scl) : ah);
+    sc[ph][(tq3_scale_off(D, 0, t, g) - 12 * D) / 2] = sbl;
+    sc[ph][(tq3_scale_off(D, 0, t, g + 2) - 12 * D) / 2] = sbh;
+    const Thresholds thl = thresholds(half_bits_to_float(sbl)), thh = thresholds(half_bits_to_float(sbh));
+    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
+    // channel 8 j + e of the pair sits in triple j G + 4 (g / 4) + 2 gg + e / 4
+    // of the row, slot 2 (e % 4) (group g) or 2 (e % 4) + 1 (group g + 2);
+    // channels 8 j + 4 e4 .. + 3 of a group are its dword 2 j + e4
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w2[2];
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const int k = 2 * j + e4;
+        const uint32_t wl = word_of(c[k >> 2], k & 3), wh = word_of(c[2 + (k >> 2)], k & 3);
+        const float2 l01 = fp8x2<false, SCALED>(wl, scl), l23 = fp8x2<true, SCALED>(wl, scl);
+        const float2 h01 = fp8x2<false, SCALED>(wh, scl), h23 = fp8x2<true, SCALED>(wh, scl);
+        const float xl[4] = {l01.x, l01.y, l23.x, l23.y}, xh[4] = {h01.x, h01.y, h23.x, h23.y};
+        uint32_t w = 0;
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {   // slots 7..4, then 3..0
+          CodeMasks m[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int slot = 4 * half + 3 - i;
+            m[i] = (slot & 1) ? code_masks(xh[slot >> 1], thh) : code_masks(xl[slot >> 1], thl);
+          }
+          w = push4(w, m);
+        }
+        w2[e4] = w ^ kFlipHigh;
+      }
+      *reinterpret_cast<uint2*>(&tw[ph][t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (g & 3)]) = make_uint2(w2[0], w2[1]);
+    }
+  } else if (valid) {
+    const int j = r8 / (2 * G), g = (r8 >> 1) % G, hh = r8 & 1;
+    const float scl = lt.v_scale[layer];
+    uint4 q[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) q[r] = *reinterpret_cast<const uint4*>(in + (kPage + 4 * j + r) * D + 32 * g + 16 * hh);
+    Thresholds th[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = absmax_fp8x16(q[r]);
+      const float am = fmaxf(a, lane_xor<1>(a));      // the partner lane holds the other half
+      const uint16_t sb = tq3_scale_bits(SCALED ? __fmul_rn(am, scl) : am);
+      if (hh == 0) sc[ph][(tq3_scale_off(D, 1, 4 * j + r, g) - 12 * D) / 2] = sb;
+      th[r] = thresholds(half_bits_to_float(sb));
+    }
+    // channel pair (a, a + 1), a = 32 g + 16 hh + 2 pc, is triple
+    // (16 j + n) G + p of the V codes; the 8 pairs are consecutive triples;
+    // slot 2 r + ci holds (channel a + ci, token 4 j + r)
+    const int tb = 2 * D + (j * 16 + (32 * g + 16 * hh) / (D / 16)) * G;
+    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
+    uint32_t w8[8];
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) {
+      float2 xv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xv[r] = (pc & 1) ? fp8x2<true, SCALED>(word_of(c[r], pc >> 1), scl) : fp8x2<false, SCALED>(word_of(c[r], pc >> 1), scl);
+      uint32_t w = 0;
+#pragma unroll
+      for (int half = 1; half >= 0; --half) {
+        CodeMasks m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 4 * half + 3 - i;
+          m[i] = code_masks((slot & 1) ? xv[slot >> 1].y : xv[slot >> 1].x, th[slot >> 1]);
+        }
+        w = push4(w, m);
+      }
+      w8[pc] = w ^ kFlipHigh;
+    }
+    uint4* dstw = reinterpret_cast<uint4*>(&tw[ph][tb]);
+    dstw[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+    dstw[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+  }
+  __syncthreads();
+
+  // four triples = 12 bytes per store; then the scales as 16-byte chunks
+  for (int e = threadIdx.x; e < PH * (NTRI / 4); e += 128) {
+    const int p = e / (NTRI / 4), tau = e - p * (NTRI / 4);
+    uint8_t* o = outp[p];
+    if (!o) continue;
+    const uint4 w = reinterpret_cast<const uint4*>(tw[p])[tau];
+    const u3v b3 = {w.x | (w.y << 24), (w.y >> 8) | (w.z << 16), (w.z >> 16) | (w.w << 8)};
+    *reinterpret_cast<u3v*>(o + 12 * tau) = b3;
+  }
+  for (int e = threadIdx.x; e < PH * (2 * D / 16); e += 128) {
+    const int p = e / (2 * D / 16), c = e - p * (2 * D / 16);
+    uint8_t* o = outp[p];
+    if (!o) continue;
+    reinterpret_cast<uint4*>(o + 12 * D)[c] = reinterpret_cast<const uint4*>(sc[p])[c];
+  }
+}
+
 hipError_t launch_demote_listed(const Geometry& g, const LayerTable& lt, int n_layers, const int32_t* src,
                                 const int32_t* dst, int n, const int32_t* n_dev, const TableUpdate* upd,
                                 hipStream_t stream) {
   if (n == 0 || n_layers == 0) return hipSuccess;
   dim3 grid(n_layers * n * g.hkv);
   const TableUpdate u = upd ? *upd : TableUpdate{nullptr, nullptr, nullptr, nullptr, nullptr};
-  // layers with rotated TQ3 pages take the instance with the rotation
-  if (g.d == 256) {
-    if (lt.any_signs)
-      hipLaunchKernelGGL((demote_kernel<256, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
-                         n_dev, u);
+  // layers with rotated TQ3 pages take the instance with the rotation; plain
+  // pools the mask-based one
+  const int items = n_layers * n * g.hkv;
+  if (!lt.any_signs) {
+    bool scaled = false;
+    for (int l = 0; l < n_layers; ++l) scaled = scaled || lt.k_scale[l] != 1.0f || lt.v_scale[l] != 1.0f;
+    const int wgs = g.d == 256 ? items : (items + 1) / 2;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(wgs), dim3(128), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst, n_dev, u,
+                         items);
+    };
+    if (g.d == 256)
+      scaled ? go(demote_plain_kernel<256, true>) : go(demote_plain_kernel<256, false>);
     else
-      hipLaunchKernelGGL((demote_kernel<256, false>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src,
-                         dst, n_dev, u);
+      scaled ? go(demote_plain_kernel<128, true>) : go(demote_plain_kernel<128, false>);
+  } else if (g.d == 256) {
+    hipLaunchKernelGGL((demote_kernel<256, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
+                       n_dev, u);
   } else {
-    if (lt.any_signs)
-      hipLaunchKernelGGL((demote_kernel<128, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
-                         n_dev, u);
-    else
-      hipLaunchKernelGGL((demote_kernel<128, false>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src,
-                         dst, n_dev, u);
+    hipLaunchKernelGGL((demote_kernel<128, true>), grid, dim3(256), 0, stream, lt, n, g.n_fp8, g.n_tq3, g.hkv, src, dst,
+                       n_dev, u);
   }
   return hipGetLastError();
 }

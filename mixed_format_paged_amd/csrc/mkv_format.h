@@ -80,12 +80,21 @@ __device__ inline float e4m3_decode(uint32_t c) {
 
 // ---- TQ3 ------------------------------------------------------------------
 
+// fl32(a / 3) for finite a: the product with fl32(1/3), corrected by its
+// exact remainder (one fma) and a second fma.  Checked against IEEE fp32
+// division for every finite non-negative fp32 a; a = inf gives NaN.
+__device__ inline float div3_rn(float a) {
+  constexpr float c = 0x1.555556p-2f;                  // fl32(1/3)
+  const float q = a * c;
+  return fmaf(fmaf(-3.0f, q, a), c, q);
+}
+
 // s = fp16_RNE(fl32(a / 3)), saturating at 65504.  Returned as fp16 bits.
 __device__ inline uint16_t tq3_scale_bits(float absmax) {
-  float r = __fdiv_rn(absmax, 3.0f);
+  float r = div3_rn(absmax);
   __half h = __float2half_rn(r);
   uint16_t bits = __half_as_ushort(h);
-  if ((bits & 0x7fffu) == 0x7c00u) bits = 0x7bffu;     // inf -> 65504
+  if ((bits & 0x7c00u) == 0x7c00u) bits = 0x7bffu;     // inf (and the NaN of a = inf) -> 65504
   return bits;
 }
 
