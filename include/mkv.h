@@ -136,12 +136,12 @@ typedef struct {
  *            TQ3 codes of y = c H (signs . x), H the Sylvester-Hadamard matrix
  *            applied by the fast transform in fp32, stage s pairing channels i
  *            and i + 2^s as (a + b, a - b) for s = 0, 1, ..., and c = 1/16 at
- *            head_dim 256, 1/8 at 128.  Demotion rotates;
- *            single-query decode with the matrix-core kernels rotates the
- *            queries of TQ3 pages and rotates their partial states back.
- *            Multi-query decode (n_query > 1), G > 8, materialisation and the
- *            VALU baseline kernels return MKV_ERR_RANGE for such a pool.  FP8
- *            pages are never rotated. */
+ *            head_dim 256, 1/8 at 128.  Demotion rotates; decode with the
+ *            matrix-core kernels (single- and multi-query, any G) rotates the
+ *            queries of TQ3 pages and rotates their partial states back;
+ *            materialisation takes TQ3 values back through the same fast
+ *            transform in fp32.  The VALU baseline kernels return
+ *            MKV_ERR_RANGE for such a pool.  FP8 pages are never rotated. */
 typedef struct {
   uint8_t* fp8_slab;
   uint8_t* tq3_slab;
@@ -386,7 +386,10 @@ int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_w
  *    logical page page_lo + i.
  * Element values: an FP8 page gives bf16_RNE(fl32(decode(e) * scale)) with the
  * pool's k_scale / v_scale; a TQ3 page gives bf16_RNE((u - 4) * s) (exact in
- * fp32 before the rounding).  A page's format follows its id (< n_fp8: FP8);
+ * fp32 before the rounding); a rotated TQ3 page (tq3_signs) gives
+ * bf16_RNE(signs . (H y) / 16) per token row, y = (u - 4) * s and H applied by
+ * the format's fast transform in fp32 (stage s pairs channels i and i + 2^s),
+ * the butterflies being the only rounding before the bf16 one.  A page's format follows its id (< n_fp8: FP8);
  * the tier map is not read.  A logical page outside the request's block
  * table, or an id outside the pool, gives bf16 NaN (0x7FC0) for all its
  * elements.  Tokens past the request's seq_len are converted like the
@@ -449,7 +452,7 @@ int mkv_lifecycle_release(const mkv_layout* layout, const mkv_pool* pool,
  * the measured baseline.  Process-wide; a call reads the setting once, when
  * it starts, so calls running on other threads are not affected mid-way.
  * Under 0, mkv_append_attend, multi-query decode and rotated TQ3 pools
- * return MKV_ERR_RANGE.  Returns MKV_OK, or MKV_ERR_RANGE for another kind. */
+ * return MKV_ERR_RANGE (the baseline covers plain single-query decode).  Returns MKV_OK, or MKV_ERR_RANGE for another kind. */
 int mkv_set_partial_kind(int32_t kind);
 
 /* Synchronise `stream` and return the device status bits (MKV_DEV_*) left in

@@ -279,10 +279,8 @@ int prepare_decode(const mkv_layout* layout, const mkv_pool* pools, int32_t n_la
       if ((rc = check_pool(&pools[l], g, true, true, true))) return rc;
       if (pools[l].n_fp8 != pools[0].n_fp8 || pools[l].n_tq3 != pools[0].n_tq3 || pools[l].tier != pools[0].tier)
         return fail(MKV_ERR_RANGE, "layer %d: pools must share n_fp8, n_tq3 and the tier map", l);
-      if (pools[l].tq3_signs && (n_query > 1 || g->G > kRowBlock || !g->partial_kind))
-        return fail(MKV_ERR_RANGE,
-                    "layer %d: rotated TQ3 pages need single-query decode, at most 8 query heads per KV head and "
-                    "the matrix-core kernels", l);
+      if (pools[l].tq3_signs && !g->partial_kind)
+        return fail(MKV_ERR_RANGE, "layer %d: rotated TQ3 pages need the matrix-core kernels", l);
       if (lt) set_layer(lt, l, pools[l]);
     }
   }
@@ -590,7 +588,6 @@ static int mkv_materialize_impl(const mkv_layout* layout, const mkv_pool* pool, 
   int rc = check_layout(layout, &g);
   if (rc) return rc;
   if ((rc = check_pool(pool, &g, true, true, false))) return rc;
-  if (pool->tq3_signs) return fail(MKV_ERR_RANGE, "materialisation of rotated TQ3 pages is not supported");
   if (!batch) return fail(MKV_ERR_NULL, "batch is NULL");
   if (b < 0 || b >= batch->batch || page_lo < 0 || n_pages < 0)
     return fail(MKV_ERR_RANGE, "b %d (batch %d) / page_lo %d / n_pages %d", b, batch->batch, page_lo, n_pages);
@@ -601,7 +598,7 @@ static int mkv_materialize_impl(const mkv_layout* layout, const mkv_pool* pool, 
   if (!aligned16(k_out) || !aligned16(v_out)) return fail(MKV_ERR_ALIGN, "k_out and v_out must be 16-byte aligned");
   hipError_t e = launch_materialize(g, pool->fp8_slab, pool->tq3_slab, pool->k_scale, pool->v_scale,
                                     batch->bt_offsets, batch->bt_pages, batch->bt_capacity, b, page_lo,
-                                    n_pages, k_out, v_out, as_stream(stream));
+                                    n_pages, k_out, v_out, pool->tq3_signs, as_stream(stream));
   return e == hipSuccess ? MKV_OK : hip_fail(e, "materialize launch");
 }
 

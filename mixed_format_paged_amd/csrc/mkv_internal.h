@@ -212,7 +212,8 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* fp8_slab, const uint8
 hipError_t launch_materialize(const Geometry& g, const uint8_t* fp8_slab, const uint8_t* tq3_slab,
                               float k_scale, float v_scale, const int32_t* bt_offsets,
                               const int32_t* bt_pages, int bt_capacity, int b, int page_lo,
-                              int n_pages, uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
+                              int n_pages, uint16_t* k_out, uint16_t* v_out, const int8_t* signs,
+                              hipStream_t stream);
 hipError_t launch_plan(const Geometry& g, const uint8_t* tier, const int32_t* bt_offsets,
                        const int32_t* bt_pages, const int32_t* seq_lens, const Plan& plan,
                        hipStream_t stream);

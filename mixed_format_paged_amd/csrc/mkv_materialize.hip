@@ -9,6 +9,11 @@
 //
 // Element values: FP8 page bf16_RNE(fl32(decode(e) * scale)); TQ3 page
 // bf16_RNE((u - 4) * s), where (u - 4) * s is exact in fp32 (11 + 3 bits).
+// Rotated TQ3 pages (the layer has a sign vector; the codes are those of
+// y = c H (signs . x)): per token row, the exact y = (u - 4) s goes through the
+// format's fast transform in fp32 (stage s = 0, 1, ... pairs channels i and
+// i + 2^s as (a + b, a - b)), and x = signs . (H y) / (c d), c d = 16 (exact),
+// then bf16_RNE.
 // One workgroup per (logical page, KV head): an FP8 page-head converts from
 // global memory directly (hardware E4M3 decode, exact); a TQ3 head block
 // (14 d bytes) is first staged in LDS, each thread decodes whole triples (8
@@ -32,18 +37,19 @@ __device__ inline uint32_t bf16_rne(float x) {
 
 }  // namespace
 
-template <int D>
+template <int D, bool ROT>
 __global__ void __launch_bounds__(kThreads) materialize_kernel(
     const uint8_t* __restrict__ fp8_slab, const uint8_t* __restrict__ tq3_slab, int n_fp8, int n_tq3,
     float k_scale, float v_scale, int hkv, const int32_t* __restrict__ bt_offsets,
     const int32_t* __restrict__ bt_pages, int bt_capacity, int b, int page_lo, int n_pages,
-    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
+    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, const int8_t* __restrict__ signs) {
   constexpr int C8 = D / 8;                          // 16-byte output chunks per token row
   constexpr int kChunks = 2 * kPage * C8;            // K and V chunks of a page-head
   constexpr int G = D / 32;                          // 32-channel scale groups
   constexpr int NTRI = 2 * D;                        // triples of K (and of V) in a head block
   __shared__ __align__(16) uint8_t blk[14 * D];
   __shared__ __align__(16) uint16_t tile[2][kPage][D];   // bf16 bits of a TQ3 page-head, [K/V][token][channel]
+  __shared__ __align__(16) float ftile[ROT ? 2 : 1][ROT ? kPage : 1][ROT ? D : 1];   // rotated: fp32 rows
   const int off0 = bt_offsets[b], off1 = bt_offsets[b + 1];
   const long units = (long)n_pages * hkv;
   for (long unit = blockIdx.x; unit < units; unit += gridDim.x) {
@@ -77,7 +83,11 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
 #pragma unroll
           for (int sl = 0; sl < 8; ++sl) {
             const float v = (float)((int)((w >> (3 * sl)) & 7u) - 4) * ((sl & 1) ? s1 : s0);
-            tile[0][t][32 * ((sl & 1) ? g1 : g0) + cb + (sl >> 1)] = (uint16_t)bf16_rne(v);
+            const int c = 32 * ((sl & 1) ? g1 : g0) + cb + (sl >> 1);
+            if (ROT)
+              ftile[0][t][c] = v;
+            else
+              tile[0][t][c] = (uint16_t)bf16_rne(v);
           }
         } else {
           const int jq = x / (16 * G), rem = x % (16 * G), n = rem / G, p = rem % G;
@@ -89,12 +99,35 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
 #pragma unroll
             for (int ci = 0; ci < 2; ++ci) {
               const int sl = tq3_v_slot(ci, r);
-              tile[1][t][c0 + ci] = (uint16_t)bf16_rne((float)((int)((w >> (3 * sl)) & 7u) - 4) * sc);
+              const float v = (float)((int)((w >> (3 * sl)) & 7u) - 4) * sc;
+              if (ROT)
+                ftile[1][t][c0 + ci] = v;
+              else
+                tile[1][t][c0 + ci] = (uint16_t)bf16_rne(v);
             }
           }
         }
       }
       __syncthreads();
+      if (ROT) {
+        // H y for each of the 2 x 16 rows, stage by stage, then the signs and 1/16
+        for (int hs = 1; hs < D; hs <<= 1) {
+          for (int pp = threadIdx.x; pp < 2 * kPage * (D / 2); pp += kThreads) {
+            const int row = pp / (D / 2), r = pp % (D / 2);
+            float* const rr = &ftile[row / kPage][row % kPage][(r / hs) * 2 * hs + r % hs];
+            const float a = rr[0], b2 = rr[hs];
+            rr[0] = a + b2;
+            rr[hs] = a - b2;
+          }
+          __syncthreads();
+        }
+        for (int e = threadIdx.x; e < 2 * kPage * D; e += kThreads) {
+          const int kv = e / (kPage * D), t = (e / D) % kPage, c = e % D;
+          const float v = ftile[kv][t][c] * 0.0625f;
+          tile[kv][t][c] = (uint16_t)bf16_rne(signs[c] < 0 ? -v : v);
+        }
+        __syncthreads();
+      }
     }
     for (int q = threadIdx.x; q < kChunks; q += kThreads) {
       const int kv = q / (kPage * C8), t = (q / C8) % kPage, c8 = q % C8;
@@ -125,18 +158,19 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(
 hipError_t launch_materialize(const Geometry& g, const uint8_t* fp8_slab, const uint8_t* tq3_slab,
                               float k_scale, float v_scale, const int32_t* bt_offsets,
                               const int32_t* bt_pages, int bt_capacity, int b, int page_lo,
-                              int n_pages, uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
+                              int n_pages, uint16_t* k_out, uint16_t* v_out, const int8_t* signs,
+                              hipStream_t stream) {
   const long units = (long)n_pages * g.hkv;
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)(units < 8192 ? units : 8192));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, fp8_slab, tq3_slab, g.n_fp8, g.n_tq3, k_scale, v_scale,
+                       g.hkv, bt_offsets, bt_pages, bt_capacity, b, page_lo, n_pages, k_out, v_out, signs);
+  };
   if (g.d == 256)
-    hipLaunchKernelGGL(materialize_kernel<256>, grid, dim3(kThreads), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
-                       g.n_tq3, k_scale, v_scale, g.hkv, bt_offsets, bt_pages, bt_capacity, b, page_lo, n_pages, k_out,
-                       v_out);
+    signs ? go(materialize_kernel<256, true>) : go(materialize_kernel<256, false>);
   else
-    hipLaunchKernelGGL(materialize_kernel<128>, grid, dim3(kThreads), 0, stream, fp8_slab, tq3_slab, g.n_fp8,
-                       g.n_tq3, k_scale, v_scale, g.hkv, bt_offsets, bt_pages, bt_capacity, b, page_lo, n_pages, k_out,
-                       v_out);
+    signs ? go(materialize_kernel<128, true>) : go(materialize_kernel<128, false>);
   return hipGetLastError();
 }
 

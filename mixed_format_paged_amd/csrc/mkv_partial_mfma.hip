@@ -306,7 +306,12 @@ template <int D>
 constexpr int kLds16 = Geo<D>::kRing + 2 * Geo<D>::kSq + Geo<D>::kRowMax + Geo<D>::kKsum;
 template <int D>
 constexpr int kSmemBytes16 = kLds16<D> > MergeLayout<D>::bytes(16) ? kLds16<D> : MergeLayout<D>::bytes(16);
-static_assert(kSmemBytes<256> <= 160 * 1024 && kSmemBytes16<256> <= 160 * 1024, "LDS of one workgroup");
+// rotated 16-row instances: the merge layout, then [16][D] rows for the back-rotation
+template <int D>
+constexpr int kRotBytes16 = MergeLayout<D>::bytes(16) + 16 * D * 4;
+template <int D>
+constexpr int kSmemRot16 = kSmemBytes16<D> > kRotBytes16<D> ? kSmemBytes16<D> : kRotBytes16<D>;
+static_assert(kSmemBytes<256> <= 160 * 1024 && kSmemRot16<256> <= 160 * 1024, "LDS of one workgroup");
 
 template <typename T>
 __device__ inline T lds_load(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
@@ -945,6 +950,28 @@ __device__ __forceinline__ void run_item(
   auto state_at = [&](int i, int c) { return (size_t)(c / kStateSlice) * slice_stride + i * kStateSlice + c % kStateSlice; };
   const float l_tot = sum_xor32(sum_xor16(st.l_run));   // sum over the four token rows of column n
   uint32_t opq = 0;
+  // rotated TQ3 (uniform): the summed state rows acc' (rows x D in LDS at
+  // rbuf) go back to the cache's channels, acc = signs . (H acc') / (c d),
+  // c d = 16, H by the fast transform (stage s pairs channels i and i + 2^s)
+  const int8_t* const sgn = (ROT && tq3) ? lt.signs[layer] : nullptr;
+  auto rotate_back_store = [&](float* rbuf, int rows) {
+    for (int hs = 1; hs < D; hs <<= 1) {
+      __syncthreads();
+      for (int pp = threadIdx.x; pp < rows * D / 2; pp += kThreads) {
+        const int i = pp / (D / 2), r = pp - i * (D / 2);
+        float* const rr = rbuf + i * D + (r / hs) * 2 * hs + r % hs;
+        const float a = rr[0], b2 = rr[hs];
+        rr[0] = a + b2;
+        rr[hs] = a - b2;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
+      const int c = idx % D;
+      const float v = rbuf[idx] * 0.0625f;       // 1 / (c d) = 1/16 at d = 128 and 256
+      __builtin_nontemporal_store(sgn[c] < 0 ? -v : v, pa_out + state_at(idx / D, c));
+    }
+  };
   if constexpr (RB == 16) {
   __syncthreads();                              // the staging block becomes the merge buffer
   // an opaque zero offset for the merge-buffer addresses below: it keeps the
@@ -987,16 +1014,21 @@ __device__ __forceinline__ void run_item(
       }
       __syncthreads();
       const int rows_p = rb.rows - 8 * pass < 8 ? rb.rows - 8 * pass : 8;
+      float* const rbuf = so + MergeLayout<D>::bytes(16) / 4;   // rotated: [16][D], after the merge layout
       for (int idx = threadIdx.x; idx < rows_p * D; idx += kThreads) {
         const int i = idx / D, c = idx - (idx / D) * D;
         const float* src = so + opq + MergeLayout<D>::at(0, i, c / (D / 16), c % (D / 16));
         float acc = 0.0f;
 #pragma unroll 4
         for (int w = 0; w < kWaves; ++w) acc += src[w * MergeLayout<D>::kWave];
-        __builtin_nontemporal_store(acc, pa_out + state_at(8 * pass + i, c));
+        if (ROT && sgn)
+          rbuf[(8 * pass + i) * D + c] = acc;
+        else
+          __builtin_nontemporal_store(acc, pa_out + state_at(8 * pass + i, c));
       }
       __syncthreads();                                  // the layout is rewritten by the next pass
     }
+    if (ROT && sgn) rotate_back_store(so + MergeLayout<D>::bytes(16) / 4, rb.rows);
   if (threadIdx.x < rb.rows) {
     const int i = threadIdx.x + opq;
     const float M = sM[i];
@@ -1076,29 +1108,13 @@ __device__ __forceinline__ void run_item(
     return acc;
   };
 
-  const int8_t* const sgn = (ROT && tq3) ? lt.signs[layer] : nullptr;
-  if (ROT && sgn) {                                     // rotated TQ3 (uniform): acc = signs . (H acc') / (c d)
+  if (ROT && sgn) {                                     // rotated TQ3 (uniform)
     float* const rbuf = so + kOwnBytes<D> / 4;          // [rows][D], after the regions and weights
     for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
       const int i = idx / D, c = idx - (idx / D) * D;
       rbuf[idx] = sum_at(i, c);
     }
-    for (int hs = 1; hs < D; hs <<= 1) {
-      __syncthreads();
-      for (int pp = threadIdx.x; pp < rb.rows * D / 2; pp += kThreads) {
-        const int i = pp / (D / 2), r = pp - i * (D / 2);
-        float* const rr = rbuf + i * D + (r / hs) * 2 * hs + r % hs;
-        const float a = rr[0], b2 = rr[hs];
-        rr[0] = a + b2;
-        rr[hs] = a - b2;
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
-      const int c = idx % D;
-      const float v = rbuf[idx] * 0.0625f;       // 1 / (c d) = 1/16 at d = 128 and 256
-      __builtin_nontemporal_store(sgn[c] < 0 ? -v : v, pa_out + state_at(idx / D, c));
-    }
+    rotate_back_store(rbuf, rb.rows);
   } else {
     for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
       const int i = idx / D, c = idx - (idx / D) * D;
@@ -1120,14 +1136,14 @@ __device__ __forceinline__ void run_item(
 // the request's last two logical pages.
 // RB: query rows per item, 8 (MFMA rows 0..7, remainders in 8..15) or, for
 // multi-query blocks, 16 (remainders through second MFMAs; 48 KB of LDS).
-// ROT: some layer has rotated TQ3 pages (single-query only): TQ3 items read
-// q_t (the rotated queries) and rotate their partial states back.
+// ROT: some layer has rotated TQ3 pages: TQ3 items read q_t (the rotated
+// queries) and rotate their partial states back.
 template <int D, int MODE, bool MQ, int RB, bool ROT = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(kAttendWavesPerSimd, kAttendWavesPerSimd))) attend_kernel(
         LayerTable lt, int n_layers, int hkv, int G, const float* __restrict__ q, const float* __restrict__ q_t,
         size_t q_ls, float qscale, Plan plan, AppendIn ap) {
-  __shared__ __align__(16) uint8_t smem[RB == 16 ? kSmemBytes16<D> : kSmemBytes<D>];
+  __shared__ __align__(16) uint8_t smem[RB == 16 ? (ROT ? kSmemRot16<D> : kSmemBytes16<D>) : kSmemBytes<D>];
 
   static_assert(kWaves == kItemWaves, "a chunk-table entry holds the first page of every wave");
   const int nblk = MQ ? plan.nblk : 1;
@@ -1238,11 +1254,12 @@ template <int MODE, bool MQ, int RB>
 static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layers, const float* q,
                             size_t q_ls, float qscale, const Plan& plan, const AppendIn& ap,
                             hipStream_t stream) {
-  // rotated TQ3 pages read rotated queries (single-query decode only; the
-  // host rejects rotated pools for several query tokens)
+  // rotated TQ3 pages read rotated queries (every query row of the launch:
+  // batch x query tokens x heads per layer); FP8-only launches need none
   const float* q_t = q;
-  if (lt.any_signs && !MQ) {
-    const int rows = plan.batch * g.hq;
+  const bool rot = lt.any_signs && MODE != kFp8Only;
+  if (rot) {
+    const int rows = plan.batch * (MQ ? plan.n_query : 1) * g.hq;
     if (rows > 0) {
       if (g.d == 256)
         hipLaunchKernelGGL(rotate_q_kernel<256>, dim3(n_layers * rows), dim3(256), 0, stream, q, plan.q_rot, rows, lt);
@@ -1253,18 +1270,17 @@ static void launch_attend_t(const Geometry& g, const LayerTable& lt, int n_layer
   }
   // partials per layer bound the items of either format, or of both together
   const dim3 grid = attend_grid((long)n_layers * g.hkv * plan.np_cap * (MQ ? plan.nblk : 1)), block(kThreads);
-  const bool rot = lt.any_signs && !MQ;
   if (g.d == 256) {
     if (rot)
-      hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB, !MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                         q_t, q_ls, qscale, plan, ap);
+      hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB, MODE != kFp8Only>), grid, block, 0, stream, lt, n_layers,
+                         g.hkv, g.G, q, q_t, q_ls, qscale, plan, ap);
     else
       hipLaunchKernelGGL((attend_kernel<256, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                          q_t, q_ls, qscale, plan, ap);
   } else {
     if (rot)
-      hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB, !MQ>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
-                         q_t, q_ls, qscale, plan, ap);
+      hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB, MODE != kFp8Only>), grid, block, 0, stream, lt, n_layers,
+                         g.hkv, g.G, q, q_t, q_ls, qscale, plan, ap);
     else
       hipLaunchKernelGGL((attend_kernel<128, MODE, MQ, RB>), grid, block, 0, stream, lt, n_layers, g.hkv, g.G, q,
                          q_t, q_ls, qscale, plan, ap);

@@ -11,12 +11,19 @@ cache holds:
 * FP8 page: x = fl32(decode(e) * scale) (the same fp32 product the TQ3 demote
   starts from), then bf16.
 * TQ3 page: x = (u - 4) * s, exact in fp32, then bf16.
+* Rotated TQ3 page (the pool has a sign vector): y = (u - 4) * s is the
+  rotated value; x = signs . (H y) / (c d) with H applied by the format's
+  fast transform in fp32 (oracle.rotation.unrotate_f32: the butterflies are
+  the only rounding), then bf16.  The pages fix no dense form of rotated
+  pages; this one spends no precision beyond fp32 and inverts the demote
+  side's transform stage by stage.
 
 Every function is pinned by tests/test_oracle_dense.py.
 """
 import numpy as np
 
 from . import pool as opool
+from . import rotation
 from .layout import PAGE
 
 BF16_NAN = 0x7FC0
@@ -53,13 +60,16 @@ def bf16_to_float(bits):
 
 def page_fp32(pool, pid):
     """The fp32 values a page holds, [Hkv][2][16][d]: fl32(decode(e) * scale) for
-    an FP8 page, (u - 4) * s for a TQ3 page (exact in fp32)."""
+    an FP8 page, (u - 4) * s for a TQ3 page (exact in fp32), and for a rotated
+    TQ3 page those values taken back through unrotate_f32."""
     pid = int(pid)
     if pid < pool.n_fp8:
         return opool.fp8_page_values(pool, pid)
-    vals = opool.page_values(pool, pid)                        # float64, exact
+    vals = opool.tq3_page_codes_values(pool, pid)              # float64, exact
     f32 = vals.astype(np.float32)
     assert np.array_equal(f32.astype(np.float64), vals), "TQ3 values are exact in fp32"
+    if pool.signs is not None:
+        return rotation.unrotate_f32(f32, pool.signs)
     return f32
 
 

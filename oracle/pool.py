@@ -104,7 +104,17 @@ def page_values(pool, pid):
         e = pool.fp8[pid].reshape(pool.Hkv, 2, PAGE, pool.d)
         x = fp8.e4m3_decode(e)
         return x * np.array([float(pool.k_scale), float(pool.v_scale)])[None, :, None, None]
-    assert pid < pool.n_fp8 + pool.n_tq3
+    out = tq3_page_codes_values(pool, pid)
+    if pool.signs is not None:
+        out = rotation.unrotate_f64(out, pool.signs)             # back to the channels of the cache
+    return out
+
+
+def tq3_page_codes_values(pool, pid):
+    """(u - 4) s of every code of TQ3 page pid, float64 [Hkv][2][16][d] (exact):
+    for a rotated pool these are the rotated values y, before unrotation."""
+    pid = int(pid)
+    assert pool.n_fp8 <= pid < pool.n_fp8 + pool.n_tq3
     hb = tq3_head_bytes(pool.d)
     out = np.zeros((pool.Hkv, 2, PAGE, pool.d))
     blk_all = pool.tq3[pid - pool.n_fp8]
@@ -113,8 +123,6 @@ def page_values(pool, pid):
         G = pool.d // tq3.GROUP
         out[h, 0] = tq3.dequantize_groups(uK.reshape(PAGE, G, tq3.GROUP), sK).reshape(PAGE, pool.d)
         out[h, 1] = tq3.dequantize_groups(uV.reshape(PAGE, G, tq3.GROUP), sV).reshape(PAGE, pool.d)
-    if pool.signs is not None:
-        out = rotation.unrotate_f64(out, pool.signs)             # back to the channels of the cache
     return out
 
 

@@ -70,6 +70,17 @@ def unrotate_f64(y, signs):
     return (y @ H) * np.asarray(signs, dtype=np.float64) / (rot_scale(d) * d)
 
 
+def unrotate_f32(y, signs):
+    """x = signs . (H y) / (c d) in fp32, H by the fast transform in the
+    format's stage order (fwht_f32); signs and 1 / (c d) (a power of two) are
+    exact.  This is the value a dense (materialised) copy of a rotated TQ3
+    page holds: y = (u - 4) s is exact in fp32, so only the butterflies round."""
+    y = np.asarray(y, dtype=np.float32)
+    d = y.shape[-1]
+    s = np.asarray(signs).astype(np.float32)
+    return (fwht_f32(y) * s * np.float32(1.0 / (rot_scale(d) * d))).astype(np.float32)
+
+
 def rotate_query_f64(q, signs):
     """q' = H (signs . q) / (c d) in fp64, so that q' . rotate(k) = q . k."""
     q = np.asarray(q, dtype=np.float64)

@@ -312,23 +312,29 @@ def test_append_attend_equals_append_then_attend():
     assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
 
 
-@pytest.mark.parametrize("d,scales", [(128, (0.75, 1.25)), (256, (1.0, 1.0))])
-def test_materialize_bitexact(d, scales):
+@pytest.mark.parametrize("d,scales,rotated", [(128, (0.75, 1.25), False), (256, (1.0, 1.0), False),
+                                              (128, (0.75, 1.25), True), (256, (1.0, 1.0), True)])
+def test_materialize_bitexact(d, scales, rotated):
     """mkv_materialize on the oracle's own pool bytes equals the oracle's dense
     bf16 bits: whole requests, a range starting inside and running past the
-    end of a block table (NaN pages), and an id outside the pool."""
-    from oracle import dense as OD
+    end of a block table (NaN pages), and an id outside the pool.  rotated:
+    the layer's TQ3 pages are rotated TQ3 (dense values through the fp32
+    inverse transform)."""
+    from oracle import dense as OD, rotation as OR
     w = W.scaled(W.WORKLOADS["tiny-1x1024-d128"], d=d, B=3, lengths=("list", (1024, 300, 17)))
     st = W.make_structure(w)
     vals = W.layer_values(w, st, 0)
-    pool, bt = OB.build_layer(w, st, [x.numpy() for x in vals["k"]], [x.numpy() for x in vals["v"]], *scales)
+    signs = OR.random_signs(d, 17) if rotated else None
+    pool, bt = OB.build_layer(w, st, [x.numpy() for x in vals["k"]], [x.numpy() for x in vals["v"]], *scales,
+                              signs=signs)
     bt = bt.copy()
     bt[int(st.bt_offsets[2])] = pool.n_fp8 + pool.n_tq3 + 3          # request 2, page 0: not in the pool
     dev = "cuda"
     fp8_d = torch.from_numpy(pool.fp8).to(dev)
     tq3_d = torch.from_numpy(pool.tq3).to(dev)
     tier_d = torch.from_numpy(pool.tier).to(dev)
-    pd = M.make_pool(fp8_d, tq3_d, tier_d, pool.n_fp8, pool.n_tq3, *scales)
+    sg = None if signs is None else torch.as_tensor(signs, device=dev)
+    pd = M.make_pool(fp8_d, tq3_d, tier_d, pool.n_fp8, pool.n_tq3, *scales, tq3_signs=sg)
     batch = M.make_batch(torch.as_tensor(st.bt_offsets, dtype=torch.int32, device=dev),
                          torch.as_tensor(bt, dtype=torch.int32, device=dev),
                          torch.as_tensor(st.seq_lens, dtype=torch.int32, device=dev))

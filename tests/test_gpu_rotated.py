@@ -4,9 +4,9 @@ before the TQ3 rule; oracle/rotation.py).
 Bit-exact: the demoted bytes (the rotation's fp32 butterflies run in the
 format's stage order on both sides).  Within the attention bar (max-abs 2e-3,
 rel-L2 1e-3, lse 1e-3): decode over mixed pools with rotated TQ3 pages,
-against the oracle's decode over the same pool definition (dequantise, rotate
-back in fp64, dense fp64 attention).  Entry points that do not take rotated
-pages refuse them.
+single-query (8- and 16-row items) and multi-query, against the oracle's
+decode over the same pool definition (dequantise, rotate back in fp64, dense
+fp64 attention).  The VALU baseline kernels refuse rotated pools.
 """
 import math
 
@@ -63,6 +63,11 @@ ROT = [
                                lengths=("list", (500, 0, 1025)), recent_tokens=64)),
     ("heads-16q-2kv-d128", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, Hq=16, Hkv=2,
                                     lengths=("list", (257, 1200)), recent_tokens=32)),
+    # more than 8 query heads per KV head: the 16-row items
+    ("heads-40q-4kv", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=2, L=2, Hq=40, Hkv=4,
+                               lengths=("list", (900, 333)), recent_tokens=64)),
+    ("heads-32q-2kv-d128", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=2, Hq=32, Hkv=2,
+                                    lengths=("list", (600, 1100)), recent_tokens=32)),
 ]
 
 
@@ -102,21 +107,47 @@ def test_rotated_decode_parity(name, w):
         compare(o1.cpu().numpy(), ref[li][2], l1.cpu().numpy(), ref[li][3], f"{name} single layer {li}")
 
 
-def test_rotated_pools_refused_where_unsupported():
+@pytest.mark.parametrize("T,d,hq,hkv", [(2, 256, 24, 4), (5, 128, 16, 2), (3, 256, 8, 8)])
+def test_rotated_multi_query_decode_parity(T, d, hq, hkv):
+    """mkv_decode_attn_multi over rotated TQ3 pages (layer 0 rotated, layer 1
+    plain, one launch): each request's last T tokens as causal queries against
+    the oracle's decode over the same pool definition; rows per KV head T G =
+    12 (16-row block), 40 (16-row blocks, the last part-filled) and 3 (8-row
+    block).  recent = 16 tokens puts logical page n - 2 in TQ3, so the causal
+    mask also runs on a rotated page."""
+    from oracle import attention as OA
+    M.set_partial_kind(1)
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=4, L=2, d=d, Hq=hq, Hkv=hkv,
+                 lengths=("list", (1300, 2, 0, 517)), recent_tokens=16)
+    st = W.make_structure(w)
+    signs = [OR.random_signs(d, 300 + T), None]
+    dw = DeviceWorkload(w, st, "cuda", keep_values=True, gen_device="cpu", tq3_signs=signs)
+    ref = oracle_side(w, st, dw.values, signs)
+    layout = (w.Hq, w.Hkv, w.d)
+    L, B = 2, w.B
+    g = torch.Generator()
+    g.manual_seed(200 + T)
+    q = torch.randn((L, B, T, w.Hq, w.d), generator=g)
+    ws = torch.empty(M.mkv_decode_workspace_bytes_multi(layout, B, dw.bt.numel(), L, T), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((L, B, T, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((L, B, T, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn_multi(layout, dw.cache.pools, dw.batch(), q.to("cuda").contiguous(), 1 / math.sqrt(w.d), out,
+                            lse, ws)
+    torch.cuda.synchronize()
+    assert M.mkv_workspace_status(ws) == 0
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for li, (pool, bt, _, _) in enumerate(ref):
+        o_ref, l_ref = OA.decode_batch_multi(pool, q[li].numpy(), st.bt_offsets, bt, st.seq_lens)
+        compare(o[li].reshape(-1, w.d), o_ref.reshape(-1, w.d), l[li].reshape(-1), l_ref.reshape(-1),
+                f"rotated T={T} d={d} layer {li}")
+
+
+def test_rotated_pools_refused_by_the_valu_baseline():
     w = W.scaled(W.WORKLOADS["batch-8x16384"], B=2, lengths=("fixed", 300), recent_tokens=64)
     st = W.make_structure(w)
     dw = DeviceWorkload(w, st, "cuda", tq3_signs=[OR.random_signs(w.d, 1)])
     layout = (w.Hq, w.Hkv, w.d)
-    T = 2
-    ws = torch.empty(M.mkv_decode_workspace_bytes_multi(layout, w.B, dw.bt.numel(), 1, T), dtype=torch.uint8,
-                     device="cuda")
-    q = torch.zeros((1, w.B, T, w.Hq, w.d), device="cuda")
-    out = torch.empty_like(q)
-    with pytest.raises(M.MkvError):
-        M.mkv_decode_attn_multi(layout, dw.cache.pools, dw.batch(), q, 0.0625, out, None, ws)
-    K = torch.empty((16, w.Hkv, w.d), dtype=torch.int16, device="cuda")
-    with pytest.raises(M.MkvError):
-        M.mkv_materialize(layout, dw.cache.pools[0], dw.batch(), 0, 0, 1, K, K.clone())
     M.set_partial_kind(0)
     try:
         ws1 = torch.empty(M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")

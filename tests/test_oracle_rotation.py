@@ -126,3 +126,61 @@ def test_value_path_matches_pool_path_with_signs():
     q = rng.standard_normal((3, d)).astype(np.float32)
     o, lse = OA.decode_attention(q, K, V)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# ---- unrotate_f32: the dense value of a rotated TQ3 element -----------------
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_unrotate_f32_spikes_are_exact(d):
+    # y = v e_k: every butterfly adds a zero, so x = signs . H[:, k] v / (c d) exactly
+    s = R.random_signs(d, 3 + d)
+    H = R.sylvester(d)
+    for k, v in ((0, 1.5), (1, -0.375), (d - 1, 6144.0), (d // 3, 2.0 ** -20)):
+        y = np.zeros(d, dtype=np.float32)
+        y[k] = v
+        want = (s.astype(np.float64) * H[:, k] * v / (R.rot_scale(d) * d)).astype(np.float32)
+        assert np.array_equal(R.unrotate_f32(y, s), want)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_unrotate_f32_inverts_the_rotation_on_integers(d):
+    # small integers: every fp32 sum of both transforms is exact, c and 1/(c d)
+    # are powers of two, so the round trip returns x bit for bit
+    rng = np.random.default_rng(5)
+    s = R.random_signs(d, 9)
+    x = rng.integers(-64, 65, (7, d)).astype(np.float32)
+    assert np.array_equal(R.unrotate_f32(R.rotate_f32(x, s), s), x)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_unrotate_f32_within_the_butterfly_bound(d):
+    # each of the log2(d) stages rounds every element once, by at most 2^-24 of
+    # a partial sum, itself at most sum |y|: |fp32 - exact| <= log2(d) 2^-24 sum|y| / (c d)
+    rng = np.random.default_rng(6)
+    s = R.random_signs(d, 10)
+    y = (rng.standard_normal((50, d)) * np.exp(rng.uniform(-8, 8, (50, 1)))).astype(np.float32)
+    got = R.unrotate_f32(y, s).astype(np.float64)
+    exact = R.unrotate_f64(y, s)
+    bound = np.log2(d) * 2.0 ** -24 * np.abs(y.astype(np.float64)).sum(axis=-1, keepdims=True) / (R.rot_scale(d) * d)
+    assert (np.abs(got - exact) <= bound * (1 + 1e-12)).all()
+    assert (np.abs(got - exact) > 0).any()                 # the fp32 path does round somewhere
+
+
+def test_dense_values_of_a_rotated_page_take_the_fp32_inverse():
+    from oracle import dense as OD
+    d, hkv, n = 128, 2, 2
+    rng = np.random.default_rng(12)
+    s = R.random_signs(d, 4)
+    rot = OP.Pool(hkv, d, n, n, 0.75, 1.25, signs=s)
+    raw = rng.integers(0, 256, (n, rot.fp8.shape[1])).astype(np.uint8)
+    raw[(raw & 0x7F) == 0x7F] = 0x7E
+    rot.fp8[:] = raw
+    OP.demote(rot, np.arange(n), n + np.arange(n))
+    for p in range(n):
+        y = OP.tq3_page_codes_values(rot, n + p)
+        got = OD.page_fp32(rot, n + p)
+        assert got.dtype == np.float32
+        assert np.array_equal(got, R.unrotate_f32(y.astype(np.float32), s))
+        # and it is the fp64 page value to within the butterfly bound
+        bound = np.log2(d) * 2.0 ** -24 * np.abs(y).sum(axis=-1, keepdims=True) / 16
+        assert (np.abs(got - OP.page_values(rot, n + p)) <= bound * (1 + 1e-12)).all()
