@@ -969,7 +969,7 @@ __device__ __forceinline__ void run_item(
     for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
       const int c = idx % D;
       const float v = rbuf[idx] * 0.0625f;       // 1 / (c d) = 1/16 at d = 128 and 256
-      __builtin_nontemporal_store(sgn[c] < 0 ? -v : v, pa_out + state_at(idx / D, c));
+      pa_out[state_at(idx / D, c)] = sgn[c] < 0 ? -v : v;
     }
   };
   if constexpr (RB == 16) {
@@ -1024,7 +1024,7 @@ __device__ __forceinline__ void run_item(
         if (ROT && sgn)
           rbuf[(8 * pass + i) * D + c] = acc;
         else
-          __builtin_nontemporal_store(acc, pa_out + state_at(8 * pass + i, c));
+          pa_out[state_at(8 * pass + i, c)] = acc;
       }
       __syncthreads();                                  // the layout is rewritten by the next pass
     }
@@ -1118,7 +1118,7 @@ __device__ __forceinline__ void run_item(
   } else {
     for (int idx = threadIdx.x; idx < rb.rows * D; idx += kThreads) {
       const int i = idx / D, c = idx - (idx / D) * D;
-      __builtin_nontemporal_store(sum_at(i, c), pa_out + state_at(i, c));   // streamed out: read once, by the merge
+      pa_out[state_at(i, c)] = sum_at(i, c);   // ordinary stores: the merge, next on the stream, reads them from the caches
     }
   }
   }
