@@ -54,6 +54,9 @@ def parse():
                     help="only run a plain device copy of BYTES bytes 5 times (counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many eager steps (for rocprofv3), print nothing else")
+    ap.add_argument("--item-trace", type=int, default=0, metavar="REPS",
+                    help="only trace REPS partial-attention launches with the item-trace build "
+                         "(mixed_format_paged_amd/libmkv_trace.so) and print their per-workgroup timeline")
     return ap.parse_args()
 
 
@@ -188,6 +191,59 @@ class Runner:
             ms = sorted(a.elapsed_time(b) for a, b in evs)
             res[name] = (sum(ms) / len(ms), ms[len(ms) // 2])
         return res
+
+
+def item_trace(runner, reps):
+    """Per-workgroup timeline of the partial-attention launch, from the
+    item-trace build (mkv_debug_item_trace: the 100 MHz constant clock at
+    points of each workgroup's item).  Each repetition runs partials + merge
+    on two layers back to back, then partials on a third, and reads the trace
+    of that last launch.  Returns a dict of percentiles (p10, p50, p90, max)
+    in microseconds, pooled over the repetitions."""
+    import numpy as np
+    torch, M = runner.torch, runner.M
+    lay, bat, ws, L = runner.layout, runner.batch, runner.ws, runner.w.L
+    M.mkv_decode_plan(lay, runner.dw.cache.pools[0], bat, 1, ws)
+    part = lambda l: M.mkv_attend_partials(lay, [runner.dw.cache.pools[l]], bat, runner.q[l], runner.sm_scale, ws)
+    merge = lambda l: M.mkv_merge(lay, 1, bat, runner.out[l], runner.lse[l], ws)
+    keys = ("entry", "fragments_built", "first_page_landed", "page_loop", "loop_end_spread_in_wg",
+            "last_loop_end_to_stored", "stored", "stored_tq3_items", "stored_fp8_items")
+    acc = {k: [] for k in keys}
+    buf = np.zeros((4096, 32), dtype=np.uint64)
+    items = None
+    for i in range(reps + 1):
+        l0 = (3 * i) % L
+        part(l0)
+        merge(l0)
+        part((l0 + 1) % L)
+        merge((l0 + 1) % L)
+        part((l0 + 2) % L)
+        torch.cuda.synchronize()
+        M.mkv_debug_item_trace(buf)
+        if i == 0:
+            continue                                    # warm-up
+        info = buf[:, 3].astype(np.int64)
+        used = (info & 0xFFFFFFFF) > 0
+        t = buf[used].astype(np.int64)
+        items = int(used.sum())
+        us = lambda x: (x - t[:, 0].min()) / 100.0     # 100 MHz clock -> us from the first entry
+        first, lend = t[:, 4:16], t[:, 16:28]
+        valid = first > 0
+        acc["entry"] += list(us(t[:, 0]))
+        acc["fragments_built"] += list((t[:, 1] - t[:, 0]) / 100.0)
+        acc["first_page_landed"] += list(((first - t[:, [0]]) / 100.0)[valid])
+        acc["page_loop"] += list(((lend - first) / 100.0)[valid])
+        for wg in range(t.shape[0]):
+            v = valid[wg]
+            if v.any():
+                acc["loop_end_spread_in_wg"].append((lend[wg][v].max() - lend[wg][v].min()) / 100.0)
+                acc["last_loop_end_to_stored"].append((t[wg, 2] - lend[wg][v].max()) / 100.0)
+        acc["stored"] += list(us(t[:, 2]))
+        tq3 = ((t[:, 3] >> 32) & 0xFF) == 1
+        acc["stored_tq3_items"] += list(us(t[tq3, 2]))
+        acc["stored_fp8_items"] += list(us(t[~tq3, 2]))
+    pct = lambda v: [round(float(x), 2) for x in np.percentile(np.array(v), [10, 50, 90, 100])] if v else None
+    return {"workgroups": items, "reps": reps, **{k: pct(v) for k, v in acc.items()}}
 
 
 def time_materialize(runner, reps=8):
@@ -700,6 +756,13 @@ def main():
     if a.copy_calibration:
         copy_calibration(a.copy_calibration, 5)
         return
+    if a.item_trace:
+        trace_lib = os.path.join(ROOT, "mixed_format_paged_amd", "libmkv_trace.so")
+        if not os.path.exists(trace_lib):
+            print("bench.py --item-trace needs the trace build: python -m mixed_format_paged_amd.build --item-trace",
+                  file=sys.stderr)
+            sys.exit(2)
+        os.environ["MKV_LIB_PATH"] = trace_lib           # read when the package is first imported
     import torch
     import workloads as W
     w = W.WORKLOADS[a.workload]
@@ -707,6 +770,18 @@ def main():
     print(f"[bench] building {w.name} cache on the GPU ...", file=sys.stderr, flush=True)
     r = Runner(w, st, kernel=a.kernel, fused_append=not a.separate_append)
     print(f"[bench] built in {r.build_s:.1f} s", file=sys.stderr, flush=True)
+    if a.item_trace:
+        for _ in range(3):
+            r.step()
+        torch.cuda.synchronize()
+        rep_ = item_trace(r, a.item_trace)
+        print("[bench] item trace of the partial-attention launch (us; p10, p50, p90, max over workgroups "
+              "or waves; entry, stored: from the launch's first entry; the others per workgroup or wave)",
+              file=sys.stderr, flush=True)
+        for k, v in rep_.items():
+            print(f"  {k:<26} {v}", flush=True)
+        print(json.dumps({"item_trace": rep_, "workload": w.name}), flush=True)
+        return
     if a.profile_steps:
         for _ in range(a.profile_steps):
             r.step()

@@ -375,6 +375,20 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool,
  * XOR of every unit's first word. */
 int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
 
+/* Item trace (measurement support): in a library built with
+ * -DMKV_ITEM_TRACE=1 (`python -m mixed_format_paged_amd.build --item-trace`,
+ * libmkv_trace.so), the attention kernels record for each workgroup w
+ * (w < 4096) 32 words from word 32 w: the 100 MHz constant clock at entry
+ * (word 0), once the query fragments of its item are built (1), once the
+ * item's partial state is stored (2); the item as pages | tq3 << 32 |
+ * KV head << 40 | request << 48 (3); for wave v < 12, the clock when its first
+ * page has landed (4 + v) and when it leaves its page loop (16 + v).  A
+ * workgroup that runs several items keeps its last one.  Copies the first
+ * min(words, 4096 * 32) words to host memory `host` (synchronous, after the
+ * device's pending work).  MKV_ERR_RANGE from a library built without the
+ * trace (the product build records nothing). */
+int mkv_debug_item_trace(uint64_t* host, size_t words);
+
 /* Materialise: dequantise logical pages [page_lo, page_lo + n_pages) of
  * request b to dense bfloat16 K and V.  The pages' quality profile runs on
  * materialised pages while their decode path reads the mixed pages in place

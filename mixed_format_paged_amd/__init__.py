@@ -16,7 +16,7 @@ __all__ = [
     "mkv_debug_gather", "mkv_stream_read", "mkv_workspace_status", "mkv_demote_pages_layers", "mkv_decode_plan",
     "mkv_attend_fp8", "mkv_attend_tq3", "mkv_attend_partials", "mkv_merge", "mkv_attend", "mkv_append_attend", "mkv_materialize", "mkv_lifecycle_workspace_bytes", "mkv_lifecycle_step",
     "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
-    "mkv_last_error", "mkv_set_partial_kind", "set_partial_kind",
+    "mkv_last_error", "mkv_set_partial_kind", "set_partial_kind", "mkv_debug_item_trace",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
     "MKV_DEV_BAD_PAGE_ID", "MKV_DEV_BAD_TIER", "MKV_DEV_BAD_SEQ_LEN", "MKV_DEV_NO_FREE_PAGE",
 ]
@@ -97,6 +97,7 @@ def lib():
         "mkv_status_string": (ctypes.c_char_p, [c_i32]),
         "mkv_last_error": (ctypes.c_char_p, []),
         "mkv_set_partial_kind": (c_i32, [c_i32]),
+        "mkv_debug_item_trace": (c_i32, [c_vp, c_sz]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -290,6 +291,15 @@ def mkv_debug_gather(layout, pool, bt_offsets, bt_pages, b, n_pages, out, stream
                                          _ptr(bt_offsets, torch.int32, "bt_offsets"),
                                          _ptr(bt_pages, torch.int32, "bt_pages"), int(b), int(n_pages),
                                          _ptr(out, torch.uint8, "out"), _stream(stream)))
+
+
+def mkv_debug_item_trace(host):
+    """Copy the item trace of an MKV_ITEM_TRACE=1 build into host, a
+    C-contiguous numpy uint64 array (up to 4096 x 32 words)."""
+    import numpy as np
+    if not isinstance(host, np.ndarray) or host.dtype != np.uint64 or not host.flags.c_contiguous:
+        raise MkvError(-101, "host must be a C-contiguous numpy uint64 array")
+    return _check(lib().mkv_debug_item_trace(host.ctypes.data, host.size))
 
 
 def mkv_stream_read(src, sink, nbytes=None, stream=None):

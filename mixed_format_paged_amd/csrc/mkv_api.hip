@@ -582,6 +582,14 @@ static int mkv_stream_read_impl(const void* src, size_t bytes, uint32_t* sink, s
   return e == hipSuccess ? MKV_OK : hip_fail(e, "stream-read launch");
 }
 
+static int mkv_debug_item_trace_impl(uint64_t* host, size_t words) {
+  if (!host) return fail(MKV_ERR_NULL, "host is required");
+  const int rc = read_item_trace(host, words);
+  if (rc == -1) return fail(MKV_ERR_RANGE, "this library is not an item-trace build (MKV_ITEM_TRACE=1)");
+  if (rc != 0) return fail(MKV_ERR_HIP, "item-trace copy failed");
+  return MKV_OK;
+}
+
 static int mkv_materialize_impl(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,
                     int32_t page_lo, int32_t n_pages, uint16_t* k_out, uint16_t* v_out, void* stream) {
   Geometry g{};
@@ -774,6 +782,10 @@ int mkv_debug_gather(const mkv_layout* layout, const mkv_pool* pool, const int32
 
 int mkv_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
   return debug_finish(mkv_stream_read_impl(src, bytes, sink, sink_words, stream), stream, nullptr, "mkv_stream_read");
+}
+
+int mkv_debug_item_trace(uint64_t* host, size_t words) {
+  return debug_finish(mkv_debug_item_trace_impl(host, words), nullptr, nullptr, "mkv_debug_item_trace");
 }
 
 int mkv_materialize(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch, int32_t b,

@@ -214,6 +214,13 @@ hipError_t launch_materialize(const Geometry& g, const uint8_t* fp8_slab, const 
                               const int32_t* bt_pages, int bt_capacity, int b, int page_lo,
                               int n_pages, uint16_t* k_out, uint16_t* v_out, const int8_t* signs,
                               hipStream_t stream);
+// Item trace of the attention kernels (built with MKV_ITEM_TRACE=1 only):
+// kTraceBlocks workgroups x kTraceSlots 64-bit words.  read_item_trace copies
+// up to `words` of them to host memory: 0 on success, -1 when the library is
+// not a trace build, -2 when the copy fails.
+constexpr int kTraceBlocks = 4096, kTraceSlots = 32;
+int read_item_trace(uint64_t* host, size_t words);
+
 hipError_t launch_plan(const Geometry& g, const uint8_t* tier, const int32_t* bt_offsets,
                        const int32_t* bt_pages, const int32_t* seq_lens, const Plan& plan,
                        hipStream_t stream);

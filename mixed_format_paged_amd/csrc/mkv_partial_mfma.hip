@@ -53,6 +53,28 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kItemWaves;
 constexpr int kThreads = 64 * kWaves;
+
+// Item trace (measurement support): a build with -DMKV_ITEM_TRACE=1, made
+// into its own library, records per workgroup the constant 100 MHz clock
+// (s_memrealtime) at points of its work item: slot 0 at entry, 1 once the
+// query fragments are built, 2 once the partial state is stored, 3 the item
+// (pages | tq3 << 32 | KV head << 40 | request << 48), 4 + w when wave w's
+// first page has landed, 16 + w when wave w leaves its page loop (the last
+// item of a workgroup that runs several).  mkv_debug_item_trace reads it back.
+// The product build compiles none of it.
+#ifndef MKV_ITEM_TRACE
+#define MKV_ITEM_TRACE 0
+#endif
+constexpr bool kItemTrace = MKV_ITEM_TRACE != 0;
+__device__ uint64_t g_item_trace[kItemTrace ? kTraceBlocks * kTraceSlots : 1];
+// every lane of the calling wave stores the same word (wave-uniform callers)
+__device__ inline void trace_mark(int slot, uint64_t value) {
+  if constexpr (kItemTrace) g_item_trace[(blockIdx.x % kTraceBlocks) * kTraceSlots + slot] = value;
+}
+__device__ inline void trace_time(int slot) {
+  if constexpr (kItemTrace) trace_mark(slot, __builtin_amdgcn_s_memrealtime());
+}
+__device__ inline bool wave0() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0; }
 // The running max moves only when a page's max exceeds it by more than
 // kRescale (log2 units), so p <= 2^15 stays finite in fp16.
 constexpr float kRescale = 15.0f;
@@ -837,6 +859,7 @@ __device__ __forceinline__ void run_item(
     }
   }
   __syncthreads();
+  if (kItemTrace && wave0()) trace_time(1);
 
   // TQ3: B operand of the offset MFMA.  Lane (n, j), k = 4 j + e: minus four
   // times column n's sum over group (4 j + e) % NG, fp16 hi for k < NG, the
@@ -889,6 +912,7 @@ __device__ __forceinline__ void run_item(
         wait_vmem<0>();                       // the last page has landed
       }
       s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
+      if (kItemTrace && k == 0) trace_time(4 + wave);
       __builtin_amdgcn_sched_barrier(0);
       const int e = chunk_page(k);            // page of the chunk
       const int ntok = (e == count - 1) ? last_tok : kPage;
@@ -920,6 +944,7 @@ __device__ __forceinline__ void run_item(
     for (int k = 0; k < my_pages; ++k) {
       progress_prio(s_left, wave, my_pages - k);
       wait_vmem<kRows>();                     // K of page k has landed
+      if (kItemTrace && k == 0) trace_time(4 + wave);
       __builtin_amdgcn_sched_barrier(0);
       const int e = chunk_page(k);
       const int ntok = (e == count - 1) ? last_tok : kPage;
@@ -941,6 +966,7 @@ __device__ __forceinline__ void run_item(
     }
   }
   __builtin_amdgcn_s_setprio(0);
+  if (kItemTrace) trace_time(16 + wave);
   wait_vmem<0>();                               // no staging load may land after this point
   const float vscale = vup;
   // this block's rows from r0 (part_acc_index / part_ml_index layout)
@@ -1122,6 +1148,10 @@ __device__ __forceinline__ void run_item(
     }
   }
   }
+  if (kItemTrace && wave0()) {
+    trace_time(2);
+    trace_mark(3, (uint64_t)count | ((uint64_t)tq3 << 32) | ((uint64_t)h << 40) | ((uint64_t)b << 48));
+  }
 }
 
 
@@ -1146,6 +1176,7 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ __align__(16) uint8_t smem[RB == 16 ? (ROT ? kSmemRot16<D> : kSmemBytes16<D>) : kSmemBytes<D>];
 
   static_assert(kWaves == kItemWaves, "a chunk-table entry holds the first page of every wave");
+  if (kItemTrace && wave0()) trace_time(0);
   const int nblk = MQ ? plan.nblk : 1;
   // Items: the TQ3 ones first, then the FP8 ones; within a format item
   // ((chunk L + layer) Hkv + h) nblk + blk, so an item's chunk does not depend
@@ -1354,6 +1385,14 @@ hipError_t launch_partial_mfma(int which, const Geometry& g, const LayerTable& l
   else
     launch_attend_t<kBoth, false, 8>(g, lt, n_layers, q, q_layer_stride, qscale, plan, ap, stream);
   return hipGetLastError();
+}
+
+int read_item_trace(uint64_t* host, size_t words) {
+  if (!kItemTrace) return -1;
+  const size_t n = words < (size_t)kTraceBlocks * kTraceSlots ? words : (size_t)kTraceBlocks * kTraceSlots;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_item_trace), n * sizeof(uint64_t), 0, hipMemcpyDeviceToHost) == hipSuccess
+             ? 0
+             : -2;
 }
 
 }  // namespace mkv

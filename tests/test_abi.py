@@ -85,6 +85,16 @@ def test_host_validation_codes():
     assert _call_decode((24, 4, 256), pool, empty) == 0
 
 
+@pytest.mark.skipif("trace" in os.path.basename(M.LIB_PATH), reason="the item-trace build records a trace")
+def test_item_trace_needs_the_trace_build():
+    # the product build records no item trace: a range error, before any HIP call
+    L = M.lib()
+    buf = (ctypes.c_uint64 * 64)()
+    assert L.mkv_debug_item_trace(buf, 64) == -5
+    assert b"item-trace" in L.mkv_last_error()
+    assert L.mkv_debug_item_trace(None, 64) == -1
+
+
 def test_workspace_is_bounded_not_cache_sized():
     # The workspace holds the plan (8 bytes of page lists per block-table
     # entry) and the split-K partial states, whose count is capped by a
