@@ -823,6 +823,10 @@ def main():
         "ms_per_step_p10": round(r.step_p10, 5), "ms_per_step_p90": round(r.step_p90, 5),
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        # the same with the attention launches' measured HBM bytes (FETCH_SIZE + WRITE_SIZE per launch from
+        # the committed counter summary, times the layers) in place of the algorithmic KV bytes
+        "pct_hbm_peak_measured_bytes": (round(100 * traffic * w.L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+                                        if traffic else None),
         "device_status": status,
         "roofline": {"bound": "hbm", "kernel": "attend_kernel: FP8 + TQ3 partial attention, one layer",
                      "achieved": round(layer_bytes / (k_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
