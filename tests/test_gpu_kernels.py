@@ -170,6 +170,11 @@ SMALL = [
                                     lengths=("list", (257, 1200)), recent_tokens=32)),
     ("heads-3q-1kv", W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=2, Hq=3, Hkv=1,
                               lengths=("list", (64, 800)), recent_tokens=32)),
+    # more than 1,024 requests, many of them empty or a part of one page: the
+    # plan keeps its per-request offsets in global memory (past its LDS rows)
+    # and the attention workgroups each take several work items
+    ("batch-1100-short", W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=1100,
+                                  lengths=("list", tuple((37 * i) % 120 for i in range(1100))), recent_tokens=32)),
 ]
 
 
