@@ -439,6 +439,34 @@ def test_lifecycle_steps_match_the_oracle(rotated):
     same("after the failing step")
 
 
+def test_multi_query_decode_parity_past_the_plan_lds_rows():
+    """Multi-query decode with 1,100 requests of 0 to 119 tokens (several
+    shorter than T): the causal-mask rows the items read from the plan
+    (previous page's format and index, last page's tokens) come from its
+    per-request rows in global memory."""
+    M.set_partial_kind(1)
+    T = 3
+    w = W.scaled(W.WORKLOADS["tiny-1x1024-d128"], B=1100, L=1,
+                 lengths=("list", tuple((37 * i) % 120 for i in range(1100))), recent_tokens=16)
+    st, dw, ref = _both(w)
+    layout = (w.Hq, w.Hkv, w.d)
+    B = w.B
+    g = torch.Generator()
+    g.manual_seed(7)
+    q = torch.randn((1, B, T, w.Hq, w.d), generator=g)
+    wsb = M.mkv_decode_workspace_bytes_multi(layout, B, dw.bt.numel(), 1, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((1, B, T, w.Hq, w.d), float("nan"), device="cuda")
+    lse = torch.full((1, B, T, w.Hq), float("nan"), device="cuda")
+    M.mkv_decode_attn_multi(layout, dw.cache.pools, dw.batch(), q.to("cuda").contiguous(), 1 / math.sqrt(w.d), out, lse,
+                            ws)
+    assert M.mkv_workspace_status(ws) == 0
+    pool, bt, _, _ = ref[0]
+    o_ref, l_ref = OA.decode_batch_multi(pool, q[0].numpy(), st.bt_offsets, bt, st.seq_lens)
+    compare(out.cpu().numpy()[0].reshape(-1, w.d), o_ref.reshape(-1, w.d), lse.cpu().numpy()[0].reshape(-1),
+            l_ref.reshape(-1), "T=3, 1,100 requests")
+
+
 @pytest.mark.parametrize("T,d,recent,hq,hkv", [(2, 256, 64, 24, 4), (5, 256, 16, 24, 4), (16, 128, 16, 24, 4),
                                                (3, 128, 64, 24, 4), (4, 256, 16, 4, 2), (2, 128, 16, 16, 2),
                                                (3, 256, 64, 8, 8)])
