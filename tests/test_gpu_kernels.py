@@ -467,6 +467,52 @@ def test_multi_query_decode_parity_past_the_plan_lds_rows():
             l_ref.reshape(-1), "T=3, 1,100 requests")
 
 
+def test_lifecycle_past_one_planning_block():
+    """mkv_lifecycle_step with 1,100 requests (more than the 1,024 threads of
+    its planning workgroup, so every pass runs over two blocks of requests):
+    40 steps with appends, a recent window of one page, so that 2,200 pages
+    age into TQ3; tables, free stacks and every slab byte agree with the
+    oracle bit for bit."""
+    from oracle import lifecycle as LC
+    hq, hkv, d, R, B, cap = 2, 1, 128, 1, 1100, 4
+    n_fp8, n_tq3 = 3 * B, 3 * B
+    layout = (hq, hkv, d)
+    rng = np.random.default_rng(11)
+    tier = np.full(n_fp8 + n_tq3, OP.TIER_FREE, dtype=np.uint8)
+    pool = OP.Pool(hkv, d, n_fp8, n_tq3, tier=tier)
+    t = LC.Tables(np.arange(B + 1) * cap, np.full(B * cap, -1), np.zeros(B, dtype=np.int64), tier,
+                  rng.permutation(n_fp8), n_fp8 + rng.permutation(n_tq3), [n_fp8, n_tq3])
+    i32 = lambda x: torch.as_tensor(np.asarray(x), dtype=torch.int32, device="cuda").contiguous()
+    fp8_d, tq3_d = torch.from_numpy(pool.fp8).to("cuda"), torch.from_numpy(pool.tq3).to("cuda")
+    tier_d = torch.from_numpy(tier).to("cuda")
+    pd = M.make_pool(fp8_d, tq3_d, tier_d, n_fp8, n_tq3)
+    offs_d, bt_d, sl_d = i32(t.bt_offsets), i32(t.bt_pages), i32(t.seq_lens)
+    ff_d, tf_d, tops_d = i32(t.fp8_free), i32(t.tq3_free), i32(t.tops)
+    ws = torch.zeros(M.mkv_lifecycle_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    T = 40
+    k = rng.standard_normal((B, T, 1, hkv, d)).astype(np.float32) * 3
+    v = rng.standard_normal((B, T, 1, hkv, d)).astype(np.float32) * 3
+    for step in range(T):
+        assert LC.step([pool], t, R) == 0
+        M.mkv_lifecycle_step(layout, [pd], offs_d, bt_d, sl_d, tier_d, ff_d, tf_d, tops_d, R, ws)
+        assert M.mkv_workspace_status(ws) == 0, step
+        kk, vv = k[:, step], v[:, step]
+        OP.append(pool, kk, vv, t.bt_offsets, t.bt_pages, t.seq_lens - 1)
+        M.mkv_append(layout, pd, torch.from_numpy(kk.copy()).to("cuda"), torch.from_numpy(vv.copy()).to("cuda"),
+                     offs_d, bt_d, sl_d - 1)
+        if step in (20, T - 1):
+            torch.cuda.synchronize()
+            assert np.array_equal(bt_d.cpu().numpy(), t.bt_pages), step
+            assert np.array_equal(sl_d.cpu().numpy(), t.seq_lens), step
+            assert np.array_equal(tier_d.cpu().numpy(), tier), step
+            assert list(tops_d.cpu().numpy()) == list(t.tops), step
+            assert np.array_equal(ff_d.cpu().numpy()[:t.tops[0]], t.fp8_free[:t.tops[0]]), step
+            assert np.array_equal(tf_d.cpu().numpy()[:t.tops[1]], t.tq3_free[:t.tops[1]]), step
+            assert np.array_equal(fp8_d.cpu().numpy(), pool.fp8), step
+            assert np.array_equal(tq3_d.cpu().numpy(), pool.tq3), step
+    assert int((tier == OP.TIER_S).sum()) == 2 * B
+
+
 @pytest.mark.parametrize("T,d,recent,hq,hkv", [(2, 256, 64, 24, 4), (5, 256, 16, 24, 4), (16, 128, 16, 24, 4),
                                                (3, 128, 64, 24, 4), (4, 256, 16, 4, 2), (2, 128, 16, 16, 2),
                                                (3, 256, 64, 8, 8)])
