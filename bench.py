@@ -159,6 +159,7 @@ class Runner:
         torch.cuda.synchronize()
         per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
         self.step_p10 = per[int(0.1 * (steps - 1))]
+        self.step_median = per[(steps - 1) // 2]
         self.step_p90 = per[int(0.9 * (steps - 1))]
         return evs[0].elapsed_time(evs[-1]) / steps
 
@@ -820,7 +821,8 @@ def main():
                    "append": "separate launch" if a.separate_append else "inside the attend launch"},
         "tokens_per_s": round(w.B / (ms * 1e-3), 2),
         "kv_token_layers_per_s": round(int(st.seq_lens.sum()) * w.L / (ms * 1e-3), 1),
-        "ms_per_step_p10": round(r.step_p10, 5), "ms_per_step_p90": round(r.step_p90, 5),
+        "ms_per_step_p10": round(r.step_p10, 5), "ms_per_step_median": round(r.step_median, 5),
+        "ms_per_step_p90": round(r.step_p90, 5),
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         # the same with the attention launches' measured HBM bytes (FETCH_SIZE + WRITE_SIZE per launch from
