@@ -605,6 +605,36 @@ def time_config(name, copies=1, passes=8, units=2):
     per = sorted(evs[i].elapsed_time(evs[i + 1]) / w.L for i in range(passes))
     ms = evs[0].elapsed_time(evs[-1]) / passes / w.L
     status = M.mkv_workspace_status(ws)
+    # the same passes with one plan for all copies (they share the tables), as
+    # a model with several layers runs them: plan once, then partials + merge
+    # per copy; per-layer time = pass time / copies
+    ms_shared = None
+    if w.L > 1:
+        def shared_pass():
+            M.mkv_decode_plan(lay, dw.cache.pools[0], bat, 1, ws)
+            for l in range(w.L):
+                if demote:
+                    dw.cache.demote(l, dw.d_src, dw.d_dst)
+                M.mkv_attend_partials(lay, [dw.cache.pools[l]], bat, q[l], sm, ws)
+                M.mkv_merge(lay, 1, bat, out[l], lse[l], ws)
+        with torch.cuda.stream(s):
+            shared_pass()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph2):
+            shared_pass()
+        graph2.replay()
+        torch.cuda.synchronize()
+        a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a2.record()
+        for _ in range(passes):
+            graph2.replay()
+        b2.record()
+        torch.cuda.synchronize()
+        ms_shared = a2.elapsed_time(b2) / passes / w.L
+        status |= M.mkv_workspace_status(ws)
+        del graph2
     # the demotion alone, same launch sizes
     dem = None
     if demote:
@@ -642,6 +672,10 @@ def time_config(name, copies=1, passes=8, units=2):
            "sampled_parity": {"units": len(picks), "max_abs": worst, "rel_l2": worst_rel,
                               "pass": bool(worst <= 2e-3 and worst_rel <= 1e-3)},
            "device_status": status, "build_s": round(build_s, 1)}
+    if ms_shared is not None:
+        res["plan_shared_by_copies"] = {"ms_per_layer": round(ms_shared, 5),
+                                        "kv_gbs": round(layer_bytes / (ms_shared * 1e-3) / 1e9, 2),
+                                        "note": "one plan per pass for all copies, as a model's layers share it"}
     if dem is not None:
         res["demote_then_decode"] = dict(dem, note="each pass demotes the aging pages, then decodes the layer")
     del dw, ws, out, lse, q, graph
