@@ -154,18 +154,41 @@ __global__ void __launch_bounds__(kClassifyThreads) plan_classify(
   }
 }
 
+// The per-request rows in LDS (batches up to kPlanLdsRows - 1 requests):
+// counts, error bits, tail, last page's format, block-table offset, then the
+// chunk and partial offsets the kernel computes.
+enum { L_NF, L_NT, L_INVAL, L_TAIL, L_LAST, L_BTO, L_CF, L_CT, L_PO, kLdsRowCount };
+
 __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ bt_offsets, Plan plan) {
   __shared__ uint64_t sh[128];
+  __shared__ int s_rows[kLdsRowCount][kPlanLdsRows];
   const int tid = threadIdx.x;
   const int B = plan.batch;
-  int* nf_row = req_row(plan, R_NF);
-  int* nt_row = req_row(plan, R_NT);
+  // One round of loads up front: the per-request rows plan_classify wrote;
+  // everything after reads them, and the offsets computed here, from LDS
+  // (with a batch past kPlanLdsRows - 1, from global memory as written).  The
+  // page lists stay in global memory: the tables read 12 ids per chunk.
+  const bool rows_lds = B + 1 <= kPlanLdsRows;            // uniform
+  if (rows_lds) {
+    for (int b = tid; b < B; b += 1024) {
+      s_rows[L_NF][b] = req_row(plan, R_NF)[b];
+      s_rows[L_NT][b] = req_row(plan, R_NT)[b];
+      s_rows[L_INVAL][b] = req_row(plan, R_INVALID)[b];
+      s_rows[L_TAIL][b] = req_row(plan, R_TAIL)[b];
+      s_rows[L_LAST][b] = req_row(plan, R_LASTFMT)[b];
+      s_rows[L_BTO][b] = bt_offsets[b];
+    }
+  }
+  __syncthreads();
+  const int* nf_row = rows_lds ? s_rows[L_NF] : req_row(plan, R_NF);
+  const int* nt_row = rows_lds ? s_rows[L_NT] : req_row(plan, R_NT);
+  const int* inval = rows_lds ? s_rows[L_INVAL] : req_row(plan, R_INVALID);
   // totals of pages per format, and the OR of every request's error bits
   int sf = 0, st = 0, serr = 0;
   for (int b = tid; b < B; b += 1024) {
     sf += nf_row[b];
     st += nt_row[b];
-    serr |= req_row(plan, R_INVALID)[b];
+    serr |= inval[b];
   }
   uint64_t tot2;
   block_exclusive_scan<1024>(pack2(sf, st), &tot2, sh);
@@ -202,21 +225,24 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
   int carry_f = 0, carry_t = 0, carry_p = 0;
   for (int base = 0; base < B; base += 1024) {
     const int b = base + tid;
-    int nfc = 0, ntc = 0, np = 0;
+    int nfc = 0, ntc = 0;
     if (b < B) {
       nfc = fp8_chunk_count(nf_row[b], ppt);
       ntc = (nt_row[b] + ppt - 1) / ppt;
-      np = nfc + ntc;
     }
     uint64_t t2;
     const uint64_t e2 = block_exclusive_scan<1024>(pack2(nfc, ntc), &t2, sh);
     const int ef = lo32(e2), et = hi32(e2), ep = ef + et;
     const int tf = lo32(t2), tt = hi32(t2), tp = tf + tt;
-    (void)np;
     if (b < B) {
       req_row(plan, R_CF_OFF)[b] = carry_f + ef;   // chunk offsets (exclusive) per format
       req_row(plan, R_CT_OFF)[b] = carry_t + et;
       req_row(plan, R_POFF)[b] = carry_p + ep;
+      if (rows_lds) {
+        s_rows[L_CF][b] = carry_f + ef;
+        s_rows[L_CT][b] = carry_t + et;
+        s_rows[L_PO][b] = carry_p + ep;
+      }
     }
     carry_f += tf; carry_t += tt; carry_p += tp;
   }
@@ -233,48 +259,25 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     plan.totals[T_NP] = carry_p;
     plan.totals[T_PPF] = ppt;
     plan.totals[T_PPT] = ppt;
+    if (rows_lds) {
+      s_rows[L_CF][B] = carry_f;
+      s_rows[L_CT][B] = carry_t;
+      s_rows[L_PO][B] = carry_p;
+    }
   }
   __syncthreads();
-  const int* cf = req_row(plan, R_CF_OFF);
-  const int* ct = req_row(plan, R_CT_OFF);
-  const int* po = req_row(plan, R_POFF);
-  const int* tail = req_row(plan, R_TAIL);
-  const int* lastfmt = req_row(plan, R_LASTFMT);
-  const int* nf_b = nf_row;
-  const int* nt_b = nt_row;
-  const int* bto = bt_offsets;
-  // With a batch that fits, the per-request rows the chunk tables read are
-  // copied to LDS in one round of loads (the owning request's binary search
-  // and its row reads then stay on chip).
-  __shared__ int s_rows[8][kPlanLdsRows];
-  if (B + 1 <= kPlanLdsRows) {                            // uniform
-    for (int i = tid; i <= B; i += 1024) {
-      s_rows[0][i] = cf[i];
-      s_rows[1][i] = ct[i];
-      s_rows[2][i] = po[i];
-      if (i < B) {
-        s_rows[3][i] = tail[i];
-        s_rows[4][i] = lastfmt[i];
-        s_rows[5][i] = nf_row[i];
-        s_rows[6][i] = nt_row[i];
-        s_rows[7][i] = bt_offsets[i];
-      }
-    }
-    __syncthreads();
-    cf = s_rows[0];
-    ct = s_rows[1];
-    po = s_rows[2];
-    tail = s_rows[3];
-    lastfmt = s_rows[4];
-    nf_b = s_rows[5];
-    nt_b = s_rows[6];
-    bto = s_rows[7];
-  }
+  const int* cf = rows_lds ? s_rows[L_CF] : req_row(plan, R_CF_OFF);
+  const int* ct = rows_lds ? s_rows[L_CT] : req_row(plan, R_CT_OFF);
+  const int* po = rows_lds ? s_rows[L_PO] : req_row(plan, R_POFF);
+  const int* tail = rows_lds ? s_rows[L_TAIL] : req_row(plan, R_TAIL);
+  const int* lastfmt = rows_lds ? s_rows[L_LAST] : req_row(plan, R_LASTFMT);
+  const int* bto = rows_lds ? s_rows[L_BTO] : bt_offsets;
   // chunk tables, one thread per chunk; the owning request by binary search
   for (int fmt = 0; fmt < 2; ++fmt) {
     const int* co = fmt ? ct : cf;
     const int total = co[B];
-    const int* cnt = fmt ? nt_b : nf_b;
+    const int* cnt = fmt ? nt_row : nf_row;
+    const int* lst = fmt ? plan.list_t : plan.list_f;
     int4* out = fmt ? plan.chunks_t : plan.chunks_f;
     for (int c = tid; c < total && c < plan.table_cap; c += 1024) {
       int lo = 0, hi = B - 1;                 // last b with co[b] <= c
@@ -293,7 +296,6 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
       const int last_tok = holds_tail ? tail[b] : 16;
       const int pidx = po[b] + (fmt ? (cf[b + 1] - cf[b]) : 0) + local;
       const int first = bto[b] + start;
-      const int* lst = fmt ? plan.list_t : plan.list_f;
       int4* const ent = out + (kChunkInts / 4) * c;
       ent[0] = make_int4(b, first, count | (last_tok << 16) | (holds_tail ? kChunkHoldsTail : 0), pidx);
       int fid[kItemWaves];
