@@ -825,7 +825,8 @@ def main():
         time_materialize(r, reps=2)
         time_demote_pack(r, reps=2)
         time_lifecycle(r, reps=3)
-        time_multi_query(r, reps=2)
+        if a.kernel == "mfma":
+            time_multi_query(r, reps=2)
         print(f"[bench] profile run: {a.profile_steps} eager steps done", file=sys.stderr, flush=True)
         return
     ms = r.time_steps(a.steps, a.warmup, graph=not a.no_graph)
@@ -837,8 +838,9 @@ def main():
     mat_ms, mat_read, mat_written = time_materialize(r)
     dem_ms, dem_bytes = time_demote_pack(r)
     lc_ms, lc_demoted = time_lifecycle(r)
-    mq_ms = time_multi_query(r, T=4)
-    rot = time_rotated(r)
+    # multi-query decode and rotated TQ3 run on the matrix-core kernels only
+    mq_ms = time_multi_query(r, T=4) if a.kernel == "mfma" else None
+    rot = time_rotated(r) if a.kernel == "mfma" else None
     traffic = recorded_traffic(w.name)
     status = r.M.mkv_workspace_status(r.ws)
     value = kv_bytes / (ms * 1e-3) / 1e9
@@ -884,10 +886,10 @@ def main():
         "lifecycle_step_page_boundary": {"avg_ms": round(lc_ms, 5), "layers": w.L,
                                          "pages_demoted_per_layer": lc_demoted},
         # each request's last 4 tokens as causal queries, one layer per call (plan + partials + merge)
-        "multi_query_4_tokens": {"avg_ms_per_layer": round(mq_ms, 5),
-                                 "query_tokens_per_s": round(w.B * 4 / (mq_ms * 1e-3), 1),
-                                 "kv_gbs_per_query_token": round(4 * layer_bytes / (mq_ms * 1e-3) / 1e9, 2),
-                                 "vs_single_query_launch": round(mq_ms / k_avg, 3)},
+        "multi_query_4_tokens": None if mq_ms is None else {
+            "avg_ms_per_layer": round(mq_ms, 5), "query_tokens_per_s": round(w.B * 4 / (mq_ms * 1e-3), 1),
+            "kv_gbs_per_query_token": round(4 * layer_bytes / (mq_ms * 1e-3) / 1e9, 2),
+            "vs_single_query_launch": round(mq_ms / k_avg, 3)},
         "rotated_tq3_one_layer": rot,
         "stream_ceiling": stream_ceiling(),
     }
