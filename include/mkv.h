@@ -29,6 +29,9 @@
  *    the request's block table) are recorded in the workspace status word
  *    (read it with mkv_workspace_status) and the affected requests' outputs
  *    are set to NaN.  NaN or Inf inputs are outside the contract.
+ *  - The library keeps no device state of its own that calls share (except
+ *    the array of mkv_decode_attn_noalloc): calls whose workspaces and outputs
+ *    are disjoint may run concurrently on different streams.
  */
 #ifndef MKV_H
 #define MKV_H

@@ -439,6 +439,47 @@ def test_lifecycle_steps_match_the_oracle(rotated):
     same("after the failing step")
 
 
+def test_decode_on_two_streams_with_their_own_workspaces(kind):
+    """Decode calls with disjoint workspaces and outputs, enqueued on two
+    streams and interleaved, give the same bytes as the same calls run one
+    after the other: the library keeps no device state of its own that such
+    calls could share."""
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=4, L=2, lengths=("list", (3000, 17, 1500, 2200)),
+                 recent_tokens=64)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    layout = (w.Hq, w.Hkv, w.d)
+    wsb = M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    out = [torch.full((w.B, w.Hq, w.d), float("nan"), device="cuda") for _ in range(2)]
+    lse = [torch.full((w.B, w.Hq), float("nan"), device="cuda") for _ in range(2)]
+    q = [dw.q[l].contiguous() for l in range(2)]
+    sm = 1 / math.sqrt(w.d)
+
+    def decode(l):
+        M.mkv_decode_attn(layout, dw.cache.pools[l], dw.batch(), q[l], sm, out[l], lse[l], ws[l])
+
+    decode(0)
+    decode(1)
+    torch.cuda.synchronize()
+    ref = [(out[l].cpu().numpy().copy(), lse[l].cpu().numpy().copy()) for l in range(2)]
+    assert M.mkv_workspace_status(ws[0]) == 0 and M.mkv_workspace_status(ws[1]) == 0
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for l in range(2):
+        streams[l].wait_stream(torch.cuda.current_stream())
+        out[l].fill_(float("nan"))
+        lse[l].fill_(float("nan"))
+    for _ in range(5):
+        for l in range(2):
+            with torch.cuda.stream(streams[l]):
+                decode(l)
+    torch.cuda.synchronize()
+    for l in range(2):
+        assert np.array_equal(out[l].cpu().numpy(), ref[l][0]), l
+        assert np.array_equal(lse[l].cpu().numpy(), ref[l][1]), l
+        assert M.mkv_workspace_status(ws[l]) == 0
+
+
 def test_multi_query_decode_parity_past_the_plan_lds_rows():
     """Multi-query decode with 1,100 requests of 0 to 119 tokens (several
     shorter than T): the causal-mask rows the items read from the plan
