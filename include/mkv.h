@@ -59,7 +59,8 @@ enum {
   MKV_DEV_BAD_PAGE_ID = 1,   /* block-table entry outside [0, n_fp8 + n_tq3)        */
   MKV_DEV_BAD_TIER = 2,      /* tier byte contradicts the slab the id points into   */
   MKV_DEV_BAD_SEQ_LEN = 4,   /* seq_len < 0 or longer than the request's block table */
-  MKV_DEV_NO_FREE_PAGE = 8   /* lifecycle: too few free ids, or a stack top outside its array */
+  MKV_DEV_NO_FREE_PAGE = 8,  /* lifecycle: too few free ids, or a stack top outside its array */
+  MKV_DEV_NO_PLAN = 16       /* attend / merge on a workspace that holds no plan for this batch */
 };
 
 /* Tier map values: one byte per physical page id.  Recent and Anchor pages
@@ -286,7 +287,13 @@ int mkv_decode_attn_layers(const mkv_layout* layout, const mkv_pool* pools,
  * mkv_merge: the log-sum-exp merge of those partial states into out / lse.
  * q, out, lse and pools as in mkv_decode_attn_layers.  The plan must come from
  * mkv_decode_plan with the same layout, batch descriptor and tier state;
- * between mkv_attend_* and mkv_merge the workspace must not be reused. */
+ * between mkv_attend_* and mkv_merge the workspace must not be reused.  The
+ * plan stamps the workspace with a word derived from the batch, the
+ * block-table capacity and the query tokens; a partial-attention or merge call
+ * that finds no matching stamp (no plan was made in this workspace, or one for
+ * another batch) reads no plan data: it sets MKV_DEV_NO_PLAN in the status and
+ * the merge writes NaN outputs.  A stale plan for the same batch shape is not
+ * detected. */
 int mkv_decode_plan(const mkv_layout* layout, const mkv_pool* pool, const mkv_batch* batch,
                     int32_t n_layers, void* ws, size_t ws_bytes, void* stream);
 int mkv_attend_fp8(const mkv_layout* layout, const mkv_pool* pools, int32_t n_layers,

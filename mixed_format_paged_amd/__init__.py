@@ -18,7 +18,7 @@ __all__ = [
     "mkv_lifecycle_release", "mkv_decode_workspace_bytes_multi", "mkv_decode_attn_multi", "mkv_status_string",
     "mkv_last_error", "mkv_set_partial_kind", "set_partial_kind", "mkv_debug_item_trace",
     "LIB_PATH", "TIER_RECENT", "TIER_ANCHOR", "TIER_STALE", "TIER_FREE",
-    "MKV_DEV_BAD_PAGE_ID", "MKV_DEV_BAD_TIER", "MKV_DEV_BAD_SEQ_LEN", "MKV_DEV_NO_FREE_PAGE",
+    "MKV_DEV_BAD_PAGE_ID", "MKV_DEV_BAD_TIER", "MKV_DEV_BAD_SEQ_LEN", "MKV_DEV_NO_FREE_PAGE", "MKV_DEV_NO_PLAN",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MKV_LIB_PATH") or os.path.join(_HERE, "libmkv.so")
 
 TIER_RECENT, TIER_ANCHOR, TIER_STALE, TIER_FREE = 0, 1, 2, 0xFF
-MKV_DEV_BAD_PAGE_ID, MKV_DEV_BAD_TIER, MKV_DEV_BAD_SEQ_LEN, MKV_DEV_NO_FREE_PAGE = 1, 2, 4, 8
+MKV_DEV_BAD_PAGE_ID, MKV_DEV_BAD_TIER, MKV_DEV_BAD_SEQ_LEN, MKV_DEV_NO_FREE_PAGE, MKV_DEV_NO_PLAN = 1, 2, 4, 8, 16
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 

@@ -46,7 +46,7 @@ __host__ __device__ inline int max_size_chunks(int bt_capacity) {
 }
 constexpr int kMaxG = 8;              // query rows of an 8-row block (attend wave states, merge row groups)
 constexpr int kMaxGroup = 16;         // query heads per KV head supported (more than 8: 16-row blocks)
-constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8;
+constexpr int kDevBadPageId = 1, kDevBadTier = 2, kDevBadSeqLen = 4, kDevNoFreePage = 8, kDevNoPlan = 16;
 
 // Per-request plan fields, each an int32[batch + 1] row of req[].
 enum ReqField {
@@ -69,6 +69,7 @@ enum TotalField {
   T_NP,          // partials per layer
   T_PPF,         // FP8 chunk size in TQ3 pages (each FP8 page weighs 4/3)
   T_PPT,         // pages per TQ3 chunk
+  T_STAMP,       // plan_stamp of the plan (written last by the planning kernel)
   T_FIELDS = 16
 };
 
@@ -116,6 +117,18 @@ struct Plan {
   int nblk;
   int rowblk;           // rows per block: 8, or 16 for multi-query with more than 8 rows
 };
+// The word a plan leaves in totals[T_STAMP], from the fields its consumers
+// must share with it (batch, block-table capacity, table capacity, query
+// tokens).  The kernels that read a plan check it first: a workspace that
+// holds no plan for this batch is refused (kDevNoPlan, NaN outputs), not read.
+__host__ __device__ inline int32_t plan_stamp(const Plan& p) {
+  uint32_t h = 0x6d6b7650u;
+  h = (h ^ (uint32_t)p.batch) * 0x9E3779B1u;
+  h = (h ^ (uint32_t)p.bt_capacity) * 0x85EBCA77u;
+  h = (h ^ (uint32_t)p.table_cap) * 0xC2B2AE3Du;
+  h = (h ^ (uint32_t)p.n_query) * 0x27D4EB2Fu;
+  return (int32_t)(h ^ (h >> 15));
+}
 // Partial-state layout: the states one merge workgroup reads (one layer, KV
 // head and 32-channel slice; a request's consecutive partials; all R rows)
 // form one contiguous run, R * 32 floats per partial.

@@ -66,6 +66,9 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
   const cptr lastfmt = (cptr)req_row(plan, R_LASTFMT);
   const int hq = hkv * Gh;
   const int tid = threadIdx.x;
+  // a workspace without this batch's plan is refused (NaN outputs), not read
+  const bool planned = plan.totals[T_STAMP] == plan_stamp(plan);
+  if (!planned && blockIdx.x == 0 && tid == 0) atomicOr(plan.status, kDevNoPlan);
   const int qc = tid % kQuads, pi = (tid / kQuads) % kMaxG, sub = tid / (kQuads * kMaxG);
   // 32-bit unsigned item arithmetic (far below 2^31 items per launch)
   const unsigned items = (unsigned)(n_layers * B * hkv * NRG * NS);
@@ -86,9 +89,9 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(int n_layers, int hkv, 
     const int r0 = rg * kMaxG;
     const int G = R - r0 < kMaxG ? R - r0 : kMaxG;          // rows of this group
     const bool live = pi < G;
-    const int p0 = poff[b], np = poff[b + 1] - p0;
-    const int bad_append = (appended && lastfmt[b] == 1) ? kDevBadTier : 0;
-    const int bad = inval[b] | bad_append;
+    const int p0 = planned ? poff[b] : 0, np = planned ? poff[b + 1] - p0 : 0;
+    const int bad_append = (planned && appended && lastfmt[b] == 1) ? kDevBadTier : 0;
+    const int bad = planned ? (inval[b] | bad_append) : kDevNoPlan;
     if (bad_append && layer == 0 && h == 0 && rg == 0 && cs == 0 && tid == 0) atomicOr(plan.status, bad_append);
     float* out_row = out + layer * out_ls + out_at(layer, b, h, r0 + (live ? pi : 0)) * D + cs * kSliceC;
     float* lse_l = lse ? lse + layer * lse_ls : nullptr;

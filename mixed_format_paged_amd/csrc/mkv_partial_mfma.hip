@@ -1189,6 +1189,11 @@ __global__ void __launch_bounds__(kThreads)
   const int spec = (int)(blockIdx.x / per_chunk);
   const i16v cd_spec = (MODE != kFp8Only && plan.table_cap > 0) ? tab_t[spec < plan.table_cap ? spec : plan.table_cap - 1]
                                                                  : i16v{};
+  // a workspace without this batch's plan is refused, not read
+  if (plan.totals[T_STAMP] != plan_stamp(plan)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(plan.status, kDevNoPlan);
+    return;
+  }
   const int ncf = MODE == kTq3Only ? 0 : plan.totals[T_NCF];
   const int nct = MODE == kFp8Only ? 0 : plan.totals[T_NCT];
   const unsigned items_t = per_chunk * nct;

@@ -39,6 +39,11 @@ __global__ void __launch_bounds__(256) partial_valu_kernel(
   __shared__ float alpha_s[kMaxGroup], m_s[kMaxGroup], l_s[kMaxGroup];
   constexpr int kPer = kMaxGroup * D / 256;
   const int tid = threadIdx.x;
+  // a workspace without this batch's plan is refused, not read
+  if (plan.totals[T_STAMP] != plan_stamp(plan)) {
+    if (blockIdx.x == 0 && tid == 0) atomicOr(plan.status, kDevNoPlan);
+    return;
+  }
   const int n_chunks = plan.totals[TQ3 ? T_NCT : T_NCF];
   const int4* chunks = TQ3 ? plan.chunks_t : plan.chunks_f;
   const int32_t* list = TQ3 ? plan.list_t : plan.list_f;

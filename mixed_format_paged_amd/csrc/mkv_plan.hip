@@ -259,6 +259,7 @@ __global__ void __launch_bounds__(1024) plan_chunks(const int32_t* __restrict__ 
     plan.totals[T_NP] = carry_p;
     plan.totals[T_PPF] = ppt;
     plan.totals[T_PPT] = ppt;
+    plan.totals[T_STAMP] = plan_stamp(plan);
     if (rows_lds) {
       s_rows[L_CF][B] = carry_f;
       s_rows[L_CT][B] = carry_t;

@@ -439,6 +439,35 @@ def test_lifecycle_steps_match_the_oracle(rotated):
     same("after the failing step")
 
 
+def test_attend_on_a_workspace_without_a_plan_is_refused(kind):
+    """The phase calls need a plan from mkv_decode_plan in their workspace.  On
+    a zeroed workspace (no plan stamp) the partial kernels read nothing, the
+    merge writes NaN and the status gets MKV_DEV_NO_PLAN; after a plan the
+    same call decodes normally."""
+    w = W.scaled(W.WORKLOADS["ragged-32x4096-65536"], B=3, L=1, lengths=("list", (900, 40, 1600)),
+                 recent_tokens=64)
+    st = W.make_structure(w)
+    dw = DeviceWorkload(w, st, "cuda")
+    layout, sm = (w.Hq, w.Hkv, w.d), 1 / math.sqrt(w.d)
+    ws = torch.zeros(M.mkv_decode_workspace_bytes(layout, w.B, dw.bt.numel(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((1, w.B, w.Hq, w.d), device="cuda")
+    lse = torch.zeros((1, w.B, w.Hq), device="cuda")
+    q = dw.q[:1].contiguous()
+    M.mkv_attend(layout, dw.cache.pools[:1], dw.batch(), q, sm, out, lse, ws)
+    status = M.mkv_workspace_status(ws)
+    assert status & M.MKV_DEV_NO_PLAN
+    assert np.all(np.isnan(out.cpu().numpy())) and np.all(np.isnan(lse.cpu().numpy()))
+    M.mkv_decode_plan(layout, dw.cache.pools[0], dw.batch(), 1, ws)
+    M.mkv_attend(layout, dw.cache.pools[:1], dw.batch(), q, sm, out, lse, ws)
+    assert M.mkv_workspace_status(ws) == 0
+    o_ref = torch.empty_like(out[0])
+    l_ref = torch.empty_like(lse[0])
+    ws2 = torch.empty_like(ws)
+    M.mkv_decode_attn(layout, dw.cache.pools[0], dw.batch(), q[0], sm, o_ref, l_ref, ws2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out[0].cpu().numpy(), o_ref.cpu().numpy())
+
+
 def test_decode_on_two_streams_with_their_own_workspaces(kind):
     """Decode calls with disjoint workspaces and outputs, enqueued on two
     streams and interleaved, give the same bytes as the same calls run one
