@@ -54,6 +54,8 @@ def parse():
                     help="only run a plain device copy of BYTES bytes 5 times (counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many eager steps (for rocprofv3), print nothing else")
+    ap.add_argument("--pack-only", type=int, default=0, metavar="REPS",
+                    help="only time the pack of 8,192 random pages (REPS launches back to back) and print it")
     ap.add_argument("--item-trace", type=int, default=0, metavar="REPS",
                     help="only trace REPS partial-attention launches with the item-trace build "
                          "(mixed_format_paged_amd/libmkv_trace.so) and print their per-workgroup timeline")
@@ -790,6 +792,20 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration, 5)
+        return
+    if a.pack_only:
+        import types
+        import torch
+        import workloads as W
+        import mixed_format_paged_amd as M
+        w = W.WORKLOADS[a.workload]
+        r = types.SimpleNamespace(torch=torch, M=M, layout=(w.Hq, w.Hkv, w.d))
+        time_demote_pack(r, reps=1)
+        ms, nbytes = time_demote_pack(r, reps=a.pack_only)
+        print(json.dumps({"demote_pack_8192_pages": {"avg_us": round(ms * 1e3, 2), "bytes": nbytes,
+                                                      "gbs": round(nbytes / ms / 1e6, 1),
+                                                      "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)},
+                          "workload": w.name}), flush=True)
         return
     if a.item_trace:
         trace_lib = os.path.join(ROOT, "mixed_format_paged_amd", "libmkv_trace.so")

@@ -39,6 +39,11 @@ __device__ inline float lane_xor(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, t, 0x141, 0xf, 0xf, false));
 }
 
+template <int GB>
+__device__ inline uint32_t lane_xor(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, lane_xor<GB>(__builtin_bit_cast(float, x)));
+}
+
 template <int D, bool ROT = false>
 __global__ void __launch_bounds__(256) demote_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
@@ -281,15 +286,97 @@ __device__ inline uint4 reread(uint4 q) {
   return q;
 }
 
+// ---- unscaled pages: codes from the FP8 bytes, four at a time -------------
+//
+// With the layer scale 1, x is decode(e) exactly, and |x| grows with the
+// byte's magnitude field e & 0x7f.  Each compare of the code rule is then a
+// compare of that field against a code-space threshold of the group:
+// C1 = [|x| > s/2], C2 = B = [|x| >= 3s/2] and C3 = [|x| > 5s/2] hold iff
+// the field exceeds T1, T2 and T3, the largest codes whose values are at
+// most s/2, below 3s/2 and at most 5s/2.  The byte sum field + (0x7f - T)
+// has bit 7 set iff the field exceeds T, and no byte carries into the next.
+// Since C3 => C2 => C1: D = C1 ^ C2 ^ C3 and N = sign & C1, so u0 = D,
+// u1 = C2 ^ (N & D) and u2 = !N, each as bit 7 of its byte.  (NaN codes are
+// outside the input contract; their field, 0x7f, exceeds every threshold.)
+
+// Largest E4M3 magnitude code whose value is at most t (t >= 0, inf
+// allowed): exponent and top three mantissa bits of t in the normal range,
+// floor(512 t) below 2^-6, 0x7e from 448 up.
+__device__ inline uint32_t e4m3_floor_code(float t) {
+  const uint32_t n = (__float_as_uint(t) >> 20) - 960u;
+  const uint32_t c = t < 0x1p-6f ? (uint32_t)(t * 512.0f) : n;
+  return c < 126u ? c : 126u;
+}
+
+// 0x7f - T1, 0x7f - T2, 0x7f - T3 of a group (T2 from the float just below
+// 3s/2: a code's value is below 3s/2 iff it is at most that float)
+struct Keys {
+  uint32_t k1, k2, k3;
+};
+
+__device__ inline Keys code_keys(const Thresholds& th) {
+  return {127u - e4m3_floor_code(th.t1), 127u - e4m3_floor_code(__uint_as_float(__float_as_uint(th.t2) - 1u)),
+          127u - e4m3_floor_code(th.t3)};
+}
+
+// Three-input bitwise functions as one v_bitop3 each: the truth table's bit
+// (a b c) (a the most significant) is the result for those input bits, so a
+// is 0xf0, b is 0xcc and c is 0xaa.
+template <uint32_t kTable>
+__device__ inline uint32_t bitop3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, kTable);
+}
+constexpr uint32_t kXor3 = (0xf0 ^ 0xcc ^ 0xaa) & 0xff;                     // a ^ b ^ c
+constexpr uint32_t kXorAnd = (0xf0 ^ (0xcc & 0xaa)) & 0xff;                 // a ^ (b & c)
+constexpr uint32_t kSelA = ((0xf0 & 0xaa) | (0xcc & ~0xaa)) & 0xff;         // c ? a : b, bit by bit
+constexpr uint32_t kSelNotA = ((~0xf0 & 0xaa) | (0xcc & ~0xaa)) & 0xff;     // c ? ~a : b
+constexpr uint32_t kSelBNotA = ((0xcc & 0xaa) | (~0xf0 & ~0xaa)) & 0xff;    // c ? b : ~a
+
+// Byte 0 of k in all four bytes (v_perm: selector 0 picks byte 0 of the
+// second operand)
+__device__ inline uint32_t bytes4(uint32_t k) { return __builtin_amdgcn_perm(0u, k, 0u); }
+
+// Bit 7 of each byte: u0, u1 and N of that byte's code (the other bits are
+// not used); k1..k3 hold each byte's keys
+struct Planes {
+  uint32_t u0, u1, n;
+};
+
+__device__ inline Planes code_planes(uint32_t x, uint32_t k1, uint32_t k2, uint32_t k3) {
+  const uint32_t a = x & 0x7f7f7f7fu;
+  const uint32_t s1 = a + k1, s2 = a + k2, s3 = a + k3;
+  const uint32_t d = bitop3<kXor3>(s1, s2, s3);
+  const uint32_t n = x & s1;
+  return {d, bitop3<kXorAnd>(s2, n, d), n};
+}
+
+// Bits 2..7 of byte i: the code of byte i of l (bits 2..4) and of h (5..7)
+__device__ inline uint32_t pair_fields(const Planes& l, const Planes& h) {
+  uint32_t f = bitop3<kSelNotA>(h.n, h.u1 >> 1, 0x80808080u);   // !N of h at bit 7, u1 at 6
+  f = bitop3<kSelA>(f, h.u0 >> 2, 0xc0c0c0c0u);                  // u0 of h at 5
+  f = bitop3<kSelBNotA>(l.n >> 3, f, 0xe0e0e0e0u);               // !N of l at 4
+  f = bitop3<kSelA>(f, l.u1 >> 4, 0xf0f0f0f0u);                  // u1 of l at 3
+  return bitop3<kSelA>(f, l.u0 >> 5, 0xf8f8f8f8u);               // u0 of l at 2
+}
+
+// The four 6-bit fields at bits 8 i + 2 .. 8 i + 7 -> bits 6 i .. 6 i + 5
+// (a triple word: slot 2 i the code of byte i of l, slot 2 i + 1 of h)
+__device__ inline uint32_t compact_fields(uint32_t f) {
+  const uint32_t y = bitop3<kSelA>(f >> 2, f >> 4, 0x003f003fu);
+  return bitop3<kSelA>(y, y >> 4, 0x00000fffu);
+}
+
 // Workgroup of 128 threads: wave 0 builds the K triples, wave 1 the V
 // triples, of PH (layer, page, KV head) items (8 G threads each per wave).
 // SCALED: some layer of the launch has a k_scale or v_scale other than 1
 // (every value is then multiplied by its layer's scale; by 1 it is exact).
 // A thread codes 64 FP8 bytes: K, token row t of groups g (gg = g mod 4 in
 // {0, 1}) and g + 2; V, tokens 4 j .. 4 j + 3 of channels 32 g + 16 hh .. + 15.
-// It keeps them as bytes and converts each value twice (once for the
-// group's maximum, once, 8 at a time, for its triple), which keeps the
-// registers few and the waves per SIMD many.
+// It keeps them as bytes, which keeps the registers few and the waves per
+// SIMD many: each value is converted once for the group's maximum; the
+// unscaled instance then codes the bytes four at a time in code space, the
+// scaled one converts each value again, 8 at a time, for the compares of
+// its triple.
 template <int D, bool SCALED>
 __global__ void __launch_bounds__(128) demote_plain_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
@@ -347,10 +434,26 @@ __global__ void __launch_bounds__(128) demote_plain_kernel(
     sc[ph][(tq3_scale_off(D, 0, t, g) - 12 * D) / 2] = sbl;
     sc[ph][(tq3_scale_off(D, 0, t, g + 2) - 12 * D) / 2] = sbh;
     const Thresholds thl = thresholds(half_bits_to_float(sbl)), thh = thresholds(half_bits_to_float(sbh));
-    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
     // channel 8 j + e of the pair sits in triple j G + 4 (g / 4) + 2 gg + e / 4
     // of the row, slot 2 (e % 4) (group g) or 2 (e % 4) + 1 (group g + 2);
     // channels 8 j + 4 e4 .. + 3 of a group are its dword 2 j + e4
+    if constexpr (!SCALED) {
+      const Keys kl = code_keys(thl), kh = code_keys(thh);
+      const uint32_t l1 = bytes4(kl.k1), l2 = bytes4(kl.k2), l3 = bytes4(kl.k3);
+      const uint32_t h1 = bytes4(kh.k1), h2 = bytes4(kh.k2), h3 = bytes4(kh.k3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const int k = 2 * j + e4;
+          const uint32_t wl = word_of(q[k >> 2], k & 3), wh = word_of(q[2 + (k >> 2)], k & 3);
+          w2[e4] = compact_fields(pair_fields(code_planes(wl, l1, l2, l3), code_planes(wh, h1, h2, h3)));
+        }
+        *reinterpret_cast<uint2*>(&tw[ph][t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (g & 3)]) = make_uint2(w2[0], w2[1]);
+      }
+    } else {
+    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t w2[2];
@@ -376,45 +479,80 @@ __global__ void __launch_bounds__(128) demote_plain_kernel(
       }
       *reinterpret_cast<uint2*>(&tw[ph][t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (g & 3)]) = make_uint2(w2[0], w2[1]);
     }
+    }
   } else if (valid) {
     const int j = r8 / (2 * G), g = (r8 >> 1) % G, hh = r8 & 1;
     const float scl = lt.v_scale[layer];
     uint4 q[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) q[r] = *reinterpret_cast<const uint4*>(in + (kPage + 4 * j + r) * D + 32 * g + 16 * hh);
-    Thresholds th[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = absmax_fp8x16(q[r]);
-      const float am = fmaxf(a, lane_xor<1>(a));      // the partner lane holds the other half
-      const uint16_t sb = tq3_scale_bits(SCALED ? __fmul_rn(am, scl) : am);
-      if (hh == 0) sc[ph][(tq3_scale_off(D, 1, 4 * j + r, g) - 12 * D) / 2] = sb;
-      th[r] = thresholds(half_bits_to_float(sb));
-    }
     // channel pair (a, a + 1), a = 32 g + 16 hh + 2 pc, is triple
     // (16 j + n) G + p of the V codes; the 8 pairs are consecutive triples;
     // slot 2 r + ci holds (channel a + ci, token 4 j + r)
     const int tb = 2 * D + (j * 16 + (32 * g + 16 * hh) / (D / 16)) * G;
-    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
     uint32_t w8[8];
+    if constexpr (!SCALED) {
+      // The two lanes of a group each hold half of the four tokens' rows:
+      // lane hh forms the scales and keys of tokens 2 hh and 2 hh + 1 from
+      // both halves' maxima, and the lanes swap keys.  Byte r of a key is
+      // token 4 j + r's.
+      float a[4];
 #pragma unroll
-    for (int pc = 0; pc < 8; ++pc) {
-      float2 xv[4];
+      for (int r = 0; r < 4; ++r) a[r] = absmax_fp8x16(q[r]);
+      const float am0 = fmaxf(hh ? a[2] : a[0], lane_xor<1>(hh ? a[0] : a[2]));
+      const float am1 = fmaxf(hh ? a[3] : a[1], lane_xor<1>(hh ? a[1] : a[3]));
+      const uint16_t sb0 = tq3_scale_bits(am0), sb1 = tq3_scale_bits(am1);
+      sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh, g) - 12 * D) / 2] = sb0;
+      sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh + 1, g) - 12 * D) / 2] = sb1;
+      const Keys c0 = code_keys(thresholds(half_bits_to_float(sb0))), c1 = code_keys(thresholds(half_bits_to_float(sb1)));
+      const int sh = 16 * hh;
+      uint32_t k1 = (c0.k1 | c1.k1 << 8) << sh, k2 = (c0.k2 | c1.k2 << 8) << sh, k3 = (c0.k3 | c1.k3 << 8) << sh;
+      k1 |= lane_xor<1>(k1);
+      k2 |= lane_xor<1>(k2);
+      k3 |= lane_xor<1>(k3);
+      // the bytes of dword kq of the four token rows, regrouped so that byte
+      // r is token r's: bytes 0 and 1 of each row make word 2 kq, bytes 2
+      // and 3 word 2 kq + 1
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        xv[r] = (pc & 1) ? fp8x2<true, SCALED>(word_of(c[r], pc >> 1), scl) : fp8x2<false, SCALED>(word_of(c[r], pc >> 1), scl);
-      uint32_t w = 0;
-#pragma unroll
-      for (int half = 1; half >= 0; --half) {
-        CodeMasks m[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int slot = 4 * half + 3 - i;
-          m[i] = code_masks((slot & 1) ? xv[slot >> 1].y : xv[slot >> 1].x, th[slot >> 1]);
-        }
-        w = push4(w, m);
+      for (int kq = 0; kq < 4; ++kq) {
+        const uint32_t x0 = word_of(q[0], kq), x1 = word_of(q[1], kq), x2 = word_of(q[2], kq), x3 = word_of(q[3], kq);
+        const uint32_t e01 = __builtin_amdgcn_perm(x1, x0, 0x05010400u), e23 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+        const uint32_t f01 = __builtin_amdgcn_perm(x1, x0, 0x07030602u), f23 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+        w8[2 * kq] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(e23, e01, 0x05040100u), k1, k2, k3),
+                                                code_planes(__builtin_amdgcn_perm(e23, e01, 0x07060302u), k1, k2, k3)));
+        w8[2 * kq + 1] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(f23, f01, 0x05040100u), k1, k2, k3),
+                                                    code_planes(__builtin_amdgcn_perm(f23, f01, 0x07060302u), k1, k2, k3)));
       }
-      w8[pc] = w ^ kFlipHigh;
+    } else {
+      Thresholds th[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = absmax_fp8x16(q[r]);
+        const float am = fmaxf(a, lane_xor<1>(a));      // the partner lane holds the other half
+        const uint16_t sb = tq3_scale_bits(__fmul_rn(am, scl));
+        if (hh == 0) sc[ph][(tq3_scale_off(D, 1, 4 * j + r, g) - 12 * D) / 2] = sb;
+        th[r] = thresholds(half_bits_to_float(sb));
+      }
+      const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc) {
+        float2 xv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          xv[r] = (pc & 1) ? fp8x2<true, SCALED>(word_of(c[r], pc >> 1), scl) : fp8x2<false, SCALED>(word_of(c[r], pc >> 1), scl);
+        uint32_t w = 0;
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {
+          CodeMasks m[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int slot = 4 * half + 3 - i;
+            m[i] = code_masks((slot & 1) ? xv[slot >> 1].y : xv[slot >> 1].x, th[slot >> 1]);
+          }
+          w = push4(w, m);
+        }
+        w8[pc] = w ^ kFlipHigh;
+      }
     }
     uint4* dstw = reinterpret_cast<uint4*>(&tw[ph][tb]);
     dstw[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);

@@ -84,6 +84,8 @@ def test_demote_bitexact_random_bytes(d):
     raw[1, :] = 0                                       # all-zero groups (s = 0)
     raw[2, :] &= 0x87                                   # tiny magnitudes only (subnormal e4m3, fp16 subnormal scales)
     raw[3, ::7] = 0x7E                                  # saturated maxima
+    raw[4, :] &= 0x9F                                   # magnitudes below 0.12: thresholds on both sides of 2^-6
+    raw[5, :] &= 0x8F                                   # magnitudes below 0.03
     for ks, vs in ((1.0, 1.0), (0.001, 37.0), (2.0 ** -20, 1500.0)):
         pool = OP.Pool(hkv, d, n, n, ks, vs)
         pool.fp8[:] = raw
