@@ -193,30 +193,18 @@ __global__ void __launch_bounds__(256) demote_kernel(
     reinterpret_cast<uint4*>(out + 12 * D)[e] = reinterpret_cast<const uint4*>(sc)[e];
 }
 
-// ---- plain pages: codes from lane masks -----------------------------------
+// ---- plain pages: the code rule -------------------------------------------
 //
-// The code of x against its group's scale s is decided by three compares,
-// each a lane mask of the wave, the second against a threshold the first
-// selects: B = [|x| >= 3s/2], D = [|x| > (B ? 5s/2 : s/2)] and N = [x < -s/2].
-// The magnitude m = [|x| > s/2] + [|x| >= 3s/2] + [|x| > 5s/2] is then 2 B + D,
-// and the code u = 4 + m (x >= 0) or 4 - m (x < 0; N is then m > 0) has
+// The code of x against its group's scale s: B = [|x| >= 3s/2],
+// D = [|x| > (B ? 5s/2 : s/2)] and N = [x < -s/2].  The magnitude
+// m = [|x| > s/2] + [|x| >= 3s/2] + [|x| > 5s/2] is 2 B + D, and the code
+// u = 4 + m (x >= 0) or 4 - m (x < 0; N is then m > 0) has
 //   u0 = D (4 + m and 4 - m are odd together),
 //   u1 = B ^ (N & D) (4 - m is 3 or 2 for m = 1, 2; 4 + m is 6 or 7 for m >= 2),
-//   u2 = !N,
-// so the scalar unit spends two ops on a code, and each bit goes into its
-// triple word with one carry-in add (w = 2 w + bit of this lane).  A thread
-// builds whole triples: a K thread takes one token row of the groups g and
-// g + 2 that share K triples, a V thread the four tokens of one token
-// quarter in half of a group (its partner lane holds the other half for the
-// group's maxima).
-
-// w <- 2 w + (this lane's bit of mask)
-__device__ inline uint32_t push_bit(uint32_t w, uint64_t mask) {
-  uint32_t r;
-  uint64_t carry_out;
-  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(mask));
-  return r;
-}
+//   u2 = !N.
+// A thread builds whole triples: a K thread takes one token row of the
+// groups g and g + 2 that share K triples, a V thread the four tokens of one
+// token quarter in half of a group (its partner lane holds the other half).
 
 struct Thresholds {
   float t1, t2, t3;   // s/2, 3s/2, 5s/2 (exact); +inf for s = 0
@@ -225,41 +213,6 @@ struct Thresholds {
 __device__ inline Thresholds thresholds(float s) {
   const float z = s == 0.0f ? INFINITY : s;
   return {0.5f * z, 1.5f * z, 2.5f * z};
-}
-
-constexpr uint32_t kFlipHigh = 0x924924u;   // bit 3k + 2 of each of the 8 slots
-
-// The masks of one code
-struct CodeMasks {
-  uint64_t B, D, N;
-};
-
-__device__ inline CodeMasks code_masks(float x, const Thresholds& th) {
-  const float ax = fabsf(x);
-  const bool b = ax >= th.t2;
-  return {__builtin_amdgcn_ballot_w64(b), __builtin_amdgcn_ballot_w64(ax > (b ? th.t3 : th.t1)),
-          __builtin_amdgcn_ballot_w64(x < -th.t1)};
-}
-
-// Push 4 codes (3 bits each, high bit first) from their masks.  The masks
-// of the 4 are formed before the first push, so the compares of the others
-// fill the wait between a compare and the select that reads its mask.
-__device__ inline uint32_t push4(uint32_t w, const CodeMasks (&m)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w = push_bit(w, m[i].N);                          // !u2, flipped by kFlipHigh
-    w = push_bit(w, m[i].B ^ (m[i].N & m[i].D));
-    w = push_bit(w, m[i].D);
-  }
-  return w;
-}
-
-// Two FP8 bytes (bytes 0, 1 or 2, 3 of w) -> fp32 (exact), times scl when
-// SCALED (the fp32 product the format defines x as; unscaled, x * 1 is x)
-template <bool HI, bool SCALED>
-__device__ inline float2 fp8x2(uint32_t w, float scl) {
-  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
-  return SCALED ? make_float2(__fmul_rn(v[0], scl), __fmul_rn(v[1], scl)) : make_float2(v[0], v[1]);
 }
 
 // Largest |decode| of 16 FP8 bytes.  With the layer scale: the largest
@@ -279,17 +232,10 @@ __device__ inline float absmax_fp8x16(const uint4 q) {
 
 __device__ inline uint32_t word_of(const uint4& q, int i) { return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w; }
 
-// The bytes again for the code pass: opaque to the compiler, so it converts
-// them anew instead of keeping the first pass's 64 values live
-__device__ inline uint4 reread(uint4 q) {
-  asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-  return q;
-}
-
-// ---- unscaled pages: codes from the FP8 bytes, four at a time -------------
+// ---- codes from the FP8 bytes, four at a time -------------------------------
 //
 // With the layer scale 1, x is decode(e) exactly, and |x| grows with the
-// byte's magnitude field e & 0x7f.  Each compare of the code rule is then a
+// byte's magnitude field e & 0x7f (with a scale too: see below).  Each compare of the code rule is then a
 // compare of that field against a code-space threshold of the group:
 // C1 = [|x| > s/2], C2 = B = [|x| >= 3s/2] and C3 = [|x| > 5s/2] hold iff
 // the field exceeds T1, T2 and T3, the largest codes whose values are at
@@ -317,6 +263,29 @@ struct Keys {
 __device__ inline Keys code_keys(const Thresholds& th) {
   return {127u - e4m3_floor_code(th.t1), 127u - e4m3_floor_code(__uint_as_float(__float_as_uint(th.t2) - 1u)),
           127u - e4m3_floor_code(th.t3)};
+}
+
+// With a layer scale, x = fl32(decode(e) scl) is still monotone in the
+// magnitude field, and T is the largest code c whose product fl32(value(c)
+// scl) is at most t (below t for T2).  The floor code of t / scl, from an
+// approximate reciprocal, is within one code of T: codes are at least 1/16
+// apart relatively, the quotient and the products near a nonzero threshold
+// (normal fp32 numbers) within 2^-22.  The exact products of that code and
+// the next decide (code 127 decodes to NaN, which is never at most t).
+template <bool STRICT>
+__device__ inline uint32_t scaled_floor_code(float t, float scl, float rscl) {
+  const uint32_t c = e4m3_floor_code(t * rscl);
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c | (c + 1u) << 8, 1.0f, false);
+  const float p0 = __fmul_rn(v[0], scl), p1 = __fmul_rn(v[1], scl);
+  const bool ok0 = STRICT ? p0 < t : p0 <= t, ok1 = STRICT ? p1 < t : p1 <= t;
+  return ok1 ? c + 1u : ok0 ? c : c - 1u;                 // c = 0 is always ok (t > 0)
+}
+
+template <bool SCALED>
+__device__ inline Keys group_keys(const Thresholds& th, float scl, float rscl) {
+  if constexpr (!SCALED) return code_keys(th);
+  return {127u - scaled_floor_code<false>(th.t1, scl, rscl), 127u - scaled_floor_code<true>(th.t2, scl, rscl),
+          127u - scaled_floor_code<false>(th.t3, scl, rscl)};
 }
 
 // Three-input bitwise functions as one v_bitop3 each: the truth table's bit
@@ -373,10 +342,8 @@ __device__ inline uint32_t compact_fields(uint32_t f) {
 // A thread codes 64 FP8 bytes: K, token row t of groups g (gg = g mod 4 in
 // {0, 1}) and g + 2; V, tokens 4 j .. 4 j + 3 of channels 32 g + 16 hh .. + 15.
 // It keeps them as bytes, which keeps the registers few and the waves per
-// SIMD many: each value is converted once for the group's maximum; the
-// unscaled instance then codes the bytes four at a time in code space, the
-// scaled one converts each value again, 8 at a time, for the compares of
-// its triple.
+// SIMD many: each value is converted once for the group's maximum, and the
+// codes come from the bytes, four at a time, in code space.
 template <int D, bool SCALED>
 __global__ void __launch_bounds__(128) demote_plain_kernel(
     LayerTable lt, int n, int n_fp8, int n_tq3, int hkv, const int32_t* __restrict__ src,
@@ -437,48 +404,20 @@ __global__ void __launch_bounds__(128) demote_plain_kernel(
     // channel 8 j + e of the pair sits in triple j G + 4 (g / 4) + 2 gg + e / 4
     // of the row, slot 2 (e % 4) (group g) or 2 (e % 4) + 1 (group g + 2);
     // channels 8 j + 4 e4 .. + 3 of a group are its dword 2 j + e4
-    if constexpr (!SCALED) {
-      const Keys kl = code_keys(thl), kh = code_keys(thh);
-      const uint32_t l1 = bytes4(kl.k1), l2 = bytes4(kl.k2), l3 = bytes4(kl.k3);
-      const uint32_t h1 = bytes4(kh.k1), h2 = bytes4(kh.k2), h3 = bytes4(kh.k3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t w2[2];
-#pragma unroll
-        for (int e4 = 0; e4 < 2; ++e4) {
-          const int k = 2 * j + e4;
-          const uint32_t wl = word_of(q[k >> 2], k & 3), wh = word_of(q[2 + (k >> 2)], k & 3);
-          w2[e4] = compact_fields(pair_fields(code_planes(wl, l1, l2, l3), code_planes(wh, h1, h2, h3)));
-        }
-        *reinterpret_cast<uint2*>(&tw[ph][t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (g & 3)]) = make_uint2(w2[0], w2[1]);
-      }
-    } else {
-    const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
+    const float rscl = __builtin_amdgcn_rcpf(scl);
+    const Keys kl = group_keys<SCALED>(thl, scl, rscl), kh = group_keys<SCALED>(thh, scl, rscl);
+    const uint32_t l1 = bytes4(kl.k1), l2 = bytes4(kl.k2), l3 = bytes4(kl.k3);
+    const uint32_t h1 = bytes4(kh.k1), h2 = bytes4(kh.k2), h3 = bytes4(kh.k3);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t w2[2];
 #pragma unroll
       for (int e4 = 0; e4 < 2; ++e4) {
         const int k = 2 * j + e4;
-        const uint32_t wl = word_of(c[k >> 2], k & 3), wh = word_of(c[2 + (k >> 2)], k & 3);
-        const float2 l01 = fp8x2<false, SCALED>(wl, scl), l23 = fp8x2<true, SCALED>(wl, scl);
-        const float2 h01 = fp8x2<false, SCALED>(wh, scl), h23 = fp8x2<true, SCALED>(wh, scl);
-        const float xl[4] = {l01.x, l01.y, l23.x, l23.y}, xh[4] = {h01.x, h01.y, h23.x, h23.y};
-        uint32_t w = 0;
-#pragma unroll
-        for (int half = 1; half >= 0; --half) {   // slots 7..4, then 3..0
-          CodeMasks m[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int slot = 4 * half + 3 - i;
-            m[i] = (slot & 1) ? code_masks(xh[slot >> 1], thh) : code_masks(xl[slot >> 1], thl);
-          }
-          w = push4(w, m);
-        }
-        w2[e4] = w ^ kFlipHigh;
+        const uint32_t wl = word_of(q[k >> 2], k & 3), wh = word_of(q[2 + (k >> 2)], k & 3);
+        w2[e4] = compact_fields(pair_fields(code_planes(wl, l1, l2, l3), code_planes(wh, h1, h2, h3)));
       }
       *reinterpret_cast<uint2*>(&tw[ph][t * (D / 8) + j * G + 4 * (g >> 2) + 2 * (g & 3)]) = make_uint2(w2[0], w2[1]);
-    }
     }
   } else if (valid) {
     const int j = r8 / (2 * G), g = (r8 >> 1) % G, hh = r8 & 1;
@@ -491,68 +430,39 @@ __global__ void __launch_bounds__(128) demote_plain_kernel(
     // slot 2 r + ci holds (channel a + ci, token 4 j + r)
     const int tb = 2 * D + (j * 16 + (32 * g + 16 * hh) / (D / 16)) * G;
     uint32_t w8[8];
-    if constexpr (!SCALED) {
-      // The two lanes of a group each hold half of the four tokens' rows:
-      // lane hh forms the scales and keys of tokens 2 hh and 2 hh + 1 from
-      // both halves' maxima, and the lanes swap keys.  Byte r of a key is
-      // token 4 j + r's.
-      float a[4];
+    // The two lanes of a group each hold half of the four tokens' rows:
+    // lane hh forms the scales and keys of tokens 2 hh and 2 hh + 1 from
+    // both halves' maxima, and the lanes swap keys.  Byte r of a key is
+    // token 4 j + r's.
+    float a[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = absmax_fp8x16(q[r]);
-      const float am0 = fmaxf(hh ? a[2] : a[0], lane_xor<1>(hh ? a[0] : a[2]));
-      const float am1 = fmaxf(hh ? a[3] : a[1], lane_xor<1>(hh ? a[1] : a[3]));
-      const uint16_t sb0 = tq3_scale_bits(am0), sb1 = tq3_scale_bits(am1);
-      sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh, g) - 12 * D) / 2] = sb0;
-      sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh + 1, g) - 12 * D) / 2] = sb1;
-      const Keys c0 = code_keys(thresholds(half_bits_to_float(sb0))), c1 = code_keys(thresholds(half_bits_to_float(sb1)));
-      const int sh = 16 * hh;
-      uint32_t k1 = (c0.k1 | c1.k1 << 8) << sh, k2 = (c0.k2 | c1.k2 << 8) << sh, k3 = (c0.k3 | c1.k3 << 8) << sh;
-      k1 |= lane_xor<1>(k1);
-      k2 |= lane_xor<1>(k2);
-      k3 |= lane_xor<1>(k3);
-      // the bytes of dword kq of the four token rows, regrouped so that byte
-      // r is token r's: bytes 0 and 1 of each row make word 2 kq, bytes 2
-      // and 3 word 2 kq + 1
+    for (int r = 0; r < 4; ++r) a[r] = absmax_fp8x16(q[r]);
+    const float am0 = fmaxf(hh ? a[2] : a[0], lane_xor<1>(hh ? a[0] : a[2]));
+    const float am1 = fmaxf(hh ? a[3] : a[1], lane_xor<1>(hh ? a[1] : a[3]));
+    const uint16_t sb0 = tq3_scale_bits(SCALED ? __fmul_rn(am0, scl) : am0);
+    const uint16_t sb1 = tq3_scale_bits(SCALED ? __fmul_rn(am1, scl) : am1);
+    sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh, g) - 12 * D) / 2] = sb0;
+    sc[ph][(tq3_scale_off(D, 1, 4 * j + 2 * hh + 1, g) - 12 * D) / 2] = sb1;
+    const float rscl = __builtin_amdgcn_rcpf(scl);
+    const Keys c0 = group_keys<SCALED>(thresholds(half_bits_to_float(sb0)), scl, rscl);
+    const Keys c1 = group_keys<SCALED>(thresholds(half_bits_to_float(sb1)), scl, rscl);
+    const int sh = 16 * hh;
+    uint32_t k1 = (c0.k1 | c1.k1 << 8) << sh, k2 = (c0.k2 | c1.k2 << 8) << sh, k3 = (c0.k3 | c1.k3 << 8) << sh;
+    k1 |= lane_xor<1>(k1);
+    k2 |= lane_xor<1>(k2);
+    k3 |= lane_xor<1>(k3);
+    // the bytes of dword kq of the four token rows, regrouped so that byte
+    // r is token r's: bytes 0 and 1 of each row make word 2 kq, bytes 2
+    // and 3 word 2 kq + 1
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const uint32_t x0 = word_of(q[0], kq), x1 = word_of(q[1], kq), x2 = word_of(q[2], kq), x3 = word_of(q[3], kq);
-        const uint32_t e01 = __builtin_amdgcn_perm(x1, x0, 0x05010400u), e23 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
-        const uint32_t f01 = __builtin_amdgcn_perm(x1, x0, 0x07030602u), f23 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-        w8[2 * kq] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(e23, e01, 0x05040100u), k1, k2, k3),
-                                                code_planes(__builtin_amdgcn_perm(e23, e01, 0x07060302u), k1, k2, k3)));
-        w8[2 * kq + 1] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(f23, f01, 0x05040100u), k1, k2, k3),
-                                                    code_planes(__builtin_amdgcn_perm(f23, f01, 0x07060302u), k1, k2, k3)));
-      }
-    } else {
-      Thresholds th[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = absmax_fp8x16(q[r]);
-        const float am = fmaxf(a, lane_xor<1>(a));      // the partner lane holds the other half
-        const uint16_t sb = tq3_scale_bits(__fmul_rn(am, scl));
-        if (hh == 0) sc[ph][(tq3_scale_off(D, 1, 4 * j + r, g) - 12 * D) / 2] = sb;
-        th[r] = thresholds(half_bits_to_float(sb));
-      }
-      const uint4 c[4] = {reread(q[0]), reread(q[1]), reread(q[2]), reread(q[3])};
-#pragma unroll
-      for (int pc = 0; pc < 8; ++pc) {
-        float2 xv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          xv[r] = (pc & 1) ? fp8x2<true, SCALED>(word_of(c[r], pc >> 1), scl) : fp8x2<false, SCALED>(word_of(c[r], pc >> 1), scl);
-        uint32_t w = 0;
-#pragma unroll
-        for (int half = 1; half >= 0; --half) {
-          CodeMasks m[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int slot = 4 * half + 3 - i;
-            m[i] = code_masks((slot & 1) ? xv[slot >> 1].y : xv[slot >> 1].x, th[slot >> 1]);
-          }
-          w = push4(w, m);
-        }
-        w8[pc] = w ^ kFlipHigh;
-      }
+    for (int kq = 0; kq < 4; ++kq) {
+      const uint32_t x0 = word_of(q[0], kq), x1 = word_of(q[1], kq), x2 = word_of(q[2], kq), x3 = word_of(q[3], kq);
+      const uint32_t e01 = __builtin_amdgcn_perm(x1, x0, 0x05010400u), e23 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+      const uint32_t f01 = __builtin_amdgcn_perm(x1, x0, 0x07030602u), f23 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+      w8[2 * kq] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(e23, e01, 0x05040100u), k1, k2, k3),
+                                              code_planes(__builtin_amdgcn_perm(e23, e01, 0x07060302u), k1, k2, k3)));
+      w8[2 * kq + 1] = compact_fields(pair_fields(code_planes(__builtin_amdgcn_perm(f23, f01, 0x05040100u), k1, k2, k3),
+                                                  code_planes(__builtin_amdgcn_perm(f23, f01, 0x07060302u), k1, k2, k3)));
     }
     uint4* dstw = reinterpret_cast<uint4*>(&tw[ph][tb]);
     dstw[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
