@@ -310,11 +310,11 @@ def time_multi_query(runner, T=4, reps=8):
     return sum(a.elapsed_time(b) for a, b in evs) / reps
 
 
-def time_demote_pack(runner, n_pages=8192, reps=10):
+def time_demote_pack(runner, n_pages=8192, reps=10, scales=(1.0, 1.0)):
     """The pack kernel at the 64 requests x 128 aging pages scale: n_pages FP8
     pages of random E4M3 bytes (no NaN codes) demoted into n_pages TQ3 slots,
-    one layer (mkv_demote_pages), timed with HIP events.  Returns (avg ms, bytes
-    read + written)."""
+    one layer (mkv_demote_pages) with layer scales (k_scale, v_scale), timed
+    with HIP events.  Returns (avg ms, bytes read + written)."""
     torch, M = runner.torch, runner.M
     lay = runner.layout
     fb, tb = M.mkv_fp8_page_bytes(lay), M.mkv_tq3_page_bytes(lay)
@@ -324,7 +324,7 @@ def time_demote_pack(runner, n_pages=8192, reps=10):
     fp8 += (fp8 >= 0x7F).to(torch.uint8)              # skip the NaN codes 0x7F and 0xFF
     tq3 = torch.empty((n_pages, tb), dtype=torch.uint8, device="cuda")
     tier = torch.full((2 * n_pages,), M.TIER_FREE, dtype=torch.uint8, device="cuda")
-    pool = M.make_pool(fp8, tq3, tier, n_pages, n_pages)
+    pool = M.make_pool(fp8, tq3, tier, n_pages, n_pages, k_scale=scales[0], v_scale=scales[1])
     src = torch.arange(n_pages, dtype=torch.int32, device="cuda")
     dst = src + n_pages
     M.mkv_demote_pages(lay, pool, src, dst)
@@ -853,6 +853,7 @@ def main():
     k_avg, k_med = kt["partials"]
     mat_ms, mat_read, mat_written = time_materialize(r)
     dem_ms, dem_bytes = time_demote_pack(r)
+    dem_s_ms, _ = time_demote_pack(r, scales=(0.37, 2.5))
     lc_ms, lc_demoted = time_lifecycle(r)
     # multi-query decode and rotated TQ3 run on the matrix-core kernels only
     mq_ms = time_multi_query(r, T=4) if a.kernel == "mfma" else None
@@ -898,6 +899,9 @@ def main():
         "demote_pack_8192_pages": {"avg_ms": round(dem_ms, 5), "bytes": dem_bytes,
                                    "gbs": round(dem_bytes / (dem_ms * 1e-3) / 1e9, 2),
                                    "frac_of_peak": round(dem_bytes / (dem_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        # the same pack with layer scales other than 1 (k_scale 0.37, v_scale 2.5)
+        "demote_pack_8192_pages_scaled": {"avg_ms": round(dem_s_ms, 5), "scales": [0.37, 2.5],
+                                          "frac_of_peak": round(dem_bytes / (dem_s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         # mkv_lifecycle_step at a page boundary: FP8 pops, aging into TQ3 in all layers, table updates
         "lifecycle_step_page_boundary": {"avg_ms": round(lc_ms, 5), "layers": w.L,
                                          "pages_demoted_per_layer": lc_demoted},
