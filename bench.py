@@ -787,7 +787,7 @@ def cpu_baseline(runner, units):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {a.gpus}",
               file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
