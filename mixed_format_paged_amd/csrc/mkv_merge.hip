@@ -7,7 +7,7 @@
 //   o = sum_p acc_p w_p / L,  lse = (M + log2 L) * ln 2.
 // One launch merges any number of partials per request.  A workgroup takes
 // (layer, request, KV head, group of up to 8 query rows, slice of 32
-// channels), 512 threads (a KV head has R = T G rows: T query tokens per
+// channels), 256 threads (a KV head has R = T G rows: T query tokens per
 // request times G heads; row r = t G + g goes to out[b][t][h G + g]):
 //   1. each (row, 4-channel column) of the slice is shared by kSubs threads,
 //      each taking every kSubs-th partial: its (m, l) pairs and states are
@@ -29,7 +29,7 @@ __device__ inline const int* req_row(const Plan& p, int field) { return p.req + 
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kSliceC = kStateSlice;             // channels per workgroup: one slice of the state layout
 constexpr int kQuads = kSliceC / 4;              // float4 columns of a slice
 constexpr int kSubs = kThreads / (kMaxG * kQuads);   // threads sharing one (head, float4 column)
